@@ -1,0 +1,52 @@
+"""Element decode for the oracle (test infrastructure; see oracle/__init__.py).
+
+bf16: the upper half of an IEEE fp32 word, so widening is exact.
+e4m3fn [OCP E4M3; the RFC's Proposed Change names this OCP format as distinct
+from MI300's e4m3fnuz]: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
+exponent 0 is subnormal (M/8 * 2^-6); exponent 15 with mantissa 7 is NaN and
+there are no infinities, so the largest finite magnitude is 448.
+"""
+import math
+
+import numpy as np
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """uint16 bf16 bit patterns -> float64 (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_value(code: int) -> float:
+    """Value of one e4m3fn byte, from the bit-field definition."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exp = (code >> 3) & 0xF
+    man = code & 0x7
+    if exp == 0xF and man == 0x7:
+        return math.nan
+    if exp == 0:
+        return sign * (man / 8.0) * 2.0 ** -6
+    return sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+
+
+_E4M3FN = np.array([e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3fn(codes) -> np.ndarray:
+    """uint8 e4m3fn codes -> float64 code values (no scale applied)."""
+    return _E4M3FN[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode_kv(raw, kv_dtype: str, scale=None) -> np.ndarray:
+    """Raw KV element codes -> dequantized float64 values.
+
+    bf16 codes decode exactly; fp8 codes decode to code value x per-tensor scale
+    (the scale is a plain multiplier applied in fp64).
+    """
+    if kv_dtype == "bf16":
+        return decode_bf16(raw)
+    if kv_dtype == "fp8":
+        v = decode_e4m3fn(raw)
+        return v if scale is None else v * float(scale)
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")

@@ -1,0 +1,97 @@
+"""Length-aware segment planner and the fixed split it replaces (test
+infrastructure; see oracle/__init__.py).
+
+[PR, Modifications]: one segment length T is chosen from the batch's sequence
+lengths — the smallest T for which the total segment count stays within
+num_CUs / kv_heads and no sequence needs more than seg_max segments — and a work
+list of (sequence << 16 | segment) words is written, padded with -1, together
+with a per-query-token segment count that the reduce reads. The kernel takes
+the tiles per segment from the first plan word.
+
+[PR, Motivation]: the fixed split gives every sequence
+max(1, min(64, pow2floor(256 / (bs * kv_heads)))) segments.
+
+Readings (pages silent; also in the design notes):
+  * T counts pages ("tiles" = 16-token pages), searched over all integers
+    1..max(max_pages, 1); feasibility is monotone in T, so the smallest is unique;
+  * no feasible T (more non-empty sequences than num_CUs // kv_heads): T is the
+    longest sequence's page count, i.e. one segment per non-empty sequence;
+  * num_CUs / kv_heads is floored; the work list has max(that, bs) entries;
+  * work list order: sequence-major, segments ascending;
+  * per-token count: the number of the sequence's segments that hold at least
+    one key the token may see, ceil(visible / (T * P)).
+"""
+from .attention import visible_keys
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def plan_segments(seq_lens, cu_seqlens_q, kv_heads, page_size, num_cus, seg_max,
+                  causal=1):
+    """Returns (plan, tok_nseg) as Python int lists.
+
+    plan[0] = T (pages per segment); plan[1 + k] = (i << 16) | s for the k-th
+    work item, -1 past the last; len(plan) = 1 + max(num_cus // kv_heads, bs).
+    tok_nseg[t] = segments of t's sequence holding keys t may see.
+    """
+    lens = [int(v) for v in seq_lens]
+    bs = len(lens)
+    # step 1: pages per sequence, the CU budget per kv head, the longest sequence
+    pages = [_ceil_div(L, page_size) for L in lens]
+    cap = num_cus // kv_heads
+    longest = max(pages) if pages else 0
+
+    # step 2: feasibility of a candidate segment length
+    def feasible(T):
+        segs = [_ceil_div(n, T) for n in pages]
+        return sum(segs) <= cap and max(segs, default=0) <= seg_max
+
+    # step 3: smallest feasible T, scanning upward; fallback when none is
+    upper = max(longest, 1)
+    T = None
+    for cand in range(1, upper + 1):
+        if feasible(cand):
+            T = cand
+            break
+    if T is None:
+        T = upper
+
+    # step 4: segments per sequence and the sequence-major work list
+    nseg = [_ceil_div(n, T) for n in pages]
+    items = []
+    for i in range(bs):
+        for s in range(nseg[i]):
+            items.append((i << 16) | s)
+
+    # step 5: pad with -1 to the work-list capacity
+    width = max(cap, bs)
+    assert len(items) <= width
+    plan = [T] + items + [-1] * (width - len(items))
+
+    # step 6: per-query-token segment counts
+    tok_nseg = []
+    for i in range(bs):
+        qn = int(cu_seqlens_q[i + 1]) - int(cu_seqlens_q[i])
+        for j in range(qn):
+            vis = visible_keys(lens[i], qn, j, causal)
+            tok_nseg.append(_ceil_div(vis, T * page_size))
+    return plan, tok_nseg
+
+
+def pow2floor(v: int) -> int:
+    """Largest power of two <= v; 0 for v <= 0."""
+    v = int(v)
+    if v <= 0:
+        return 0
+    p = 1
+    while p * 2 <= v:
+        p *= 2
+    return p
+
+
+def fixed_split_segments(bs: int, kv_heads: int, num_cus: int = 256,
+                         seg_max: int = 64) -> int:
+    """Segments per sequence under the fixed split [PR, Motivation]."""
+    return max(1, min(seg_max, pow2floor(num_cus // (bs * kv_heads))))

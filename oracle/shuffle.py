@@ -1,0 +1,60 @@
+"""Standard <-> shuffled KV page repack (test infrastructure; see
+oracle/__init__.py).
+
+[RFC, Background and Proposed Change §4]: a standard block holds, per head,
+N token rows of 2D channels (K then V). The shuffled layout keeps K and V in
+separate planes with x = 16 // element_size elements grouped per 16 bytes:
+  K plane block [H, D/x, N, x]: element (c, n, i) is token n's K channel c*x + i;
+  V plane block [H, N/x, D, x]: element (g, d, i) is token g*x + i's V channel d.
+Written here as explicit destination <- source index maps; the inverse reads
+the same maps backwards. Pure data movement: bit-exact on element codes.
+"""
+import numpy as np
+
+
+def _maps(H, N, D, x):
+    """Source coordinates (h, n, ch) in the standard block for every element
+    of the K plane [H, D/x, N, x] and of the V plane [H, N/x, D, x]."""
+    h, c, n, i = np.meshgrid(np.arange(H), np.arange(D // x), np.arange(N),
+                             np.arange(x), indexing="ij")
+    k_src = (h, n, c * x + i)
+    h2, g, d, i2 = np.meshgrid(np.arange(H), np.arange(N // x), np.arange(D),
+                               np.arange(x), indexing="ij")
+    v_src = (h2, g * x + i2, D + d)
+    return k_src, v_src
+
+
+def shuffle_blocks(std, block_ids=None, elem_bytes=None):
+    """std [B, H, N, 2D] element codes -> (k_plane [B, H, D/x, N, x],
+    v_plane [B, H, N/x, D, x]) for the listed blocks (all when None).
+
+    Blocks not listed are left as zeros in the returned planes; callers compare
+    only the listed ones.
+    """
+    std = np.asarray(std)
+    B, H, N, D2 = std.shape
+    D = D2 // 2
+    e = std.dtype.itemsize if elem_bytes is None else elem_bytes
+    x = 16 // e
+    kp = np.zeros((B, H, D // x, N, x), dtype=std.dtype)
+    vp = np.zeros((B, H, N // x, D, x), dtype=std.dtype)
+    k_src, v_src = _maps(H, N, D, x)
+    ids = range(B) if block_ids is None else [int(b) for b in block_ids]
+    for b in ids:
+        kp[b] = std[b][k_src]
+        vp[b] = std[b][v_src]
+    return kp, vp
+
+
+def unshuffle_blocks(k_plane, v_plane, elem_bytes=None):
+    """Inverse of shuffle_blocks: planes -> standard [B, H, N, 2D]."""
+    k_plane = np.asarray(k_plane)
+    v_plane = np.asarray(v_plane)
+    B, H, Dx, N, x = k_plane.shape
+    D = Dx * x
+    std = np.zeros((B, H, N, 2 * D), dtype=k_plane.dtype)
+    k_src, v_src = _maps(H, N, D, x)
+    for b in range(B):
+        std[b][k_src] = k_plane[b]
+        std[b][v_src] = v_plane[b]
+    return std

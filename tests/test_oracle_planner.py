@@ -1,0 +1,140 @@
+"""Pins for the oracle's segment planner and fixed split (CPU only)."""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from conftest import load_golden
+from workloads import configs
+
+
+def _cu(q_lens):
+    return [0] + list(itertools.accumulate(q_lens))
+
+
+def _expand(case):
+    if "seq_lens" in case:
+        return case["seq_lens"], case["q_lens"]
+    v, n = case["seq_lens_repeat"]
+    qv, qn = case["q_lens_repeat"]
+    return [v] * n, [qv] * qn
+
+
+@pytest.mark.parametrize("case", load_golden("planner_hand_examples.json")["cases"],
+                         ids=lambda c: c["name"])
+def test_hand_derived_examples(case):
+    lens, ql = _expand(case)
+    plan, tok = oracle.plan_segments(lens, _cu(ql), case["kv_heads"], 16,
+                                     case["num_cus"], case["seg_max"], case["causal"])
+    assert plan[0] == case["T"]
+    assert len(plan) == 1 + case["width"]
+    items = [w for w in plan[1:] if w != -1]
+    if "items" in case:
+        assert items == case["items"]
+        assert tok == case["tok_nseg"]
+    else:
+        assert len(items) == case["n_items"]
+        assert set(tok) == {case["tok_nseg_all"]}
+    n = len(items)
+    assert all(w == -1 for w in plan[1 + n:])
+
+
+def _brute_force_T(pages, cap, seg_max):
+    """Every T tried, the per-sequence segments counted by walking pages."""
+    best = None
+    upper = max(max(pages, default=0), 1)
+    for T in range(upper, 0, -1):
+        counts = []
+        for n in pages:
+            c, covered = 0, 0
+            while covered < n:
+                covered += T
+                c += 1
+            counts.append(c)
+        if sum(counts) <= cap and max(counts, default=0) <= seg_max:
+            best = T
+    return best if best is not None else upper
+
+
+def test_brute_force_and_invariants_random():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        bs = int(rng.integers(1, 9))
+        lens = [int(v) for v in rng.integers(0, 400, size=bs)]
+        if trial % 7 == 0:
+            lens[0] = 0
+        ql = [int(v) for v in rng.integers(1, 5, size=bs)]
+        kvh = int(rng.choice([1, 2, 4, 8]))
+        ncu = int(rng.integers(1, 40))
+        smax = int(rng.integers(1, 9))
+        causal = int(rng.integers(0, 2))
+        plan, tok = oracle.plan_segments(lens, _cu(ql), kvh, 16, ncu, smax, causal)
+        pages = [-(-L // 16) for L in lens]
+        cap = ncu // kvh
+        T = plan[0]
+        assert T == _brute_force_T(pages, cap, smax)
+        width = max(cap, bs)
+        assert len(plan) == 1 + width
+        items = [w for w in plan[1:] if w != -1]
+        k = len(items)
+        assert all(w == -1 for w in plan[1 + k:])            # -1 only after the end
+        pairs = [(w >> 16, w & 0xFFFF) for w in items]
+        assert len(set(pairs)) == k                           # each (seq, seg) once
+        assert pairs == sorted(pairs)                          # sequence-major
+        nseg = [-(-n // T) for n in pages]
+        assert pairs == [(i, s) for i in range(bs) for s in range(nseg[i])]
+        feasible = sum(nseg) <= cap and max(nseg) <= smax
+        if feasible and T > 1:
+            prev = [-(-n // (T - 1)) for n in pages]
+            assert not (sum(prev) <= cap and max(prev) <= smax)   # T is the smallest
+        if not feasible:
+            assert T == max(max(pages), 1)
+            assert all(c <= 1 for c in nseg)
+        t = 0
+        for i in range(bs):
+            for j in range(ql[i]):
+                assert tok[t] <= nseg[i]
+                assert tok[t] <= max(smax, 1)
+                vis = min(max(lens[i] - ql[i] + j + 1, 0), lens[i]) if causal else lens[i]
+                # the count covers the visible keys and no segment beyond them
+                assert tok[t] * T * 16 >= vis
+                assert (tok[t] - 1) * T * 16 < vis or tok[t] == 0
+                t += 1
+
+
+def test_fixed_split_printed_values():
+    g = load_golden("fixed_split_values.json")
+    for c in g["cases"]:
+        for bs in range(c["bs_from"], c["bs_to"] + 1):
+            assert oracle.fixed_split_segments(bs, c["kv_heads"], g["num_cus"],
+                                               g["seg_max"]) == c["segments"], (bs, c)
+    lr = g["long_request"]
+    assert lr["tokens"] // lr["segments"] == lr["segment_tokens"]
+
+
+def test_pow2floor():
+    assert [oracle.pow2floor(v) for v in [0, 1, 2, 3, 4, 7, 8, 255, 256]] == \
+        [0, 1, 2, 2, 4, 4, 8, 128, 256]
+
+
+def test_uniform_lengths_match_fixed_split():
+    """With equal lengths and a feasible plan the planner gives every sequence the
+    fixed split's segment count: the verify 16 x 119k row of the benchmark table
+    shows identical times for both arms."""
+    cfg = configs.UNIFORM_VERIFY
+    plan, _ = oracle.plan_segments(cfg.seq_lens, _cu(cfg.q_lens), cfg.kv_heads, 16,
+                                   cfg.num_cus, cfg.seg_max, 1)
+    per_seq = sum(1 for w in plan[1:] if w != -1) // cfg.bs
+    assert per_seq == oracle.fixed_split_segments(cfg.bs, cfg.kv_heads) == 8
+
+
+def test_all_configs_plan_bounds():
+    for cfg in configs.CONFIGS:
+        plan, tok = oracle.plan_segments(cfg.seq_lens, _cu(cfg.q_lens), cfg.kv_heads,
+                                         cfg.page_size, cfg.num_cus, cfg.seg_max,
+                                         cfg.causal)
+        items = [w for w in plan[1:] if w != -1]
+        assert len(items) * cfg.kv_heads <= max(cfg.num_cus, cfg.bs * cfg.kv_heads)
+        assert len(tok) == cfg.total_q
+        assert max(tok) <= cfg.seg_max

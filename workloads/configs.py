@@ -1,0 +1,87 @@
+"""The five synthetic workloads: tiny correctness case, uniform long verify,
+skewed agentic verify, fp8 KV, and shuffled-page decode.
+
+Shapes follow the split-KV PR (sglang #39172, "[AMD] gfx950 assembly attention:
+length-aware split-KV for dynamic workload", Accuracy Tests and Benchmarking and
+Profiling) and, for the shuffled-page decode, the page-conversion RFC (vLLM
+#59111, "NixlConnector: convert standard KV pages to ROCm AITER shuffled pages
+on the decode side", Decode section: batch 64-128, 8k context, 16-token pages).
+
+Length lists are literals written by `workloads/make_lengths.py`.
+"""
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+# written by make_lengths.skew_lengths(): bs=20, sum 2,320,000
+SKEW_LENS = [0, 1, 5, 17, 247999, 14719, 247999, 107452, 120562, 152813, 25149,
+             150337, 79806, 247999, 237602, 133244, 143097, 97199, 66000, 248000]
+SKEW_Q = [4, 4, 4, 2, 2, 3, 3, 3, 4, 2, 4, 1, 1, 4, 4, 2, 1, 2, 1, 4]
+
+# written by make_lengths.fp8_lengths(): bs=64, median 8140, max 131072
+FP8_LENS = [3673, 6607, 63486, 18438, 1087, 8140, 3803, 9836, 1132, 11031, 10945,
+            56962, 12096, 15356, 1304, 131072, 775, 31792, 5458, 2771, 3653, 3583,
+            13080, 7154, 50798, 862, 8161, 2733, 21287, 604, 5366, 10610, 1318,
+            27543, 10207, 28286, 26674, 2453, 3069, 6378, 20568, 23348, 3420, 3880,
+            3069, 3991, 6112, 6965, 103154, 4392, 5742, 14405, 2535, 5204, 8327,
+            21241, 1622, 44306, 5309, 10091, 23237, 18475, 30169, 10138]
+FP8_Q = [4, 4, 1, 4, 2, 1, 4, 1, 1, 4, 1, 3, 2, 1, 2, 3, 1, 1, 4, 3, 2, 3, 4, 3,
+         3, 1, 1, 3, 3, 2, 3, 2, 4, 2, 3, 3, 3, 3, 3, 3, 1, 1, 2, 1, 4, 1, 3, 2,
+         4, 2, 1, 1, 4, 3, 4, 2, 3, 3, 3, 3, 1, 4, 3, 3]
+
+
+@dataclass
+class Config:
+    name: str
+    seq_lens: List[int]
+    q_lens: List[int]
+    q_heads: int
+    kv_heads: int
+    head_dim: int = 128
+    page_size: int = 16
+    kv_dtype: str = "bf16"          # "bf16" or "fp8" (OCP e4m3fn codes)
+    layout: str = "standard"        # "standard" [H,N,2D] or "shuffled" planes
+    num_cus: int = 256
+    seg_max: int = 64
+    causal: int = 1
+    k_scale: Optional[float] = None
+    v_scale: Optional[float] = None
+    seed: int = 0
+    extra_blocks: int = 8           # unused pool blocks, poison-filled
+    note: str = field(default="", compare=False)
+
+    @property
+    def bs(self):
+        return len(self.seq_lens)
+
+    @property
+    def total_q(self):
+        return int(sum(self.q_lens))
+
+    @property
+    def max_q(self):
+        return int(max(self.q_lens)) if self.q_lens else 1
+
+    @property
+    def elem_bytes(self):
+        return 1 if self.kv_dtype == "fp8" else 2
+
+    def kv_bytes(self):
+        """Bytes of K and V the sequences hold: sum(L) * kv_heads * 2 * D * e."""
+        return int(sum(self.seq_lens)) * self.kv_heads * 2 * self.head_dim * self.elem_bytes
+
+
+TINY = Config("tiny", [37, 100], [1, 1], 8, 2, seed=1,
+              note="bs=2, L={37,100}, q=1, 8/2 heads, bf16, random page table")
+UNIFORM_VERIFY = Config("uniform_verify", [119_000] * 16, [4] * 16, 32, 2, seed=2,
+                        note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), bf16, permuted page table")
+AGENTIC_SKEW = Config("agentic_skew", SKEW_LENS, SKEW_Q, 32, 2, seed=3,
+                      note="bs=20, 2.32M tokens, lognormal + {0,1,5,17,248k}, q 1..4, bf16")
+FP8_KV = Config("fp8_kv", FP8_LENS, FP8_Q, 16, 2, kv_dtype="fp8",
+                k_scale=0.0173, v_scale=0.0211, seed=4,
+                note="bs=64 lognormal (median 8k, max 128k), q 1..4, 16/2 heads, e4m3fn KV")
+SHUFFLED_DECODE = Config("shuffled_decode", [8192] * 128, [1] * 128, 32, 8,
+                         layout="shuffled", seed=5,
+                         note="bs=128 x 8k, q=1, 32/8 heads, bf16, standard pages repacked")
+
+CONFIGS = [TINY, UNIFORM_VERIFY, AGENTIC_SKEW, FP8_KV, SHUFFLED_DECODE]
+BY_NAME = {c.name: c for c in CONFIGS}
