@@ -1,0 +1,249 @@
+"""Benchmark: paged split-KV decode/verify attention on one MI355X.
+
+One step = one forward of one attention layer over a batch already resident
+in HBM: the length-aware plan (plan_build), the segment kernel and the split
+reduce. The metric is the attention call (segment + reduce): microseconds per
+call and effective KV TB/s = sum_i L_i * kv_heads * 2 * head_dim * bytes / time,
+also as a fraction of the 8 TB/s HBM peak. Per-kernel durations come from HIP
+events recorded on the stream the kernels run on. For shuffled-page workloads
+the standard->shuffled repack runs once before the timed steps and is timed on
+its own.
+
+Prints ONE JSON line (rank 0). Default workload: the uniform verify batch
+(bs=16 x 119k tokens, 4 query tokens, 32/2 heads, bf16). `--all` adds the other
+workloads to the line under "workloads".
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="uniform_verify")
+    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=2,
+                    help="sequences of the workload the CPU oracle is timed on")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "split_kv_paged_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(cfg_name, src_hash):
+    """HBM bytes per segment-kernel launch from committed rocprofv3 PMC
+    summaries, only if they were taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "segment_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    e = d.get(cfg_name)
+    if not e or e.get("kernel_source_hash") != src_hash:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def time_workload(cfg, steps, warmup, torch, skv, gen):
+    dev = "cuda:0"
+    case = gen.make_case(cfg, dev)
+    st = torch.cuda.current_stream()
+    res = {}
+    kv_a, kv_b = case.kv, None
+    if cfg.layout == "shuffled":
+        for _ in range(2):
+            kp, vp = skv.kv_page_shuffle(case.kv)
+        n = 5
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n):
+            skv.kv_page_shuffle(case.kv, kp, vp)
+        e1.record(st)
+        torch.cuda.synchronize()
+        sh_us = e0.elapsed_time(e1) * 1e3 / n
+        moved = 2 * case.kv.numel() * case.kv.element_size()
+        res["shuffle_us"] = sh_us
+        res["shuffle_gbs"] = moved / sh_us / 1e3
+        kv_a, kv_b = kp, vp
+    rows = cfg.total_q * cfg.q_heads * cfg.seg_max
+    part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
+    part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    out = torch.empty((cfg.total_q, cfg.q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    plan = torch.empty(skv.plan_words(cfg.bs, cfg.kv_heads, cfg.num_cus), dtype=torch.int32,
+                       device=dev)
+    tok = torch.empty(cfg.total_q, dtype=torch.int32, device=dev)
+    kw = dict(kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=cfg.num_cus,
+              seg_max=cfg.seg_max, kv_dtype=cfg.kv_dtype, layout=cfg.layout,
+              k_scale=case.k_scale, v_scale=case.v_scale, causal=cfg.causal)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(st)
+        skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, cfg.kv_heads,
+                       cfg.num_cus, cfg.seg_max, cfg.causal, plan=plan, tok_nseg=tok)
+        if ev:
+            ev[1].record(st)
+        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
+                         case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
+        if ev:
+            ev[2].record(st)
+        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
+                         seg_max=cfg.seg_max, out=out)
+        if ev:
+            ev[3].record(st)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    plan_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / steps
+    seg_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1e3 / steps
+    red_us = sum(e[2].elapsed_time(e[3]) for e in evs) * 1e3 / steps
+    step_us = sum(e[0].elapsed_time(e[3]) for e in evs) * 1e3 / steps
+    segs = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in evs)
+    kvb = cfg.kv_bytes()
+    call_us = seg_us + red_us
+    res.update(dict(
+        workload=cfg.name, kv_bytes=kvb, plan_us=plan_us, segment_us=seg_us,
+        segment_us_p10=segs[len(segs) // 10], segment_us_p90=segs[(9 * len(segs)) // 10],
+        reduce_us=red_us, attn_us_per_call=call_us, step_us=step_us, wall_s=wall,
+        kv_tb_s=kvb / call_us / 1e6, frac_of_hbm_peak=kvb / call_us / 1e3 / HBM_PEAK_GBS,
+        segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
+    del case, part_o, part_lse, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, n_seqs, gen, np):
+    """The oracle as it stands on a bounded sample of the workload: all query
+    rows of the first n_seqs sequences, on the host cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    sub = gen.small_config(cfg, cfg.seq_lens[:n_seqs], cfg.q_lens[:n_seqs])
+    case = gen.make_case(sub, "cpu")
+    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    kv = gen.raw_kv(case)
+    cu = case.cu_seqlens_q.numpy()
+    rows = [(t, h) for i in range(n_seqs) for t in range(cu[i], cu[i + 1])
+            for h in range(cfg.q_heads)]
+    t0 = time.perf_counter()
+    oracle.decode_attention(q, kv, cfg.kv_dtype, case.page_table.numpy(), case.seq_lens.numpy(),
+                            cu, cfg.kv_heads, cfg.page_size, cfg.causal, cfg.k_scale,
+                            cfg.v_scale, rows=rows)
+    dt = time.perf_counter() - t0
+    sample_bytes = sum(cfg.seq_lens[:n_seqs]) * cfg.kv_heads * 2 * cfg.head_dim * cfg.elem_bytes
+    return {"value": sample_bytes / dt / 1e12, "unit": "TB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": dt,
+            "sample": f"{cfg.name}: all {len(rows)} query rows of the first {n_seqs} "
+                      f"sequences ({sample_bytes} KV bytes), numpy fp64 oracle",
+            "host": platform.processor() or platform.machine(),
+            "host_cpus": os.cpu_count()}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import split_kv_paged_amd as skv
+    from workloads import configs, gen
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    skv.load()
+    if a.copy_probe:
+        x = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 5}))
+        return
+    cfg = configs.BY_NAME[a.config]
+    head = time_workload(cfg, a.steps, a.warmup, torch, skv, gen)
+    props = torch.cuda.get_device_properties(0)
+    src_hash = kernel_source_hash()
+    traffic = traffic_from_profiles(cfg.name, src_hash)
+    seg_gbs = head["segment_gb_s"]
+    line = {
+        "metric": "paged decode-attn effective KV TB/s (attention + reduce; us/call and "
+                  "fraction of HBM peak alongside)",
+        "value": round(head["kv_tb_s"], 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(head["step_us"] / 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.kv_dtype == "bf16" else "fp8-e4m3fn",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.note}", "bs": cfg.bs,
+                   "total_kv_tokens": int(sum(cfg.seq_lens)), "q_heads": cfg.q_heads,
+                   "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim,
+                   "page_size": cfg.page_size, "kv_dtype": cfg.kv_dtype,
+                   "layout": cfg.layout, "num_cus": cfg.num_cus, "seg_max": cfg.seg_max,
+                   "parallelism": "single GPU"},
+        "us_per_call": round(head["attn_us_per_call"], 2),
+        "frac_of_hbm_peak": round(head["frac_of_hbm_peak"], 4),
+        "breakdown_us": {k: round(head[k], 2) for k in
+                         ("plan_us", "segment_us", "segment_us_p10", "segment_us_p90",
+                          "reduce_us", "step_us")},
+        "roofline": {"bound": "hbm", "kernel": "segment attention",
+                     "achieved": round(seg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(seg_gbs / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes_per_launch": head["kv_bytes"],
+                     "traffic": traffic, "kernel_source_hash": src_hash},
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if a.all:
+        wl = []
+        for c in configs.CONFIGS:
+            if c.name == cfg.name:
+                continue
+            r = time_workload(c, max(10, a.steps // 2), a.warmup, torch, skv, gen)
+            wl.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+        line["workloads"] = wl
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seqs, gen, np)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

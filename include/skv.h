@@ -1,0 +1,190 @@
+/*
+ * skv.h — C ABI of libskv: paged split-KV decode/verify attention for MI355X
+ * (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [PR]  sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware
+ *         split-KV for dynamic workload" — Motivation (the fixed split: one
+ *         work-group per segment, sequence and KV head), Modifications (the
+ *         length-aware planner, its work list and per-token segment counts,
+ *         the segment kernel's work-list prologue, the split reduce).
+ *   [RFC] vLLM RFC #59111, "NixlConnector: convert standard KV pages to ROCm
+ *         AITER shuffled pages on the decode side" — Background (standard
+ *         [H, N, 2D] pages and shuffled K [H, D/x, N, x] / V [H, N/x, D, x]
+ *         planes, x = 16 / element bytes), Proposed Change §4 (converting the
+ *         received blocks).
+ *
+ * Conventions for every call:
+ *   - Pointer arguments are DEVICE pointers owned by the caller (except the
+ *     `stream`, a hipStream_t passed as void*; NULL is the null stream).
+ *   - The library never allocates, frees or synchronizes and keeps no global
+ *     state; calls only enqueue work on `stream`. Grid sizes depend on the
+ *     host integers alone and no device data is read back, so every call may
+ *     be captured into a HIP graph.
+ *   - Return value: SKV_OK, or an error code below; on error nothing was
+ *     enqueued. Host-checkable argument errors are detected before any HIP
+ *     call, so they can be tested without a GPU.
+ *   - Device data must satisfy the stated contract (lengths, page ids,
+ *     cu_seqlens_q); a violation is undefined behaviour and is not detected.
+ *
+ * Element types: Q and the output are bf16 (IEEE binary32 upper half). KV is
+ * bf16 or OCP e4m3fn fp8 (kv_dtype 1) with per-tensor fp32 dequant scales.
+ * Supported geometry: head_dim 128, page_size 16, 1..4 query tokens per
+ * sequence, (q_heads / kv_heads) * max_q <= 64.
+ */
+#ifndef SKV_H_
+#define SKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum skv_status {
+  SKV_OK = 0,
+  SKV_EINVAL = 1,        /* NULL required pointer, bad size or relation   */
+  SKV_EUNSUPPORTED = 2,  /* valid but outside the supported geometry      */
+  SKV_ELAUNCH = 3        /* the HIP launch itself failed                  */
+};
+
+enum skv_layout { SKV_LAYOUT_STANDARD = 0, SKV_LAYOUT_SHUFFLED = 1 };
+enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1 };
+
+/* Number of int32 words of a plan: 1 + max(num_cus / kv_heads, bs).
+ * [PR, Modifications]: one word for the segment length, then the work list,
+ * whose capacity covers both the per-kv-head CU budget and one segment per
+ * sequence (the fallback when no segment length fits the budget).
+ * Returns 0 if an argument is not positive. */
+size_t skv_plan_words(int bs, int kv_heads, int num_cus);
+
+/* Bytes of the partial-result workspace: part_o fp32 [total_q, q_heads,
+ * seg_max, head_dim] followed by part_lse fp32 [total_q, q_heads, seg_max].
+ * Returns 0 if an argument is not positive. */
+size_t skv_workspace_bytes(int total_q, int q_heads, int head_dim, int seg_max);
+
+/* Length-aware segment planner [PR, Modifications].
+ *
+ * In:  seq_lens int32 [bs] (KV tokens per sequence, the sequence's own query
+ *      tokens included, 0 <= L); cu_seqlens_q int32 [bs + 1] (prefix sums of
+ *      query tokens, cu[0] = 0, cu[bs] = total_q).
+ * Out: plan int32 [skv_plan_words(bs, kv_heads, num_cus)]:
+ *        plan[0] = T, pages per segment: the smallest T >= 1 for which
+ *          sum_i ceil(ceil(L_i/P)/T) <= num_cus / kv_heads and
+ *          max_i ceil(ceil(L_i/P)/T) <= seg_max; when no T qualifies, the
+ *          longest sequence's page count (one segment per sequence);
+ *        plan[1 + k] = (i << 16) | s for the k-th (sequence i, segment s),
+ *          sequence-major with segments ascending, then -1 to the end.
+ *      tok_nseg int32 [total_q]: for query token t of sequence i,
+ *        ceil(visible_t / (T * page_size)) where visible_t is the number of
+ *        keys t may see (causal: a sequence's q query tokens are its last q
+ *        KV tokens, so query j sees L - q + j + 1 keys, clamped to [0, L];
+ *        non-causal: L).
+ * One single-work-group launch; integer arithmetic only.
+ * Errors: EINVAL for NULL pointers, bs < 1, bs >= 32768, total_q < 1,
+ * kv_heads < 1, num_cus < 1, seg_max outside [1, 65535]; EUNSUPPORTED for
+ * page_size != 16. */
+int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
+                   int total_q, int kv_heads, int page_size, int num_cus,
+                   int seg_max, int causal, int32_t* plan, int32_t* tok_nseg,
+                   void* stream);
+
+/* Paged decode/verify attention: the segment kernel, then the split reduce
+ * [PR, Motivation and Modifications].
+ *
+ * q            bf16 [total_q, q_heads, head_dim]
+ * kv_a, kv_b   layout STANDARD: kv_a = pages [num_blocks, kv_heads, page_size,
+ *              2 * head_dim] (per token: K channels then V channels), kv_b NULL;
+ *              layout SHUFFLED: kv_a = K plane [num_blocks, kv_heads,
+ *              head_dim/x, page_size, x], kv_b = V plane [num_blocks, kv_heads,
+ *              page_size/x, head_dim, x], x = 16 / element bytes [RFC, Background]
+ * kv_dtype     SKV_KV_BF16 or SKV_KV_FP8_E4M3FN
+ * page_table   int32 [bs, pt_stride]; entry [i, p] is the block holding tokens
+ *              [16p, 16p + 16) of sequence i; entries at p >= ceil(L_i/16) are
+ *              never read
+ * seq_lens, cu_seqlens_q, bs, total_q   as for skv_plan_build
+ * max_q        an upper bound of the query tokens of any sequence (1..4)
+ * q_heads, kv_heads   grouped-query heads: q head h reads kv head h / (q_heads/kv_heads)
+ * k_scale, v_scale    device fp32 scalars: required for fp8 (dequantized value =
+ *              code value * scale), NULL for bf16
+ * causal       1: bottom-right causal mask as in skv_plan_build; 0: all L keys
+ * plan, tok_nseg      from skv_plan_build with the same bs, kv_heads, num_cus,
+ *              seg_max, causal and page_size
+ * part_o, part_lse    workspace of skv_workspace_bytes(): part_o fp32
+ *              [total_q, q_heads, seg_max, head_dim] (each segment's
+ *              softmax-normalized output), part_lse fp32 [total_q, q_heads,
+ *              seg_max] (natural-log sum-exp); entries s >= tok_nseg[t] are
+ *              unspecified
+ * out          bf16 [total_q, q_heads, head_dim], round-to-nearest-even;
+ *              a token that sees no key gets zeros
+ * out_lse      fp32 [total_q, q_heads] or NULL; -inf where no key is visible
+ * Scale: softmax(q.k / sqrt(head_dim)).
+ * Errors: EINVAL for NULL required pointers, non-positive sizes, q_heads not a
+ * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
+ * scales present for bf16 or missing for fp8, kv_b NULL for SHUFFLED or
+ * non-NULL for STANDARD, pt_stride < 1, an unknown layout or dtype;
+ * EUNSUPPORTED for head_dim != 128, page_size != 16, max_q > 4,
+ * (q_heads/kv_heads) * max_q > 64. */
+int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
+                          int layout, int kv_dtype, const int32_t* page_table,
+                          int pt_stride, const int32_t* seq_lens,
+                          const int32_t* cu_seqlens_q, int bs, int total_q,
+                          int max_q, int q_heads, int kv_heads, int head_dim,
+                          int page_size, const float* k_scale,
+                          const float* v_scale, int causal, const int32_t* plan,
+                          const int32_t* tok_nseg, int num_cus, int seg_max,
+                          float* part_o, float* part_lse, void* out,
+                          float* out_lse, void* stream);
+
+/* The segment kernel of skv_paged_decode_attn alone: writes the partials
+ * (part_o, part_lse) of every (token, q head, segment) that the plan lists,
+ * without merging them. Arguments and errors as for skv_paged_decode_attn
+ * (minus out and out_lse). skv_paged_decode_attn = this call followed by
+ * skv_split_reduce on the same stream. Partials of several calls (e.g. over
+ * disjoint page ranges) can be merged with skv_split_reduce. */
+int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layout,
+                     int kv_dtype, const int32_t* page_table, int pt_stride,
+                     const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
+                     int total_q, int max_q, int q_heads, int kv_heads, int head_dim,
+                     int page_size, const float* k_scale, const float* v_scale,
+                     int causal, const int32_t* plan, const int32_t* tok_nseg,
+                     int num_cus, int seg_max, float* part_o, float* part_lse,
+                     void* stream);
+
+/* Split reduce alone [PR, Modifications]: for every (t, h), merges the first
+ * tok_nseg[t] partials by log-sum-exp: M = max_s lse_s,
+ * lse = M + ln sum_s exp(lse_s - M), out = sum_s exp(lse_s - lse) * o_s.
+ * tok_nseg[t] == 0 gives zeros and lse -inf. Values of tok_nseg[t] above
+ * seg_max are clamped to seg_max.
+ * Layouts as for skv_paged_decode_attn; out bf16 [total_q, q_heads, head_dim];
+ * out_lse may be NULL.
+ * Errors: EINVAL for NULL required pointers, non-positive sizes, seg_max
+ * outside [1, 65535]; EUNSUPPORTED for head_dim != 128. */
+int skv_split_reduce(const float* part_o, const float* part_lse,
+                     const int32_t* tok_nseg, int total_q, int q_heads,
+                     int head_dim, int seg_max, void* out, float* out_lse,
+                     void* stream);
+
+/* Standard -> shuffled page repack [RFC, Background and Proposed Change §4].
+ * For each listed block b (block_ids int32 [num_blocks]; NULL = blocks
+ * 0..num_blocks-1) and head h:
+ *   k_plane[b, h, c, n, i] = std_cache[b, h, n, c*x + i]
+ *   v_plane[b, h, g, d, i] = std_cache[b, h, g*x + i, head_dim + d]
+ * with x = 16 / elem_bytes. Pure byte movement, bit-exact. Out of place: the
+ * source must not overlap the planes. Blocks not listed are left untouched.
+ * Errors: EINVAL for NULL required pointers, num_blocks < 1, kv_heads < 1;
+ * EUNSUPPORTED for head_dim != 128, page_size != 16, elem_bytes not 1 or 2. */
+int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
+                        const int32_t* block_ids, int num_blocks, int kv_heads,
+                        int page_size, int head_dim, int elem_bytes,
+                        void* stream);
+
+/* Static text for a status code. */
+const char* skv_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKV_H_ */

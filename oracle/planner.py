@@ -21,6 +21,8 @@ Readings (pages silent; also in the design notes):
   * per-token count: the number of the sequence's segments that hold at least
     one key the token may see, ceil(visible / (T * P)).
 """
+import numpy as np
+
 from .attention import visible_keys
 
 
@@ -43,10 +45,13 @@ def plan_segments(seq_lens, cu_seqlens_q, kv_heads, page_size, num_cus, seg_max,
     cap = num_cus // kv_heads
     longest = max(pages) if pages else 0
 
-    # step 2: feasibility of a candidate segment length
+    # step 2: feasibility of a candidate segment length (numpy only to keep
+    # the upward scan affordable for 10^5-page sequences)
+    pages_np = np.asarray(pages, dtype=np.int64)
+
     def feasible(T):
-        segs = [_ceil_div(n, T) for n in pages]
-        return sum(segs) <= cap and max(segs, default=0) <= seg_max
+        segs = -(-pages_np // T)
+        return int(segs.sum()) <= cap and int(segs.max(initial=0)) <= seg_max
 
     # step 3: smallest feasible T, scanning upward; fallback when none is
     upper = max(longest, 1)

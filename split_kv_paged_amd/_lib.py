@@ -1,0 +1,225 @@
+"""ctypes binding of libskv.so (include/skv.h), with the same function names.
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the computation runs in libskv's kernels.
+Loading fails loudly when the library has not been built — there is no
+fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libskv.so")
+
+SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_ELAUNCH = 0, 1, 2, 3
+LAYOUT = {"standard": 0, "shuffled": 1}
+KV_DTYPE = {"bf16": 0, "fp8": 1}
+
+_c_int, _c_sz, _p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGNATURES = {
+    "skv_plan_words": (_c_sz, [_c_int, _c_int, _c_int]),
+    "skv_workspace_bytes": (_c_sz, [_c_int, _c_int, _c_int, _c_int]),
+    "skv_plan_build": (_c_int, [_p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _c_int, _p, _p, _p]),
+    "skv_paged_decode_attn": (_c_int, [_p, _p, _p, _c_int, _c_int, _p, _c_int, _p, _p,
+                                       _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _p, _p, _c_int, _p, _p, _c_int, _c_int,
+                                       _p, _p, _p, _p, _p]),
+    "skv_segment_attn": (_c_int, [_p, _p, _p, _c_int, _c_int, _p, _c_int, _p, _p,
+                                  _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _c_int, _p, _p, _c_int, _p, _p, _c_int, _c_int,
+                                  _p, _p, _p]),
+    "skv_split_reduce": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _p]),
+    "skv_kv_page_shuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _p]),
+    "skv_strerror": (ctypes.c_char_p, [_c_int]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+_lib = None
+
+
+class SkvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({strerror(status)})")
+
+
+def load():
+    """Load libskv.so once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run python -m split_kv_paged_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def strerror(status):
+    return load().skv_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status, where):
+    if status != SKV_OK:
+        raise SkvError(status, where)
+
+
+def _need(t, dtype, name, numel=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name}: needs {numel} elements, has {t.numel()}")
+
+
+def plan_words(bs, kv_heads, num_cus):
+    return int(load().skv_plan_words(bs, kv_heads, num_cus))
+
+
+def workspace_bytes(total_q, q_heads, head_dim, seg_max):
+    return int(load().skv_workspace_bytes(total_q, q_heads, head_dim, seg_max))
+
+
+def plan_build(seq_lens, cu_seqlens_q, total_q, kv_heads, num_cus, seg_max, causal=1,
+               page_size=16, plan=None, tok_nseg=None, stream=None):
+    """Enqueue the planner; returns (plan int32 [plan_words], tok_nseg int32 [total_q]).
+
+    total_q is a host integer (cu_seqlens_q[-1]) so that nothing is read back."""
+    bs = seq_lens.numel()
+    dev = seq_lens.device
+    if plan is None:
+        plan = torch.empty(plan_words(bs, kv_heads, num_cus), dtype=torch.int32, device=dev)
+    if tok_nseg is None:
+        tok_nseg = torch.empty(max(total_q, 1), dtype=torch.int32, device=dev)
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(cu_seqlens_q, torch.int32, "cu_seqlens_q", bs + 1)
+    _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    _need(tok_nseg, torch.int32, "tok_nseg")
+    st = load().skv_plan_build(_ptr(seq_lens), _ptr(cu_seqlens_q), bs, total_q, kv_heads,
+                               page_size, num_cus, seg_max, int(causal), _ptr(plan),
+                               _ptr(tok_nseg), _stream(stream))
+    _check(st, "skv_plan_build")
+    return plan, tok_nseg
+
+
+def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_nseg,
+                      *, kv_heads, max_q, num_cus, seg_max, kv_dtype="bf16",
+                      layout="standard", k_scale=None, v_scale=None, causal=1,
+                      part_o=None, part_lse=None, out=None, out_lse=None,
+                      page_size=16, stream=None):
+    """Enqueue segment attention + split reduce; returns (out bf16, out_lse or None)."""
+    total_q, q_heads, head_dim = q.shape
+    bs = seq_lens.numel()
+    dev = q.device
+    rows = total_q * q_heads * seg_max
+    if part_o is None:
+        part_o = torch.empty(rows * head_dim, dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty((total_q, q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    _need(q, torch.bfloat16, "q")
+    _need(out, torch.bfloat16, "out", total_q * q_heads * head_dim)
+    _need(part_o, torch.float32, "part_o", rows * head_dim)
+    _need(part_lse, torch.float32, "part_lse", rows)
+    _need(page_table, torch.int32, "page_table")
+    _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    _need(tok_nseg, torch.int32, "tok_nseg", total_q)
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", total_q * q_heads)
+    for t, n in ((kv_a, "kv_a"), (kv_b, "kv_b")):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    st = load().skv_paged_decode_attn(
+        _ptr(q), _ptr(kv_a), _ptr(kv_b), LAYOUT[layout], KV_DTYPE[kv_dtype],
+        _ptr(page_table), page_table.shape[1], _ptr(seq_lens), _ptr(cu_seqlens_q), bs,
+        total_q, max_q, q_heads, kv_heads, head_dim, page_size, _ptr(k_scale),
+        _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
+        _ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(out_lse), _stream(stream))
+    _check(st, "skv_paged_decode_attn")
+    return out, out_lse
+
+
+def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_nseg,
+                 *, kv_heads, max_q, num_cus, seg_max, part_o, part_lse, kv_dtype="bf16",
+                 layout="standard", k_scale=None, v_scale=None, causal=1, page_size=16,
+                 stream=None):
+    """Enqueue the segment kernel alone (partials only)."""
+    total_q, q_heads, head_dim = q.shape
+    bs = seq_lens.numel()
+    rows = total_q * q_heads * seg_max
+    _need(q, torch.bfloat16, "q")
+    _need(part_o, torch.float32, "part_o", rows * head_dim)
+    _need(part_lse, torch.float32, "part_lse", rows)
+    _need(page_table, torch.int32, "page_table")
+    _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    _need(tok_nseg, torch.int32, "tok_nseg", total_q)
+    st = load().skv_segment_attn(
+        _ptr(q), _ptr(kv_a), _ptr(kv_b), LAYOUT[layout], KV_DTYPE[kv_dtype],
+        _ptr(page_table), page_table.shape[1], _ptr(seq_lens), _ptr(cu_seqlens_q), bs,
+        total_q, max_q, q_heads, kv_heads, head_dim, page_size, _ptr(k_scale),
+        _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
+        _ptr(part_o), _ptr(part_lse), _stream(stream))
+    _check(st, "skv_segment_attn")
+    return part_o, part_lse
+
+
+def split_reduce(part_o, part_lse, tok_nseg, *, total_q, q_heads, seg_max, head_dim=128,
+                 out=None, out_lse=None, stream=None):
+    dev = part_o.device
+    if out is None:
+        out = torch.empty((total_q, q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    rows = total_q * q_heads * seg_max
+    _need(part_o, torch.float32, "part_o", rows * head_dim)
+    _need(part_lse, torch.float32, "part_lse", rows)
+    _need(tok_nseg, torch.int32, "tok_nseg", total_q)
+    _need(out, torch.bfloat16, "out", total_q * q_heads * head_dim)
+    st = load().skv_split_reduce(_ptr(part_o), _ptr(part_lse), _ptr(tok_nseg), total_q,
+                                 q_heads, head_dim, seg_max, _ptr(out), _ptr(out_lse),
+                                 _stream(stream))
+    _check(st, "skv_split_reduce")
+    return out, out_lse
+
+
+def kv_page_shuffle(std_cache, k_plane=None, v_plane=None, block_ids=None, stream=None):
+    """Standard pages [B, H, N, 2D] -> (K plane [B, H, D/x, N, x], V plane [B, H, N/x, D, x])."""
+    B, H, N, D2 = std_cache.shape
+    D = D2 // 2
+    e = std_cache.element_size()
+    x = 16 // e
+    if k_plane is None:
+        k_plane = torch.empty((B, H, D // x, N, x), dtype=std_cache.dtype, device=std_cache.device)
+    if v_plane is None:
+        v_plane = torch.empty((B, H, N // x, D, x), dtype=std_cache.dtype, device=std_cache.device)
+    for t, n in ((std_cache, "std_cache"), (k_plane, "k_plane"), (v_plane, "v_plane")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    nb = B
+    if block_ids is not None:
+        _need(block_ids, torch.int32, "block_ids")
+        nb = block_ids.numel()
+    st = load().skv_kv_page_shuffle(_ptr(std_cache), _ptr(k_plane), _ptr(v_plane),
+                                    _ptr(block_ids), nb, H, N, D, e, _stream(stream))
+    _check(st, "skv_kv_page_shuffle")
+    return k_plane, v_plane

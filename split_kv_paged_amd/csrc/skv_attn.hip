@@ -1,0 +1,53 @@
+// Segment-attention launcher: picks the matrix-core or the vector-ALU kernel
+// from the number of query rows a work-group carries (GQA group x max query
+// tokens) and launches a 1-D grid over the work list x kv heads.
+//
+// sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
+// for dynamic workload", Modifications: the attention kernel is launched as
+// a 1-D grid over the work list; padding entries (-1) exit at once.
+#include "skv_attn_common.h"
+#include "skv.h"
+
+namespace skv {
+
+int launch_segments_mfma(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
+                         hipStream_t st);
+int launch_segments_valu(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
+                         hipStream_t st);
+
+// Rows at or below this go to the VALU kernel; above it, 16-row MFMA tiles.
+constexpr int kValuMaxRows = 8;
+
+int launch_segments(const AttnArgs& a, void* stream) {
+  SegParams sp;
+  sp.q = static_cast<const uint16_t*>(a.q);
+  sp.kv_a = static_cast<const uint8_t*>(a.kv_a);
+  sp.kv_b = static_cast<const uint8_t*>(a.kv_b);
+  sp.page_table = a.page_table;
+  sp.seq_lens = a.seq_lens;
+  sp.cu_q = a.cu_seqlens_q;
+  sp.plan = a.plan;
+  sp.k_scale = a.k_scale;
+  sp.v_scale = a.v_scale;
+  sp.part_o = a.part_o;
+  sp.part_lse = a.part_lse;
+  sp.pt_stride = a.pt_stride;
+  sp.bs = a.bs;
+  sp.Hq = a.q_heads;
+  sp.Hkv = a.kv_heads;
+  sp.G = a.q_heads / a.kv_heads;
+  sp.seg_max = a.seg_max;
+  sp.causal = a.causal;
+  const long long grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) *
+                         a.kv_heads;
+  if (grid > 0x7fffffffLL) return SKV_EUNSUPPORTED;
+  const int e = a.kv_dtype == SKV_KV_FP8_E4M3FN ? 1 : 2;
+  const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
+  const int rows = sp.G * a.max_q;
+  auto st = static_cast<hipStream_t>(stream);
+  if (rows <= kValuMaxRows)
+    return launch_segments_valu(sp, e, shuf, rows, static_cast<int>(grid), st);
+  return launch_segments_mfma(sp, e, shuf, rows, static_cast<int>(grid), st);
+}
+
+}  // namespace skv

@@ -1,0 +1,80 @@
+// Internal declarations shared by the host-side C ABI (skv_api.cpp), the
+// host-only argument checks (skv_validate.cpp) and the kernel launchers
+// (*.hip). Not part of the public interface.
+#ifndef SKV_INTERNAL_H_
+#define SKV_INTERNAL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace skv {
+
+constexpr int kHeadDim = 128;
+constexpr int kPageSize = 16;
+constexpr int kMaxQ = 4;
+constexpr int kMaxRows = 64;     // (q_heads / kv_heads) * max_q
+constexpr int kMaxBs = 32767;    // seq << 16 stays a non-negative int32
+constexpr int kMaxSegMax = 65535;
+
+// ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
+int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
+                    int total_q, int kv_heads, int page_size, int num_cus,
+                    int seg_max, const void* plan, const void* tok_nseg);
+int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
+                    int layout, int kv_dtype, const void* page_table,
+                    int pt_stride, const void* seq_lens,
+                    const void* cu_seqlens_q, int bs, int total_q, int max_q,
+                    int q_heads, int kv_heads, int head_dim, int page_size,
+                    const void* k_scale, const void* v_scale,
+                    const void* plan, const void* tok_nseg, int num_cus,
+                    int seg_max, const void* part_o, const void* part_lse,
+                    const void* out);
+int check_reduce_args(const void* part_o, const void* part_lse,
+                      const void* tok_nseg, int total_q, int q_heads,
+                      int head_dim, int seg_max, const void* out);
+int check_shuffle_args(const void* std_cache, const void* k_plane,
+                       const void* v_plane, int num_blocks, int kv_heads,
+                       int page_size, int head_dim, int elem_bytes);
+
+inline int plan_width(int bs, int kv_heads, int num_cus) {
+  int cap = num_cus / kv_heads;
+  return cap > bs ? cap : bs;
+}
+
+// ---- kernel launchers (*.hip); return an skv_status ------------------------
+struct AttnArgs {
+  const void* q;
+  const void* kv_a;
+  const void* kv_b;
+  int layout, kv_dtype;
+  const int32_t* page_table;
+  int pt_stride;
+  const int32_t* seq_lens;
+  const int32_t* cu_seqlens_q;
+  int bs, total_q, max_q, q_heads, kv_heads;
+  const float* k_scale;
+  const float* v_scale;
+  int causal;
+  const int32_t* plan;
+  const int32_t* tok_nseg;
+  int num_cus, seg_max;
+  float* part_o;
+  float* part_lse;
+  void* out;
+  float* out_lse;
+};
+
+int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
+                int total_q, int kv_heads, int num_cus, int seg_max,
+                int causal, int32_t* plan, int32_t* tok_nseg, void* stream);
+int launch_segments(const AttnArgs& a, void* stream);
+int launch_reduce(const float* part_o, const float* part_lse,
+                  const int32_t* tok_nseg, int total_q, int q_heads,
+                  int seg_max, void* out, float* out_lse, void* stream);
+int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
+                   const int32_t* block_ids, int num_blocks, int kv_heads,
+                   int elem_bytes, void* stream);
+
+}  // namespace skv
+
+#endif  // SKV_INTERNAL_H_

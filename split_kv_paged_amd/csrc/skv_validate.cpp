@@ -1,0 +1,73 @@
+// Host-only argument checks for the C ABI. Pure C++ (no HIP headers) so the
+// error conventions documented in include/skv.h are testable without a GPU.
+#include "skv_internal.h"
+
+#include "skv.h"
+
+namespace skv {
+
+int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
+                    int total_q, int kv_heads, int page_size, int num_cus,
+                    int seg_max, const void* plan, const void* tok_nseg) {
+  if (!seq_lens || !cu_seqlens_q || !plan || !tok_nseg) return SKV_EINVAL;
+  if (bs < 1 || bs > kMaxBs || total_q < 1 || kv_heads < 1 || num_cus < 1)
+    return SKV_EINVAL;
+  if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
+  if (page_size != kPageSize) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
+                    int layout, int kv_dtype, const void* page_table,
+                    int pt_stride, const void* seq_lens,
+                    const void* cu_seqlens_q, int bs, int total_q, int max_q,
+                    int q_heads, int kv_heads, int head_dim, int page_size,
+                    const void* k_scale, const void* v_scale,
+                    const void* plan, const void* tok_nseg, int num_cus,
+                    int seg_max, const void* part_o, const void* part_lse,
+                    const void* out) {
+  if (!q || !kv_a || !page_table || !seq_lens || !cu_seqlens_q || !plan ||
+      !tok_nseg || !part_o || !part_lse || !out)
+    return SKV_EINVAL;
+  if (layout != SKV_LAYOUT_STANDARD && layout != SKV_LAYOUT_SHUFFLED)
+    return SKV_EINVAL;
+  if (kv_dtype != SKV_KV_BF16 && kv_dtype != SKV_KV_FP8_E4M3FN)
+    return SKV_EINVAL;
+  if ((layout == SKV_LAYOUT_SHUFFLED) != (kv_b != nullptr)) return SKV_EINVAL;
+  const bool fp8 = kv_dtype == SKV_KV_FP8_E4M3FN;
+  if (fp8 && (!k_scale || !v_scale)) return SKV_EINVAL;
+  if (!fp8 && (k_scale || v_scale)) return SKV_EINVAL;
+  if (bs < 1 || bs > kMaxBs || total_q < 1 || q_heads < 1 || kv_heads < 1 ||
+      num_cus < 1 || pt_stride < 1 || head_dim < 1 || page_size < 1)
+    return SKV_EINVAL;
+  if (q_heads % kv_heads != 0) return SKV_EINVAL;
+  if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
+  if (max_q < 1) return SKV_EINVAL;
+  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (max_q > kMaxQ) return SKV_EUNSUPPORTED;
+  if ((q_heads / kv_heads) * max_q > kMaxRows) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+int check_reduce_args(const void* part_o, const void* part_lse,
+                      const void* tok_nseg, int total_q, int q_heads,
+                      int head_dim, int seg_max, const void* out) {
+  if (!part_o || !part_lse || !tok_nseg || !out) return SKV_EINVAL;
+  if (total_q < 1 || q_heads < 1 || head_dim < 1) return SKV_EINVAL;
+  if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
+  if (head_dim != kHeadDim) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+int check_shuffle_args(const void* std_cache, const void* k_plane,
+                       const void* v_plane, int num_blocks, int kv_heads,
+                       int page_size, int head_dim, int elem_bytes) {
+  if (!std_cache || !k_plane || !v_plane) return SKV_EINVAL;
+  if (num_blocks < 1 || kv_heads < 1 || page_size < 1 || head_dim < 1)
+    return SKV_EINVAL;
+  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
+}  // namespace skv

@@ -1,0 +1,136 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol the header
+declares, and rejects bad arguments before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import split_kv_paged_amd as skv
+from split_kv_paged_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "skv.h")
+P = ctypes.c_void_p(4096)       # a non-NULL pointer value that is never dereferenced
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(skv_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declarations_are_exported():
+    lib = skv.load()
+    names = _declared()
+    assert names == sorted(skv.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_sizes():
+    assert skv.plan_words(16, 2, 256) == 129
+    assert skv.plan_words(128, 8, 256) == 129
+    assert skv.plan_words(2, 2, 256) == 129
+    assert skv.plan_words(300, 1, 256) == 301
+    assert skv.plan_words(0, 2, 256) == 0
+    assert skv.workspace_bytes(64, 32, 128, 64) == 64 * 32 * 64 * (128 + 1) * 4
+    assert skv.workspace_bytes(0, 32, 128, 64) == 0
+
+
+def test_strerror():
+    assert skv.strerror(0) == "ok"
+    assert skv.strerror(1) == "invalid argument"
+    assert skv.strerror(2) == "unsupported geometry or type"
+    assert skv.strerror(3) == "kernel launch failed"
+    assert skv.strerror(99) == "unknown status"
+
+
+def _plan(**kw):
+    a = dict(seq_lens=P, cu=P, bs=2, total_q=2, kv_heads=2, page_size=16, num_cus=256,
+             seg_max=64, causal=1, plan=P, tok=P)
+    a.update(kw)
+    return skv.load().skv_plan_build(a["seq_lens"], a["cu"], a["bs"], a["total_q"],
+                                     a["kv_heads"], a["page_size"], a["num_cus"],
+                                     a["seg_max"], a["causal"], a["plan"], a["tok"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seq_lens=None), 1), (dict(cu=None), 1), (dict(plan=None), 1), (dict(tok=None), 1),
+    (dict(bs=0), 1), (dict(bs=32768), 1), (dict(total_q=0), 1), (dict(kv_heads=0), 1),
+    (dict(num_cus=0), 1), (dict(seg_max=0), 1), (dict(seg_max=65536), 1),
+    (dict(page_size=32), 2),
+])
+def test_plan_build_errors(kw, code):
+    assert _plan(**kw) == code
+
+
+def _attn(**kw):
+    a = dict(q=P, kv_a=P, kv_b=None, layout=0, kv_dtype=0, pt=P, pt_stride=8, seq_lens=P,
+             cu=P, bs=2, total_q=2, max_q=1, q_heads=8, kv_heads=2, head_dim=128,
+             page_size=16, k_scale=None, v_scale=None, causal=1, plan=P, tok=P,
+             num_cus=256, seg_max=64, part_o=P, part_lse=P, out=P, out_lse=None)
+    a.update(kw)
+    return skv.load().skv_paged_decode_attn(
+        a["q"], a["kv_a"], a["kv_b"], a["layout"], a["kv_dtype"], a["pt"], a["pt_stride"],
+        a["seq_lens"], a["cu"], a["bs"], a["total_q"], a["max_q"], a["q_heads"],
+        a["kv_heads"], a["head_dim"], a["page_size"], a["k_scale"], a["v_scale"],
+        a["causal"], a["plan"], a["tok"], a["num_cus"], a["seg_max"], a["part_o"],
+        a["part_lse"], a["out"], a["out_lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(kv_a=None), 1), (dict(pt=None), 1), (dict(plan=None), 1),
+    (dict(tok=None), 1), (dict(part_o=None), 1), (dict(part_lse=None), 1), (dict(out=None), 1),
+    (dict(seq_lens=None), 1), (dict(cu=None), 1),
+    (dict(layout=2), 1), (dict(kv_dtype=2), 1),
+    (dict(layout=1), 1),                                  # shuffled needs the V plane
+    (dict(kv_b=P), 1),                                    # standard takes no V plane
+    (dict(kv_dtype=1), 1),                                # fp8 needs scales
+    (dict(k_scale=P, v_scale=P), 1),                      # bf16 takes none
+    (dict(kv_dtype=1, k_scale=P), 1),
+    (dict(q_heads=12, kv_heads=8), 1), (dict(bs=0), 1), (dict(bs=40000), 1),
+    (dict(total_q=0), 1), (dict(max_q=0), 1), (dict(seg_max=0), 1), (dict(seg_max=70000), 1),
+    (dict(pt_stride=0), 1), (dict(num_cus=0), 1), (dict(kv_heads=0), 1),
+    (dict(head_dim=64), 2), (dict(page_size=32), 2), (dict(max_q=5), 2),
+    (dict(q_heads=32, kv_heads=2, max_q=8), 2),           # rows 128 > 64 (max_q checked first)
+    (dict(q_heads=64, kv_heads=2, max_q=3), 2),           # rows 96 > 64
+])
+def test_attn_errors(kw, code):
+    assert _attn(**kw) == code
+
+
+def _reduce(**kw):
+    a = dict(po=P, pl=P, tok=P, total_q=2, q_heads=8, head_dim=128, seg_max=64, out=P)
+    a.update(kw)
+    return skv.load().skv_split_reduce(a["po"], a["pl"], a["tok"], a["total_q"], a["q_heads"],
+                                       a["head_dim"], a["seg_max"], a["out"], None, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(po=None), 1), (dict(pl=None), 1), (dict(tok=None), 1), (dict(out=None), 1),
+    (dict(total_q=0), 1), (dict(q_heads=0), 1), (dict(seg_max=0), 1), (dict(seg_max=65536), 1),
+    (dict(head_dim=64), 2),
+])
+def test_reduce_errors(kw, code):
+    assert _reduce(**kw) == code
+
+
+def _shuffle(**kw):
+    a = dict(src=P, k=P, v=P, ids=None, nb=4, h=2, ps=16, hd=128, e=2)
+    a.update(kw)
+    return skv.load().skv_kv_page_shuffle(a["src"], a["k"], a["v"], a["ids"], a["nb"], a["h"],
+                                          a["ps"], a["hd"], a["e"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
+    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+])
+def test_shuffle_errors(kw, code):
+    assert _shuffle(**kw) == code
+
+
+def test_python_binding_raises_on_error_status():
+    with pytest.raises(_lib.SkvError) as ei:
+        _lib._check(2, "x")
+    assert ei.value.status == 2

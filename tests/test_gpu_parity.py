@@ -1,0 +1,220 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_kv_paged_amd as skv
+from gpu_harness import TOL, compare, oracle_plan, run_hip, run_oracle, say
+from workloads import configs, gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skv.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cu(q):
+    return [0] + list(itertools.accumulate(q))
+
+
+# ---- planner: bit-exact ------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", configs.CONFIGS, ids=lambda c: c.name)
+def test_plan_bit_exact_on_configs(cfg):
+    say("plan", cfg.name)
+    meta = gen.layout_metadata(cfg)
+    sl = torch.as_tensor(meta["seq_lens"], device=DEV)
+    cu = torch.as_tensor(meta["cu"], device=DEV)
+    plan, tok = skv.plan_build(sl, cu, cfg.total_q, cfg.kv_heads, cfg.num_cus, cfg.seg_max,
+                               cfg.causal)
+    want_plan, want_tok = oracle.plan_segments(cfg.seq_lens, meta["cu"], cfg.kv_heads, 16,
+                                               cfg.num_cus, cfg.seg_max, cfg.causal)
+    assert plan.cpu().tolist() == want_plan
+    assert tok.cpu().tolist() == want_tok
+
+
+def test_plan_bit_exact_fuzz():
+    rng = np.random.default_rng(2024)
+    for trial in range(120):
+        bs = int(rng.integers(1, 301))
+        big = trial % 3 == 0
+        lens = rng.integers(0, 300_001 if big else 3000, size=bs)
+        lens[rng.random(bs) < 0.1] = 0
+        ql = rng.integers(1, 5, size=bs)
+        kvh = int(rng.choice([1, 2, 4, 8]))
+        ncu = int(rng.integers(4, 305))
+        smax = int(rng.integers(1, 65))
+        causal = int(rng.integers(0, 2))
+        sl = torch.as_tensor(lens.astype(np.int32), device=DEV)
+        cu_h = np.array(_cu(ql.tolist()), dtype=np.int32)
+        cu = torch.as_tensor(cu_h, device=DEV)
+        plan, tok = skv.plan_build(sl, cu, int(cu_h[-1]), kvh, ncu, smax, causal)
+        wp, wt = oracle.plan_segments(lens.tolist(), cu_h, kvh, 16, ncu, smax, causal)
+        assert plan.cpu().tolist() == wp, (trial, bs, kvh, ncu, smax)
+        assert tok.cpu().tolist() == wt, trial
+
+
+def test_plan_large_batch():
+    rng = np.random.default_rng(7)
+    bs = 32767
+    lens = rng.integers(0, 5000, size=bs).astype(np.int32)
+    ql = np.ones(bs, dtype=np.int64)
+    cu_h = np.array(_cu(ql.tolist()), dtype=np.int32)
+    plan, tok = skv.plan_build(torch.as_tensor(lens, device=DEV), torch.as_tensor(cu_h, device=DEV),
+                               bs, 1, 256, 64, 1)
+    wp, wt = oracle.plan_segments(lens.tolist(), cu_h, 1, 16, 256, 64, 1)
+    assert plan.cpu().tolist() == wp and tok.cpu().tolist() == wt
+
+
+# ---- page shuffle: bit-exact -------------------------------------------------
+
+@pytest.mark.parametrize("e,H,subset", [(2, 1, False), (2, 3, False), (2, 8, True),
+                                         (1, 2, False), (1, 3, True), (2, 2, True)])
+def test_shuffle_bit_exact(e, H, subset):
+    say("shuffle", e, H, subset)
+    g = torch.Generator(device=DEV).manual_seed(11 + H)
+    B = 37
+    n_el = B * H * 16 * 256
+    raw = torch.randint(0, 256, (n_el * e,), generator=g, device=DEV, dtype=torch.uint8)
+    std = raw.view(torch.int16 if e == 2 else torch.uint8).view(B, H, 16, 256)
+    if e == 2:
+        std = std.view(torch.bfloat16)
+    x = 16 // e
+    kp = torch.full((B, H, 128 // x, 16, x), 7, dtype=std.dtype, device=DEV) if e == 1 else \
+        torch.zeros((B, H, 128 // x, 16, x), dtype=std.dtype, device=DEV)
+    vp = torch.zeros((B, H, 16 // x, 128, x), dtype=std.dtype, device=DEV)
+    ids = None
+    if subset:
+        ids_h = np.random.default_rng(H).choice(B, size=11, replace=False).astype(np.int32)
+        ids = torch.as_tensor(ids_h, device=DEV)
+    before_k = (kp.view(torch.uint8) if e == 1 else kp.view(torch.int16)).cpu().numpy()
+    skv.kv_page_shuffle(std, kp, vp, block_ids=ids)
+    torch.cuda.synchronize()
+    host = (std.view(torch.int16).cpu().numpy().view(np.uint16) if e == 2
+            else std.cpu().numpy())
+    wk, wv = oracle.shuffle_blocks(host, block_ids=None if ids is None else ids_h)
+    gk = kp.view(torch.int16).cpu().numpy().view(np.uint16) if e == 2 else kp.cpu().numpy()
+    gv = vp.view(torch.int16).cpu().numpy().view(np.uint16) if e == 2 else vp.cpu().numpy()
+    listed = range(B) if ids is None else ids_h
+    for b in listed:
+        assert np.array_equal(gk[b], wk[b]) and np.array_equal(gv[b], wv[b]), b
+    if ids is not None:
+        for b in set(range(B)) - set(ids_h.tolist()):
+            assert np.array_equal(gk[b], before_k[b].view(gk.dtype)), "unlisted block written"
+
+
+# ---- attention parity on small and edge cases --------------------------------
+
+CASES = [
+    # name, seq_lens, q_lens, Hq, Hkv, dtype, layout, causal, num_cus, seg_max
+    ("tiny_std", [37, 100], [1, 1], 8, 2, "bf16", "standard", 1, 256, 64),
+    ("tiny_shuf", [37, 100], [1, 1], 8, 2, "bf16", "shuffled", 1, 256, 64),
+    ("valu8_ragged", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "standard", 1, 64, 8),
+    ("valu8_shuf", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "shuffled", 1, 64, 8),
+    ("valu_fp8_std", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "standard", 1, 40, 16),
+    ("valu_fp8_shuf", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "shuffled", 1, 40, 16),
+    ("mfma1_g16_q1", [0, 1, 5, 17, 4000, 2333], [1, 1, 1, 1, 1, 1], 32, 2, "bf16", "standard", 1, 256, 64),
+    ("mfma2_g8_q4", [1, 5, 17, 900, 3000], [4, 3, 2, 4, 1], 16, 2, "bf16", "standard", 1, 32, 64),
+    ("mfma4_g16_q4", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "bf16", "standard", 1, 64, 64),
+    ("mfma4_g16_q4_shuf", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "bf16", "shuffled", 1, 64, 64),
+    ("mfma4_noncausal", [3, 60, 2000], [4, 4, 4], 32, 2, "bf16", "standard", 0, 48, 64),
+    ("mfma_fp8_std", [1, 8, 700, 4100], [4, 1, 3, 2], 16, 2, "fp8", "standard", 1, 64, 64),
+    ("mfma_fp8_shuf", [1, 8, 700, 4100], [4, 1, 3, 2], 16, 2, "fp8", "shuffled", 1, 64, 64),
+    ("mfma_g4_q3", [33, 1000], [3, 3], 16, 4, "bf16", "standard", 1, 256, 64),
+    ("seg_max_binds", [1600, 16, 9999], [2, 4, 3], 16, 2, "bf16", "standard", 1, 512, 3),
+    ("infeasible_fallback", [100, 200, 300, 400, 500], [1, 2, 3, 4, 1], 8, 4, "bf16", "standard", 1, 8, 64),
+]
+
+
+def _mk(name, lens, ql, hq, hkv, dt, layout, causal, ncu, smax, seed=5, poison="finite"):
+    base = configs.FP8_KV if dt == "fp8" else configs.TINY
+    cfg = gen.small_config(base, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
+                           causal=causal, num_cus=ncu, seg_max=smax, seed=seed)
+    return gen.make_case(cfg, DEV, poison=poison)
+
+
+@pytest.mark.parametrize("spec", CASES, ids=lambda c: c[0])
+def test_attention_matches_oracle(spec):
+    say("attn", spec[0])
+    case = _mk(*spec)
+    hip = run_hip(case)
+    wp, wt = oracle_plan(case)
+    assert hip["plan"] == wp and hip["tok"] == wt
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, case.cfg.kv_dtype)
+    say(spec[0], r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3, r
+
+
+@pytest.mark.parametrize("spec", [CASES[2], CASES[8], CASES[12]], ids=lambda c: c[0])
+def test_nan_poison_does_not_leak(spec):
+    a = run_hip(_mk(*spec, poison="finite"))
+    b = run_hip(_mk(*spec, poison="nan"))
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.all(np.isfinite(b["out"]))
+
+
+@pytest.mark.parametrize("spec", [CASES[1], CASES[9]], ids=lambda c: c[0])
+def test_deterministic(spec):
+    case = _mk(*spec)
+    a = run_hip(case)
+    b = run_hip(case)
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_fp8_codes_decode_exactly():
+    """A one-token sequence returns its V row: every e4m3fn code (NaN codes
+    aside) must come back as its exact value (v_scale = 1)."""
+    cfg = gen.small_config(configs.FP8_KV, [1, 1], [1, 1], q_heads=2, kv_heads=1,
+                           k_scale=1.0, v_scale=1.0, seed=3)
+    case = gen.make_case(cfg, DEV)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[codes == 0x7F] = 0
+    codes[codes == 0xFF] = 0
+    table = case.page_table.cpu().numpy()
+    for i in range(2):
+        case.kv[int(table[i, 0]), 0, 0, 128:] = torch.as_tensor(codes[128 * i:128 * (i + 1)],
+                                                                 device=DEV)
+    hip = run_hip(case)
+    want = oracle.decode_e4m3fn(codes).reshape(2, 128)
+    for i in range(2):
+        for h in range(2):
+            assert np.array_equal(hip["out"][i, h], want[i]), (i, h)
+
+
+def test_split_reduce_alone():
+    rng = np.random.default_rng(3)
+    total_q, hq, smax, D = 9, 4, 7, 128
+    nseg = rng.integers(0, smax + 1, size=total_q).astype(np.int32)
+    po = rng.standard_normal((total_q, hq, smax, D)).astype(np.float32)
+    pl = (rng.standard_normal((total_q, hq, smax)) * 4).astype(np.float32)
+    out, lse = skv.split_reduce(torch.as_tensor(po.reshape(-1), device=DEV),
+                                torch.as_tensor(pl.reshape(-1), device=DEV),
+                                torch.as_tensor(nseg, device=DEV), total_q=total_q,
+                                q_heads=hq, seg_max=smax,
+                                out_lse=torch.empty(total_q * hq, device=DEV))
+    torch.cuda.synchronize()
+    out = out.float().cpu().numpy()
+    lse = lse.cpu().numpy().reshape(total_q, hq)
+    for t in range(total_q):
+        for h in range(hq):
+            k = int(nseg[t])
+            wo, wl = oracle.lse_merge(po[t, h, :k].astype(np.float64),
+                                      pl[t, h, :k].astype(np.float64), D)
+            np.testing.assert_allclose(out[t, h], wo, atol=1e-2, rtol=0)
+            if k == 0:
+                assert lse[t, h] == -np.inf and np.all(out[t, h] == 0)
+            else:
+                assert abs(lse[t, h] - wl) <= 1e-5 * max(1.0, abs(wl))
