@@ -7,152 +7,188 @@
 // sequence's query rows for that kv head over the segment's pages and writes a
 // per-segment partial; the work-group decodes (seq, seg) from the work list.
 //
-// MI355X design (one work-group per CU by construction of the plan):
-//  * 256 threads = 4 wave64s, one per SIMD (waves_per_eu 1 -> 512 VGPRs each).
-//    The segment is cut into 32-token blocks (two pages); wave w takes blocks
-//    w, w+4, ... and keeps its own online-softmax state, so the main loop has
-//    no work-group barrier. Waves merge once at the end through LDS.
-//  * Scores are computed transposed, S^T = K.Q^T, with v_mfma_f32_16x16x32_bf16:
-//    the A operand is 16 tokens x 32 channels of K (one 16-byte load per
-//    lane), the B operand 32 channels x 16 query rows of Q, held in registers
-//    for the whole segment. Two token tiles are interleaved (tile a takes
-//    tokens 8j+{0..3}, tile b 8j+{4..7} of each 8-token group j) so that the
-//    C layout leaves each lane with 8 consecutive tokens of one query row:
-//    exactly the B operand (P^T) of the P.V product, with no lane shuffles.
-//  * O^T = V^T.P^T: the A operand is 16 channels x 32 tokens of V. In the
-//    shuffled layout a 16-byte V chunk already is x tokens of one channel (a
-//    direct load); standard pages are staged through a per-wave LDS tile and
-//    read back transposed.
-//  * Online softmax in the exp2 domain with the row max/sum in registers;
-//    the block max is reduced across the four 16-lane groups with lane
-//    permutes. Masked lanes are forced to -inf; V rows of page-tail slots are
-//    zeroed so poison (even NaN) never reaches the accumulator.
+// MI355X design (the plan keeps about one work-group per CU, so one
+// work-group must keep a CU's share of HBM bandwidth in flight by itself):
+//  * KV pages stream into an LDS ring of NS stages with direct-to-LDS DMA
+//    (global_load_lds_dwordx4: 16 bytes per lane, no VGPRs held). All four
+//    waves issue the DMA of each stage, one (page, K or V half) unit at a time,
+//    so every DMA instruction reads from a single page. Up to NS-1 stages
+//    (>= 96 KB) are in flight per CU; one barrier per stage.
+//  * Wave w owns query-row tile w % NRT (16 rows) and block w / NRT of each
+//    stage, so a stage holds 4/NRT 32-token blocks and every wave has work.
+//    Q (16 rows) lives in registers; the O^T accumulator is 32 registers.
+//  * Scores are computed transposed per page, S^T = K.Q^T, with
+//    v_mfma_f32_16x16x32_bf16: the C layout leaves each lane 4 tokens of one
+//    row per page, and the two pages of a block form exactly the B operand
+//    (P^T, 8 tokens) of O^T += V^T.P^T, with no lane shuffles.
+//  * DMA lane->chunk maps are chosen for the readers: K operands are read back
+//    as contiguous 16-byte lanes; standard-layout bf16 V is read with gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16: four tokens of one channel per
+//    lane from one instruction) and stored with an XOR swizzle on the 16-byte
+//    chunk index so the rows those reads touch spread over the banks;
+//    standard fp8 V uses byte reads; shuffled-layout V already holds x tokens
+//    of one channel per 16-byte chunk (the reason that layout exists).
+//  * Online softmax in the exp2 domain with the row max/sum in registers; the
+//    block max is reduced across the four 16-lane groups with lane permutes;
+//    the accumulator is rescaled only when a row max moved. Masked lanes are
+//    forced to -inf and V of tokens past the segment end is zeroed, so stale
+//    LDS or page-tail poison (even NaN) never reaches the accumulator.
 //  * fp8 e4m3fn KV is widened to bf16 exactly before the MFMA; k_scale folds
 //    into the score scale and v_scale into the output.
-//  * The next block's K/V loads are issued before the current block is
-//    computed (register double buffering, 16 KB in flight per wave).
 #include "skv_attn_common.h"
 #include "skv.h"
 
 namespace skv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kBlockTok = 32;
 constexpr int kD = kHeadDim;
+constexpr int kRingBudget = 128 * 1024;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
-template <int E>
-struct Geo {
-  static constexpr int kStdTile = kPageSize * 2 * kD * E;   // (block, head) bytes, standard
-  static constexpr int kPlaneTile = kPageSize * kD * E;     // (block, head) bytes, one plane
-  static constexpr int kStdRow = 2 * kD * E;                 // one token row, standard
-  static constexpr int kKLoads = E == 2 ? 8 : 4;             // 16-byte K loads per lane per block
-  static constexpr int kVStdLoads = E == 2 ? 8 : 4;          // 16-byte V chunks per lane (standard)
-  static constexpr int kVRowLds = kD * E + 16;               // padded LDS row (standard V)
-};
-
-// channel base of the 8 channels a lane feeds into MFMA k-step kk (0..3)
-template <int E>
-__device__ __forceinline__ int kdim_base(int kk, int j4) {
-  if constexpr (E == 2) return 32 * kk + 8 * j4;
-  else return 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
+// waves per work-group: 8 (two per SIMD, hiding each other's latencies) when
+// the ring still holds four stages of the larger stage that implies, else 4
+template <int E, int NRT>
+constexpr int waves_for() {
+  return 2 * (2 * (8 / NRT)) * kPageSize * kD * E * 4 <= kRingBudget ? 8 : 4;
 }
 
-template <int E, bool SHUF>
-struct BlockRegs {
-  uint4 k[Geo<E>::kKLoads];
-  uint4 v[8];            // SHUF && E==2: V^T operands; standard: raw chunks (E==2: 8, E==1: 4)
-  uint2 v8[8];           // SHUF && E==1: 8 fp8 codes per operand
+template <int E, int NRT>
+struct Ring {
+  static constexpr int kWaves = waves_for<E, NRT>();
+  static constexpr int kUnitBytes = kPageSize * kD * E;          // one page's K (or V) half
+  static constexpr int kUnitInstr = kUnitBytes / 1024;            // DMA instructions per unit
+  static constexpr int kBlocks = kWaves / NRT;                    // 32-token blocks per stage
+  static constexpr int kPages = 2 * kBlocks;
+  static constexpr int kStageTok = 16 * kPages;
+  static constexpr int kStageBytes = 2 * kPages * kUnitBytes;
+  static constexpr int kUnitsPerWave = 2 * kPages / kWaves;
+  static_assert(kUnitsPerWave >= 1, "every wave issues DMA");
+  static constexpr int kInstrPerWave = kUnitsPerWave * kUnitInstr;
+  static constexpr int kNS0 = kRingBudget / kStageBytes;
+  static constexpr int kNS = kNS0 > 8 ? 8 : kNS0;
+  static_assert(kNS >= 2, "ring needs two stages");
+  static_assert((kNS - 2) * kInstrPerWave <= 63, "vmcnt range");
+  static constexpr int kStdTile = kPageSize * 2 * kD * E;        // standard (block, head)
+  static constexpr int kStdRow = 2 * kD * E;
 };
 
-template <int E, bool SHUF>
-__device__ __forceinline__ void load_block(const SegParams& p, const SegItem& it,
-                                           const int32_t* ptab, int blk, int lane,
-                                           BlockRegs<E, SHUF>& r) {
-  using Gm = Geo<E>;
-  const int r16 = lane & 15, j4 = lane >> 4;
-  const int tok0 = it.seg_start + blk * kBlockTok;        // page aligned
-  const int page0 = tok0 >> 4;
-  const bool has1 = tok0 + 16 < it.seg_end;
-  const int pid0 = ptab[page0];
-  const int pid1 = has1 ? ptab[page0 + 1] : pid0;
-  const size_t hs = static_cast<size_t>(p.Hkv);
-  const size_t head0 = static_cast<size_t>(pid0) * hs + it.g;
-  const size_t head1 = static_cast<size_t>(pid1) * hs + it.g;
-  const uint8_t* ka0 = p.kv_a + head0 * (SHUF ? Gm::kPlaneTile : Gm::kStdTile);
-  const uint8_t* ka1 = p.kv_a + head1 * (SHUF ? Gm::kPlaneTile : Gm::kStdTile);
+// s_waitcnt vmcnt(N): the DMA loads this wave issued before the last N are done
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-  // K: tile tb, token tau = 8*(r16/4) + r16%4 + 4*tb (page tau/16, slot tau%16)
+// work-group barrier that is also a compiler memory barrier, with no implied
+// wait on outstanding vector-memory loads (the DMA ring stays in flight)
+__device__ __forceinline__ void barrier_keep_loads() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_stages(int k) {
+  // wait until at most k stages' worth (k * STEP instructions) remain in flight
+  if constexpr (MAXK >= 6) { if (k >= 6) { wait_vmcnt<6 * STEP>(); return; } }
+  if constexpr (MAXK >= 5) { if (k == 5) { wait_vmcnt<5 * STEP>(); return; } }
+  if constexpr (MAXK >= 4) { if (k == 4) { wait_vmcnt<4 * STEP>(); return; } }
+  if constexpr (MAXK >= 3) { if (k == 3) { wait_vmcnt<3 * STEP>(); return; } }
+  if constexpr (MAXK >= 2) { if (k == 2) { wait_vmcnt<2 * STEP>(); return; } }
+  if constexpr (MAXK >= 1) { if (k == 1) { wait_vmcnt<1 * STEP>(); return; } }
+  wait_vmcnt<0>();
+}
+
+// 16 bytes per lane, global -> LDS at lds_base + lane * 16 (lds_base uniform).
+// Issued from inline asm so that the only waits on it are the explicit
+// per-stage vmcnt waits (the compiler would otherwise drain every in-flight
+// DMA before each LDS read).
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Issue this wave's DMA units of one stage. Unit u of the stage is (page u/2,
+// K half if u even, V half if odd); wave w issues units [w*UPW, (w+1)*UPW).
+// Pages past the segment end are read from the segment's first page (same
+// instruction count keeps vmcnt exact; their tokens are masked and zeroed).
+template <int E, bool SHUF, int NRT>
+__device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& it,
+                                            const int* pids, uint8_t* slot, int wave,
+                                            int lane) {
+  using R = Ring<E, NRT>;
+  const int r16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
-  for (int tb = 0; tb < 2; ++tb) {
-    const int tau = 8 * (r16 >> 2) + (r16 & 3) + 4 * tb;
-    const int pg = tau >> 4, slot = tau & 15;
-    const uint8_t* base = pg ? ka1 : ka0;
-    const bool ok = pg == 0 || has1;
-    constexpr int per = Gm::kKLoads / 2;
+  for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
+    const int u = wave * R::kUnitsPerWave + uw;
+    const int pg = u >> 1;
+    const bool vhalf = u & 1;
+    const size_t head = static_cast<size_t>(pids[uw]) * p.Hkv + it.g;
+    uint8_t* dst = slot + (2 * pg + (vhalf ? 1 : 0)) * R::kUnitBytes;
+    if (!vhalf) {
+      const uint8_t* tile = p.kv_a + head * (SHUF ? R::kUnitBytes : R::kStdTile);
 #pragma unroll
-    for (int u = 0; u < per; ++u) {
-      // E==2: u = kk, channels 32kk + 8j4 ; E==1: u = kk pair, channels 64u + 16j4
-      const int ch = E == 2 ? 32 * u + 8 * j4 : 64 * u + 16 * j4;
-      size_t off;
-      if constexpr (SHUF) off = (static_cast<size_t>(ch * E / 16) * kPageSize + slot) * 16;
-      else off = static_cast<size_t>(slot) * Gm::kStdRow + ch * E;
-      r.k[tb * per + u] = ok ? *reinterpret_cast<const uint4*>(base + off) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  if constexpr (SHUF) {
-    const uint8_t* vb0 = p.kv_b + head0 * Gm::kPlaneTile;
-    const uint8_t* vb1 = p.kv_b + head1 * Gm::kPlaneTile;
-    const int pg = j4 >> 1;
-    const uint8_t* vb = pg ? vb1 : vb0;
-    const bool ok = pg == 0 || has1;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + r16;
-      if constexpr (E == 2) {
-        const size_t off = (static_cast<size_t>(j4 & 1) * kD + d) * 16;
-        r.v[dt] = ok ? *reinterpret_cast<const uint4*>(vb + off) : make_uint4(0, 0, 0, 0);
-      } else {
-        const size_t off = static_cast<size_t>(d) * 16 + 8 * (j4 & 1);
-        r.v8[dt] = ok ? *reinterpret_cast<const uint2*>(vb + off) : make_uint2(0, 0);
+      for (int i = 0; i < R::kUnitInstr; ++i) {
+        // lane reads the 16 bytes compute-lane `lane` needs for k-step i
+        size_t off;
+        if constexpr (SHUF) {
+          off = (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16;
+        } else {
+          const int byte = E == 2 ? (32 * i + 8 * j4) * 2 : 64 * i + 16 * j4;
+          off = static_cast<size_t>(r16) * R::kStdRow + byte;
+        }
+        dma16(tile + off, dst + i * 1024);
       }
-    }
-  } else {
-    constexpr int cpr = kD * E / 16;                      // V chunks per token row
+    } else {
 #pragma unroll
-    for (int u = 0; u < Gm::kVStdLoads; ++u) {
-      const int ci = u * 64 + lane;
-      const int tok = ci / cpr, c = ci % cpr;
-      const int pg = tok >> 4, slot = tok & 15;
-      const uint8_t* base = pg ? ka1 : ka0;
-      const bool ok = pg == 0 || has1;
-      const size_t off = static_cast<size_t>(slot) * Gm::kStdRow + kD * E + c * 16;
-      r.v[u] = ok ? *reinterpret_cast<const uint4*>(base + off) : make_uint4(0, 0, 0, 0);
+      for (int i = 0; i < R::kUnitInstr; ++i) {
+        size_t off;
+        if constexpr (SHUF) {
+          off = static_cast<size_t>(i * 64 + lane) * 16;          // plane copied as is
+        } else {
+          // LDS row tau, position c' holds chunk c = c' ^ f(tau)
+          constexpr int kCpr = kD * E / 16;                       // chunks per V row
+          const int tau = i * (64 / kCpr) + lane / kCpr;
+          const int cp = lane % kCpr;
+          const int c = cp ^ (E == 2 ? 2 * (tau & 7) : ((tau >> 2) & 3));
+          off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
+        }
+        const uint8_t* base = SHUF ? p.kv_b + head * R::kUnitBytes
+                                   : p.kv_a + head * R::kStdTile;
+        dma16(base + off, dst + i * 1024);
+      }
     }
   }
 }
 
 template <int E, bool SHUF, int NRT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__((64 * Ring<E, NRT>::kWaves))
+__attribute__((amdgpu_waves_per_eu((Ring<E, NRT>::kWaves / 4), (Ring<E, NRT>::kWaves / 4))))
 void seg_mfma_kernel(SegParams p) {
-  using Gm = Geo<E>;
-  constexpr int kVTile = kBlockTok * Gm::kVRowLds;               // per-wave V tile
-  constexpr int kMergeSlot = 8 * NRT * 64 * 16;                  // one wave's O^T
-  constexpr int kLdsBytes = (SHUF ? 0 : kWaves * kVTile) > 2 * kMergeSlot
-                                ? kWaves * kVTile : 2 * kMergeSlot;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  __shared__ float sm_m[kWaves][16 * NRT];
-  __shared__ float sm_l[kWaves][16 * NRT];
+  using R = Ring<E, NRT>;
+  constexpr int kNS = R::kNS;
+  constexpr int kWaves = R::kWaves;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kNS * R::kStageBytes];
+  __shared__ float sm_m[kWaves][16];
+  __shared__ float sm_l[kWaves][16];
 
   const SegItem it = decode_item(p);
   if (!it.valid) return;                                          // work-group uniform
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, j4 = lane >> 4;
+  const int rt = wave % NRT, bis = wave / NRT;
   const int nrt = (it.rows + 15) >> 4;
+  const bool active = rt < nrt;                                   // wave-uniform
   const int ntok = it.seg_end - it.seg_start;
-  const int nblk = (ntok + kBlockTok - 1) / kBlockTok;
-  const int32_t* ptab = p.page_table + static_cast<size_t>(it.seq) * p.pt_stride;
+  const int nst = (ntok + R::kStageTok - 1) / R::kStageTok;
+  const int seg_page0 = it.seg_start >> 4;
+  const int seg_pages = (ntok + 15) >> 4;
+  // page ids are read through the constant address space: scalar loads, so
+  // waiting on them never waits on the vector-memory (DMA) queue
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
   float sm_scale = kScoreScaleLog2;
   float out_scale = 1.f;
   if constexpr (E == 1) {
@@ -160,256 +196,257 @@ void seg_mfma_kernel(SegParams p) {
     out_scale = p.v_scale[0];
   }
 
-  int lim[NRT];
-  bf16x8_t qb[NRT][4];
+  // page ids of this wave's units for a stage (pages past the end -> first page)
+  auto load_pids = [&](int st, int* out) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int n = 16 * rt + r16;
-    lim[rt] = row_limit(it, n, p.G, p.causal);
-    const bool ok = n < it.rows;
+    for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
+      const int pg = st * R::kPages + ((wave * R::kUnitsPerWave + uw) >> 1);
+      out[uw] = ptab[pg < seg_pages ? pg : 0];
+    }
+  };
+
+  // ---- Q rows of this wave's tile (B operand of S^T = K.Q^T) ----
+  const int n = 16 * rt + r16;
+  const int lim = row_limit(it, n, p.G, p.causal);
+  bf16x8_t qb[4];
+  {
+    const bool ok = active && n < it.rows;
     const int t = it.c0 + (ok ? n / p.G : 0);
     const int h = it.g * p.G + (ok ? n % p.G : 0);
     const uint16_t* qr = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qr + kdim_base<E>(kk, j4))
-                         : make_uint4(0, 0, 0, 0);
-      qb[rt][kk] = as_bf16x8(v);
+      const int ch = E == 2 ? 32 * kk + 8 * j4 : 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
+      qb[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qr + ch) : make_uint4(0, 0, 0, 0));
     }
+    // consume Q here, before any DMA is in flight: otherwise the compiler's
+    // wait for these loads lands inside the loop and drains the DMA ring
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qb[kk]));
   }
 
-  f32x4_t oacc[8][NRT];
-  float m[NRT], l[NRT];
+  // ---- prologue: stages 0 .. NS-2 in flight ----
+  int pid_next[R::kUnitsPerWave];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    m[rt] = -INFINITY;
-    l[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
-
-  uint8_t* vt = lds + wave * kVTile;                              // standard V tile
-  BlockRegs<E, SHUF> cur, nxt;
-  if (wave < nblk) load_block<E, SHUF>(p, it, ptab, wave, lane, cur);
-
-  for (int blk = wave; blk < nblk; blk += kWaves) {
-    if (blk + kWaves < nblk) load_block<E, SHUF>(p, it, ptab, blk + kWaves, lane, nxt);
-    const int tok0 = it.seg_start + blk * kBlockTok;
-    const bool tail = tok0 + kBlockTok > it.seg_end;
-
-    // ---- standard layout: V chunks -> LDS (tail slots zeroed) ----
-    if constexpr (!SHUF) {
-      constexpr int cpr = kD * E / 16;
-#pragma unroll
-      for (int u = 0; u < Gm::kVStdLoads; ++u) {
-        const int ci = u * 64 + lane;
-        const int tok = ci / cpr, c = ci % cpr;
-        uint4 v = cur.v[u];
-        if (tail && tok0 + tok >= it.seg_end) v = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(vt + tok * Gm::kVRowLds + c * 16) = v;
-      }
+  for (int s = 0; s < kNS - 1; ++s) {
+    if (s < nst) {
+      int pids[R::kUnitsPerWave];
+      load_pids(s, pids);
+      issue_stage<E, SHUF, NRT>(p, it, pids, ring + s * R::kStageBytes, wave, lane);
     }
+  }
+  if (kNS - 1 < nst) load_pids(kNS - 1, pid_next);
 
-    // ---- S^T = K.Q^T ----
-    f32x4_t sacc[2][NRT];
+  f32x4_t oacc[8];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+  for (int dt = 0; dt < 8; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;
+
+  for (int i = 0; i < nst; ++i) {
+    // stage i landed (own DMA), then everyone's; stage i-1 is free again
+    {
+      const int later = min(kNS - 2, nst - 1 - i);
+      wait_vmcnt_stages<R::kInstrPerWave, kNS - 2>(later);
+    }
+    barrier_keep_loads();
+    if (i + kNS - 1 < nst) {
+      issue_stage<E, SHUF, NRT>(p, it, pid_next, ring + ((i + kNS - 1) % kNS) * R::kStageBytes,
+                                wave, lane);
+      if (i + kNS < nst) load_pids(i + kNS, pid_next);
+    }
+    if (!active) continue;
+
+    const uint8_t* slot = ring + (i % kNS) * R::kStageBytes;
+    const int tok0 = it.seg_start + i * R::kStageTok + bis * 32;   // this wave's block
+    if (tok0 >= it.seg_end) continue;
+    const uint8_t* kU[2] = {slot + (2 * (2 * bis)) * R::kUnitBytes,
+                            slot + (2 * (2 * bis + 1)) * R::kUnitBytes};
+    const uint8_t* vU[2] = {kU[0] + R::kUnitBytes, kU[1] + R::kUnitBytes};
+
+    // ---- S^T per page ----
+    f32x4_t sacc[2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
       bf16x8_t kop[4];
       if constexpr (E == 2) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kop[kk] = as_bf16x8(cur.k[tb * 4 + kk]);
+        for (int kk = 0; kk < 4; ++kk)
+          kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kU[pg] + kk * 1024 + lane * 16));
       } else {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          kop[2 * u] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cur.k[tb * 2 + u].x, cur.k[tb * 2 + u].y)));
-          kop[2 * u + 1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cur.k[tb * 2 + u].z, cur.k[tb * 2 + u].w)));
+          const uint4 c = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
+          kop[2 * u] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.x, c.y)));
+          kop[2 * u + 1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.z, c.w)));
         }
       }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) {
-        if (rt < nrt) {
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[rt][kk], acc, 0, 0, 0);
-          sacc[tb][rt] = acc;
-        }
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[kk], acc, 0, 0, 0);
+      sacc[pg] = acc;
     }
 
-    // ---- online softmax; P^T operand per row tile ----
-    bf16x8_t pb[NRT];
+    // ---- online softmax (row n = 16*rt + r16; 8 tokens per lane) ----
+    float s[8];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      if (rt < nrt) {
-        float s[8];
-        float bm = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int pos = tok0 + 8 * j4 + e;
-          const float v = sacc[e >> 2][rt][e & 3] * sm_scale;
-          s[e] = pos < lim[rt] ? v : -INFINITY;
-          bm = fmaxf(bm, s[e]);
-        }
-        bm = fmaxf(bm, __shfl_xor(bm, 16));
-        bm = fmaxf(bm, __shfl_xor(bm, 32));
-        const float mn = fmaxf(m[rt], bm);
-        const float mu = mn == -INFINITY ? 0.f : mn;
-        const float alpha = fast_exp2(m[rt] - mu);
-        float ps = 0.f;
-        uint32_t pk[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
-          ps += a + b;
-          pk[e >> 1] = pack_bf16x2(a, b);
-        }
-        l[rt] = l[rt] * alpha + ps;
-        m[rt] = mn;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) oacc[dt][rt] *= alpha;
-        pb[rt] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
+      const float v = sacc[e >> 2][e & 3] * sm_scale;
+      s[e] = pos < lim ? v : -INFINITY;
+      bm = fmaxf(bm, s[e]);
     }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {     // some row max moved
+      const float alpha = fast_exp2(m - mu);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[dt] *= alpha;
+      m = mn;
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
+      l += a + b;
+      pk[e >> 1] = pack_bf16x2(a, b);
+    }
+    const bf16x8_t pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
-    // ---- O^T += V^T.P^T ----
+    // ---- O^T += V^T.P^T ; element e: page e/4, token 4*j4 + e%4 ----
+    const bool tail = tok0 + 32 > it.seg_end;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
-      uint4 vw;
+      const int d = 16 * dt + r16;
+      uint32_t w[4];
       if constexpr (SHUF && E == 2) {
-        vw = cur.v[dt];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const uint2 v = *reinterpret_cast<const uint2*>(
+              vU[pg] + ((j4 >> 1) * kD + d) * 16 + (j4 & 1) * 8);
+          w[2 * pg] = v.x;
+          w[2 * pg + 1] = v.y;
+        }
       } else if constexpr (SHUF) {
-        vw = fp8x8_to_bf16x8(cur.v8[dt]);
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4);
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4);
+        const uint4 c = fp8x8_to_bf16x8(make_uint2(a, b));
+        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
       } else if constexpr (E == 2) {
-        const uint8_t* col = vt + (8 * j4) * Gm::kVRowLds + (16 * dt + r16) * 2;
-        uint32_t w[4];
+        // transposing LDS read: in each 16-lane group, lane i receives element
+        // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
+        // token 4*j4 + j/4, channels 16dt + 4(j%4) .. +3, so lane i ends up
+        // with tokens 4*j4 .. 4*j4+3 of channel 16dt + i.
+        const int tau = 4 * j4 + (r16 >> 2);
+        const int cp = (2 * dt + ((r16 >> 1) & 1)) ^ (2 * (tau & 7));
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4i16_t*)(
+                  (__attribute__((address_space(3))) uint8_t*)(vU[pg]) +
+                  tau * (kD * 2) + cp * 16 + (r16 & 1) * 8));
+          const uint2 u = __builtin_bit_cast(uint2, v);
+          w[2 * pg] = u.x;
+          w[2 * pg + 1] = u.y;
+        }
+      } else {
+        const int cp = dt ^ j4;
+        uint32_t x[2];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg) {
+          const uint8_t* col = vU[pg] + (4 * j4) * kD + cp * 16 + r16;
+          uint32_t v = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) v |= static_cast<uint32_t>(col[b * kD]) << (8 * b);
+          x[pg] = v;
+        }
+        const uint4 c = fp8x8_to_bf16x8(make_uint2(x[0], x[1]));
+        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+      }
+      if (tail) {                    // zero V of tokens past the segment end
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(col + (2 * q2) * Gm::kVRowLds);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(col + (2 * q2 + 1) * Gm::kVRowLds);
-          w[q2] = lo | (hi << 16);
-        }
-        vw = make_uint4(w[0], w[1], w[2], w[3]);
-      } else {
-        const uint8_t* col = vt + (8 * j4) * Gm::kVRowLds + 16 * dt + r16;
-        uint32_t w[2];
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-          uint32_t x = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            x |= static_cast<uint32_t>(col[(4 * q2 + b) * Gm::kVRowLds]) << (8 * b);
-          w[q2] = x;
-        }
-        vw = fp8x8_to_bf16x8(make_uint2(w[0], w[1]));
-      }
-      if constexpr (SHUF) {
-        if (tail) {                      // zero V of tokens past the segment end
-          uint32_t w[4] = {vw.x, vw.y, vw.z, vw.w};
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            const int pos = tok0 + 8 * j4 + 2 * q2;
-            if (pos >= it.seg_end) w[q2] = 0;
-            else if (pos + 1 >= it.seg_end) w[q2] &= 0xffffu;
-          }
-          vw = make_uint4(w[0], w[1], w[2], w[3]);
+          const int pos = tok0 + 16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1);
+          if (pos >= it.seg_end) w[q2] = 0;
+          else if (pos + 1 >= it.seg_end) w[q2] &= 0xffffu;
         }
       }
-      const bf16x8_t vop = as_bf16x8(vw);
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
-        if (rt < nrt)
-          oacc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[rt], oacc[dt][rt], 0, 0, 0);
+      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, oacc[dt], 0, 0, 0);
     }
-    cur = nxt;
   }
 
-  // ---- merge the four waves ----
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    l[rt] += __shfl_xor(l[rt], 16);
-    l[rt] += __shfl_xor(l[rt], 32);
-  }
-  __syncthreads();                       // V tiles are dead; LDS is reused below
-  if (j4 == 0) {
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-      sm_m[wave][16 * rt + r16] = m[rt];
-      sm_l[wave][16 * rt + r16] = l[rt];
+  // ---- row sums across the four lane groups ----
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+
+  constexpr int kShare = kWaves / NRT;          // waves sharing a row tile
+  float M = m, Ls = l;
+  if constexpr (kShare > 1) {
+    wait_vmcnt<0>();
+    __syncthreads();                            // ring is dead; reuse it
+    f32x4_t* oslot = reinterpret_cast<f32x4_t*>(ring);
+    if (j4 == 0) {
+      sm_m[wave][r16] = m;
+      sm_l[wave][r16] = l;
     }
-  }
-  __syncthreads();
-  float Lsum[NRT], Mrow[NRT];
+    if (bis > 0) {
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int row = 16 * rt + r16;
-    float M = -INFINITY;
+      for (int dt = 0; dt < 8; ++dt) oslot[(wave * 8 + dt) * 64 + lane] = oacc[dt];
+    }
+    __syncthreads();
+    if (bis > 0 || !active) return;
+    M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][row]);
+    for (int b = 0; b < kShare; ++b) M = fmaxf(M, sm_m[rt + NRT * b][r16]);
     const float mu = M == -INFINITY ? 0.f : M;
-    float Ls = 0.f;
+    const float f0 = fast_exp2(m - mu);
+    Ls = l * f0;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) Ls += sm_l[w][row] * fast_exp2(sm_m[w][row] - mu);
-    Lsum[rt] = Ls;
-    Mrow[rt] = mu;
-    const float f = fast_exp2(m[rt] - mu);
+    for (int dt = 0; dt < 8; ++dt) oacc[dt] *= f0;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oacc[dt][rt] *= f;
-  }
-  f32x4_t* slot = reinterpret_cast<f32x4_t*>(lds);
-  auto slot_at = [&](int s, int dt, int rt) -> f32x4_t& {
-    return slot[((s * 8 + dt) * NRT + rt) * 64 + lane];
-  };
-  if (wave >= 2) {
+    for (int b = 1; b < kShare; ++b) {
+      const int w2 = rt + NRT * b;
+      const float f = fast_exp2(sm_m[w2][r16] - mu);
+      Ls += sm_l[w2][r16] * f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) slot_at(wave - 2, dt, rt) = oacc[dt][rt];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) oacc[dt][rt] += slot_at(wave, dt, rt);
-  }
-  __syncthreads();
-  if (wave == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) slot_at(0, dt, rt) = oacc[dt][rt];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    const int n = 16 * rt + r16;
-    if (n >= it.rows) continue;
-    const int t = it.c0 + n / p.G;
-    const int h = it.g * p.G + n % p.G;
-    const size_t prow = (static_cast<size_t>(t) * p.Hq + h) * p.seg_max + it.seg;
-    const bool any = Lsum[rt] > 0.f;
-    const float inv = any ? out_scale / Lsum[rt] : 0.f;
-    float* po = p.part_o + prow * kD;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      f32x4_t o = (oacc[dt][rt] + slot_at(0, dt, rt)) * inv;
-      *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * j4) = o;
+      for (int dt = 0; dt < 8; ++dt) oacc[dt] += oslot[(w2 * 8 + dt) * 64 + lane] * f;
     }
-    if (j4 == 0)
-      p.part_lse[prow] = any ? (Mrow[rt] + fast_log2(Lsum[rt])) * kLn2 : -INFINITY;
+    M = mu;
+  } else {
+    if (!active) return;
+    M = m == -INFINITY ? 0.f : m;
   }
+
+  // ---- write this row tile's partial ----
+  if (n >= it.rows) return;
+  const int t = it.c0 + n / p.G;
+  const int h = it.g * p.G + n % p.G;
+  const size_t prow = (static_cast<size_t>(t) * p.Hq + h) * p.seg_max + it.seg;
+  const bool any = Ls > 0.f;
+  const float inv = any ? out_scale / Ls : 0.f;
+  float* po = p.part_o + prow * kD;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<f32x4_t*>(po + 16 * dt + 4 * j4) = oacc[dt] * inv;
+  if (j4 == 0) p.part_lse[prow] = any ? (M + fast_log2(Ls)) * kLn2 : -INFINITY;
 }
 
 template <int E, bool SHUF>
 int launch_mfma_e(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   if (nrt <= 1)
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 1>), dim3(grid), dim3(kThreads), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 1>), dim3(grid),
+                       dim3(64 * Ring<E, 1>::kWaves), 0, st, sp);
   else if (nrt <= 2)
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 2>), dim3(grid), dim3(kThreads), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 2>), dim3(grid),
+                       dim3(64 * Ring<E, 2>::kWaves), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 4>), dim3(grid), dim3(kThreads), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 4>), dim3(grid),
+                       dim3(64 * Ring<E, 4>::kWaves), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
