@@ -53,13 +53,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// four OCP e4m3fn codes -> four bf16 (exact: 3 mantissa bits, 2^-9..448)
+// four OCP e4m3fn codes -> four bf16, two codes per v_cvt_scalef32_pk_bf16_fp8
+// (scale 1; exact: 3 mantissa bits, 2^-9..448; word select 0 = bytes 0,1)
 __device__ __forceinline__ uint2 fp8x4_to_bf16x4(uint32_t w) {
-  const f32x2_t lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
-  const f32x2_t hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
-  return make_uint2(
-      __builtin_amdgcn_perm(__float_as_uint(lo[1]), __float_as_uint(lo[0]), 0x07060302u),
-      __builtin_amdgcn_perm(__float_as_uint(hi[1]), __float_as_uint(hi[0]), 0x07060302u));
+  const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 w) {

@@ -26,8 +26,9 @@
 //    transposing LDS read (ds_read_b64_tr_b16: four tokens of one channel per
 //    lane from one instruction) and stored with an XOR swizzle on the 16-byte
 //    chunk index so the rows those reads touch spread over the banks;
-//    standard fp8 V uses byte reads; shuffled-layout V already holds x tokens
-//    of one channel per 16-byte chunk (the reason that layout exists).
+//    standard fp8 V likewise with ds_read_b64_tr_b8 (eight tokens of one
+//    channel per lane); shuffled-layout V already holds x tokens of one
+//    channel per 16-byte chunk (the reason that layout exists).
 //  * Online softmax in the exp2 domain with the row max/sum in registers; the
 //    block max is reduced across the four 16-lane groups with lane permutes;
 //    the accumulator is rescaled only when a row max moved. Masked lanes are
@@ -44,6 +45,7 @@ namespace {
 constexpr int kD = kHeadDim;
 constexpr int kRingBudget = 128 * 1024;
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
 // waves per work-group: 8 (two per SIMD, hiding each other's latencies) when
 // the ring still holds four stages of the larger stage that implies, else 4
@@ -150,7 +152,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
           constexpr int kCpr = kD * E / 16;                       // chunks per V row
           const int tau = i * (64 / kCpr) + lane / kCpr;
           const int cp = lane % kCpr;
-          const int c = cp ^ (E == 2 ? 2 * (tau & 7) : ((tau >> 2) & 3));
+          const int c = cp ^ (E == 2 ? 2 * (tau & 7) : ((tau >> 1) & 7));
           off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
         }
         const uint8_t* base = SHUF ? p.kv_b + head * R::kUnitBytes
@@ -354,17 +356,17 @@ void seg_mfma_kernel(SegParams p) {
           w[2 * pg + 1] = u.y;
         }
       } else {
-        const int cp = dt ^ j4;
-        uint32_t x[2];
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-          const uint8_t* col = vU[pg] + (4 * j4) * kD + cp * 16 + r16;
-          uint32_t v = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) v |= static_cast<uint32_t>(col[b * kD]) << (8 * b);
-          x[pg] = v;
-        }
-        const uint4 c = fp8x8_to_bf16x8(make_uint2(x[0], x[1]));
+        // transposing byte read: in each 16-lane group, lane i receives byte
+        // i%8 of the 8 bytes read by lane 2k + i/8 (k = 0..7). Lane j reads
+        // page j/8, token 4*j4 + (j/2)%4, channels 16dt + 8(j%2) .. +7, so lane
+        // i ends up with the block's 8 tokens of channel 16dt + i.
+        const int tau = 4 * j4 + ((r16 >> 1) & 3);
+        const int cp = dt ^ ((tau >> 1) & 7);
+        const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32_t*)(
+                (__attribute__((address_space(3))) uint8_t*)(vU[r16 >> 3]) +
+                tau * kD + cp * 16 + (r16 & 1) * 8));
+        const uint4 c = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
         w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
       }
       if (tail) {                    // zero V of tokens past the segment end
