@@ -22,13 +22,12 @@
 //    row per page, and the two pages of a block form exactly the B operand
 //    (P^T, 8 tokens) of O^T += V^T.P^T, with no lane shuffles.
 //  * DMA lane->chunk maps are chosen for the readers: K operands are read back
-//    as contiguous 16-byte lanes; standard-layout bf16 V is read with gfx950's
-//    transposing LDS read (ds_read_b64_tr_b16: four tokens of one channel per
-//    lane from one instruction) and stored with an XOR swizzle on the 16-byte
-//    chunk index so the rows those reads touch spread over the banks;
-//    standard fp8 V likewise with ds_read_b64_tr_b8 (eight tokens of one
-//    channel per lane); shuffled-layout V already holds x tokens of one
-//    channel per 16-byte chunk (the reason that layout exists).
+//    as contiguous 16-byte lanes; standard-layout V is stored chunk-major
+//    ([channel chunk][token]) and read with gfx950's transposing LDS reads
+//    (ds_read_b64_tr_b16 / _tr_b8: four or eight tokens of one channel per
+//    lane from one instruction, 512 contiguous bytes per wave, a constant
+//    offset per channel tile); shuffled-layout V already holds x tokens of
+//    one channel per 16-byte chunk (the reason that layout exists).
 //  * Online softmax in the exp2 domain with the row max/sum in registers; the
 //    block max is reduced across the four 16-lane groups with lane permutes;
 //    the accumulator is rescaled only when a row max moved. Masked lanes are
@@ -43,7 +42,7 @@ namespace skv {
 namespace {
 
 constexpr int kD = kHeadDim;
-constexpr int kRingBudget = 128 * 1024;
+constexpr int kRingBudget = 128 * 1024;   // measured faster than the full 160 KB
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
@@ -148,11 +147,17 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
         if constexpr (SHUF) {
           off = static_cast<size_t>(i * 64 + lane) * 16;          // plane copied as is
         } else {
-          // LDS row tau, position c' holds chunk c = c' ^ f(tau)
-          constexpr int kCpr = kD * E / 16;                       // chunks per V row
-          const int tau = i * (64 / kCpr) + lane / kCpr;
-          const int cp = lane % kCpr;
-          const int c = cp ^ (E == 2 ? 2 * (tau & 7) : ((tau >> 1) & 7));
+          // chunk-major tile: bf16 [chunk pair u][token tau][32 B], fp8
+          // [chunk c][token tau][16 B]; instruction i covers 1 KB of it
+          int tau, c;
+          if constexpr (E == 2) {
+            const int u = 2 * i + (lane >> 5);
+            tau = (lane >> 1) & 15;
+            c = 2 * u + (lane & 1);
+          } else {
+            c = 4 * i + (lane >> 4);
+            tau = lane & 15;
+          }
           off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
         }
         const uint8_t* base = SHUF ? p.kv_b + head * R::kUnitBytes
@@ -170,9 +175,13 @@ void seg_mfma_kernel(SegParams p) {
   using R = Ring<E, NRT>;
   constexpr int kNS = R::kNS;
   constexpr int kWaves = R::kWaves;
+  // the ring is the kernel's only LDS; after the loop it is reused for the
+  // cross-wave merge (per-wave O^T tiles, then row max and sum)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kNS * R::kStageBytes];
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
+  static_assert(kWaves * 8 * 64 * 16 + 2 * kWaves * 16 * 4 <= kNS * R::kStageBytes,
+                "merge scratch fits in the ring");
+  float(*sm_m)[16] = reinterpret_cast<float(*)[16]>(ring + kWaves * 8 * 64 * 16);
+  float(*sm_l)[16] = reinterpret_cast<float(*)[16]>(ring + kWaves * 8 * 64 * 16 + kWaves * 16 * 4);
 
   const SegItem it = decode_item(p);
   if (!it.valid) return;                                          // work-group uniform
@@ -321,6 +330,11 @@ void seg_mfma_kernel(SegParams p) {
 
     // ---- O^T += V^T.P^T ; element e: page e/4, token 4*j4 + e%4 ----
     const bool tail = tok0 + 32 > it.seg_end;
+    const int vend = it.seg_end - tok0;       // tokens of the block before the end
+    // per-lane part of the transposing-read address in the chunk-major V tile
+    const int vtr_off = E == 2 ? (4 * j4 + (r16 >> 2)) * 32 + ((r16 >> 1) & 1) * 16 + (r16 & 1) * 8
+                               : (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;
+    const uint8_t* vU8 = vU[r16 >> 3];        // fp8: lanes 0-7 of a group read page 0
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + r16;
@@ -341,16 +355,14 @@ void seg_mfma_kernel(SegParams p) {
       } else if constexpr (E == 2) {
         // transposing LDS read: in each 16-lane group, lane i receives element
         // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
-        // token 4*j4 + j/4, channels 16dt + 4(j%4) .. +3, so lane i ends up
-        // with tokens 4*j4 .. 4*j4+3 of channel 16dt + i.
-        const int tau = 4 * j4 + (r16 >> 2);
-        const int cp = (2 * dt + ((r16 >> 1) & 1)) ^ (2 * (tau & 7));
+        // token 4*j4 + j/4, channels 16dt + 4(j%4) .. +3 (chunk pair dt of the
+        // chunk-major tile), so lane i ends up with tokens 4*j4 .. 4*j4+3 of
+        // channel 16dt + i. The 64 lanes cover 512 contiguous bytes.
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
           const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16_t*)(
-                  (__attribute__((address_space(3))) uint8_t*)(vU[pg]) +
-                  tau * (kD * 2) + cp * 16 + (r16 & 1) * 8));
+                  (__attribute__((address_space(3))) uint8_t*)(vU[pg]) + vtr_off + dt * 512));
           const uint2 u = __builtin_bit_cast(uint2, v);
           w[2 * pg] = u.x;
           w[2 * pg + 1] = u.y;
@@ -360,21 +372,17 @@ void seg_mfma_kernel(SegParams p) {
         // i%8 of the 8 bytes read by lane 2k + i/8 (k = 0..7). Lane j reads
         // page j/8, token 4*j4 + (j/2)%4, channels 16dt + 8(j%2) .. +7, so lane
         // i ends up with the block's 8 tokens of channel 16dt + i.
-        const int tau = 4 * j4 + ((r16 >> 1) & 3);
-        const int cp = dt ^ ((tau >> 1) & 7);
         const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) v2i32_t*)(
-                (__attribute__((address_space(3))) uint8_t*)(vU[r16 >> 3]) +
-                tau * kD + cp * 16 + (r16 & 1) * 8));
+                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256));
         const uint4 c = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
         w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
       }
       if (tail) {                    // zero V of tokens past the segment end
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) {
-          const int pos = tok0 + 16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1);
-          if (pos >= it.seg_end) w[q2] = 0;
-          else if (pos + 1 >= it.seg_end) w[q2] &= 0xffffu;
+          const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
+          w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
         }
       }
       oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

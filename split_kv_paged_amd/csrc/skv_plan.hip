@@ -8,11 +8,16 @@
 // padded with -1, is written with a per-query-token segment count.
 //
 // MI355X design: one 1024-thread work-group; integer math only. Feasibility is
-// monotone in T (every per-sequence count ceil(n/T) is non-increasing), so a
-// binary search over [1, max pages] returns the same T as a linear scan in
-// O(log) block-wide reductions. The work list is emitted with a block-wide
-// exclusive scan over per-sequence segment counts. Nothing depends on device
-// data for the launch shape, so the launch is graph-capture safe.
+// monotone in T (every per-sequence count ceil(n/T) is non-increasing), so the
+// smallest feasible T is found by search between exact bounds (below):
+//  * small batches (bs <= 32): a 1024-ary search — each thread tests one
+//    candidate T against all page counts (cached in LDS), the smallest
+//    feasible candidate bounds the next pass (a few passes for any length);
+//  * large batches: a binary search whose feasibility test is a block-wide
+//    reduction over the sequences.
+// The work list is written after a block-wide exclusive scan (wave scans
+// plus one pass over the wave totals). The launch shape never depends on
+// device data, so the launch is graph-capture safe.
 #include <hip/hip_runtime.h>
 
 #include "skv.h"
@@ -23,6 +28,7 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kWaves = kPlanThreads / 64;
+constexpr int kSmallBs = 32;         // candidate search up to this batch size
 
 __device__ __forceinline__ int pages_of(int L) {
   // ceil(L / 16) without forming L + 15 (L may be close to INT_MAX)
@@ -54,48 +60,133 @@ __device__ void block_sum_max(long long& s, int& m, long long* red_s, int* red_m
   }
 }
 
+// Block-wide exclusive scan of one int per thread; also returns the total.
+__device__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(incl, off);
+    if (lane >= off) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = wave_tot[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  return before + incl - v;
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
     int bs, int kv_heads, int num_cus, int seg_max, int causal,
     int32_t* __restrict__ plan, int32_t* __restrict__ tok_nseg) {
   __shared__ long long red_s[kWaves];
   __shared__ int red_m[kWaves];
-  __shared__ int scan[kPlanThreads];
+  __shared__ int wave_tot[kWaves];
+  __shared__ int pages_lds[kSmallBs];
+  __shared__ int pass_best;
 
   const int tid = threadIdx.x;
   const int cap = num_cus / kv_heads;
   const int width = cap > bs ? cap : bs;
 
-  // longest sequence in pages
-  long long dummy = 0;
-  int mx = 0;
-  for (int i = tid; i < bs; i += kPlanThreads) mx = max(mx, pages_of(seq_lens[i]));
-  block_sum_max(dummy, mx, red_s, red_m);
+  // longest sequence, total pages and non-empty sequences
+  long long tot = 0;
+  int mx = 0, nonempty = 0;
+  for (int i = tid; i < bs; i += kPlanThreads) {
+    const int n = pages_of(seq_lens[i]);
+    if (bs <= kSmallBs) pages_lds[i] = n;
+    mx = max(mx, n);
+    tot += n;
+    nonempty += n > 0;
+  }
+  block_sum_max(tot, mx, red_s, red_m);         // also publishes pages_lds
+  {
+    long long ne = nonempty;
+    int unused = 0;
+    block_sum_max(ne, unused, red_s, red_m);
+    nonempty = static_cast<int>(ne);
+  }
   const int upper = mx > 1 ? mx : 1;
 
-  // feasible(T): sum_i ceil(n_i/T) <= cap and max_i ceil(n_i/T) <= seg_max
-  auto feasible = [&](int T) {
-    long long s = 0;
-    int m = 0;
-    for (int i = tid; i < bs; i += kPlanThreads) {
-      const int c = ceil_div_pos(pages_of(seq_lens[i]), T);
-      s += c;
-      m = max(m, c);
-    }
-    block_sum_max(s, m, red_s, red_m);
-    return s <= cap && m <= seg_max;
-  };
-
+  // Bounds on the answer. Necessary: sum ceil(n/T) >= sum n / T, so
+  // T >= ceil(tot / cap); max ceil(n/T) <= seg_max iff T >= ceil(mx / seg_max).
+  // Sufficient (k = non-empty sequences < cap): sum ceil(n/T) <= tot/T + k, so
+  // T_ub = max(ceil(tot / (cap - k)), ceil(mx / seg_max)) is feasible. Some T
+  // is feasible iff k <= cap (T = upper gives k segments of one each).
   int T;
-  if (!feasible(upper)) {
-    T = upper;                           // one segment per non-empty sequence
+  if (nonempty > cap) {
+    T = upper;                                  // one segment per non-empty sequence
   } else {
-    int lo = 1, hi = upper;              // invariant: feasible(hi)
-    while (lo < hi) {
-      const int mid = lo + ((hi - lo) >> 1);
-      if (feasible(mid)) hi = mid; else lo = mid + 1;
+    const long long need_sm = (static_cast<long long>(mx) + seg_max - 1) / seg_max;
+    long long lo0 = cap > 0 ? (tot + cap - 1) / cap : 1;
+    lo0 = lo0 > need_sm ? lo0 : need_sm;
+    lo0 = lo0 < 1 ? 1 : lo0;
+    long long hi0 = upper;
+    if (nonempty < cap) {
+      long long ub = (tot + (cap - nonempty) - 1) / (cap - nonempty);
+      ub = ub > need_sm ? ub : need_sm;
+      ub = ub < 1 ? 1 : ub;
+      hi0 = ub < hi0 ? ub : hi0;
     }
-    T = hi;
+    if (lo0 > hi0) lo0 = hi0;                   // cannot happen; keeps the search sane
+    int lo = static_cast<int>(lo0), hi = static_cast<int>(hi0);   // hi feasible, lo-1 not
+    if (bs <= kSmallBs) {
+      // 1024-ary search: each thread tests one candidate against all page counts
+      auto feasible_local = [&](int t) {
+        long long sum = 0;
+        int m = 0;
+        for (int i = 0; i < bs; ++i) {
+          const int c = ceil_div_pos(pages_lds[i], t);
+          sum += c;
+          m = max(m, c);
+        }
+        return sum <= cap && m <= seg_max;
+      };
+      while (true) {
+        if (lo >= hi) { T = hi; break; }
+        const long long span = static_cast<long long>(hi) - lo + 1;
+        const int step = static_cast<int>((span + kPlanThreads - 1) / kPlanThreads);
+        const long long cand = static_cast<long long>(lo) + static_cast<long long>(tid) * step;
+        if (tid == 0) pass_best = 0x7fffffff;
+        __syncthreads();
+        if (cand <= hi && feasible_local(static_cast<int>(cand))) atomicMin(&pass_best, tid);
+        __syncthreads();
+        const int best = pass_best;
+        __syncthreads();
+        if (best == 0x7fffffff) {     // answer lies after the last candidate tested
+          const int kmax = min(kPlanThreads - 1, static_cast<int>((hi - lo) / step));
+          lo = lo + kmax * step + 1;
+          continue;
+        }
+        const int tb = lo + best * step;
+        if (best == 0 || step == 1) { T = tb; break; }
+        lo = lo + (best - 1) * step + 1;
+        hi = tb;
+      }
+    } else {
+      auto feasible = [&](int t) {
+        long long sum = 0;
+        int m = 0;
+        for (int i = tid; i < bs; i += kPlanThreads) {
+          const int c = ceil_div_pos(pages_of(seq_lens[i]), t);
+          sum += c;
+          m = max(m, c);
+        }
+        block_sum_max(sum, m, red_s, red_m);
+        return sum <= cap && m <= seg_max;
+      };
+      while (lo < hi) {
+        const int mid = lo + ((hi - lo) >> 1);
+        if (feasible(mid)) hi = mid; else lo = mid + 1;
+      }
+      T = hi;
+    }
   }
 
   // exclusive scan of segment counts over contiguous per-thread chunks
@@ -103,16 +194,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   const int i0 = min(bs, tid * chunk), i1 = min(bs, i0 + chunk);
   int local = 0;
   for (int i = i0; i < i1; ++i) local += ceil_div_pos(pages_of(seq_lens[i]), T);
-  scan[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kPlanThreads; off <<= 1) {
-    const int v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  const int total = scan[kPlanThreads - 1];
-  int pos = scan[tid] - local;
+  int total;
+  int pos = block_exclusive_scan(local, wave_tot, total);
   for (int i = i0; i < i1; ++i) {
     const int ns = ceil_div_pos(pages_of(seq_lens[i]), T);
     for (int s = 0; s < ns; ++s) plan[1 + pos + s] = (i << 16) | s;

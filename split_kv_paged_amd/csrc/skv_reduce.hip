@@ -66,6 +66,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
       sum += v;
     }
     lse = M + logf(sum);
+#pragma unroll 4
     for (int s = 0; s < nseg; ++s) {
       const float w = expf(lse_p[s] - lse);
       const float2 o = reinterpret_cast<const float2*>(o_p + s * kHeadDim)[lane];
