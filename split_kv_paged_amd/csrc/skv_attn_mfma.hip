@@ -228,12 +228,15 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ch = E == 2 ? 32 * kk + 8 * j4 : 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
-      qb[kk] = as_bf16x8(ok ? *reinterpret_cast<const uint4*>(qr + ch) : make_uint4(0, 0, 0, 0));
+      qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + ch));   // padding rows read row 0
     }
     // consume Q here, before any DMA is in flight: otherwise the compiler's
     // wait for these loads lands inside the loop and drains the DMA ring
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) asm volatile("" : "+v"(qb[kk]));
+    for (int kk = 0; kk < 4; ++kk) {
+      asm volatile("" : "+v"(qb[kk]));
+      if (!ok) qb[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
   }
 
   // ---- prologue: stages 0 .. NS-2 in flight ----

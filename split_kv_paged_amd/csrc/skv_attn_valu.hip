@@ -8,23 +8,29 @@
 // list and leaves on -1.
 //
 // MI355X design:
-//  * 256 threads = 4 wave64s, one per SIMD; the segment is cut into blocks of
-//    four pages (two at 8 rows, to bound registers) handed to the waves
-//    round-robin; each wave keeps its
-//    own online-softmax state and the waves merge once through LDS.
-//  * q.k: four lanes per token (a quad), each owning 32 of the 128 channels;
-//    the quad's 16-byte loads cover a token's K row contiguously. Products use
-//    v_dot2_f32_bf16 on bf16 pairs; the quad sum is two DPP quad permutes.
-//  * Row max: DPP row rotations within 16 lanes, then two lane permutes.
-//  * p.V, standard pages: lane (token phase, 8-channel chunk) loads 16-byte V
-//    row chunks (coalesced) and accumulates in fp32; p comes from a per-wave LDS
-//    buffer. Shuffled pages: a 16-byte V chunk is x tokens of one channel, so a
-//    lane owns two channels and takes v_dot2 over token pairs with bf16 p.
-//  * fp8 e4m3fn codes are widened exactly to bf16/fp32 (v_cvt_pk_f32_fp8);
-//    k_scale folds into the score scale and v_scale into the output.
-//  * Tail V rows are zeroed and masked scores forced to -inf, so poison in page
-//    tails never reaches the result. Next-block loads are issued before the
-//    current block is computed.
+//  * 4 wave64s; wave w takes pages w, w+4, ... of the segment and computes all
+//    query rows of each, so no wave needs another's data: each wave streams
+//    its pages through a private LDS ring of NS pages with direct-to-LDS DMA
+//    (global_load_lds_dwordx4, issued from inline asm) and waits only on its
+//    own vmcnt — there is no barrier in the main loop. Page ids are read
+//    through the constant address space (scalar loads), so waiting on them
+//    never drains the DMA queue.
+//  * LDS tiles are laid out for the readers: K chunk-major ([16-byte chunk]
+//    [token]) so a quad of lanes per token reads its 16-byte chunks
+//    conflict-free; standard V row-major (one token's channel chunks per
+//    lane group); shuffled V as the plane itself (x tokens of one channel per
+//    16-byte chunk).
+//  * q.k: four lanes per token (a quad), each owning 32 of the 128 channels,
+//    v_dot2_f32_bf16 on bf16 pairs, the quad sum by two DPP quad permutes.
+//    Row max: DPP row rotations within 16 lanes, then two lane permutes.
+//  * p.V, standard pages: lane (token phase, channel chunk) accumulates in
+//    fp32 with p from a per-wave LDS buffer; shuffled pages: a lane owns two
+//    channels and takes v_dot2 over token pairs with bf16 p.
+//  * fp8 e4m3fn codes are widened exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8)
+//    or fp32 (v_cvt_pk_f32_fp8); k_scale folds into the score scale and
+//    v_scale into the output.
+//  * Masked scores are forced to -inf and V of tokens past the segment end is
+//    zeroed, so page-tail poison (even NaN) never reaches the accumulator.
 #include "skv_attn_common.h"
 #include "skv.h"
 
@@ -34,94 +40,71 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kD = kHeadDim;
+constexpr int kRingPerWave = 32 * 1024;
 
-// NS pages (16-token steps) per block; E element bytes
-template <int E, int NS>
-struct VGeo {
-  static constexpr int kBlockTok = 16 * NS;
+template <int E>
+struct VRing {
+  static constexpr int kHalf = kPageSize * kD * E;            // a page's K (or V) half
+  static constexpr int kPage = 2 * kHalf;
+  static constexpr int kNS = kRingPerWave / kPage;             // pages in a wave's ring
+  static constexpr int kInstrPerPage = kPage / 1024;           // DMA instructions per page
+  static_assert((kNS - 2) * kInstrPerPage <= 63, "vmcnt range");
   static constexpr int kStdTile = kPageSize * 2 * kD * E;
-  static constexpr int kPlaneTile = kPageSize * kD * E;
   static constexpr int kStdRow = 2 * kD * E;
-  static constexpr int kKLoadsPerStep = E == 2 ? 4 : 2;      // 16-byte K loads per token quarter
-  static constexpr int kKLoads = NS * kKLoadsPerStep;        // per block
-  static constexpr int kVLoads = (E == 2 ? 4 : 2) * NS;      // 16-byte V loads per block
 };
 
-template <int E, int NS>
-struct VRegs {
-  uint4 k[VGeo<E, NS>::kKLoads];
-  uint4 v[VGeo<E, NS>::kVLoads];
-};
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-template <int E, bool SHUF, int NS>
-__device__ __forceinline__ void vload_block(const SegParams& p, const SegItem& it,
-                                            const int32_t* ptab, int blk, int lane,
-                                            VRegs<E, NS>& r) {
-  using Gm = VGeo<E, NS>;
-  const int tok0 = it.seg_start + blk * Gm::kBlockTok;
-  const int page0 = tok0 >> 4;
-  const uint8_t* ktile[NS];
-  const uint8_t* vtile[NS];
-  bool ok[NS];
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_pages(int k) {
+  if constexpr (MAXK >= 6) { if (k >= 6) { wait_vmcnt<6 * STEP>(); return; } }
+  if constexpr (MAXK >= 5) { if (k == 5) { wait_vmcnt<5 * STEP>(); return; } }
+  if constexpr (MAXK >= 4) { if (k == 4) { wait_vmcnt<4 * STEP>(); return; } }
+  if constexpr (MAXK >= 3) { if (k == 3) { wait_vmcnt<3 * STEP>(); return; } }
+  if constexpr (MAXK >= 2) { if (k == 2) { wait_vmcnt<2 * STEP>(); return; } }
+  if constexpr (MAXK >= 1) { if (k == 1) { wait_vmcnt<1 * STEP>(); return; } }
+  wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// One page (this wave's) into its ring slot: K half chunk-major
+// [c][token][16 B]; V half row-major [token][channels] (standard) or the
+// plane as is (shuffled).
+template <int E, bool SHUF>
+__device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it, int pid,
+                                           uint8_t* slot, int lane) {
+  using R = VRing<E>;
+  const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
+  const uint8_t* ktile = p.kv_a + head * (SHUF ? R::kHalf : R::kStdTile);
+  const uint8_t* vtile = SHUF ? p.kv_b + head * R::kHalf : ktile;
 #pragma unroll
-  for (int pg = 0; pg < NS; ++pg) {
-    ok[pg] = tok0 + 16 * pg < it.seg_end;
-    const int pid = ok[pg] ? ptab[page0 + pg] : 0;
-    const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
+  for (int i = 0; i < R::kHalf / 1024; ++i) {
+    const int c = 4 * i + (lane >> 4), tau = lane & 15;
+    const size_t off = SHUF ? static_cast<size_t>(i * 64 + lane) * 16
+                            : static_cast<size_t>(tau) * R::kStdRow + c * 16;
+    dma16(ktile + off, slot + i * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < R::kHalf / 1024; ++i) {
+    size_t off;
     if constexpr (SHUF) {
-      ktile[pg] = p.kv_a + head * Gm::kPlaneTile;
-      vtile[pg] = p.kv_b + head * Gm::kPlaneTile;
+      off = static_cast<size_t>(i * 64 + lane) * 16;
     } else {
-      ktile[pg] = p.kv_a + head * Gm::kStdTile;
-      vtile[pg] = ktile[pg];
+      constexpr int kCpr = kD * E / 16;                  // chunks per V row
+      const int tau = i * (64 / kCpr) + lane / kCpr, c = lane % kCpr;
+      off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
     }
-  }
-  const int tq = lane >> 2, qq = lane & 3;
-  // K: step st = page st, token tq; quarter qq
-#pragma unroll
-  for (int st = 0; st < NS; ++st) {
-#pragma unroll
-    for (int k = 0; k < Gm::kKLoadsPerStep; ++k) {
-      size_t off;
-      if constexpr (SHUF) off = (static_cast<size_t>(4 * k + qq) * kPageSize + tq) * 16;
-      else off = static_cast<size_t>(tq) * Gm::kStdRow + 64 * k + 16 * qq;
-      r.k[st * Gm::kKLoadsPerStep + k] =
-          ok[st] ? *reinterpret_cast<const uint4*>(ktile[st] + off) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  if constexpr (!SHUF) {
-    // lane (phase tp, chunk c); tokens tp + kPh * u
-    constexpr int kCh = kD * E / 16;           // chunks per V row: 16 (bf16) / 8 (fp8)
-    constexpr int kPh = 64 / kCh;              // token phases: 4 / 8
-    const int tp = lane / kCh, c = lane % kCh;
-#pragma unroll
-    for (int u = 0; u < Gm::kVLoads; ++u) {
-      const int tau = tp + kPh * u;
-      const int pg = tau >> 4, slot = tau & 15;
-      const size_t off = static_cast<size_t>(slot) * Gm::kStdRow + kD * E + c * 16;
-      r.v[u] = ok[pg] ? *reinterpret_cast<const uint4*>(vtile[pg] + off) : make_uint4(0, 0, 0, 0);
-    }
-  } else if constexpr (E == 2) {
-    // channel d = lane + 64*h, 8-token group g (page g/2, in-page group g%2)
-#pragma unroll
-    for (int g = 0; g < 2 * NS; ++g)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int pg = g >> 1;
-        const size_t off = (static_cast<size_t>(g & 1) * kD + lane + 64 * h) * 16;
-        r.v[2 * g + h] = ok[pg] ? *reinterpret_cast<const uint4*>(vtile[pg] + off)
-                                : make_uint4(0, 0, 0, 0);
-      }
-  } else {
-    // x = 16: one chunk per (page, channel) holds the page's 16 tokens
-#pragma unroll
-    for (int pg = 0; pg < NS; ++pg)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const size_t off = static_cast<size_t>(lane + 64 * h) * 16;
-        r.v[2 * pg + h] = ok[pg] ? *reinterpret_cast<const uint4*>(vtile[pg] + off)
-                                 : make_uint4(0, 0, 0, 0);
-      }
+    dma16(vtile + off, slot + R::kHalf + i * 1024);
   }
 }
 
@@ -134,12 +117,13 @@ __device__ __forceinline__ float max_over_tokens(float v) {
   return v;
 }
 
-template <int E, bool SHUF, int RM, int NS>
+template <int E, bool SHUF, int RM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void seg_valu_kernel(SegParams p) {
-  using Gm = VGeo<E, NS>;
-  constexpr int kBlockTok = Gm::kBlockTok;
-  constexpr int kPBytes = SHUF ? RM * kBlockTok * 2 : kBlockTok * RM * 4;
+  using R = VRing<E>;
+  constexpr int kNS = R::kNS;
+  constexpr int kPBytes = SHUF ? RM * 16 * 2 : 16 * RM * 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves][kRingPerWave];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[kWaves][kPBytes];
   __shared__ __attribute__((aligned(16))) float oslot[kWaves][RM][kD];
   __shared__ float sm_m[kWaves][RM];
@@ -147,11 +131,15 @@ void seg_valu_kernel(SegParams p) {
 
   const SegItem it = decode_item(p);
   if (!it.valid) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tq = lane >> 2, qq = lane & 3;
-  const int ntok = it.seg_end - it.seg_start;
-  const int nblk = (ntok + kBlockTok - 1) / kBlockTok;
-  const int32_t* ptab = p.page_table + static_cast<size_t>(it.seq) * p.pt_stride;
+  const int seg_page0 = it.seg_start >> 4;
+  const int seg_pages = (it.seg_end - it.seg_start + 15) >> 4;
+  const int np = seg_pages > wave ? (seg_pages - wave + kWaves - 1) / kWaves : 0;
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
   float sm_scale = kScoreScaleLog2;
   float out_scale = 1.f;
   if constexpr (E == 1) {
@@ -159,7 +147,7 @@ void seg_valu_kernel(SegParams p) {
     out_scale = p.v_scale[0];
   }
 
-  // Q rows (bf16 pairs) for this lane's 32 channels
+  // Q rows (bf16 pairs) for this lane's 32 channels; consumed before any DMA
   uint4 qr[RM][4];
   int lim[RM];
 #pragma unroll
@@ -171,11 +159,26 @@ void seg_valu_kernel(SegParams p) {
     const uint16_t* q = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      // E==2: chunk k=u -> channels 32u + 8qq; E==1: (k=u/2, half u%2) -> 64k + 16qq + 8h
+      // E==2: chunk 4u+qq -> channels 32u + 8qq; E==1: chunk 4(u/2)+qq, half u%2
       const int ch = E == 2 ? 32 * u + 8 * qq : 64 * (u >> 1) + 16 * qq + 8 * (u & 1);
-      qr[r][u] = okr ? *reinterpret_cast<const uint4*>(q + ch) : make_uint4(0, 0, 0, 0);
+      qr[r][u] = *reinterpret_cast<const uint4*>(q + ch);   // padding rows read row 0
     }
   }
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      asm volatile("" : "+v"(qr[r][u].x), "+v"(qr[r][u].y), "+v"(qr[r][u].z), "+v"(qr[r][u].w));
+      if (r >= it.rows) qr[r][u] = make_uint4(0, 0, 0, 0);
+    }
+
+  uint8_t* wring = ring[wave];
+  // page ids: this wave's k-th page is seg page wave + 4k
+  auto pid_of = [&](int k) { return ptab[wave + kWaves * k]; };
+#pragma unroll
+  for (int k = 0; k < kNS - 1; ++k)
+    if (k < np) issue_page<E, SHUF>(p, it, pid_of(k), wring + k * R::kPage, lane);
+  int pid_next = kNS - 1 < np ? pid_of(kNS - 1) : 0;
 
   constexpr int kAcc = SHUF ? 2 : (E == 2 ? 8 : 16);
   float acc[RM][kAcc];
@@ -187,120 +190,103 @@ void seg_valu_kernel(SegParams p) {
 #pragma unroll
     for (int a = 0; a < kAcc; ++a) acc[r][a] = 0.f;
   }
-
   uint8_t* pw = pbuf[wave];
-  VRegs<E, NS> cur, nxt;
-  if (wave < nblk) vload_block<E, SHUF, NS>(p, it, ptab, wave, lane, cur);
 
-  for (int blk = wave; blk < nblk; blk += kWaves) {
-    if (blk + kWaves < nblk) vload_block<E, SHUF, NS>(p, it, ptab, blk + kWaves, lane, nxt);
-    const int tok0 = it.seg_start + blk * kBlockTok;
-    const bool tail = tok0 + kBlockTok > it.seg_end;
+  for (int k = 0; k < np; ++k) {
+    wait_vmcnt_pages<R::kInstrPerPage, kNS - 2>(min(kNS - 2, np - 1 - k));
+    if (k + kNS - 1 < np) {
+      issue_page<E, SHUF>(p, it, pid_next, wring + ((k + kNS - 1) % kNS) * R::kPage, lane);
+      if (k + kNS < np) pid_next = pid_of(k + kNS);
+    }
+    const uint8_t* sK = wring + (k % kNS) * R::kPage;
+    const uint8_t* sV = sK + R::kHalf;
+    const int tok0 = it.seg_start + 16 * (wave + kWaves * k);
+    const int vend = it.seg_end - tok0;        // tokens of this page before the end
+    const bool tail = vend < 16;
 
-    // ---- scores: s[st][r] for token 16*st + tq ----
-    float s[NS][RM];
+    // ---- scores: token tq, this lane's quarter of the channels ----
+    uint4 kw[4];
+    if constexpr (E == 2) {
 #pragma unroll
-    for (int st = 0; st < NS; ++st) {
-      uint4 kw[4];
-      if constexpr (E == 2) {
+      for (int u = 0; u < 4; ++u)
+        kw[u] = *reinterpret_cast<const uint4*>(sK + u * 1024 + (16 * qq + tq) * 16);
+    } else {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) kw[u] = cur.k[st * 4 + u];
-      } else {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const uint4 c = cur.k[st * 2 + k];
-          kw[2 * k] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
-          kw[2 * k + 1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
-        }
+      for (int u = 0; u < 2; ++u) {
+        const uint4 c = *reinterpret_cast<const uint4*>(sK + u * 1024 + (16 * qq + tq) * 16);
+        kw[2 * u] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
+        kw[2 * u + 1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
       }
+    }
+    float s[RM];
 #pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        float a = 0.f;
+    for (int r = 0; r < RM; ++r) {
+      float a = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a = dot2_bf16(kw[u].x, qr[r][u].x, a);
-          a = dot2_bf16(kw[u].y, qr[r][u].y, a);
-          a = dot2_bf16(kw[u].z, qr[r][u].z, a);
-          a = dot2_bf16(kw[u].w, qr[r][u].w, a);
-        }
-        a += dpp<kDppQuadXor1>(a);
-        a += dpp<kDppQuadXor2>(a);
-        const int pos = tok0 + 16 * st + tq;
-        s[st][r] = pos < lim[r] ? a * sm_scale : -INFINITY;
+      for (int u = 0; u < 4; ++u) {
+        a = dot2_bf16(kw[u].x, qr[r][u].x, a);
+        a = dot2_bf16(kw[u].y, qr[r][u].y, a);
+        a = dot2_bf16(kw[u].z, qr[r][u].z, a);
+        a = dot2_bf16(kw[u].w, qr[r][u].w, a);
       }
+      a += dpp<kDppQuadXor1>(a);
+      a += dpp<kDppQuadXor2>(a);
+      s[r] = tok0 + tq < lim[r] ? a * sm_scale : -INFINITY;
     }
 
     // ---- online softmax per row; p to the wave's LDS buffer ----
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      float bm = s[0][r];
-#pragma unroll
-      for (int st = 1; st < NS; ++st) bm = fmaxf(bm, s[st][r]);
-      bm = max_over_tokens(bm);
+      const float bm = max_over_tokens(s[r]);
       const float mn = fmaxf(m[r], bm);
       const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = fast_exp2(m[r] - mu);
-      float ps = 0.f;
+      if (mn != m[r]) {                        // row max moved (wave-uniform)
+        const float alpha = fast_exp2(m[r] - mu);
+        l[r] *= alpha;
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        s[st][r] = fast_exp2(s[st][r] - mu);
-        ps += s[st][r];
+        for (int a = 0; a < kAcc; ++a) acc[r][a] *= alpha;
+        m[r] = mn;
       }
-      l[r] = l[r] * alpha + ps;
-      m[r] = mn;
-#pragma unroll
-      for (int a = 0; a < kAcc; ++a) acc[r][a] *= alpha;
+      s[r] = fast_exp2(s[r] - mu);
+      l[r] += s[r];
     }
     if constexpr (!SHUF) {
-      // p[tau][r] fp32, written by quarter 0 of each token quad
-      if (qq == 0) {
+      if (qq == 0) {                           // p[tau][r] fp32
+        float* dst = reinterpret_cast<float*>(pw) + tq * RM;
 #pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          float* dst = reinterpret_cast<float*>(pw) + (16 * st + tq) * RM;
-#pragma unroll
-          for (int r4 = 0; r4 < RM; r4 += 4)
-            *reinterpret_cast<float4*>(dst + r4) =
-                make_float4(s[st][r4], s[st][r4 + 1], s[st][r4 + 2], s[st][r4 + 3]);
-        }
+        for (int r4 = 0; r4 < RM; r4 += 4)
+          *reinterpret_cast<float4*>(dst + r4) = make_float4(s[r4], s[r4 + 1], s[r4 + 2], s[r4 + 3]);
       }
-    } else {
-      // p[r][tau] bf16; quarter qq writes rows qq, qq + 4
+    } else {                                   // p[r][tau] bf16; quarter qq: rows qq, qq+4
 #pragma unroll
-      for (int r = 0; r < RM; ++r) {
-        if ((r & 3) == qq) {
-#pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const __bf16 b = static_cast<__bf16>(s[st][r]);
-            *reinterpret_cast<__bf16*>(pw + (r * kBlockTok + 16 * st + tq) * 2) = b;
-          }
-        }
-      }
+      for (int r = 0; r < RM; ++r)
+        if ((r & 3) == qq)
+          *reinterpret_cast<__bf16*>(pw + (r * 16 + tq) * 2) = static_cast<__bf16>(s[r]);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- o += p.V ----
-    const int vend = it.seg_end - tok0;      // tokens >= vend are past the segment
     if constexpr (!SHUF) {
-      constexpr int kCh = kD * E / 16;
-      constexpr int kPh = 64 / kCh;
-      const int tp = lane / kCh;
+      constexpr int kCh = kD * E / 16;        // chunks per V row: 16 / 8
+      constexpr int kPh = 64 / kCh;           // token phases: 4 / 8
+      const int tp = lane / kCh, c = lane % kCh;
 #pragma unroll
-      for (int u = 0; u < Gm::kVLoads; ++u) {
+      for (int u = 0; u < 16 / kPh; ++u) {
         const int tau = tp + kPh * u;
-        uint4 v = cur.v[u];
+        uint4 v = *reinterpret_cast<const uint4*>(sV + tau * (kD * E) + c * 16);
         if (tail && tau >= vend) v = make_uint4(0, 0, 0, 0);
         float x[kAcc];
         if constexpr (E == 2) {
           x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
           x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
         } else {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int q2 = 0; q2 < 4; ++q2) {
-            const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[q2]), false);
-            const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[q2]), true);
+            const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[q2]), false);
+            const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[q2]), true);
             x[4 * q2] = a[0]; x[4 * q2 + 1] = a[1]; x[4 * q2 + 2] = b[0]; x[4 * q2 + 3] = b[1];
           }
         }
@@ -317,24 +303,24 @@ void seg_valu_kernel(SegParams p) {
       }
     } else if constexpr (E == 2) {
 #pragma unroll
-      for (int g = 0; g < 2 * NS; ++g) {
-        uint4 vv[2] = {cur.v[2 * g], cur.v[2 * g + 1]};
-        if (tail) {
+      for (int g = 0; g < 2; ++g) {
+        uint4 vv[2];
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h) {
+          vv[h] = *reinterpret_cast<const uint4*>(sV + (g * kD + lane + 64 * h) * 16);
+          if (tail) {
             uint32_t w[4] = {vv[h].x, vv[h].y, vv[h].z, vv[h].w};
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
-              const int tau = 8 * g + 2 * q2;
-              if (tau >= vend) w[q2] = 0;
-              else if (tau + 1 >= vend) w[q2] &= 0xffffu;
+              const int rel = vend - (8 * g + 2 * q2);
+              w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
             }
             vv[h] = make_uint4(w[0], w[1], w[2], w[3]);
           }
         }
 #pragma unroll
         for (int r = 0; r < RM; ++r) {
-          const uint4 pp = *reinterpret_cast<const uint4*>(pw + (r * kBlockTok + 8 * g) * 2);
+          const uint4 pp = *reinterpret_cast<const uint4*>(pw + (r * 16 + 8 * g) * 2);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             float a = acc[r][h];
@@ -347,37 +333,33 @@ void seg_valu_kernel(SegParams p) {
         }
       }
     } else {
+      uint4 vb[2][2];                          // [h][half]: 16 tokens as bf16 pairs
 #pragma unroll
-      for (int pg = 0; pg < NS; ++pg) {
-        uint4 vb[2][2];               // [h][half]: 16 tokens as bf16 pairs
+      for (int h = 0; h < 2; ++h) {
+        uint4 c = *reinterpret_cast<const uint4*>(sV + (lane + 64 * h) * 16);
+        if (tail) {
+          uint32_t w[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint4 c = cur.v[2 * pg + h];
-          if (tail) {
-            uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-            for (int b = 0; b < 16; ++b)
-              if (16 * pg + b >= vend) w[b >> 2] &= ~(0xffu << (8 * (b & 3)));
-            c = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-          vb[h][0] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
-          vb[h][1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
+          for (int b = 0; b < 16; ++b)
+            if (b >= vend) w[b >> 2] &= ~(0xffu << (8 * (b & 3)));
+          c = make_uint4(w[0], w[1], w[2], w[3]);
         }
+        vb[h][0] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
+        vb[h][1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
+      }
 #pragma unroll
-        for (int r = 0; r < RM; ++r) {
+      for (int r = 0; r < RM; ++r) {
 #pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const uint4 pp = *reinterpret_cast<const uint4*>(
-                pw + (r * kBlockTok + 16 * pg + 8 * half) * 2);
+        for (int half = 0; half < 2; ++half) {
+          const uint4 pp = *reinterpret_cast<const uint4*>(pw + (r * 16 + 8 * half) * 2);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              float a = acc[r][h];
-              a = dot2_bf16(vb[h][half].x, pp.x, a);
-              a = dot2_bf16(vb[h][half].y, pp.y, a);
-              a = dot2_bf16(vb[h][half].z, pp.z, a);
-              a = dot2_bf16(vb[h][half].w, pp.w, a);
-              acc[r][h] = a;
-            }
+          for (int h = 0; h < 2; ++h) {
+            float a = acc[r][h];
+            a = dot2_bf16(vb[h][half].x, pp.x, a);
+            a = dot2_bf16(vb[h][half].y, pp.y, a);
+            a = dot2_bf16(vb[h][half].z, pp.z, a);
+            a = dot2_bf16(vb[h][half].w, pp.w, a);
+            acc[r][h] = a;
           }
         }
       }
@@ -385,13 +367,12 @@ void seg_valu_kernel(SegParams p) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    cur = nxt;
   }
 
   // ---- per-wave totals ----
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
-    float v = l[r];                           // identical within a quad: sum over tq only
+    float v = l[r];                            // identical within a quad: sum over tq only
     v += __shfl_xor(v, 4);
     v += __shfl_xor(v, 8);
     v += __shfl_xor(v, 16);
@@ -429,6 +410,7 @@ void seg_valu_kernel(SegParams p) {
       sm_l[wave][r] = l[r];
     }
   }
+  wait_vmcnt<0>();
   __syncthreads();
 
   // ---- merge waves: thread -> (row, channel) elements ----
@@ -458,9 +440,9 @@ void seg_valu_kernel(SegParams p) {
 template <int E, bool SHUF>
 int launch_valu_e(const SegParams& sp, int rows, int grid, hipStream_t st) {
   if (rows <= 4)
-    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 4, 4>), dim3(grid), dim3(kThreads), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 4>), dim3(grid), dim3(kThreads), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 8, 2>), dim3(grid), dim3(kThreads), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 8>), dim3(grid), dim3(kThreads), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

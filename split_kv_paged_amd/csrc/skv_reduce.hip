@@ -47,31 +47,64 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
   const float* lse_p = part_lse + row * seg_max;
   const float* o_p = part_o + row * seg_max * kHeadDim;
 
-  // max over segments, 64 at a time
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nseg; s0 += 64) {
-    const int s = s0 + lane;
-    float v = s < nseg ? lse_p[s] : -INFINITY;
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    M = fmaxf(M, v);
-  }
   float2 acc = make_float2(0.f, 0.f);
   float lse = -INFINITY;
-  if (nseg > 0 && M != -INFINITY) {
-    float sum = 0.f;
+  if (nseg > 0 && nseg <= 64) {
+    // lane s holds segment s: one round of lse loads, weights formed in-lane,
+    // then every partial row is loaded up front and scaled by its weight
+    const float ls = lane < nseg ? lse_p[lane] : -INFINITY;
+    float M = ls;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if (M != -INFINITY) {
+      const float e = lane < nseg ? expf(ls - M) : 0.f;
+      float sum = e;
+      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+      lse = M + logf(sum);
+      const float w = e / sum;
+      int s = 0;
+      for (; s + 4 <= nseg; s += 4) {
+        float2 o[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          o[k] = reinterpret_cast<const float2*>(o_p + (s + k) * kHeadDim)[lane];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float wk = __shfl(w, s + k);
+          acc.x += wk * o[k].x;
+          acc.y += wk * o[k].y;
+        }
+      }
+      for (; s < nseg; ++s) {
+        const float ws = __shfl(w, s);
+        const float2 o = reinterpret_cast<const float2*>(o_p + s * kHeadDim)[lane];
+        acc.x += ws * o.x;
+        acc.y += ws * o.y;
+      }
+    }
+  } else if (nseg > 64) {
+    // general path: max, then sum, then weighted rows, 64 segments at a time
+    float M = -INFINITY;
     for (int s0 = 0; s0 < nseg; s0 += 64) {
       const int s = s0 + lane;
-      float v = s < nseg ? expf(lse_p[s] - M) : 0.f;
-      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-      sum += v;
+      float v = s < nseg ? lse_p[s] : -INFINITY;
+      for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+      M = fmaxf(M, v);
     }
-    lse = M + logf(sum);
-#pragma unroll 4
-    for (int s = 0; s < nseg; ++s) {
-      const float w = expf(lse_p[s] - lse);
-      const float2 o = reinterpret_cast<const float2*>(o_p + s * kHeadDim)[lane];
-      acc.x += w * o.x;
-      acc.y += w * o.y;
+    if (M != -INFINITY) {
+      float sum = 0.f;
+      for (int s0 = 0; s0 < nseg; s0 += 64) {
+        const int s = s0 + lane;
+        float v = s < nseg ? expf(lse_p[s] - M) : 0.f;
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        sum += v;
+      }
+      lse = M + logf(sum);
+      for (int s = 0; s < nseg; ++s) {
+        const float w = expf(lse_p[s] - lse);
+        const float2 o = reinterpret_cast<const float2*>(o_p + s * kHeadDim)[lane];
+        acc.x += w * o.x;
+        acc.y += w * o.y;
+      }
     }
   }
   const unsigned int packed = static_cast<unsigned int>(f32_to_bf16_rne(acc.x)) |

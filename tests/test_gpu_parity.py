@@ -194,9 +194,11 @@ def test_fp8_codes_decode_exactly():
             assert np.array_equal(hip["out"][i, h], want[i]), (i, h)
 
 
-def test_split_reduce_alone():
-    rng = np.random.default_rng(3)
-    total_q, hq, smax, D = 9, 4, 7, 128
+@pytest.mark.parametrize("smax", [7, 64, 100])
+def test_split_reduce_alone(smax):
+    """Both merge paths: up to 64 segments (one per lane) and more."""
+    rng = np.random.default_rng(3 + smax)
+    total_q, hq, D = 9, 4, 128
     nseg = rng.integers(0, smax + 1, size=total_q).astype(np.int32)
     po = rng.standard_normal((total_q, hq, smax, D)).astype(np.float32)
     pl = (rng.standard_normal((total_q, hq, smax)) * 4).astype(np.float32)
