@@ -132,6 +132,7 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
     res.update(dict(
         workload=cfg.name, kv_bytes=kvb, plan_us=plan_us, segment_us=seg_us,
         segment_us_p10=segs[len(segs) // 10], segment_us_p90=segs[(9 * len(segs)) // 10],
+        segment_us_median=segs[len(segs) // 2],
         reduce_us=red_us, attn_us_per_call=call_us, step_us=step_us, wall_s=wall,
         kv_tb_s=kvb / call_us / 1e6, frac_of_hbm_peak=kvb / call_us / 1e3 / HBM_PEAK_GBS,
         segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
@@ -222,8 +223,8 @@ def main():
         "us_per_call": round(head["attn_us_per_call"], 2),
         "frac_of_hbm_peak": round(head["frac_of_hbm_peak"], 4),
         "breakdown_us": {k: round(head[k], 2) for k in
-                         ("plan_us", "segment_us", "segment_us_p10", "segment_us_p90",
-                          "reduce_us", "step_us")},
+                         ("plan_us", "segment_us", "segment_us_median", "segment_us_p10",
+                          "segment_us_p90", "reduce_us", "step_us")},
         "roofline": {"bound": "hbm", "kernel": "segment attention",
                      "achieved": round(seg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(seg_gbs / HBM_PEAK_GBS, 4),

@@ -50,9 +50,18 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
   float2 acc = make_float2(0.f, 0.f);
   float lse = -INFINITY;
   if (nseg > 0 && nseg <= 64) {
-    // lane s holds segment s: one round of lse loads, weights formed in-lane,
-    // then every partial row is loaded up front and scaled by its weight
+    // lane s holds segment s. The first kPre partial rows are loaded before
+    // the weights are known, so there is one memory round trip, not two.
+    constexpr int kPre = 8;
     const float ls = lane < nseg ? lse_p[lane] : -INFINITY;
+    float2 pre[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      // rows past nseg re-read the last valid row (weight 0): entries past a
+      // token's segment count are unspecified and may hold NaN
+      const int kk = k < nseg ? k : nseg - 1;
+      pre[k] = reinterpret_cast<const float2*>(o_p + kk * kHeadDim)[lane];
+    }
     float M = ls;
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     if (M != -INFINITY) {
@@ -61,20 +70,13 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
       for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
       lse = M + logf(sum);
       const float w = e / sum;
-      int s = 0;
-      for (; s + 4 <= nseg; s += 4) {
-        float2 o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          o[k] = reinterpret_cast<const float2*>(o_p + (s + k) * kHeadDim)[lane];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float wk = __shfl(w, s + k);
-          acc.x += wk * o[k].x;
-          acc.y += wk * o[k].y;
-        }
+      for (int k = 0; k < kPre; ++k) {
+        const float wk = __shfl(w, k);           // 0 for k >= nseg
+        acc.x += wk * pre[k].x;
+        acc.y += wk * pre[k].y;
       }
-      for (; s < nseg; ++s) {
+      for (int s = kPre; s < nseg; ++s) {
         const float ws = __shfl(w, s);
         const float2 o = reinterpret_cast<const float2*>(o_p + s * kHeadDim)[lane];
         acc.x += ws * o.x;

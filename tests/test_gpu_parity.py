@@ -202,6 +202,9 @@ def test_split_reduce_alone(smax):
     nseg = rng.integers(0, smax + 1, size=total_q).astype(np.int32)
     po = rng.standard_normal((total_q, hq, smax, D)).astype(np.float32)
     pl = (rng.standard_normal((total_q, hq, smax)) * 4).astype(np.float32)
+    for t in range(total_q):                   # entries past the count are unspecified
+        po[t, :, nseg[t]:] = np.nan
+        pl[t, :, nseg[t]:] = np.nan
     out, lse = skv.split_reduce(torch.as_tensor(po.reshape(-1), device=DEV),
                                 torch.as_tensor(pl.reshape(-1), device=DEV),
                                 torch.as_tensor(nseg, device=DEV), total_q=total_q,
