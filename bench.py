@@ -35,8 +35,8 @@ def _args():
     ap.add_argument("--config", default="uniform_verify")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=2,
-                    help="sequences of the workload the CPU oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU-oracle time for the baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -141,32 +141,39 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
     return res
 
 
-def cpu_baseline(cfg, n_seqs, gen, np):
-    """The oracle as it stands on a bounded sample of the workload: all query
-    rows of the first n_seqs sequences, on the host cores."""
+def cpu_baseline(cfg, min_seconds, gen, np):
+    """The oracle as it stands, timed on the host cores on a bounded sample of
+    the workload: all query rows of one sequence at a time, in order (wrapping
+    around), until at least `min_seconds` of CPU work (and at most ~3x that)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
-    sub = gen.small_config(cfg, cfg.seq_lens[:n_seqs], cfg.q_lens[:n_seqs])
+    # inputs only for the sequences the sample can reach (generation is not timed)
+    n_gen = min(cfg.bs, 8)
+    sub = gen.small_config(cfg, cfg.seq_lens[:n_gen], cfg.q_lens[:n_gen])
     case = gen.make_case(sub, "cpu")
     q = oracle.decode_bf16(gen.raw_u16(case.q))
     kv = gen.raw_kv(case)
     cu = case.cu_seqlens_q.numpy()
-    rows = [(t, h) for i in range(n_seqs) for t in range(cu[i], cu[i + 1])
-            for h in range(cfg.q_heads)]
-    t0 = time.perf_counter()
-    oracle.decode_attention(q, kv, cfg.kv_dtype, case.page_table.numpy(), case.seq_lens.numpy(),
-                            cu, cfg.kv_heads, cfg.page_size, cfg.causal, cfg.k_scale,
-                            cfg.v_scale, rows=rows)
-    dt = time.perf_counter() - t0
-    sample_bytes = sum(cfg.seq_lens[:n_seqs]) * cfg.kv_heads * 2 * cfg.head_dim * cfg.elem_bytes
-    return {"value": sample_bytes / dt / 1e12, "unit": "TB/s", "cores": int(threads),
-            "kind": "oracle", "seconds": dt,
-            "sample": f"{cfg.name}: all {len(rows)} query rows of the first {n_seqs} "
-                      f"sequences ({sample_bytes} KV bytes), numpy fp64 oracle",
+    table, lens = case.page_table.numpy(), case.seq_lens.numpy()
+    elapsed, done, kv_bytes = 0.0, 0, 0
+    while elapsed < min_seconds and done < 64:
+        i = done % n_gen
+        rows = [(t, h) for t in range(cu[i], cu[i + 1]) for h in range(cfg.q_heads)]
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, kv, cfg.kv_dtype, table, lens, cu, cfg.kv_heads,
+                                cfg.page_size, cfg.causal, cfg.k_scale, cfg.v_scale, rows=rows)
+        elapsed += time.perf_counter() - t0
+        kv_bytes += int(lens[i]) * cfg.kv_heads * 2 * cfg.head_dim * cfg.elem_bytes
+        done += 1
+    return {"value": kv_bytes / elapsed / 1e12, "unit": "TB/s", "cores": int(threads),
+            "kind": "oracle", "seconds": round(elapsed, 3),
+            "sample": f"{cfg.name}: all query rows of {done} sequences taken in order "
+                      f"(first {n_gen} of the batch, wrapping), {kv_bytes} KV bytes, "
+                      f"numpy fp64 oracle",
             "host": platform.processor() or platform.machine(),
             "host_cpus": os.cpu_count()}
 
@@ -242,7 +249,7 @@ def main():
             wl.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         line["workloads"] = wl
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seqs, gen, np)
+        line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seconds, gen, np)
     print(json.dumps(line), flush=True)
 
 
