@@ -30,8 +30,10 @@ HBM_PEAK_GBS = 8000.0
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The first ~100 launches after the GPU has been idle run up to 40% slower
+    # (clock/power ramp); 100 warmup steps put the timed region in steady state.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="uniform_verify")
     ap.add_argument("--all", action="store_true", help="also time the other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,9 +74,10 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
     res = {}
     kv_a, kv_b = case.kv, None
     if cfg.layout == "shuffled":
-        for _ in range(2):
-            kp, vp = skv.kv_page_shuffle(case.kv)
-        n = 5
+        kp, vp = skv.kv_page_shuffle(case.kv)
+        for _ in range(max(warmup // 5, 2)):
+            skv.kv_page_shuffle(case.kv, kp, vp)
+        n = 20
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(st)
         for _ in range(n):
@@ -245,7 +248,7 @@ def main():
         for c in configs.CONFIGS:
             if c.name == cfg.name:
                 continue
-            r = time_workload(c, max(10, a.steps // 2), a.warmup, torch, skv, gen)
+            r = time_workload(c, a.steps, a.warmup, torch, skv, gen)
             wl.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
         line["workloads"] = wl
     if not a.no_cpu_baseline:
