@@ -25,7 +25,8 @@ Modules:
   attention  page gather + unsplit fp64 attention               -- pinned
   planner    length-aware segment planner, fixed split          -- pinned
   merge      per-segment partials and log-sum-exp merge         -- pinned
-  shuffle    standard <-> shuffled page repack                  -- pinned
+  shuffle    standard <-> shuffled page repack, and the in-place
+             conversion of received byte halves (+ inverse)     -- pinned
 Every function is pinned by tests under tests/test_oracle_*.py against values
 the pages print, closed forms, invariants, brute force or an independent
 library routine; none is "parity unpinned".
@@ -35,12 +36,14 @@ from .attention import (gather_standard, gather_shuffled, visible_keys,
                         attend_one, decode_attention)
 from .planner import plan_segments, fixed_split_segments, pow2floor
 from .merge import segment_partials, lse_merge, split_decode_attention
-from .shuffle import shuffle_blocks, unshuffle_blocks
+from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
+                      convert_halves, revert_to_halves)
 
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "e4m3fn_value", "decode_kv",
     "gather_standard", "gather_shuffled", "visible_keys", "attend_one",
     "decode_attention", "plan_segments", "fixed_split_segments", "pow2floor",
     "segment_partials", "lse_merge", "split_decode_attention",
-    "shuffle_blocks", "unshuffle_blocks",
+    "shuffle_blocks", "unshuffle_blocks", "halves_from_standard", "convert_halves",
+    "revert_to_halves",
 ]

@@ -58,3 +58,75 @@ def unshuffle_blocks(k_plane, v_plane, elem_bytes=None):
         std[b][k_src] = k_plane[b]
         std[b][v_src] = v_plane[b]
     return std
+
+
+# --- In-place conversion of received byte halves -----------------------------
+#
+# [RFC, Proposed Change §3 Descriptors and §4 Convert]: a decoder with separate
+# K and V planes receives a remote standard block as two virtual regions of half
+# a block each, so after the transfer the local K-plane block holds the standard
+# block's first byte half and the V-plane block its second half (not K and V).
+# The converter then rewrites each received block into the shuffled K and V
+# planes. A block's halves split at byte H*N*D*e, which is a whole number of
+# elements, so the split is taken here on element codes in the standard
+# [H, N, 2D] order. With an odd head count one head straddles the two halves; a
+# single head has its first N/2 token rows in the K plane and the rest in the V
+# plane.
+
+
+def halves_from_standard(std, block_ids=None, k_plane=None, v_plane=None, elem_bytes=None):
+    """What the transfer leaves in the planes: for each listed block b of std
+    [B, H, N, 2D], the first H*N*D element codes (standard order) go to K-plane
+    block b and the rest to V-plane block b. Planes have the shuffled shapes
+    [B, H, D/x, N, x] and [B, H, N/x, D, x] (x from the dtype); blocks not
+    listed keep what the given planes held (zeros when none are given)."""
+    std = np.asarray(std)
+    B, H, N, D2 = std.shape
+    D = D2 // 2
+    x = 16 // (std.dtype.itemsize if elem_bytes is None else elem_bytes)
+    kp = np.zeros((B, H, D // x, N, x), std.dtype) if k_plane is None else np.array(k_plane)
+    vp = np.zeros((B, H, N // x, D, x), std.dtype) if v_plane is None else np.array(v_plane)
+    half = H * N * D
+    ids = range(B) if block_ids is None else [int(b) for b in block_ids]
+    for b in ids:
+        flat = std[b].reshape(-1)
+        kp[b] = flat[:half].reshape(kp.shape[1:])
+        vp[b] = flat[half:].reshape(vp.shape[1:])
+    return kp, vp
+
+
+def convert_halves(k_plane, v_plane, block_ids=None, elem_bytes=None):
+    """Planes holding received byte halves -> planes holding the shuffled K and
+    V of the listed blocks (all when None); other blocks are unchanged. Returns
+    new arrays."""
+    kp = np.array(k_plane)
+    vp = np.array(v_plane)
+    B, H, Dx, N, x = kp.shape
+    D = Dx * x
+    k_src, v_src = _maps(H, N, D, x)
+    ids = range(B) if block_ids is None else [int(b) for b in block_ids]
+    for b in ids:
+        std = np.concatenate([kp[b].reshape(-1), vp[b].reshape(-1)]).reshape(H, N, 2 * D)
+        kp[b] = std[k_src]
+        vp[b] = std[v_src]
+    return kp, vp
+
+
+def revert_to_halves(k_plane, v_plane, block_ids=None, elem_bytes=None):
+    """Inverse of convert_halves: shuffled planes -> the byte halves of each
+    listed block's standard form; other blocks are unchanged."""
+    kp = np.array(k_plane)
+    vp = np.array(v_plane)
+    B, H, Dx, N, x = kp.shape
+    D = Dx * x
+    half = H * N * D
+    k_src, v_src = _maps(H, N, D, x)
+    ids = range(B) if block_ids is None else [int(b) for b in block_ids]
+    for b in ids:
+        std = np.zeros((H, N, 2 * D), dtype=kp.dtype)
+        std[k_src] = kp[b]
+        std[v_src] = vp[b]
+        flat = std.reshape(-1)
+        kp[b] = flat[:half].reshape(kp.shape[1:])
+        vp[b] = flat[half:].reshape(vp.shape[1:])
+    return kp, vp

@@ -16,6 +16,7 @@ import oracle.merge as merge
 import oracle.planner as planner
 import oracle.shuffle as shuffle
 import test_oracle_attention as TA
+import test_oracle_convert as TC
 import test_oracle_fp8 as TF
 import test_oracle_planner as TP
 import test_oracle_shuffle as TS
@@ -25,7 +26,7 @@ from conftest import load_golden
 def _pins():
     """(name, callable) for every pin, parametrized ones expanded."""
     pins = []
-    for mod in (TA, TF, TP, TS):
+    for mod in (TA, TC, TF, TP, TS):
         for name in dir(mod):
             if not name.startswith("test_"):
                 continue
@@ -165,6 +166,19 @@ def _shuffle_transposed(std, block_ids=None, elem_bytes=None):
     return kp2.reshape(kp.shape), vp
 
 
+def _halves_swapped(std, block_ids=None, k_plane=None, v_plane=None, elem_bytes=None):
+    kp, vp = TRUE_HALVES(std, block_ids, k_plane, v_plane, elem_bytes)
+    std = np.asarray(std)
+    B, H, N, D2 = std.shape
+    half = H * N * (D2 // 2)
+    for b in (range(B) if block_ids is None else block_ids):
+        flat = std[b].reshape(-1)                        # second half into the K plane
+        kp[b] = flat[half:].reshape(kp.shape[1:])
+        vp[b] = flat[:half].reshape(vp.shape[1:])
+    return kp, vp
+
+
+TRUE_HALVES = shuffle.halves_from_standard
 TRUE_GATHER = att.gather_standard
 TRUE_PLAN = planner.plan_segments
 TRUE_SHUFFLE = shuffle.shuffle_blocks
@@ -206,6 +220,8 @@ MUTATIONS = [
                                                   (oracle, "plan_segments", _plan_seq_count)]),
     ("K plane transposed", [(shuffle, "shuffle_blocks", _shuffle_transposed),
                             (oracle, "shuffle_blocks", _shuffle_transposed)]),
+    ("byte halves swapped", [(shuffle, "halves_from_standard", _halves_swapped),
+                             (oracle, "halves_from_standard", _halves_swapped)]),
 ]
 
 
