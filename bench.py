@@ -6,8 +6,9 @@ reduce. The metric is the attention call (segment + reduce): microseconds per
 call and effective KV TB/s = sum_i L_i * kv_heads * 2 * head_dim * bytes / time,
 also as a fraction of the 8 TB/s HBM peak. Per-kernel durations come from HIP
 events recorded on the stream the kernels run on. For shuffled-page workloads
-the standard->shuffled repack runs once before the timed steps and is timed on
-its own.
+the standard->shuffled repack runs before the timed steps and is timed on its
+own, as is the in-place conversion of the same pool received as byte halves
+(and its inverse).
 
 Prints ONE JSON line (rank 0). Default workload: the uniform verify batch
 (bs=16 x 119k tokens, 4 query tokens, 32/2 heads, bf16). `--all` adds the other
@@ -88,6 +89,33 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         moved = 2 * case.kv.numel() * case.kv.element_size()
         res["shuffle_us"] = sh_us
         res["shuffle_gbs"] = moved / sh_us / 1e3
+        # in-place conversion of the same pool received as byte halves, and back
+        B = case.kv.shape[0]
+        flat = case.kv.view(torch.uint8).view(B, -1)
+        hb = flat.shape[1] // 2
+        x = 16 // case.kv.element_size()
+        H, D = cfg.kv_heads, cfg.head_dim
+        kh = flat[:, :hb].contiguous().view(case.kv.dtype).view(B, H, D // x, 16, x)
+        vh = flat[:, hb:].contiguous().view(case.kv.dtype).view(B, H, 16 // x, D, x)
+        for _ in range(max(warmup // 10, 2)):
+            skv.kv_page_convert(kh, vh)
+            skv.kv_page_convert(kh, vh, direction="to_standard")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        to_s = to_b = 0.0
+        for _ in range(n):
+            ev[0].record(st)
+            skv.kv_page_convert(kh, vh)
+            ev[1].record(st)
+            skv.kv_page_convert(kh, vh, direction="to_standard")
+            ev[2].record(st)
+            torch.cuda.synchronize()
+            to_s += ev[0].elapsed_time(ev[1]) * 1e3 / n
+            to_b += ev[1].elapsed_time(ev[2]) * 1e3 / n
+        res["convert_us"] = to_s
+        res["convert_gbs"] = moved / to_s / 1e3
+        res["convert_back_us"] = to_b
+        res["convert_back_gbs"] = moved / to_b / 1e3
+        del kh, vh, flat
         kv_a, kv_b = kp, vp
     rows = cfg.total_q * cfg.q_heads * cfg.seg_max
     part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
@@ -243,6 +271,11 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
+    repack = {k: round(head[k], 2) for k in ("shuffle_us", "shuffle_gbs", "convert_us",
+                                             "convert_gbs", "convert_back_us",
+                                             "convert_back_gbs") if k in head}
+    if repack:
+        line["repack"] = repack
     if a.all:
         wl = []
         for c in configs.CONFIGS:

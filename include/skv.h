@@ -11,8 +11,10 @@
  *   [RFC] vLLM RFC #59111, "NixlConnector: convert standard KV pages to ROCm
  *         AITER shuffled pages on the decode side" — Background (standard
  *         [H, N, 2D] pages and shuffled K [H, D/x, N, x] / V [H, N/x, D, x]
- *         planes, x = 16 / element bytes), Proposed Change §4 (converting the
- *         received blocks).
+ *         planes, x = 16 / element bytes), Proposed Change §3 (a received
+ *         standard block arrives as two byte halves in the K- and V-plane
+ *         blocks) and §4 (converting the received blocks), Test plan (round
+ *         trips).
  *
  * Conventions for every call:
  *   - Pointer arguments are DEVICE pointers owned by the caller (except the
@@ -51,6 +53,7 @@ enum skv_status {
 
 enum skv_layout { SKV_LAYOUT_STANDARD = 0, SKV_LAYOUT_SHUFFLED = 1 };
 enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1 };
+enum skv_convert_dir { SKV_TO_SHUFFLED = 0, SKV_TO_STANDARD = 1 };
 
 /* Number of int32 words of a plan: 1 + max(num_cus / kv_heads, bs).
  * [PR, Modifications]: one word for the segment length, then the work list,
@@ -179,6 +182,42 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                         const int32_t* block_ids, int num_blocks, int kv_heads,
                         int page_size, int head_dim, int elem_bytes,
                         void* stream);
+
+/* In-place conversion of received blocks [RFC, Proposed Change §3 Descriptors
+ * and §4 Convert] and its inverse [RFC, Test plan: round trips].
+ * k_plane, v_plane: the decoder's planes, shaped like skv_kv_page_shuffle's
+ * outputs ([blocks, H, D/x, N, x] and [blocks, H, N/x, D, x], H = kv_heads);
+ * block b occupies S = kv_heads * page_size * head_dim * elem_bytes bytes at
+ * offset b * S in each plane.
+ *   SKV_TO_SHUFFLED: on entry K-plane block b holds the first S bytes of a
+ *     standard block [H, N, 2D] and V-plane block b the last S bytes (what a
+ *     transfer of the standard block as two half-block regions leaves); on
+ *     return they hold its shuffled K and V, exactly as skv_kv_page_shuffle
+ *     would write them. With an odd head count one head straddles the halves.
+ *   SKV_TO_STANDARD: the inverse; a round trip restores the planes bit for bit.
+ * block_ids int32 [num_blocks] lists DISTINCT blocks (NULL = blocks
+ * 0..num_blocks-1); a block listed twice is rewritten by two work-groups at
+ * once (undefined result). Blocks not listed are left untouched.
+ * Errors: EINVAL for NULL planes, num_blocks < 1, kv_heads < 1, a direction
+ * other than the two above; EUNSUPPORTED for head_dim != 128, page_size != 16,
+ * elem_bytes not 1 or 2, or a block (2 * S) above 128 KiB (kv_heads > 16 for
+ * bf16, > 32 for fp8): the whole block is staged in on-chip memory. */
+int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
+                        int num_blocks, int kv_heads, int page_size,
+                        int head_dim, int elem_bytes, int direction,
+                        void* stream);
+
+/* Shuffled -> standard, out of place: the inverse of skv_kv_page_shuffle
+ * [RFC, Background layouts; Test plan: round trips]. For each listed block b
+ * and head h:
+ *   std_cache[b, h, n, c*x + i]           = k_plane[b, h, c, n, i]
+ *   std_cache[b, h, g*x + i, head_dim + d] = v_plane[b, h, g, d, i]
+ * Bit-exact; the planes must not overlap std_cache; blocks not listed are left
+ * untouched. Errors as for skv_kv_page_shuffle. */
+int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
+                          void* std_cache, const int32_t* block_ids,
+                          int num_blocks, int kv_heads, int page_size,
+                          int head_dim, int elem_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* skv_strerror(int status);

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libskv.so")
 
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_ELAUNCH = 0, 1, 2, 3
 LAYOUT = {"standard": 0, "shuffled": 1}
+CONVERT_DIR = {"to_shuffled": 0, "to_standard": 1}
 KV_DTYPE = {"bf16": 0, "fp8": 1}
 
 _c_int, _c_sz, _p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
@@ -35,6 +36,10 @@ _SIGNATURES = {
     "skv_split_reduce": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _p]),
     "skv_kv_page_shuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _p]),
+    "skv_kv_page_convert": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                     _c_int, _p]),
+    "skv_kv_page_unshuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
+                                       _c_int, _p]),
     "skv_strerror": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -223,3 +228,46 @@ def kv_page_shuffle(std_cache, k_plane=None, v_plane=None, block_ids=None, strea
                                     _ptr(block_ids), nb, H, N, D, e, _stream(stream))
     _check(st, "skv_kv_page_shuffle")
     return k_plane, v_plane
+
+
+def _planes(k_plane, v_plane):
+    for t, n in ((k_plane, "k_plane"), (v_plane, "v_plane")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    if k_plane.dim() != 5 or v_plane.dim() != 5:
+        raise ValueError("planes: expected [B, H, D/x, N, x] and [B, H, N/x, D, x]")
+    B, H, Dx, N, x = k_plane.shape
+    if tuple(v_plane.shape) != (B, H, N // x, Dx * x, x) or v_plane.dtype != k_plane.dtype:
+        raise ValueError("v_plane: shape or dtype does not match k_plane")
+    return B, H, Dx * x, N, k_plane.element_size()
+
+
+def kv_page_convert(k_plane, v_plane, block_ids=None, direction="to_shuffled", stream=None):
+    """In place: K/V-plane blocks holding a standard block's two byte halves ->
+    its shuffled K and V ("to_shuffled"), or back ("to_standard")."""
+    B, H, D, N, e = _planes(k_plane, v_plane)
+    nb = B
+    if block_ids is not None:
+        _need(block_ids, torch.int32, "block_ids")
+        nb = block_ids.numel()
+    st = load().skv_kv_page_convert(_ptr(k_plane), _ptr(v_plane), _ptr(block_ids), nb, H, N,
+                                    D, e, CONVERT_DIR[direction], _stream(stream))
+    _check(st, "skv_kv_page_convert")
+    return k_plane, v_plane
+
+
+def kv_page_unshuffle(k_plane, v_plane, std_cache=None, block_ids=None, stream=None):
+    """Shuffled planes -> standard pages [B, H, N, 2D] (inverse of kv_page_shuffle)."""
+    B, H, D, N, e = _planes(k_plane, v_plane)
+    if std_cache is None:
+        std_cache = torch.empty((B, H, N, 2 * D), dtype=k_plane.dtype, device=k_plane.device)
+    if not std_cache.is_cuda or not std_cache.is_contiguous():
+        raise ValueError("std_cache: expected a contiguous device tensor")
+    nb = B
+    if block_ids is not None:
+        _need(block_ids, torch.int32, "block_ids")
+        nb = block_ids.numel()
+    st = load().skv_kv_page_unshuffle(_ptr(k_plane), _ptr(v_plane), _ptr(std_cache),
+                                      _ptr(block_ids), nb, H, N, D, e, _stream(stream))
+    _check(st, "skv_kv_page_unshuffle")
+    return std_cache

@@ -139,6 +139,29 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                              kv_heads, elem_bytes, stream);
 }
 
+int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
+                        int num_blocks, int kv_heads, int page_size,
+                        int head_dim, int elem_bytes, int direction,
+                        void* stream) {
+  int st = skv::check_convert_args(k_plane, v_plane, num_blocks, kv_heads,
+                                   page_size, head_dim, elem_bytes, direction);
+  if (st != SKV_OK) return st;
+  return skv::launch_convert(k_plane, v_plane, block_ids, num_blocks, kv_heads,
+                             elem_bytes, direction, stream);
+}
+
+int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
+                          void* std_cache, const int32_t* block_ids,
+                          int num_blocks, int kv_heads, int page_size,
+                          int head_dim, int elem_bytes, void* stream) {
+  // same argument rules as the forward repack
+  int st = skv::check_shuffle_args(std_cache, k_plane, v_plane, num_blocks,
+                                   kv_heads, page_size, head_dim, elem_bytes);
+  if (st != SKV_OK) return st;
+  return skv::launch_unshuffle(k_plane, v_plane, std_cache, block_ids,
+                               num_blocks, kv_heads, elem_bytes, stream);
+}
+
 const char* skv_strerror(int status) {
   switch (status) {
     case SKV_OK: return "ok";

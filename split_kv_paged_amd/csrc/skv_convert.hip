@@ -1,0 +1,257 @@
+// Standard <-> shuffled repack of whole units of heads through LDS: the
+// in-place conversion of received byte halves, its inverse, and the
+// out-of-place unshuffle.
+//
+// vLLM RFC #59111, "NixlConnector: convert standard KV pages to ROCm AITER
+// shuffled pages on the decode side":
+//  * Background: one block's standard form is [H, N, 2D] (per head, N token
+//    rows of K channels then V channels); the shuffled form keeps K as
+//    [H, D/x, N, x] and V as [H, N/x, D, x] in two planes, x = 16 / element
+//    bytes.
+//  * Proposed Change §3 (Descriptors): a decoder with separate K and V planes
+//    receives a remote standard block as two regions of half a block each,
+//    so after the transfer K-plane block b holds the standard block's first
+//    byte half and V-plane block b its second half.
+//  * Proposed Change §4 (Convert) and Test plan: the received blocks are
+//    converted into the shuffled planes; a round trip must restore them.
+//
+// MI355X design: one work-group per unit. A unit is a whole block (all H
+// heads) for the in-place conversion, because the two halves interleave heads:
+// writing any shuffled byte of a block destroys standard bytes of other heads
+// (with odd H one head straddles the halves), so the whole block is staged in
+// LDS before anything is written. For the out-of-place unshuffle a unit is one
+// (block, head). Phase 1 reads the unit's bytes with coalesced 16-byte loads
+// (eight in flight per thread, from clamped indexes so no load waits on a
+// branch) into an LDS image of the standard tile; after one barrier, phase 2
+// writes the destination with coalesced 16-byte stores. The standard image's
+// 16-byte chunk c of token row n is stored at column c ^ n, so the 16 rows one
+// K-plane chunk column gathers fall in distinct LDS banks. Every HBM byte is
+// read once and written once. Units must be distinct blocks: listing a block
+// twice makes two work-groups rewrite it concurrently.
+#include <hip/hip_runtime.h>
+
+#include "skv.h"
+#include "skv_internal.h"
+
+namespace skv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 8;             // 16-byte loads in flight per thread
+constexpr int kN = kPageSize;
+constexpr int kD = kHeadDim;
+
+template <int E>
+struct Geo {
+  static constexpr int kX = 16 / E;                  // elements per 16 bytes
+  static constexpr int kRowChunks = 2 * kD * E / 16; // chunks per standard row
+  static constexpr int kKChunks = kD * E / 16;       // chunks of a row's K part
+  static constexpr int kPlaneChunks = kN * kKChunks; // one head in one plane
+  static constexpr int kHeadChunks = 2 * kPlaneChunks;
+  static_assert((kRowChunks & (kRowChunks - 1)) == 0, "swizzle needs 2^k");
+};
+
+// LDS chunk index of standard chunk c of token row n of head h
+template <int E>
+__device__ __forceinline__ int slot(int h, int n, int c) {
+  using G = Geo<E>;
+  return (h * kN + n) * G::kRowChunks + (c ^ (n & (G::kRowChunks - 1)));
+}
+
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+__device__ __forceinline__ void st16(uint8_t* p, uint4 v) {
+  *reinterpret_cast<uint4*>(p) = v;
+}
+
+// Unit u covers `uh` heads starting at head h0 of block b. Its standard bytes
+// are two regions of uh*P bytes each (P = one head's plane bytes): the first
+// at sa + base*s_mul, the second at sb + base*s_mul, base = (b*H + h0)*P; its
+// shuffled bytes are at kp + base and vp + base. In place: sa = kp, sb = vp,
+// s_mul = 1. Out of place: sa = std, sb = std + P, s_mul = 2, uh = 1.
+template <int E, int CAP, bool TO_SHUF>
+__global__ __launch_bounds__(kThreads) void repack_kernel(
+    uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
+    const int32_t* __restrict__ block_ids, int kv_heads, int uh) {
+  using G = Geo<E>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[CAP];
+  const int tid = threadIdx.x;
+  const int u = blockIdx.x;
+  const int per_block = kv_heads / uh;           // units per block
+  const int li = u / per_block;
+  const int b = block_ids ? block_ids[li] : li;
+  const int h0 = (u % per_block) * uh;
+  const size_t P = static_cast<size_t>(G::kPlaneChunks) * 16;
+  const size_t base = (static_cast<size_t>(b) * kv_heads + h0) * P;
+  uint8_t* A = sa + base * s_mul;                // standard, first half
+  uint8_t* B = sb + base * s_mul;                // standard, second half
+  uint8_t* K = kp + base;
+  uint8_t* V = vp + base;
+  const int half = uh * G::kPlaneChunks;         // chunks per region
+  const int total = 2 * half;
+
+  if constexpr (TO_SHUF) {
+    // 1. standard chunks (row-major over [uh, N, 2D]) -> LDS image
+    for (int i0 = tid; i0 < total; i0 += kThreads * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        int i = i0 + k * kThreads;
+        i = i < total ? i : total - 1;
+        v[k] = ld16(i < half ? A + 16 * i : B + 16 * (i - half));
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int i = i0 + k * kThreads;
+        if (i < total) {
+          const int h = i / G::kHeadChunks, r = i % G::kHeadChunks;
+          st16(lds + 16 * slot<E>(h, r / G::kRowChunks, r % G::kRowChunks), v[k]);
+        }
+      }
+    }
+    __syncthreads();
+    // 2a. K plane: chunk o = (h, c, n) is token n's K chunk c
+    for (int o = tid; o < half; o += kThreads) {
+      const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
+      st16(K + 16 * o, ld16(lds + 16 * slot<E>(h, r % kN, r / kN)));
+    }
+    // 2b. V plane: chunk o = (h, g, d) holds tokens g*x .. g*x+x-1 of channel d
+    for (int o = tid; o < half; o += kThreads) {
+      const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
+      const int g = r / kD, d = r % kD;
+      const int cc = G::kKChunks + (d * E) / 16, off = (d * E) % 16;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t acc = 0;
+#pragma unroll
+        for (int j = 0; j < 4 / E; ++j) {
+          const int n = g * G::kX + q * (4 / E) + j;
+          const uint8_t* p = lds + 16 * slot<E>(h, n, cc) + off;
+          const uint32_t e = E == 2 ? *reinterpret_cast<const uint16_t*>(p) : *p;
+          acc |= e << (8 * E * j);
+        }
+        w[q] = acc;
+      }
+      st16(V + 16 * o, make_uint4(w[0], w[1], w[2], w[3]));
+    }
+  } else {
+    // 1a. K plane chunks -> LDS image
+    for (int o0 = tid; o0 < half; o0 += kThreads * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int o = o0 + k * kThreads;
+        v[k] = ld16(K + 16 * (o < half ? o : half - 1));
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int o = o0 + k * kThreads;
+        if (o < half) {
+          const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
+          st16(lds + 16 * slot<E>(h, r % kN, r / kN), v[k]);
+        }
+      }
+    }
+    // 1b. V plane chunks -> scattered into the rows' V parts
+    for (int o0 = tid; o0 < half; o0 += kThreads * kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int o = o0 + k * kThreads;
+        v[k] = ld16(V + 16 * (o < half ? o : half - 1));
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int o = o0 + k * kThreads;
+        if (o < half) {
+          const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
+          const int g = r / kD, d = r % kD;
+          const int cc = G::kKChunks + (d * E) / 16, off = (d * E) % 16;
+          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int j = 0; j < 4 / E; ++j) {
+              const int n = g * G::kX + q * (4 / E) + j;
+              uint8_t* p = lds + 16 * slot<E>(h, n, cc) + off;
+              const uint32_t e = w[q] >> (8 * E * j);
+              if constexpr (E == 2)
+                *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(e);
+              else
+                *p = static_cast<uint8_t>(e);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // 2. LDS image -> standard chunks
+    for (int i = tid; i < total; i += kThreads) {
+      const int h = i / G::kHeadChunks, r = i % G::kHeadChunks;
+      const uint4 v = ld16(lds + 16 * slot<E>(h, r / G::kRowChunks, r % G::kRowChunks));
+      st16(i < half ? A + 16 * i : B + 16 * (i - half), v);
+    }
+  }
+}
+
+template <int E, bool TO_SHUF>
+int launch_cap(size_t lds_bytes, unsigned units, uint8_t* sa, uint8_t* sb,
+               int s_mul, uint8_t* kp, uint8_t* vp, const int32_t* ids,
+               int kv_heads, int uh, hipStream_t st) {
+  const dim3 grid(units), block(kThreads);
+#define SKV_CAP(C)                                                                \
+  if (lds_bytes <= (C)) {                                                         \
+    hipLaunchKernelGGL((repack_kernel<E, (C), TO_SHUF>), grid, block, 0, st, sa,  \
+                       sb, s_mul, kp, vp, ids, kv_heads, uh);                     \
+    return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;                \
+  }
+  SKV_CAP(8 * 1024)
+  SKV_CAP(16 * 1024)
+  SKV_CAP(32 * 1024)
+  SKV_CAP(64 * 1024)
+  SKV_CAP(kMaxConvertBytes)
+#undef SKV_CAP
+  return SKV_EUNSUPPORTED;
+}
+
+int launch_repack(uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
+                  const int32_t* ids, long long units, int kv_heads, int uh,
+                  int elem_bytes, bool to_shuf, void* stream) {
+  if (units > 0x7fffffffLL) return SKV_EUNSUPPORTED;
+  const size_t lds = static_cast<size_t>(uh) * kPageSize * 2 * kHeadDim * elem_bytes;
+  auto st = static_cast<hipStream_t>(stream);
+  const auto n = static_cast<unsigned>(units);
+  if (elem_bytes == 2)
+    return to_shuf ? launch_cap<2, true>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st)
+                   : launch_cap<2, false>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st);
+  return to_shuf ? launch_cap<1, true>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st)
+                 : launch_cap<1, false>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st);
+}
+
+}  // namespace
+
+int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
+                   int num_blocks, int kv_heads, int elem_bytes, int direction,
+                   void* stream) {
+  auto kp = static_cast<uint8_t*>(k_plane);
+  auto vp = static_cast<uint8_t*>(v_plane);
+  return launch_repack(kp, vp, 1, kp, vp, block_ids, num_blocks, kv_heads, kv_heads,
+                       elem_bytes, direction == SKV_TO_SHUFFLED, stream);
+}
+
+int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
+                     const int32_t* block_ids, int num_blocks, int kv_heads,
+                     int elem_bytes, void* stream) {
+  auto s = static_cast<uint8_t*>(std_cache);
+  const size_t P = static_cast<size_t>(kPageSize) * kHeadDim * elem_bytes;
+  // the planes are only read in this direction
+  auto kp = const_cast<uint8_t*>(static_cast<const uint8_t*>(k_plane));
+  auto vp = const_cast<uint8_t*>(static_cast<const uint8_t*>(v_plane));
+  return launch_repack(s, s + P, 2, kp, vp, block_ids,
+                       static_cast<long long>(num_blocks) * kv_heads, kv_heads, 1,
+                       elem_bytes, false, stream);
+}
+
+}  // namespace skv

@@ -15,6 +15,7 @@ constexpr int kMaxQ = 4;
 constexpr int kMaxRows = 64;     // (q_heads / kv_heads) * max_q
 constexpr int kMaxBs = 32767;    // seq << 16 stays a non-negative int32
 constexpr int kMaxSegMax = 65535;
+constexpr int kMaxConvertBytes = 128 * 1024;   // one block staged in LDS
 
 // ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
 int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
@@ -35,6 +36,10 @@ int check_reduce_args(const void* part_o, const void* part_lse,
 int check_shuffle_args(const void* std_cache, const void* k_plane,
                        const void* v_plane, int num_blocks, int kv_heads,
                        int page_size, int head_dim, int elem_bytes);
+
+int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
+                       int kv_heads, int page_size, int head_dim,
+                       int elem_bytes, int direction);
 
 inline int plan_width(int bs, int kv_heads, int num_cus) {
   int cap = num_cus / kv_heads;
@@ -74,6 +79,12 @@ int launch_reduce(const float* part_o, const float* part_lse,
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
                    int elem_bytes, void* stream);
+int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
+                   int num_blocks, int kv_heads, int elem_bytes, int direction,
+                   void* stream);
+int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
+                     const int32_t* block_ids, int num_blocks, int kv_heads,
+                     int elem_bytes, void* stream);
 
 }  // namespace skv
 

@@ -70,4 +70,19 @@ int check_shuffle_args(const void* std_cache, const void* k_plane,
   return SKV_OK;
 }
 
+int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
+                       int kv_heads, int page_size, int head_dim,
+                       int elem_bytes, int direction) {
+  if (!k_plane || !v_plane) return SKV_EINVAL;
+  if (num_blocks < 1 || kv_heads < 1 || page_size < 1 || head_dim < 1)
+    return SKV_EINVAL;
+  if (direction != SKV_TO_SHUFFLED && direction != SKV_TO_STANDARD)
+    return SKV_EINVAL;
+  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
+  const long long block = 2LL * kv_heads * page_size * head_dim * elem_bytes;
+  if (block > kMaxConvertBytes) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
 }  // namespace skv

@@ -130,6 +130,37 @@ def test_shuffle_errors(kw, code):
     assert _shuffle(**kw) == code
 
 
+def _convert(**kw):
+    a = dict(k=P, v=P, ids=None, nb=4, h=2, ps=16, hd=128, e=2, d=0)
+    a.update(kw)
+    return skv.load().skv_kv_page_convert(a["k"], a["v"], a["ids"], a["nb"], a["h"], a["ps"],
+                                          a["hd"], a["e"], a["d"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1), (dict(d=2), 1),
+    (dict(d=-1), 1), (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+    (dict(h=17), 2), (dict(h=33, e=1), 2),               # block above 128 KiB
+])
+def test_convert_errors(kw, code):
+    assert _convert(**kw) == code
+
+
+def _unshuffle(**kw):
+    a = dict(k=P, v=P, dst=P, ids=None, nb=4, h=2, ps=16, hd=128, e=2)
+    a.update(kw)
+    return skv.load().skv_kv_page_unshuffle(a["k"], a["v"], a["dst"], a["ids"], a["nb"], a["h"],
+                                            a["ps"], a["hd"], a["e"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dst=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
+    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+])
+def test_unshuffle_errors(kw, code):
+    assert _unshuffle(**kw) == code
+
+
 def test_python_binding_raises_on_error_status():
     with pytest.raises(_lib.SkvError) as ei:
         _lib._check(2, "x")
