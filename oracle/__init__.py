@@ -34,7 +34,7 @@ library routine; none is "parity unpinned".
 from .fp8 import decode_bf16, decode_e4m3fn, e4m3fn_value, decode_kv
 from .attention import (gather_standard, gather_shuffled, visible_keys,
                         attend_one, decode_attention)
-from .planner import plan_segments, fixed_split_segments, pow2floor
+from .planner import plan_segments, fixed_split_segments, fixed_split_plan, pow2floor
 from .merge import segment_partials, lse_merge, split_decode_attention
 from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
                       convert_halves, revert_to_halves)
@@ -42,7 +42,8 @@ from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "e4m3fn_value", "decode_kv",
     "gather_standard", "gather_shuffled", "visible_keys", "attend_one",
-    "decode_attention", "plan_segments", "fixed_split_segments", "pow2floor",
+    "decode_attention", "plan_segments", "fixed_split_segments", "fixed_split_plan",
+    "pow2floor",
     "segment_partials", "lse_merge", "split_decode_attention",
     "shuffle_blocks", "unshuffle_blocks", "halves_from_standard", "convert_halves",
     "revert_to_halves",

@@ -47,16 +47,20 @@ def split_decode_attention(q, kv, kv_dtype, table, seq_lens, cu_seqlens_q,
                            kv_heads, page_size, pages_per_segment, causal=1,
                            k_scale=None, v_scale=None, planes=None):
     """Attention computed segment by segment and merged (no blocking beyond
-    the segments themselves). Returns (out, lse, nseg per token)."""
+    the segments themselves). `pages_per_segment` is one length for every
+    sequence (the planned split) or one per sequence (the fixed split).
+    Returns (out, lse, nseg per token)."""
     q = np.asarray(q, dtype=np.float64)
     total_q, Hq, D = q.shape
     G = Hq // kv_heads
     out = np.zeros((total_q, Hq, D))
     lse = np.zeros((total_q, Hq))
     nseg = np.zeros(total_q, dtype=np.int64)
-    seg_tokens = pages_per_segment * page_size
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    per_seq = np.broadcast_to(np.asarray(pages_per_segment, dtype=np.int64), lens.shape)
     cu = np.asarray(cu_seqlens_q, dtype=np.int64)
-    for i, L in enumerate(np.asarray(seq_lens, dtype=np.int64)):
+    for i, L in enumerate(lens):
+        seg_tokens = max(int(per_seq[i]), 1) * page_size
         K, V = sequence_kv(kv, kv_dtype, k_scale, v_scale, table[i], int(L),
                            page_size, planes)
         qn = int(cu[i + 1] - cu[i])

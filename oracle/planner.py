@@ -100,3 +100,27 @@ def fixed_split_segments(bs: int, kv_heads: int, num_cus: int = 256,
                          seg_max: int = 64) -> int:
     """Segments per sequence under the fixed split [PR, Motivation]."""
     return max(1, min(seg_max, pow2floor(num_cus // (bs * kv_heads))))
+
+
+def fixed_split_plan(seq_lens, cu_seqlens_q, kv_heads, page_size, num_cus=256,
+                     seg_max=64, causal=1):
+    """The fixed split as a segmentation [PR, Motivation: every sequence gets the
+    same number of KV segments; Modifications: bs == 1 runs this split].
+
+    Reading (the pages give the count, not the boundaries): sequence i's n_i
+    pages are cut into S contiguous segments of ceil(n_i / S) pages, S =
+    fixed_split_segments(...), the last shorter and trailing ones empty when
+    n_i < S. Returns (S, seg_pages per sequence, tok_nseg), tok_nseg[t] being
+    the number of t's segments that hold at least one key t may see.
+    """
+    lens = [int(v) for v in seq_lens]
+    bs = len(lens)
+    S = fixed_split_segments(bs, kv_heads, num_cus, seg_max)
+    seg_pages = [_ceil_div(_ceil_div(L, page_size), S) for L in lens]
+    tok_nseg = []
+    for i in range(bs):
+        qn = int(cu_seqlens_q[i + 1]) - int(cu_seqlens_q[i])
+        for j in range(qn):
+            vis = visible_keys(lens[i], qn, j, causal)
+            tok_nseg.append(_ceil_div(vis, seg_pages[i] * page_size) if vis > 0 else 0)
+    return S, seg_pages, tok_nseg

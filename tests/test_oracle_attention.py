@@ -235,3 +235,19 @@ def test_planned_split_equals_unsplit_and_counts_match_planner():
     assert list(nseg) == tok
     out, _ = _oracle(cfg, case)
     np.testing.assert_allclose(so, out, rtol=1e-12, atol=1e-13)
+
+
+def test_fixed_split_equals_unsplit_and_counts_match():
+    """The fixed split (per-sequence segment lengths) merges to the unsplit
+    result, and the per-token counts are the number of non-empty segments."""
+    cfg, case = _case([37, 100, 16, 1, 0, 65], [1, 4, 3, 2, 1, 4], num_cus=64)
+    S, seg_pages, tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.numpy(),
+                                                cfg.kv_heads, 16, cfg.num_cus, cfg.seg_max, 1)
+    assert S == 4 and seg_pages == [1, 2, 1, 1, 0, 2]
+    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    so, _, nseg = oracle.split_decode_attention(
+        q, gen.raw_kv(case), "bf16", case.page_table.numpy(), case.seq_lens.numpy(),
+        case.cu_seqlens_q.numpy(), 2, 16, seg_pages, 1)
+    assert list(nseg) == tok
+    out, _ = _oracle(cfg, case)
+    np.testing.assert_allclose(so, out, rtol=1e-12, atol=1e-13)

@@ -178,6 +178,13 @@ def _halves_swapped(std, block_ids=None, k_plane=None, v_plane=None, elem_bytes=
     return kp, vp
 
 
+def _fixed_floor(seq_lens, cu, kv_heads, page_size, num_cus=256, seg_max=64, causal=1):
+    S, seg_pages, tok = TRUE_FIXED(seq_lens, cu, kv_heads, page_size, num_cus, seg_max, causal)
+    pages = [-(-int(L) // page_size) for L in seq_lens]
+    return S, [max(n // S, 1) if n else 0 for n in pages], tok     # floor, not ceil
+
+
+TRUE_FIXED = planner.fixed_split_plan
 TRUE_HALVES = shuffle.halves_from_standard
 TRUE_GATHER = att.gather_standard
 TRUE_PLAN = planner.plan_segments
@@ -220,6 +227,8 @@ MUTATIONS = [
                                                   (oracle, "plan_segments", _plan_seq_count)]),
     ("K plane transposed", [(shuffle, "shuffle_blocks", _shuffle_transposed),
                             (oracle, "shuffle_blocks", _shuffle_transposed)]),
+    ("fixed split floors the segment length", [(planner, "fixed_split_plan", _fixed_floor),
+                                               (oracle, "fixed_split_plan", _fixed_floor)]),
     ("byte halves swapped", [(shuffle, "halves_from_standard", _halves_swapped),
                              (oracle, "halves_from_standard", _halves_swapped)]),
 ]

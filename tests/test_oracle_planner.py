@@ -138,3 +138,54 @@ def test_all_configs_plan_bounds():
         assert len(items) * cfg.kv_heads <= max(cfg.num_cus, cfg.bs * cfg.kv_heads)
         assert len(tok) == cfg.total_q
         assert max(tok) <= cfg.seg_max
+
+
+def test_fixed_split_plan_long_request():
+    """[PR, Motivation]: at bs 17-32 with one kv head the fixed split gives 8
+    segments, so a 248k request runs as ~31k-token segments (page granularity)."""
+    g = load_golden("fixed_split_values.json")
+    lr = g["long_request"]
+    lens = [lr["tokens"]] + [1000] * 19
+    S, seg_pages, _ = oracle.fixed_split_plan(lens, list(range(21)), 1, 16, g["num_cus"],
+                                              g["seg_max"], 1)
+    assert S == lr["segments"]
+    assert abs(seg_pages[0] * 16 - lr["segment_tokens"]) < 16
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_fixed_split_plan_brute_force(seed):
+    rng = np.random.default_rng(500 + seed)
+    bs = int(rng.integers(1, 40))
+    kv_heads = int(rng.choice([1, 2, 4, 8]))
+    num_cus = int(rng.choice([8, 64, 256, 304]))
+    seg_max = int(rng.integers(1, 65))
+    lens = [int(v) for v in rng.integers(0, 3000, size=bs)]
+    q = [int(v) for v in rng.integers(1, 5, size=bs)]
+    cu = _cu(q)
+    causal = int(rng.integers(0, 2))
+    S, seg_pages, tok = oracle.fixed_split_plan(lens, cu, kv_heads, 16, num_cus, seg_max,
+                                                causal)
+    assert S == oracle.fixed_split_segments(bs, kv_heads, num_cus, seg_max)
+    t = 0
+    for i, L in enumerate(lens):
+        n = -(-L // 16)
+        P = seg_pages[i]
+        # segments [s*P, min((s+1)*P, n)) for s < S tile the pages exactly
+        covered = [p for s in range(S) for p in range(s * P, min((s + 1) * P, n))]
+        assert covered == list(range(n))
+        for j in range(q[i]):
+            vis = L if not causal else min(max(L - q[i] + j + 1, 0), L)
+            assert tok[t] == sum(1 for s in range(S) if s * P * 16 < vis)
+            t += 1
+
+
+def test_uniform_fixed_split_equals_planned():
+    """Equal lengths: the fixed split cuts every sequence exactly as the planner
+    does (same T, same counts)."""
+    cfg = configs.UNIFORM_VERIFY
+    cu = _cu(cfg.q_lens)
+    plan, tok = oracle.plan_segments(cfg.seq_lens, cu, cfg.kv_heads, 16, cfg.num_cus,
+                                     cfg.seg_max, 1)
+    S, seg_pages, ftok = oracle.fixed_split_plan(cfg.seq_lens, cu, cfg.kv_heads, 16,
+                                                 cfg.num_cus, cfg.seg_max, 1)
+    assert S == 8 and set(seg_pages) == {plan[0]} and ftok == tok
