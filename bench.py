@@ -45,10 +45,15 @@ def _args():
     return ap.parse_args()
 
 
+# the sources the segment-attention kernels are compiled from
+SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_valu.hip",
+                   "skv_attn_common.h", "skv_internal.h")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     d = os.path.join(ROOT, "split_kv_paged_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in SEGMENT_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -167,9 +172,40 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         reduce_us=red_us, attn_us_per_call=call_us, step_us=step_us, wall_s=wall,
         kv_tb_s=kvb / call_us / 1e6, frac_of_hbm_peak=kvb / call_us / 1e3 / HBM_PEAK_GBS,
         segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
+    # the fixed split on the same batch (no plan; the segment kernel writes the
+    # per-token counts): the pages' A/B comparison, on these kernels
+    def fixed_call(ev=None):
+        if ev:
+            ev[0].record(st)
+        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
+                         case.cu_seqlens_q, None, tok, part_o=part_o, part_lse=part_lse, **kw)
+        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
+                         seg_max=cfg.seg_max, out=out)
+        if ev:
+            ev[1].record(st)
+
+    for _ in range(warmup):
+        fixed_call()
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        fixed_call(fev[i])
+    torch.cuda.synchronize()
+    fixed_us = sum(e[0].elapsed_time(e[1]) for e in fev) * 1e3 / steps
+    res.update(fixed_split_us_per_call=fixed_us, fixed_split_kv_tb_s=kvb / fixed_us / 1e6,
+               fixed_split_segments=_fixed_segments(cfg))
     del case, part_o, part_lse, out
     torch.cuda.empty_cache()
     return res
+
+
+def _fixed_segments(cfg):
+    """Segments per sequence of the fixed split: max(1, min(seg_max,
+    pow2floor(num_cus / (bs * kv_heads))))."""
+    q = cfg.num_cus // (cfg.bs * cfg.kv_heads)
+    p = 1
+    while p * 2 <= q:
+        p *= 2
+    return max(1, min(cfg.seg_max, p))
 
 
 def cpu_baseline(cfg, min_seconds, gen, np):
@@ -263,6 +299,9 @@ def main():
         "breakdown_us": {k: round(head[k], 2) for k in
                          ("plan_us", "segment_us", "segment_us_median", "segment_us_p10",
                           "segment_us_p90", "reduce_us", "step_us")},
+        "fixed_split": {"us_per_call": round(head["fixed_split_us_per_call"], 2),
+                        "kv_tb_s": round(head["fixed_split_kv_tb_s"], 4),
+                        "segments_per_seq": head["fixed_split_segments"]},
         "roofline": {"bound": "hbm", "kernel": "segment attention",
                      "achieved": round(seg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(seg_gbs / HBM_PEAK_GBS, 4),

@@ -113,7 +113,15 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  *              code value * scale), NULL for bf16
  * causal       1: bottom-right causal mask as in skv_plan_build; 0: all L keys
  * plan, tok_nseg      from skv_plan_build with the same bs, kv_heads, num_cus,
- *              seg_max, causal and page_size
+ *              seg_max, causal and page_size (planned split). plan NULL selects
+ *              the FIXED split [PR, Motivation; Modifications: bs == 1 runs it
+ *              without a plan]: every sequence gets S = max(1, min(seg_max,
+ *              pow2floor(num_cus / (bs * kv_heads)))) segments of
+ *              ceil(ceil(L_i/16) / S) pages (trailing ones empty when a sequence
+ *              has fewer than S pages), one work-group per (sequence, segment,
+ *              kv head); no plan launch is needed, and the segment kernel
+ *              WRITES tok_nseg[t] = ceil(visible_t / segment tokens) for the
+ *              reduce (tok_nseg is then an output; it is read otherwise)
  * part_o, part_lse    workspace of skv_workspace_bytes(): part_o fp32
  *              [total_q, q_heads, seg_max, head_dim] (each segment's
  *              softmax-normalized output), part_lse fp32 [total_q, q_heads,
@@ -136,13 +144,13 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           int max_q, int q_heads, int kv_heads, int head_dim,
                           int page_size, const float* k_scale,
                           const float* v_scale, int causal, const int32_t* plan,
-                          const int32_t* tok_nseg, int num_cus, int seg_max,
+                          int32_t* tok_nseg, int num_cus, int seg_max,
                           float* part_o, float* part_lse, void* out,
                           float* out_lse, void* stream);
 
 /* The segment kernel of skv_paged_decode_attn alone: writes the partials
- * (part_o, part_lse) of every (token, q head, segment) that the plan lists,
- * without merging them. Arguments and errors as for skv_paged_decode_attn
+ * (part_o, part_lse) of every (token, q head, segment) that the plan lists
+ * (with plan NULL: of the fixed split, and tok_nseg), without merging them. Arguments and errors as for skv_paged_decode_attn
  * (minus out and out_lse). skv_paged_decode_attn = this call followed by
  * skv_split_reduce on the same stream. Partials of several calls (e.g. over
  * disjoint page ranges) can be merged with skv_split_reduce. */
@@ -151,7 +159,7 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
                      const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                      int total_q, int max_q, int q_heads, int kv_heads, int head_dim,
                      int page_size, const float* k_scale, const float* v_scale,
-                     int causal, const int32_t* plan, const int32_t* tok_nseg,
+                     int causal, const int32_t* plan, int32_t* tok_nseg,
                      int num_cus, int seg_max, float* part_o, float* part_lse,
                      void* stream);
 

@@ -133,10 +133,15 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
                       layout="standard", k_scale=None, v_scale=None, causal=1,
                       part_o=None, part_lse=None, out=None, out_lse=None,
                       page_size=16, stream=None):
-    """Enqueue segment attention + split reduce; returns (out bf16, out_lse or None)."""
+    """Enqueue segment attention + split reduce; returns (out bf16, out_lse or None).
+
+    plan=None selects the fixed split (no plan launch); tok_nseg is then
+    written by the segment kernel (allocated when None)."""
     total_q, q_heads, head_dim = q.shape
     bs = seq_lens.numel()
     dev = q.device
+    if plan is None and tok_nseg is None:
+        tok_nseg = torch.empty(total_q, dtype=torch.int32, device=dev)
     rows = total_q * q_heads * seg_max
     if part_o is None:
         part_o = torch.empty(rows * head_dim, dtype=torch.float32, device=dev)
@@ -149,7 +154,8 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
     _need(part_o, torch.float32, "part_o", rows * head_dim)
     _need(part_lse, torch.float32, "part_lse", rows)
     _need(page_table, torch.int32, "page_table")
-    _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    if plan is not None:
+        _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
     _need(tok_nseg, torch.int32, "tok_nseg", total_q)
     if out_lse is not None:
         _need(out_lse, torch.float32, "out_lse", total_q * q_heads)
@@ -170,15 +176,19 @@ def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_ns
                  *, kv_heads, max_q, num_cus, seg_max, part_o, part_lse, kv_dtype="bf16",
                  layout="standard", k_scale=None, v_scale=None, causal=1, page_size=16,
                  stream=None):
-    """Enqueue the segment kernel alone (partials only)."""
+    """Enqueue the segment kernel alone (partials only). plan=None: fixed split,
+    tok_nseg written (allocated when None); returns (part_o, part_lse, tok_nseg)."""
     total_q, q_heads, head_dim = q.shape
     bs = seq_lens.numel()
+    if plan is None and tok_nseg is None:
+        tok_nseg = torch.empty(total_q, dtype=torch.int32, device=q.device)
     rows = total_q * q_heads * seg_max
     _need(q, torch.bfloat16, "q")
     _need(part_o, torch.float32, "part_o", rows * head_dim)
     _need(part_lse, torch.float32, "part_lse", rows)
     _need(page_table, torch.int32, "page_table")
-    _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    if plan is not None:
+        _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
     _need(tok_nseg, torch.int32, "tok_nseg", total_q)
     st = load().skv_segment_attn(
         _ptr(q), _ptr(kv_a), _ptr(kv_b), LAYOUT[layout], KV_DTYPE[kv_dtype],
@@ -187,7 +197,7 @@ def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_ns
         _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
         _ptr(part_o), _ptr(part_lse), _stream(stream))
     _check(st, "skv_segment_attn")
-    return part_o, part_lse
+    return part_o, part_lse, tok_nseg
 
 
 def split_reduce(part_o, part_lse, tok_nseg, *, total_q, q_heads, seg_max, head_dim=128,

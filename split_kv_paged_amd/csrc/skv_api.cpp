@@ -11,7 +11,7 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
                              const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                              int total_q, int max_q, int q_heads, int kv_heads,
                              const float* k_scale, const float* v_scale, int causal,
-                             const int32_t* plan, const int32_t* tok_nseg, int num_cus,
+                             const int32_t* plan, int32_t* tok_nseg, int num_cus,
                              int seg_max, float* part_o, float* part_lse) {
   skv::AttnArgs a;
   a.q = q;
@@ -72,7 +72,7 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
                      const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                      int total_q, int max_q, int q_heads, int kv_heads, int head_dim,
                      int page_size, const float* k_scale, const float* v_scale,
-                     int causal, const int32_t* plan, const int32_t* tok_nseg,
+                     int causal, const int32_t* plan, int32_t* tok_nseg,
                      int num_cus, int seg_max, float* part_o, float* part_lse,
                      void* stream) {
   // `out` is not used by this call; pass a non-NULL stand-in to the shared check
@@ -97,7 +97,7 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           int max_q, int q_heads, int kv_heads, int head_dim,
                           int page_size, const float* k_scale,
                           const float* v_scale, int causal, const int32_t* plan,
-                          const int32_t* tok_nseg, int num_cus, int seg_max,
+                          int32_t* tok_nseg, int num_cus, int seg_max,
                           float* part_o, float* part_lse, void* out,
                           float* out_lse, void* stream) {
   int st = skv::check_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,

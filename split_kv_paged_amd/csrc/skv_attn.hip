@@ -1,6 +1,7 @@
 // Segment-attention launcher: picks the matrix-core or the vector-ALU kernel
 // from the number of query rows a work-group carries (GQA group x max query
-// tokens) and launches a 1-D grid over the work list x kv heads.
+// tokens) and launches a 1-D grid over the work list x kv heads (planned
+// split) or over sequences x segments x kv heads (fixed split, no plan).
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Modifications: the attention kernel is launched as
@@ -38,8 +39,17 @@ int launch_segments(const AttnArgs& a, void* stream) {
   sp.G = a.q_heads / a.kv_heads;
   sp.seg_max = a.seg_max;
   sp.causal = a.causal;
-  const long long grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) *
-                         a.kv_heads;
+  sp.tok_out = nullptr;
+  sp.fixed_S = 0;
+  long long grid;
+  if (a.plan) {
+    grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) * a.kv_heads;
+  } else {
+    // fixed split: one work-group per (sequence, segment, kv head)
+    sp.fixed_S = fixed_split_count(a.bs, a.kv_heads, a.num_cus, a.seg_max);
+    sp.tok_out = a.tok_nseg;
+    grid = static_cast<long long>(sp.fixed_S) * a.bs * a.kv_heads;
+  }
   if (grid > 0x7fffffffLL) return SKV_EUNSUPPORTED;
   const int e = a.kv_dtype == SKV_KV_FP8_E4M3FN ? 1 : 2;
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;

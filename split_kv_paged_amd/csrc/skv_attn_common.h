@@ -27,7 +27,9 @@ struct SegParams {
   const float* v_scale;
   float* part_o;              // [total_q, Hq, seg_max, 128]
   float* part_lse;            // [total_q, Hq, seg_max]
+  int32_t* tok_out;           // fixed split: per-token segment counts written here
   int pt_stride, bs, Hq, Hkv, G, seg_max, causal;
+  int fixed_S;                // 0: planned split (plan); > 0: fixed split, S per sequence
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -81,14 +83,58 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 // Work-item prologue shared by all variants [sglang PR #39172, Modifications:
 // the segment kernel decodes (seq, seg) from its work-list word and leaves on
 // -1 before touching memory; tiles per segment come from the first plan word].
+// Without a plan (fixed_S > 0) the grid is (sequence, segment, kv head) and
+// each sequence's pages are cut into fixed_S segments of ceil(pages / fixed_S)
+// pages [same PR, Motivation: the fixed split gives every sequence the same
+// segment count; Modifications: bs == 1 runs it without a plan].
 struct SegItem {
   int valid;
   int seq, seg, g;
   int L, c0, qn, rows;
   int seg_start, seg_end;   // absolute token range of the segment
+  int seg_pages;            // fixed split: pages per segment of this sequence
 };
 
+__device__ __forceinline__ SegItem decode_fixed(const SegParams& p) {
+  SegItem it;
+  it.valid = 0;
+  const int widx = blockIdx.x / p.Hkv;
+  it.g = blockIdx.x - widx * p.Hkv;
+  it.seq = widx / p.fixed_S;
+  it.seg = widx - it.seq * p.fixed_S;
+  it.L = p.seq_lens[it.seq];
+  it.c0 = p.cu_q[it.seq];
+  it.qn = p.cu_q[it.seq + 1] - it.c0;
+  it.rows = p.G * it.qn;
+  const int pages = it.L <= 0 ? 0 : (it.L >> 4) + ((it.L & 15) != 0);
+  it.seg_pages = pages == 0 ? 1 : 1 + (pages - 1) / p.fixed_S;
+  const long long seg_tokens = static_cast<long long>(it.seg_pages) * kPageSize;
+  const long long s0 = it.seg * seg_tokens;
+  if (s0 >= it.L || it.qn <= 0) return it;
+  const long long s1 = s0 + seg_tokens;
+  it.seg_start = static_cast<int>(s0);
+  it.seg_end = static_cast<int>(s1 < it.L ? s1 : it.L);
+  it.valid = 1;
+  return it;
+}
+
+// Fixed split: the (sequence, segment 0, kv head 0) work-group writes its
+// tokens' segment counts, ceil(visible / segment tokens), for the reduce.
+__device__ __forceinline__ void write_fixed_counts(const SegParams& p, const SegItem& it) {
+  if (p.fixed_S == 0 || it.seg != 0 || it.g != 0) return;
+  const int j = threadIdx.x;
+  if (j >= it.qn) return;
+  int vis = it.L;
+  if (p.causal) {
+    vis = it.L - it.qn + j + 1;
+    vis = vis < 0 ? 0 : (vis > it.L ? it.L : vis);
+  }
+  const long long seg_tokens = static_cast<long long>(it.seg_pages) * kPageSize;
+  p.tok_out[it.c0 + j] = vis <= 0 ? 0 : static_cast<int>(1 + (vis - 1) / seg_tokens);
+}
+
 __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
+  if (p.fixed_S > 0) return decode_fixed(p);
   SegItem it;
   it.valid = 0;
   const int widx = blockIdx.x / p.Hkv;

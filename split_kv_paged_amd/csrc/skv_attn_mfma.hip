@@ -184,6 +184,7 @@ void seg_mfma_kernel(SegParams p) {
   float(*sm_l)[16] = reinterpret_cast<float(*)[16]>(ring + kWaves * 8 * 64 * 16 + kWaves * 16 * 4);
 
   const SegItem it = decode_item(p);
+  write_fixed_counts(p, it);
   if (!it.valid) return;                                          // work-group uniform
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -130,6 +130,7 @@ void seg_valu_kernel(SegParams p) {
   __shared__ float sm_l[kWaves][RM];
 
   const SegItem it = decode_item(p);
+  write_fixed_counts(p, it);
   if (!it.valid) return;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

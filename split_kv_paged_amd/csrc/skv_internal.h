@@ -41,6 +41,16 @@ int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
                        int kv_heads, int page_size, int head_dim,
                        int elem_bytes, int direction);
 
+// Segments per sequence of the fixed split: max(1, min(seg_max,
+// pow2floor(num_cus / (bs * kv_heads)))).
+inline int fixed_split_count(int bs, int kv_heads, int num_cus, int seg_max) {
+  const long long q = static_cast<long long>(num_cus) / (static_cast<long long>(bs) * kv_heads);
+  long long p = 1;
+  while (p * 2 <= q) p *= 2;
+  if (q < 1) p = 1;
+  return static_cast<int>(p < seg_max ? p : seg_max);
+}
+
 inline int plan_width(int bs, int kv_heads, int num_cus) {
   int cap = num_cus / kv_heads;
   return cap > bs ? cap : bs;
@@ -60,8 +70,8 @@ struct AttnArgs {
   const float* k_scale;
   const float* v_scale;
   int causal;
-  const int32_t* plan;
-  const int32_t* tok_nseg;
+  const int32_t* plan;       // NULL: fixed split
+  int32_t* tok_nseg;         // read by the reduce; written by the fixed split
   int num_cus, seg_max;
   float* part_o;
   float* part_lse;

@@ -26,8 +26,9 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     const void* plan, const void* tok_nseg, int num_cus,
                     int seg_max, const void* part_o, const void* part_lse,
                     const void* out) {
-  if (!q || !kv_a || !page_table || !seq_lens || !cu_seqlens_q || !plan ||
-      !tok_nseg || !part_o || !part_lse || !out)
+  (void)plan;   // NULL selects the fixed split
+  if (!q || !kv_a || !page_table || !seq_lens || !cu_seqlens_q || !tok_nseg ||
+      !part_o || !part_lse || !out)
     return SKV_EINVAL;
   if (layout != SKV_LAYOUT_STANDARD && layout != SKV_LAYOUT_SHUFFLED)
     return SKV_EINVAL;

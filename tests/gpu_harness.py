@@ -18,16 +18,22 @@ def say(*a):
 
 
 def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_max=None,
-            causal=None):
+            causal=None, fixed=False):
     """Plan + (optional shuffle) + attention + reduce on cuda:0. Returns a dict of
-    host copies (plan, tok_nseg, out as float64, lse) plus the device planes."""
+    host copies (plan, tok_nseg, out as float64, lse) plus the device planes.
+    fixed=True runs the fixed split (no plan; the segment kernel writes tok_nseg,
+    which starts out holding -7 so an unwritten entry shows)."""
     cfg = case.cfg
     layout = layout or cfg.layout
     num_cus = num_cus or cfg.num_cus
     seg_max = seg_max or cfg.seg_max
     causal = cfg.causal if causal is None else causal
-    plan, tok = skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, cfg.kv_heads,
-                               num_cus, seg_max, causal)
+    if fixed:
+        plan = None
+        tok = torch.full((cfg.total_q,), -7, dtype=torch.int32, device=case.q.device)
+    else:
+        plan, tok = skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q,
+                                   cfg.kv_heads, num_cus, seg_max, causal)
     if layout == "shuffled" and planes is None:
         planes = skv.kv_page_shuffle(case.kv)
     rows = cfg.total_q * cfg.q_heads * seg_max
@@ -42,7 +48,8 @@ def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_ma
         kv_dtype=cfg.kv_dtype, layout=layout, k_scale=case.k_scale, v_scale=case.v_scale,
         causal=causal, part_o=part_o, part_lse=part_lse, out_lse=out_lse)
     torch.cuda.synchronize()
-    return dict(plan=plan.cpu().numpy().tolist(), tok=tok.cpu().numpy().tolist(),
+    return dict(plan=None if plan is None else plan.cpu().numpy().tolist(),
+                tok=tok.cpu().numpy().tolist(),
                 out=out.float().cpu().numpy().astype(np.float64),
                 out_bits=gen.raw_u16(out), lse=out_lse.cpu().numpy().astype(np.float64),
                 planes=planes)

@@ -79,8 +79,10 @@ def _attn(**kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(q=None), 1), (dict(kv_a=None), 1), (dict(pt=None), 1), (dict(plan=None), 1),
+    (dict(q=None), 1), (dict(kv_a=None), 1), (dict(pt=None), 1),
     (dict(tok=None), 1), (dict(part_o=None), 1), (dict(part_lse=None), 1), (dict(out=None), 1),
+    (dict(plan=None, tok=None), 1),                       # the fixed split writes tok_nseg
+    (dict(plan=None, head_dim=64), 2),
     (dict(seq_lens=None), 1), (dict(cu=None), 1),
     (dict(layout=2), 1), (dict(kv_dtype=2), 1),
     (dict(layout=1), 1),                                  # shuffled needs the V plane

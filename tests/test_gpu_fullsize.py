@@ -119,3 +119,25 @@ def test_full_size_convert_round_trip():
     skv.kv_page_convert(kp, vp, direction="to_standard")
     torch.cuda.synchronize()
     assert torch.equal(kp, k0) and torch.equal(vp, v0)
+
+
+@pytest.mark.parametrize("name", ["agentic_skew", "fp8_kv"], ids=str)
+def test_full_size_fixed_split(name):
+    """The fixed split (no plan) on a full-size skewed batch: per-token counts
+    bit-exact, sampled rows against the oracle."""
+    cfg = configs.BY_NAME[name]
+    say("fullsize fixed", name, "generating")
+    case = gen.make_case(cfg, DEV)
+    hip = run_hip(case, fixed=True)
+    hip.pop("planes")
+    _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                             cfg.kv_heads, 16, cfg.num_cus, cfg.seg_max,
+                                             cfg.causal)
+    assert hip["tok"] == want_tok
+    assert np.all(np.isfinite(hip["out"]))
+    rows = _sample_rows(cfg, SAMPLES[name], n_heads=4, seed=9)
+    ref_out, ref_lse = run_oracle(case, rows=rows)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, cfg.kv_dtype, rows=rows)
+    say("fullsize fixed", name, r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3, r

@@ -157,6 +157,33 @@ def test_attention_matches_oracle(spec):
     assert r["lse_err"] <= 1e-3, r
 
 
+FIXED_CASES = CASES + [
+    # bs 1: the fixed split's own case (64 segments), and S = 1 (bs * kv_heads > num_cus)
+    ("bs1_long", [70000], [4], 32, 2, "bf16", "standard", 1, 256, 64),
+    ("bs1_fp8_q1", [9000], [1], 16, 2, "fp8", "shuffled", 1, 256, 64),
+    ("fixed_S1", [50, 900, 17, 3000], [1, 2, 3, 4], 16, 4, "bf16", "standard", 1, 8, 64),
+]
+
+
+@pytest.mark.parametrize("spec", FIXED_CASES, ids=lambda c: c[0])
+def test_fixed_split_matches_oracle(spec):
+    """No plan: the fixed split's segment counts bit-exact, the output within
+    tolerance of the unsplit oracle."""
+    say("fixed", spec[0])
+    case = _mk(*spec)
+    cfg = case.cfg
+    hip = run_hip(case, fixed=True)
+    _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                             cfg.kv_heads, 16, cfg.num_cus, cfg.seg_max,
+                                             cfg.causal)
+    assert hip["tok"] == want_tok
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, cfg.kv_dtype)
+    say(spec[0], r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3, r
+
+
 @pytest.mark.parametrize("spec", [CASES[2], CASES[8], CASES[12]], ids=lambda c: c[0])
 def test_nan_poison_does_not_leak(spec):
     a = run_hip(_mk(*spec, poison="finite"))
