@@ -25,8 +25,9 @@ Modules:
   attention  page gather + unsplit fp64 attention               -- pinned
   planner    length-aware segment planner, fixed split          -- pinned
   merge      per-segment partials and log-sum-exp merge         -- pinned
-  shuffle    standard <-> shuffled page repack, and the in-place
-             conversion of received byte halves (+ inverse)     -- pinned
+  shuffle    standard <-> shuffled page repack, the in-place
+             conversion of received byte halves (+ inverse), and
+             the cache writer (new tokens at their slots)       -- pinned
 Every function is pinned by tests under tests/test_oracle_*.py against values
 the pages print, closed forms, invariants, brute force or an independent
 library routine; none is "parity unpinned".
@@ -37,7 +38,8 @@ from .attention import (gather_standard, gather_shuffled, visible_keys,
 from .planner import plan_segments, fixed_split_segments, fixed_split_plan, pow2floor
 from .merge import segment_partials, lse_merge, split_decode_attention
 from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
-                      convert_halves, revert_to_halves)
+                      convert_halves, revert_to_halves, write_tokens_standard,
+                      write_tokens_shuffled)
 
 __all__ = [
     "decode_bf16", "decode_e4m3fn", "e4m3fn_value", "decode_kv",
@@ -46,5 +48,5 @@ __all__ = [
     "pow2floor",
     "segment_partials", "lse_merge", "split_decode_attention",
     "shuffle_blocks", "unshuffle_blocks", "halves_from_standard", "convert_halves",
-    "revert_to_halves",
+    "revert_to_halves", "write_tokens_standard", "write_tokens_shuffled",
 ]

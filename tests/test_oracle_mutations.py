@@ -16,6 +16,7 @@ import oracle.merge as merge
 import oracle.planner as planner
 import oracle.shuffle as shuffle
 import test_oracle_attention as TA
+import test_oracle_cache_write as TW
 import test_oracle_convert as TC
 import test_oracle_fp8 as TF
 import test_oracle_planner as TP
@@ -26,7 +27,7 @@ from conftest import load_golden
 def _pins():
     """(name, callable) for every pin, parametrized ones expanded."""
     pins = []
-    for mod in (TA, TC, TF, TP, TS):
+    for mod in (TA, TC, TF, TP, TS, TW):
         for name in dir(mod):
             if not name.startswith("test_"):
                 continue
@@ -184,6 +185,20 @@ def _fixed_floor(seq_lens, cu, kv_heads, page_size, num_cus=256, seg_max=64, cau
     return S, [max(n // S, 1) if n else 0 for n in pages], tok     # floor, not ceil
 
 
+def _write_k_transposed(k_plane, v_plane, key, value, slot_mapping):
+    kp, vp = TRUE_WRITE(k_plane, v_plane, key, value, slot_mapping)
+    B, H, Dx, N, x = kp.shape
+    c = np.arange(Dx * x)
+    for t, slot in enumerate(slot_mapping):
+        if slot < 0:
+            continue
+        b, n = divmod(int(slot), N)
+        for h in range(H):
+            kp[b, h, c % Dx, n, c // Dx] = key[t, h]          # channel split the wrong way
+    return kp, vp
+
+
+TRUE_WRITE = shuffle.write_tokens_shuffled
 TRUE_FIXED = planner.fixed_split_plan
 TRUE_HALVES = shuffle.halves_from_standard
 TRUE_GATHER = att.gather_standard
@@ -229,6 +244,9 @@ MUTATIONS = [
                             (oracle, "shuffle_blocks", _shuffle_transposed)]),
     ("fixed split floors the segment length", [(planner, "fixed_split_plan", _fixed_floor),
                                                (oracle, "fixed_split_plan", _fixed_floor)]),
+    ("cache writer K channel split transposed",
+     [(shuffle, "write_tokens_shuffled", _write_k_transposed),
+      (oracle, "write_tokens_shuffled", _write_k_transposed)]),
     ("byte halves swapped", [(shuffle, "halves_from_standard", _halves_swapped),
                              (oracle, "halves_from_standard", _halves_swapped)]),
 ]
