@@ -121,6 +121,23 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         res["convert_back_us"] = to_b
         res["convert_back_gbs"] = moved / to_b / 1e3
         del kh, vh, flat
+        # cache writer: one decode step's new token per sequence into the planes
+        tab = case.page_table
+        last = (case.seq_lens.long() - 1).clamp(min=0)
+        slots = tab.gather(1, (last // 16).view(-1, 1).int()).view(-1).long() * 16 + last % 16
+        knew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
+        vnew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
+        for _ in range(5):
+            skv.kv_cache_write(knew, vnew, slots, kp, vp)
+        ev[0].record(st)
+        for _ in range(n):
+            skv.kv_cache_write(knew, vnew, slots, kp, vp)
+        ev[1].record(st)
+        torch.cuda.synchronize()
+        res["cache_write_us"] = ev[0].elapsed_time(ev[1]) * 1e3 / n
+        res["cache_write_tokens"] = cfg.bs
+        # restore the planes for the attention steps
+        skv.kv_page_shuffle(case.kv, kp, vp)
         kv_a, kv_b = kp, vp
     rows = cfg.total_q * cfg.q_heads * cfg.seg_max
     part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
@@ -312,7 +329,8 @@ def main():
     }
     repack = {k: round(head[k], 2) for k in ("shuffle_us", "shuffle_gbs", "convert_us",
                                              "convert_gbs", "convert_back_us",
-                                             "convert_back_gbs") if k in head}
+                                             "convert_back_gbs", "cache_write_us",
+                                             "cache_write_tokens") if k in head}
     if repack:
         line["repack"] = repack
     if a.all:

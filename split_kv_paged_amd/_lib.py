@@ -40,6 +40,8 @@ _SIGNATURES = {
                                      _c_int, _p]),
     "skv_kv_page_unshuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _p]),
+    "skv_kv_cache_write": (_c_int, [_p, _p, _p, _c_int, ctypes.c_longlong, ctypes.c_longlong,
+                                    _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
     "skv_strerror": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -281,3 +283,22 @@ def kv_page_unshuffle(k_plane, v_plane, std_cache=None, block_ids=None, stream=N
                                       _ptr(block_ids), nb, H, N, D, e, _stream(stream))
     _check(st, "skv_kv_page_unshuffle")
     return std_cache
+
+
+def kv_cache_write(key, value, slot_mapping, k_plane, v_plane, stream=None):
+    """Write new tokens (key, value [T, H, D], the cache's element type; token
+    rows may be strided) into the shuffled planes at slot_mapping (int64 [T];
+    negative = padding). Returns the planes."""
+    B, H, D, N, e = _planes(k_plane, v_plane)
+    for t, n in ((key, "key"), (value, "value")):
+        if not t.is_cuda or t.dim() != 3 or t.shape[1:] != (H, D):
+            raise ValueError(f"{n}: expected a device tensor [T, {H}, {D}]")
+        if t.stride(2) != 1 or t.stride(1) != D or t.element_size() != e:
+            raise ValueError(f"{n}: heads and channels must be dense, element size {e}")
+    _need(slot_mapping, torch.int64, "slot_mapping", key.shape[0])
+    T = key.shape[0]
+    st = load().skv_kv_cache_write(_ptr(key), _ptr(value), _ptr(slot_mapping), T,
+                                   key.stride(0), value.stride(0), _ptr(k_plane),
+                                   _ptr(v_plane), B, H, N, D, e, _stream(stream))
+    _check(st, "skv_kv_cache_write")
+    return k_plane, v_plane

@@ -162,6 +162,22 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
                                num_blocks, kv_heads, elem_bytes, stream);
 }
 
+int skv_kv_cache_write(const void* key, const void* value,
+                       const int64_t* slot_mapping, int num_tokens,
+                       long long key_stride, long long value_stride,
+                       void* k_plane, void* v_plane, int num_blocks,
+                       int kv_heads, int page_size, int head_dim,
+                       int elem_bytes, void* stream) {
+  int st = skv::check_cache_write_args(key, value, slot_mapping, num_tokens,
+                                       key_stride, value_stride, k_plane, v_plane,
+                                       num_blocks, kv_heads, page_size, head_dim,
+                                       elem_bytes);
+  if (st != SKV_OK) return st;
+  return skv::launch_cache_write(key, value, slot_mapping, num_tokens, key_stride,
+                                 value_stride, k_plane, v_plane, num_blocks,
+                                 kv_heads, elem_bytes, stream);
+}
+
 const char* skv_strerror(int status) {
   switch (status) {
     case SKV_OK: return "ok";

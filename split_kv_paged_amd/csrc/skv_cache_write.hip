@@ -1,0 +1,101 @@
+// Cache writer: new tokens' K and V straight into shuffled pages.
+//
+// vLLM RFC #59111, "NixlConnector: convert standard KV pages to ROCm AITER
+// shuffled pages on the decode side", Background and Proposed Change §4: the
+// shuffled backend's writer places each token at the slot its slot mapping
+// names (block = slot / N, row = slot % N), K as [H, D/x, N, x] and V as
+// [H, N/x, D, x] per block, x = 16 / element bytes; padding tokens carry a
+// negative slot.
+//
+// MI355X design: one wave64 per (token, kv head). The token's K row is D*e
+// bytes = D/x chunks of 16 bytes, and each chunk lands whole in the K plane
+// (x consecutive channels of one row), so lanes 0 .. D/x-1 move one 16-byte
+// chunk each. In the V plane consecutive tokens of one channel share a
+// 16-byte chunk, so a token's V row scatters: lane l writes channels 2l and
+// 2l+1 (e bytes each) at stride x*e. Tokens of one block write disjoint bytes,
+// so concurrent waves need no ordering. Decode steps write few tokens; the
+// kernel is launch-bound, not bandwidth-bound.
+#include <hip/hip_runtime.h>
+
+#include "skv.h"
+#include "skv_internal.h"
+
+namespace skv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kN = kPageSize;
+constexpr int kD = kHeadDim;
+
+template <int E>
+__global__ __launch_bounds__(kThreads) void cache_write_kernel(
+    const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
+    const int64_t* __restrict__ slots, int num_tokens, long long key_stride,
+    long long value_stride, uint8_t* __restrict__ kp, uint8_t* __restrict__ vp,
+    int kv_heads, long long num_slots) {
+  constexpr int kX = 16 / E;
+  constexpr int kKChunks = kD * E / 16;
+  constexpr size_t kPlane = static_cast<size_t>(kN) * kD * E;   // one head of one block
+  const int lane = threadIdx.x & 63;
+  const long long unit = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (unit >= static_cast<long long>(num_tokens) * kv_heads) return;   // wave-uniform
+  const int t = static_cast<int>(unit / kv_heads);
+  const int h = static_cast<int>(unit % kv_heads);
+  const long long slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;                           // padding / out of range
+  const long long b = slot / kN;
+  const int n = static_cast<int>(slot % kN);
+  const size_t head = static_cast<size_t>(b) * kv_heads + h;
+  const uint8_t* krow = key + (t * key_stride + static_cast<long long>(h) * kD) * E;
+  const uint8_t* vrow = value + (t * value_stride + static_cast<long long>(h) * kD) * E;
+  uint8_t* kdst = kp + head * kPlane;
+  uint8_t* vdst = vp + head * kPlane;
+  // K: chunk c1 (channels c1*x .. c1*x + x-1) -> k_plane[b, h, c1, n, :]
+  if (lane < kKChunks) {
+    const uint4 v = *reinterpret_cast<const uint4*>(krow + 16 * lane);
+    *reinterpret_cast<uint4*>(kdst + (static_cast<size_t>(lane) * kN + n) * 16) = v;
+  }
+  // V: channel d -> v_plane[b, h, n / x, d, n % x]
+  const size_t vbase = static_cast<size_t>(n / kX) * kD * kX + n % kX;
+  const int d = 2 * lane;
+  if constexpr (E == 2) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + 2 * d);
+    reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d) * kX] =
+        static_cast<uint16_t>(w);
+    reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d + 1) * kX] =
+        static_cast<uint16_t>(w >> 16);
+  } else {
+    const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + d);
+    vdst[vbase + static_cast<size_t>(d) * kX] = static_cast<uint8_t>(w);
+    vdst[vbase + static_cast<size_t>(d + 1) * kX] = static_cast<uint8_t>(w >> 8);
+  }
+}
+
+}  // namespace
+
+int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
+                       int num_tokens, long long key_stride, long long value_stride,
+                       void* k_plane, void* v_plane, int num_blocks, int kv_heads,
+                       int elem_bytes, void* stream) {
+  const long long units = static_cast<long long>(num_tokens) * kv_heads;
+  const long long blocks = (units + kWaves - 1) / kWaves;
+  if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
+  const long long num_slots = static_cast<long long>(num_blocks) * kPageSize;
+  auto st = static_cast<hipStream_t>(stream);
+  auto k = static_cast<const uint8_t*>(key);
+  auto v = static_cast<const uint8_t*>(value);
+  auto kp = static_cast<uint8_t*>(k_plane);
+  auto vp = static_cast<uint8_t*>(v_plane);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(cache_write_kernel<2>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, k, v, slot_mapping, num_tokens, key_stride,
+                       value_stride, kp, vp, kv_heads, num_slots);
+  else
+    hipLaunchKernelGGL(cache_write_kernel<1>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kThreads), 0, st, k, v, slot_mapping, num_tokens, key_stride,
+                       value_stride, kp, vp, kv_heads, num_slots);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+}  // namespace skv

@@ -41,6 +41,12 @@ int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
                        int kv_heads, int page_size, int head_dim,
                        int elem_bytes, int direction);
 
+int check_cache_write_args(const void* key, const void* value, const void* slots,
+                           int num_tokens, long long key_stride,
+                           long long value_stride, const void* k_plane,
+                           const void* v_plane, int num_blocks, int kv_heads,
+                           int page_size, int head_dim, int elem_bytes);
+
 // Segments per sequence of the fixed split: max(1, min(seg_max,
 // pow2floor(num_cus / (bs * kv_heads)))).
 inline int fixed_split_count(int bs, int kv_heads, int num_cus, int seg_max) {
@@ -95,6 +101,10 @@ int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
 int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
                      const int32_t* block_ids, int num_blocks, int kv_heads,
                      int elem_bytes, void* stream);
+int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
+                       int num_tokens, long long key_stride, long long value_stride,
+                       void* k_plane, void* v_plane, int num_blocks, int kv_heads,
+                       int elem_bytes, void* stream);
 
 }  // namespace skv
 

@@ -86,4 +86,22 @@ int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
   return SKV_OK;
 }
 
+int check_cache_write_args(const void* key, const void* value, const void* slots,
+                           int num_tokens, long long key_stride,
+                           long long value_stride, const void* k_plane,
+                           const void* v_plane, int num_blocks, int kv_heads,
+                           int page_size, int head_dim, int elem_bytes) {
+  if (!key || !value || !slots || !k_plane || !v_plane) return SKV_EINVAL;
+  if (num_tokens < 1 || num_blocks < 1 || kv_heads < 1 || page_size < 1 ||
+      head_dim < 1)
+    return SKV_EINVAL;
+  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
+  const long long row = static_cast<long long>(kv_heads) * head_dim;
+  const int x = 16 / elem_bytes;
+  if (key_stride < row || value_stride < row) return SKV_EINVAL;
+  if (key_stride % x != 0 || value_stride % x != 0) return SKV_EINVAL;
+  return SKV_OK;
+}
+
 }  // namespace skv

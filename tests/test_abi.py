@@ -163,6 +163,24 @@ def test_unshuffle_errors(kw, code):
     assert _unshuffle(**kw) == code
 
 
+def _write(**kw):
+    a = dict(k=P, v=P, slots=P, T=4, ks=256, vs=256, kp=P, vp=P, nb=8, h=2, ps=16, hd=128, e=2)
+    a.update(kw)
+    return skv.load().skv_kv_cache_write(a["k"], a["v"], a["slots"], a["T"], a["ks"], a["vs"],
+                                         a["kp"], a["vp"], a["nb"], a["h"], a["ps"], a["hd"],
+                                         a["e"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), 1), (dict(v=None), 1), (dict(slots=None), 1), (dict(kp=None), 1),
+    (dict(vp=None), 1), (dict(T=0), 1), (dict(nb=0), 1), (dict(h=0), 1),
+    (dict(ks=255), 1), (dict(vs=128), 1), (dict(ks=260), 1),       # below H*D / not a multiple of x
+    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+])
+def test_cache_write_errors(kw, code):
+    assert _write(**kw) == code
+
+
 def test_python_binding_raises_on_error_status():
     with pytest.raises(_lib.SkvError) as ei:
         _lib._check(2, "x")

@@ -1,0 +1,120 @@
+"""GPU parity (through the C ABI) of the cache writer into shuffled pages:
+bit-exact against the CPU oracle, and a decode step that writes the newest
+tokens and then attends over them."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import split_kv_paged_amd as skv
+from gpu_harness import TOL, compare, run_oracle, say
+from workloads import configs, gen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N, D = 16, 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    skv.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(a, e):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16) if e == 2 else
+                            np.ascontiguousarray(a)).to(DEV)
+
+
+def _host(t, e):
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if e == 2 else a
+
+
+@pytest.mark.parametrize("e,H", [(2, 1), (2, 2), (2, 8), (1, 2), (1, 8)])
+def test_cache_write_bit_exact(e, H):
+    say("cache write", e, H)
+    rng = np.random.default_rng(40 + 3 * H + e)
+    dt = np.uint16 if e == 2 else np.uint8
+    x = 16 // e
+    B, T = 9, 70
+    pad = 3 * x                                            # strided token rows
+    kfull = rng.integers(0, 1 << (8 * e), size=(T, H * D + pad)).astype(dt)
+    vfull = rng.integers(0, 1 << (8 * e), size=(T, H * D + pad)).astype(dt)
+    slots = rng.choice(B * N, size=T, replace=False).astype(np.int64)
+    slots[[0, 11, 40]] = -1                                # padding tokens
+    kp0 = rng.integers(0, 1 << (8 * e), size=(B, H, D // x, N, x)).astype(dt)
+    vp0 = rng.integers(0, 1 << (8 * e), size=(B, H, N // x, D, x)).astype(dt)
+    kp, vp = _dev(kp0, e), _dev(vp0, e)
+    kd, vd = _dev(kfull, e), _dev(vfull, e)
+    key = kd[:, :H * D].view(T, H, D)
+    val = vd[:, :H * D].view(T, H, D)
+    skv.kv_cache_write(key, val, torch.as_tensor(slots, device=DEV), kp, vp)
+    torch.cuda.synchronize()
+    wk, wv = oracle.write_tokens_shuffled(kp0, vp0, kfull[:, :H * D].reshape(T, H, D),
+                                          vfull[:, :H * D].reshape(T, H, D), slots)
+    assert np.array_equal(_host(kp, e), wk)
+    assert np.array_equal(_host(vp, e), wv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_decode_step_writes_then_attends(dtype):
+    """A verify step: each sequence's last q tokens are written into the
+    shuffled cache through their slots, then attention reads them. Against the
+    oracle writing the same tokens into standard pages."""
+    say("write+attend", dtype)
+    base = configs.FP8_KV if dtype == "fp8" else configs.TINY
+    lens, ql = [40, 300, 17, 1000, 2], [2, 4, 1, 3, 1]
+    cfg = gen.small_config(base, lens, ql, q_heads=16, kv_heads=2, layout="shuffled",
+                           num_cus=64, seg_max=16, seed=21)
+    case = gen.make_case(cfg, DEV)
+    e = 2 if dtype == "bf16" else 1
+    H = cfg.kv_heads
+    table = case.page_table.cpu().numpy()
+    slots = []
+    for i, (L, q) in enumerate(zip(lens, ql)):
+        for pos in range(L - q, L):
+            slots.append(int(table[i, pos // N]) * N + pos % N)
+    slots = np.array(slots, dtype=np.int64)
+    T = len(slots)
+    # new K/V codes: copies of other real tokens' rows (unit-scale values of the
+    # batch's own distribution), so the step changes what attention sees
+    rng = np.random.default_rng(8)
+    std0 = gen.raw_kv(case)
+    real = [(i, p) for i, L in enumerate(lens) for p in range(L)]
+    pick = rng.choice(len(real), size=(2, T))
+    kv_new = np.empty((2, T, H, D), dtype=std0.dtype)
+    for w in range(2):
+        for t in range(T):
+            i, pos = real[pick[w, t]]
+            row = std0[int(table[i, pos // N]), :, pos % N]
+            kv_new[w, t] = row[:, :D] if w == 0 else row[:, D:]
+    kp, vp = skv.kv_page_shuffle(case.kv)
+    key = _dev(kv_new[0], e).view(T, H, D)
+    val = _dev(kv_new[1], e).view(T, H, D)
+    if dtype == "bf16":
+        key, val = key.view(torch.bfloat16), val.view(torch.bfloat16)
+    skv.kv_cache_write(key, val, torch.as_tensor(slots, device=DEV), kp, vp)
+    plan, tok = skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, H,
+                               cfg.num_cus, cfg.seg_max, cfg.causal)
+    out_lse = torch.empty((cfg.total_q, cfg.q_heads), dtype=torch.float32, device=DEV)
+    out, _ = skv.paged_decode_attn(case.q, kp, vp, case.page_table, case.seq_lens,
+                                   case.cu_seqlens_q, plan, tok, kv_heads=H, max_q=cfg.max_q,
+                                   num_cus=cfg.num_cus, seg_max=cfg.seg_max,
+                                   kv_dtype=dtype, layout="shuffled", k_scale=case.k_scale,
+                                   v_scale=case.v_scale, out_lse=out_lse)
+    torch.cuda.synchronize()
+    # oracle: the same tokens written into the standard pages
+    std = oracle.write_tokens_standard(std0, kv_new[0], kv_new[1], slots)
+    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    ref_out, ref_lse = oracle.decode_attention(
+        q, std, dtype, table, case.seq_lens.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
+        H, N, cfg.causal, cfg.k_scale, cfg.v_scale)
+    r = compare(out.float().cpu().numpy().astype(np.float64),
+                out_lse.cpu().numpy().astype(np.float64), ref_out, ref_lse, dtype)
+    say("write+attend", dtype, r)
+    assert r["max_abs"] <= TOL[dtype], r
+    assert r["lse_err"] <= 1e-3, r
