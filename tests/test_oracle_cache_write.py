@@ -21,8 +21,9 @@ def test_hand_derived_slot():
     assert np.count_nonzero(kp2) == H * D and np.count_nonzero(vp2) == H * D
 
 
+@pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (4, 1)])
-def test_equals_standard_write_then_shuffle(H, e):
+def test_equals_standard_write_then_shuffle(H, e, N):
     """Writing into shuffled planes equals writing into standard pages and then
     shuffling, on a cache that already holds data (untouched rows keep it);
     padding slots (-1) change nothing."""

@@ -39,10 +39,11 @@ def test_halves_are_the_byte_halves(H):
         assert vp[b].tobytes() == raw[len(raw) // 2:]
 
 
+@pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (3, 1), (4, 1)])
-def test_matches_out_of_place_shuffle_and_round_trips(H, e):
+def test_matches_out_of_place_shuffle_and_round_trips(H, e, N):
     B = 5
-    std = _ids(B, H)
+    std = np.arange(B * H * N * 2 * D, dtype=np.uint32).reshape(B, H, N, 2 * D)
     listed = [3, 0, 4]
     rng = np.random.default_rng(7)
     x = 16 // e

@@ -4,6 +4,7 @@ CPU, via monkeypatch) and check that at least one pin then fails.
 Each mutation is applied to the oracle only; the pins are the functions of
 tests/test_oracle_*.py, called directly.
 """
+import itertools
 import math
 
 import numpy as np
@@ -37,11 +38,15 @@ def _pins():
             if not params:
                 pins.append((name, fn))
                 continue
-            argnames, values = params[0].args[0], params[0].args[1]
-            names = [a.strip() for a in argnames.split(",")] if isinstance(argnames, str) else argnames
-            for v in values:
-                kw = dict(zip(names, v if len(names) > 1 else (v,)))
-                pins.append((f"{name}[{v}]", (lambda f=fn, k=kw: f(**k))))
+            axes = []                      # one list of keyword dicts per parametrize mark
+            for m in params:
+                argnames, values = m.args[0], m.args[1]
+                names = ([a.strip() for a in argnames.split(",")]
+                         if isinstance(argnames, str) else list(argnames))
+                axes.append([dict(zip(names, v if len(names) > 1 else (v,))) for v in values])
+            for combo in itertools.product(*axes):
+                kw = {k: v for d in combo for k, v in d.items()}
+                pins.append((f"{name}[{kw}]", (lambda f=fn, k=kw: f(**k))))
     return pins
 
 

@@ -7,10 +7,10 @@ from conftest import load_golden
 
 
 @pytest.mark.parametrize("case", load_golden("shuffle_offsets.json")["cases"],
-                         ids=lambda c: f'{c["plane"]}{c["elem_bytes"]}')
+                         ids=lambda c: f'{c["plane"]}{c["elem_bytes"]}N{c.get("page_size", 16)}')
 def test_hand_derived_offsets(case):
     e = case["elem_bytes"]
-    N, D = 16, 128
+    N, D = case.get("page_size", 16), 128
     std = np.zeros((1, 1, N, 2 * D), dtype=np.uint32)
     std.reshape(-1)[:] = np.arange(N * 2 * D)           # unique ids
     kp, vp = oracle.shuffle_blocks(std.astype(np.uint32), elem_bytes=e)
@@ -20,9 +20,10 @@ def test_hand_derived_offsets(case):
     assert case["token"] * 2 * D + ch == case["std_flat"]
 
 
+@pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (3, 1)])
-def test_bijection_and_inverse(H, e):
-    N, D = 16, 128
+def test_bijection_and_inverse(H, e, N):
+    D = 128
     B = 3
     std = np.arange(B * H * N * 2 * D, dtype=np.uint32).reshape(B, H, N, 2 * D)
     kp, vp = oracle.shuffle_blocks(std, elem_bytes=e)
