@@ -31,8 +31,9 @@
  *
  * Element types: Q and the output are bf16 (IEEE binary32 upper half). KV is
  * bf16 or OCP e4m3fn fp8 (kv_dtype 1) with per-tensor fp32 dequant scales.
- * Supported geometry: head_dim 128, page_size 16, 1..4 query tokens per
- * sequence, (q_heads / kv_heads) * max_q <= 64.
+ * Supported geometry: head_dim 128; page_size 16 for the planner and
+ * attention, 16 or 32 for the page repacks and the cache writer; 1..4 query
+ * tokens per sequence, (q_heads / kv_heads) * max_q <= 64.
  */
 #ifndef SKV_H_
 #define SKV_H_
@@ -185,7 +186,8 @@ int skv_split_reduce(const float* part_o, const float* part_lse,
  * with x = 16 / elem_bytes. Pure byte movement, bit-exact. Out of place: the
  * source must not overlap the planes. Blocks not listed are left untouched.
  * Errors: EINVAL for NULL required pointers, num_blocks < 1, kv_heads < 1;
- * EUNSUPPORTED for head_dim != 128, page_size != 16, elem_bytes not 1 or 2. */
+ * EUNSUPPORTED for head_dim != 128, page_size not 16 or 32, elem_bytes not 1
+ * or 2. */
 int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                         const int32_t* block_ids, int num_blocks, int kv_heads,
                         int page_size, int head_dim, int elem_bytes,
@@ -207,9 +209,10 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
  * 0..num_blocks-1); a block listed twice is rewritten by two work-groups at
  * once (undefined result). Blocks not listed are left untouched.
  * Errors: EINVAL for NULL planes, num_blocks < 1, kv_heads < 1, a direction
- * other than the two above; EUNSUPPORTED for head_dim != 128, page_size != 16,
- * elem_bytes not 1 or 2, or a block (2 * S) above 128 KiB (kv_heads > 16 for
- * bf16, > 32 for fp8): the whole block is staged in on-chip memory. */
+ * other than the two above; EUNSUPPORTED for head_dim != 128, page_size not 16
+ * or 32, elem_bytes not 1 or 2, or a block (2 * S) above 128 KiB (16-token
+ * pages: kv_heads > 16 for bf16, > 32 for fp8; half that for 32-token pages):
+ * the whole block is staged in on-chip memory. */
 int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
                         int num_blocks, int kv_heads, int page_size,
                         int head_dim, int elem_bytes, int direction,
@@ -241,7 +244,8 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
  * distinct: two tokens at one slot race. Bit-exact byte movement.
  * Errors: EINVAL for NULL pointers, num_tokens < 1, num_blocks < 1,
  * kv_heads < 1, a stride below kv_heads * head_dim or not a multiple of x;
- * EUNSUPPORTED for head_dim != 128, page_size != 16, elem_bytes not 1 or 2. */
+ * EUNSUPPORTED for head_dim != 128, page_size not 16 or 32, elem_bytes not 1
+ * or 2. */
 int skv_kv_cache_write(const void* key, const void* value,
                        const int64_t* slot_mapping, int num_tokens,
                        long long key_stride, long long value_stride,

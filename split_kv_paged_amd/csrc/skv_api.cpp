@@ -136,7 +136,7 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                                    kv_heads, page_size, head_dim, elem_bytes);
   if (st != SKV_OK) return st;
   return skv::launch_shuffle(std_cache, k_plane, v_plane, block_ids, num_blocks,
-                             kv_heads, elem_bytes, stream);
+                             kv_heads, page_size, elem_bytes, stream);
 }
 
 int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
@@ -147,7 +147,7 @@ int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
                                    page_size, head_dim, elem_bytes, direction);
   if (st != SKV_OK) return st;
   return skv::launch_convert(k_plane, v_plane, block_ids, num_blocks, kv_heads,
-                             elem_bytes, direction, stream);
+                             page_size, elem_bytes, direction, stream);
 }
 
 int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
@@ -159,7 +159,7 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
                                    kv_heads, page_size, head_dim, elem_bytes);
   if (st != SKV_OK) return st;
   return skv::launch_unshuffle(k_plane, v_plane, std_cache, block_ids,
-                               num_blocks, kv_heads, elem_bytes, stream);
+                               num_blocks, kv_heads, page_size, elem_bytes, stream);
 }
 
 int skv_kv_cache_write(const void* key, const void* value,
@@ -175,7 +175,7 @@ int skv_kv_cache_write(const void* key, const void* value,
   if (st != SKV_OK) return st;
   return skv::launch_cache_write(key, value, slot_mapping, num_tokens, key_stride,
                                  value_stride, k_plane, v_plane, num_blocks,
-                                 kv_heads, elem_bytes, stream);
+                                 kv_heads, page_size, elem_bytes, stream);
 }
 
 const char* skv_strerror(int status) {

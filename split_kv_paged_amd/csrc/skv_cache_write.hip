@@ -7,8 +7,9 @@
 // [H, N/x, D, x] per block, x = 16 / element bytes; padding tokens carry a
 // negative slot.
 //
-// MI355X design: one wave64 per (token, kv head). The token's K row is D*e
-// bytes = D/x chunks of 16 bytes, and each chunk lands whole in the K plane
+// MI355X design (16- or 32-token pages): one wave64 per (token, kv head). The
+// token's K row is D*e bytes = D/x chunks of 16 bytes, and each chunk lands
+// whole in the K plane
 // (x consecutive channels of one row), so lanes 0 .. D/x-1 move one 16-byte
 // chunk each. In the V plane consecutive tokens of one channel share a
 // 16-byte chunk, so a token's V row scatters: lane l writes channels 2l and
@@ -25,10 +26,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kN = kPageSize;
 constexpr int kD = kHeadDim;
 
-template <int E>
+template <int E, int kN>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
     const int64_t* __restrict__ slots, int num_tokens, long long key_stride,
@@ -77,24 +77,26 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
 int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
                        int num_tokens, long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int elem_bytes, void* stream) {
+                       int page_size, int elem_bytes, void* stream) {
   const long long units = static_cast<long long>(num_tokens) * kv_heads;
   const long long blocks = (units + kWaves - 1) / kWaves;
   if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
-  const long long num_slots = static_cast<long long>(num_blocks) * kPageSize;
+  const long long num_slots = static_cast<long long>(num_blocks) * page_size;
   auto st = static_cast<hipStream_t>(stream);
   auto k = static_cast<const uint8_t*>(key);
   auto v = static_cast<const uint8_t*>(value);
   auto kp = static_cast<uint8_t*>(k_plane);
   auto vp = static_cast<uint8_t*>(v_plane);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(cache_write_kernel<2>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, st, k, v, slot_mapping, num_tokens, key_stride,
-                       value_stride, kp, vp, kv_heads, num_slots);
-  else
-    hipLaunchKernelGGL(cache_write_kernel<1>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kThreads), 0, st, k, v, slot_mapping, num_tokens, key_stride,
-                       value_stride, kp, vp, kv_heads, num_slots);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+#define SKV_W(E, N)                                                                  \
+  hipLaunchKernelGGL((cache_write_kernel<E, N>), grid, block, 0, st, k, v, slot_mapping, \
+                     num_tokens, key_stride, value_stride, kp, vp, kv_heads, num_slots)
+  if (page_size == 32) {
+    if (elem_bytes == 2) SKV_W(2, 32); else SKV_W(1, 32);
+  } else {
+    if (elem_bytes == 2) SKV_W(2, 16); else SKV_W(1, 16);
+  }
+#undef SKV_W
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

@@ -17,6 +17,10 @@ constexpr int kMaxBs = 32767;    // seq << 16 stays a non-negative int32
 constexpr int kMaxSegMax = 65535;
 constexpr int kMaxConvertBytes = 128 * 1024;   // one block staged in LDS
 
+// page sizes of the repack entry points (shuffle, conversion, writer); the
+// attention path uses 16-token pages
+inline bool repack_page_size_ok(int page_size) { return page_size == 16 || page_size == 32; }
+
 // ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
 int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
                     int total_q, int kv_heads, int page_size, int num_cus,
@@ -94,17 +98,17 @@ int launch_reduce(const float* part_o, const float* part_lse,
                   int seg_max, void* out, float* out_lse, void* stream);
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
-                   int elem_bytes, void* stream);
+                   int page_size, int elem_bytes, void* stream);
 int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
-                   int num_blocks, int kv_heads, int elem_bytes, int direction,
-                   void* stream);
+                   int num_blocks, int kv_heads, int page_size, int elem_bytes,
+                   int direction, void* stream);
 int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
                      const int32_t* block_ids, int num_blocks, int kv_heads,
-                     int elem_bytes, void* stream);
+                     int page_size, int elem_bytes, void* stream);
 int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
                        int num_tokens, long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int elem_bytes, void* stream);
+                       int page_size, int elem_bytes, void* stream);
 
 }  // namespace skv
 

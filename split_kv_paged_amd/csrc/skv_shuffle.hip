@@ -6,8 +6,9 @@
 // shuffled layout stores K as [H, D/x, N, x] and V as [H, N/x, D, x] with
 // x = 16 / element bytes, and received blocks are converted block by block.
 //
-// MI355X design: one wave64 per (listed block, head). The wave copies the head's
-// whole standard tile (8 KB bf16 / 4 KB fp8) into LDS with coalesced 16-byte
+// MI355X design: one wave64 per (listed block, head); 16- or 32-token pages
+// (the RFC's decoders use both). The wave copies the head's whole standard
+// tile (8 KB bf16 / 4 KB fp8 per 16 tokens) into LDS with coalesced 16-byte
 // loads (1 KB contiguous per wave instruction), then writes both planes with
 // coalesced 16-byte stores: a K chunk is one 16-byte row chunk moved as a unit;
 // a V chunk gathers x tokens of one channel from LDS. Every HBM byte is read
@@ -23,10 +24,9 @@ namespace {
 
 constexpr int kShufThreads = 256;
 constexpr int kShufWaves = kShufThreads / 64;
-constexpr int kN = kPageSize;
 constexpr int kD = kHeadDim;
 
-template <int E>
+template <int E, int kN>
 struct ShufGeom {
   static constexpr int kX = 16 / E;                   // elements per 16 bytes
   static constexpr int kRowBytes = 2 * kD * E;        // one standard token row
@@ -36,12 +36,12 @@ struct ShufGeom {
   static constexpr int kChunks = kTileBytes / 16;     // 16-byte chunks per tile
 };
 
-template <int E>
+template <int E, int kN>
 __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ kpl,
     uint8_t* __restrict__ vpl, const int32_t* __restrict__ block_ids,
     int num_units, int kv_heads) {
-  using G = ShufGeom<E>;
+  using G = ShufGeom<E, kN>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kShufWaves][kN * G::kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.x * kShufWaves + wave;
@@ -104,27 +104,35 @@ __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
   }
 }
 
+template <int kN>
+int launch_shuffle_n(const uint8_t* s, uint8_t* k, uint8_t* v, const int32_t* block_ids,
+                     long long units, int kv_heads, int elem_bytes, hipStream_t st) {
+  const long long blocks = (units + kShufWaves - 1) / kShufWaves;
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL((shuffle_kernel<2, kN>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kShufThreads), 0, st, s, k, v, block_ids,
+                       static_cast<int>(units), kv_heads);
+  else
+    hipLaunchKernelGGL((shuffle_kernel<1, kN>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kShufThreads), 0, st, s, k, v, block_ids,
+                       static_cast<int>(units), kv_heads);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
 }  // namespace
 
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
-                   int elem_bytes, void* stream) {
+                   int page_size, int elem_bytes, void* stream) {
   const long long units = static_cast<long long>(num_blocks) * kv_heads;
-  const long long blocks = (units + kShufWaves - 1) / kShufWaves;
   if (units > 0x7fffffffLL) return SKV_EUNSUPPORTED;
   auto st = static_cast<hipStream_t>(stream);
   auto s = static_cast<const uint8_t*>(std_cache);
   auto k = static_cast<uint8_t*>(k_plane);
   auto v = static_cast<uint8_t*>(v_plane);
-  if (elem_bytes == 2)
-    hipLaunchKernelGGL(shuffle_kernel<2>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kShufThreads), 0, st, s, k, v, block_ids,
-                       static_cast<int>(units), kv_heads);
-  else
-    hipLaunchKernelGGL(shuffle_kernel<1>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(kShufThreads), 0, st, s, k, v, block_ids,
-                       static_cast<int>(units), kv_heads);
-  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+  if (page_size == 32)
+    return launch_shuffle_n<32>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
+  return launch_shuffle_n<16>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
 }
 
 }  // namespace skv

@@ -66,7 +66,7 @@ int check_shuffle_args(const void* std_cache, const void* k_plane,
   if (!std_cache || !k_plane || !v_plane) return SKV_EINVAL;
   if (num_blocks < 1 || kv_heads < 1 || page_size < 1 || head_dim < 1)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
@@ -79,7 +79,7 @@ int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
     return SKV_EINVAL;
   if (direction != SKV_TO_SHUFFLED && direction != SKV_TO_STANDARD)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   const long long block = 2LL * kv_heads * page_size * head_dim * elem_bytes;
   if (block > kMaxConvertBytes) return SKV_EUNSUPPORTED;
@@ -95,7 +95,7 @@ int check_cache_write_args(const void* key, const void* value, const void* slots
   if (num_tokens < 1 || num_blocks < 1 || kv_heads < 1 || page_size < 1 ||
       head_dim < 1)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   const long long row = static_cast<long long>(kv_heads) * head_dim;
   const int x = 16 / elem_bytes;

@@ -126,7 +126,7 @@ def _shuffle(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(src=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
-    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+    (dict(hd=64), 2), (dict(ps=64), 2), (dict(ps=8), 2), (dict(e=4), 2),
 ])
 def test_shuffle_errors(kw, code):
     assert _shuffle(**kw) == code
@@ -141,8 +141,9 @@ def _convert(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1), (dict(d=2), 1),
-    (dict(d=-1), 1), (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+    (dict(d=-1), 1), (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
     (dict(h=17), 2), (dict(h=33, e=1), 2),               # block above 128 KiB
+    (dict(h=9, ps=32), 2), (dict(h=17, ps=32, e=1), 2),
 ])
 def test_convert_errors(kw, code):
     assert _convert(**kw) == code
@@ -157,7 +158,7 @@ def _unshuffle(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dst=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
-    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+    (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
 ])
 def test_unshuffle_errors(kw, code):
     assert _unshuffle(**kw) == code
@@ -175,7 +176,7 @@ def _write(**kw):
     (dict(k=None), 1), (dict(v=None), 1), (dict(slots=None), 1), (dict(kp=None), 1),
     (dict(vp=None), 1), (dict(T=0), 1), (dict(nb=0), 1), (dict(h=0), 1),
     (dict(ks=255), 1), (dict(vs=128), 1), (dict(ks=260), 1),       # below H*D / not a multiple of x
-    (dict(hd=64), 2), (dict(ps=32), 2), (dict(e=4), 2),
+    (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
 ])
 def test_cache_write_errors(kw, code):
     assert _write(**kw) == code

@@ -12,7 +12,8 @@ from workloads import configs, gen
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-N, D = 16, 128
+D = 128
+PAGE = 16            # attention pages
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -34,9 +35,10 @@ def _host(t, e):
     return a.view(np.uint16) if e == 2 else a
 
 
-@pytest.mark.parametrize("e,H", [(2, 1), (2, 2), (2, 8), (1, 2), (1, 8)])
-def test_cache_write_bit_exact(e, H):
-    say("cache write", e, H)
+@pytest.mark.parametrize("e,H,N", [(2, 1, 16), (2, 2, 16), (2, 8, 16), (1, 2, 16), (1, 8, 16),
+                                   (2, 3, 32), (1, 4, 32)])
+def test_cache_write_bit_exact(e, H, N):
+    say("cache write", e, H, N)
     rng = np.random.default_rng(40 + 3 * H + e)
     dt = np.uint16 if e == 2 else np.uint8
     x = 16 // e
@@ -77,7 +79,7 @@ def test_decode_step_writes_then_attends(dtype):
     slots = []
     for i, (L, q) in enumerate(zip(lens, ql)):
         for pos in range(L - q, L):
-            slots.append(int(table[i, pos // N]) * N + pos % N)
+            slots.append(int(table[i, pos // PAGE]) * PAGE + pos % PAGE)
     slots = np.array(slots, dtype=np.int64)
     T = len(slots)
     # new K/V codes: copies of other real tokens' rows (unit-scale values of the
@@ -90,7 +92,7 @@ def test_decode_step_writes_then_attends(dtype):
     for w in range(2):
         for t in range(T):
             i, pos = real[pick[w, t]]
-            row = std0[int(table[i, pos // N]), :, pos % N]
+            row = std0[int(table[i, pos // PAGE]), :, pos % PAGE]
             kv_new[w, t] = row[:, :D] if w == 0 else row[:, D:]
     kp, vp = skv.kv_page_shuffle(case.kv)
     key = _dev(kv_new[0], e).view(T, H, D)
@@ -112,7 +114,7 @@ def test_decode_step_writes_then_attends(dtype):
     q = oracle.decode_bf16(gen.raw_u16(case.q))
     ref_out, ref_lse = oracle.decode_attention(
         q, std, dtype, table, case.seq_lens.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
-        H, N, cfg.causal, cfg.k_scale, cfg.v_scale)
+        H, PAGE, cfg.causal, cfg.k_scale, cfg.v_scale)
     r = compare(out.float().cpu().numpy().astype(np.float64),
                 out_lse.cpu().numpy().astype(np.float64), ref_out, ref_lse, dtype)
     say("write+attend", dtype, r)

@@ -11,7 +11,7 @@ from gpu_harness import say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-N, D = 16, 128
+D = 128
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -44,13 +44,15 @@ def _random_codes(rng, shape, e):
     return rng.integers(0, 1 << (8 * e), size=shape).astype(_np_dtype(e))
 
 
-CONVERT_CASES = [(2, 1), (2, 2), (2, 3), (2, 8), (2, 16), (1, 1), (1, 3), (1, 8), (1, 32)]
+CONVERT_CASES = [(2, 1, 16), (2, 2, 16), (2, 3, 16), (2, 8, 16), (2, 16, 16), (1, 1, 16),
+                 (1, 3, 16), (1, 8, 16), (1, 32, 16),
+                 (2, 1, 32), (2, 3, 32), (2, 8, 32), (1, 5, 32), (1, 16, 32)]
 
 
 @pytest.mark.parametrize("subset", [False, True])
-@pytest.mark.parametrize("e,H", CONVERT_CASES)
-def test_convert_in_place_and_back(e, H, subset):
-    say("convert", e, H, subset)
+@pytest.mark.parametrize("e,H,N", CONVERT_CASES)
+def test_convert_in_place_and_back(e, H, N, subset):
+    say("convert", e, H, N, subset)
     rng = np.random.default_rng(100 * H + e)
     B = 23
     x = 16 // e
@@ -77,9 +79,10 @@ def test_convert_in_place_and_back(e, H, subset):
 
 
 @pytest.mark.parametrize("subset", [False, True])
-@pytest.mark.parametrize("e,H", [(2, 1), (2, 3), (2, 8), (1, 2), (1, 5)])
-def test_unshuffle_bit_exact(e, H, subset):
-    say("unshuffle", e, H, subset)
+@pytest.mark.parametrize("e,H,N", [(2, 1, 16), (2, 3, 16), (2, 8, 16), (1, 2, 16), (1, 5, 16),
+                                   (2, 3, 32), (1, 2, 32)])
+def test_unshuffle_bit_exact(e, H, N, subset):
+    say("unshuffle", e, H, N, subset)
     rng = np.random.default_rng(7 * H + e)
     B = 19
     std = _random_codes(rng, (B, H, N, 2 * D), e)
@@ -100,10 +103,11 @@ def test_unshuffle_bit_exact(e, H, subset):
             assert np.array_equal(got[b], fill[b]), f"unlisted block {b} written"
 
 
-def test_convert_agrees_with_out_of_place_shuffle():
+@pytest.mark.parametrize("N", [16, 32])
+def test_convert_agrees_with_out_of_place_shuffle(N):
     """Same standard blocks, two routes on the GPU: the out-of-place repack and
     the in-place conversion of the byte halves write identical planes."""
-    say("convert vs shuffle")
+    say("convert vs shuffle", N)
     rng = np.random.default_rng(5)
     B, H, e = 64, 8, 2
     std = _random_codes(rng, (B, H, N, 2 * D), e)

@@ -78,21 +78,22 @@ def test_plan_large_batch():
 
 # ---- page shuffle: bit-exact -------------------------------------------------
 
-@pytest.mark.parametrize("e,H,subset", [(2, 1, False), (2, 3, False), (2, 8, True),
-                                         (1, 2, False), (1, 3, True), (2, 2, True)])
-def test_shuffle_bit_exact(e, H, subset):
-    say("shuffle", e, H, subset)
+@pytest.mark.parametrize("e,H,subset,N", [(2, 1, False, 16), (2, 3, False, 16), (2, 8, True, 16),
+                                           (1, 2, False, 16), (1, 3, True, 16), (2, 2, True, 16),
+                                           (2, 3, True, 32), (1, 5, False, 32)])
+def test_shuffle_bit_exact(e, H, subset, N):
+    say("shuffle", e, H, subset, N)
     g = torch.Generator(device=DEV).manual_seed(11 + H)
     B = 37
-    n_el = B * H * 16 * 256
+    n_el = B * H * N * 256
     raw = torch.randint(0, 256, (n_el * e,), generator=g, device=DEV, dtype=torch.uint8)
-    std = raw.view(torch.int16 if e == 2 else torch.uint8).view(B, H, 16, 256)
+    std = raw.view(torch.int16 if e == 2 else torch.uint8).view(B, H, N, 256)
     if e == 2:
         std = std.view(torch.bfloat16)
     x = 16 // e
-    kp = torch.full((B, H, 128 // x, 16, x), 7, dtype=std.dtype, device=DEV) if e == 1 else \
-        torch.zeros((B, H, 128 // x, 16, x), dtype=std.dtype, device=DEV)
-    vp = torch.zeros((B, H, 16 // x, 128, x), dtype=std.dtype, device=DEV)
+    kp = torch.full((B, H, 128 // x, N, x), 7, dtype=std.dtype, device=DEV) if e == 1 else \
+        torch.zeros((B, H, 128 // x, N, x), dtype=std.dtype, device=DEV)
+    vp = torch.zeros((B, H, N // x, 128, x), dtype=std.dtype, device=DEV)
     ids = None
     if subset:
         ids_h = np.random.default_rng(H).choice(B, size=11, replace=False).astype(np.int32)
