@@ -50,3 +50,39 @@ def decode_kv(raw, kv_dtype: str, scale=None) -> np.ndarray:
         v = decode_e4m3fn(raw)
         return v if scale is None else v * float(scale)
     raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def encode_e4m3fn(values) -> np.ndarray:
+    """float values -> e4m3fn codes: the nearest finite code value, ties to the
+    even code (round to nearest even), magnitudes at or above 448 saturate to
+    +-448, NaN gives a NaN code of the same sign. The sign of zero is kept.
+    Written as a search over the code values themselves."""
+    v = np.asarray(values, dtype=np.float64)
+    pos = _E4M3FN[:0x7F]                          # codes 0x00..0x7E, ascending values
+    out = np.empty(v.shape, dtype=np.uint8)
+    for idx, x in np.ndenumerate(v):
+        sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+        if math.isnan(x):
+            out[idx] = sign | 0x7F
+            continue
+        a = abs(x)
+        if a >= 448.0:
+            out[idx] = sign | 0x7E
+            continue
+        hi = int(np.searchsorted(pos, a, side="left"))   # first code value >= a
+        if pos[hi] == a:
+            code = hi
+        else:
+            lo = hi - 1
+            dl, dh = a - pos[lo], pos[hi] - a
+            code = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+        out[idx] = sign | code
+    return out
+
+
+def quantize_e4m3fn(bf16_bits, scale) -> np.ndarray:
+    """bf16 codes -> e4m3fn codes of value / scale, the division taken in fp32
+    (both operands are fp32 values) before rounding to the nearest code."""
+    x = decode_bf16(bf16_bits).astype(np.float32)
+    q = x / np.float32(scale)                      # IEEE fp32 division
+    return encode_e4m3fn(q.astype(np.float64))

@@ -52,3 +52,65 @@ def test_bf16_decode_matches_torch():
 def test_decode_kv_scale_is_plain_multiplier():
     codes = np.array([0x38, 0x40, 0xB8], dtype=np.uint8)
     assert list(oracle.decode_kv(codes, "fp8", 0.5)) == [0.5, 1.0, -0.5]
+
+
+def test_encode_round_trips_every_finite_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    back = oracle.encode_e4m3fn(oracle.decode_e4m3fn(codes))
+    assert np.array_equal(back, codes)
+
+
+def test_encode_midpoints_round_to_even_code():
+    """Exactly half-way between two adjacent positive codes goes to the even
+    code; one fp32 step either side goes to the nearer code."""
+    for c in range(0, 0x7E):
+        lo, hi = oracle.e4m3fn_value(c), oracle.e4m3fn_value(c + 1)
+        mid = np.float32((lo + hi) / 2)
+        assert float(mid) == (lo + hi) / 2                     # exact in fp32
+        even = c if c % 2 == 0 else c + 1
+        assert oracle.encode_e4m3fn([float(mid)])[0] == even, c
+        below = float(np.nextafter(mid, np.float32(0)))
+        above = float(np.nextafter(mid, np.float32(1000)))
+        assert oracle.encode_e4m3fn([below])[0] == c
+        assert oracle.encode_e4m3fn([above])[0] == c + 1
+        assert oracle.encode_e4m3fn([-float(mid)])[0] == 0x80 | even
+
+
+def test_encode_saturates_and_keeps_signs():
+    e = oracle.encode_e4m3fn
+    assert list(e([448.0, 449.0, 480.0, 1e30, math.inf])) == [0x7E] * 5
+    assert list(e([-448.0, -1e30, -math.inf])) == [0xFE] * 3
+    assert e([0.0])[0] == 0x00 and e([-0.0])[0] == 0x80
+    assert e([2.0 ** -10])[0] == 0x00                          # tie with 0 -> even
+    assert e([-(2.0 ** -12)])[0] == 0x80
+    n = e([math.nan, -math.nan])
+    assert all(np.isnan(oracle.decode_e4m3fn(n)))
+
+
+def test_encode_matches_torch_cast_in_range():
+    """torch's float8_e4m3fn cast (an independent implementation) agrees on
+    values inside the finite range."""
+    rng = np.random.default_rng(12)
+    v = np.concatenate([rng.normal(0, 1, 4000), rng.normal(0, 60, 4000),
+                        rng.uniform(-447.9, 447.9, 4000), rng.normal(0, 0.01, 4000)])
+    v = v.astype(np.float32)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3fn(v.astype(np.float64)), want)
+
+
+def test_quantize_divides_in_fp32():
+    """bf16 value / scale in fp32, then the nearest code: a value that is an
+    exact code value times the scale comes back as that code."""
+    scale = 0.0173
+    codes = np.array([0x01, 0x08, 0x38, 0x40, 0x55, 0x7E, 0xC4], dtype=np.uint8)
+    vals = oracle.decode_e4m3fn(codes) * np.float32(scale)
+    bits = np.asarray(vals, dtype=np.float32).view(np.uint32) >> 16    # truncate to bf16
+    q = oracle.quantize_e4m3fn(bits.astype(np.uint16), scale)
+    back = oracle.decode_e4m3fn(q)
+    x = oracle.decode_bf16(bits.astype(np.uint16))
+    # nearest code value to x / scale (fp32 division), checked by brute force
+    table = oracle.decode_e4m3fn(np.array([c for c in range(256) if c not in (0x7F, 0xFF)],
+                                          dtype=np.uint8))
+    for xi, bi in zip(x, back):
+        t = float(np.float32(xi) / np.float32(scale))
+        assert abs(bi - t) == np.min(np.abs(table - t))

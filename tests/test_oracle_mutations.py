@@ -203,6 +203,20 @@ def _write_k_transposed(k_plane, v_plane, key, value, slot_mapping):
     return kp, vp
 
 
+def _encode_ties_up(values):
+    v = np.asarray(values, dtype=np.float64)
+    pos = fp8._E4M3FN[:0x7F]
+    out = np.empty(v.shape, dtype=np.uint8)
+    for idx, x in np.ndenumerate(v):
+        sign = 0x80 if math.copysign(1.0, x) < 0 else 0
+        a = min(abs(x), 448.0)
+        hi = int(np.searchsorted(pos, a))
+        lo = max(hi - 1, 0)
+        code = hi if pos[hi] - a <= a - pos[lo] else lo       # ties away from zero
+        out[idx] = sign | code
+    return out
+
+
 TRUE_WRITE = shuffle.write_tokens_shuffled
 TRUE_FIXED = planner.fixed_split_plan
 TRUE_HALVES = shuffle.halves_from_standard
@@ -249,6 +263,8 @@ MUTATIONS = [
                             (oracle, "shuffle_blocks", _shuffle_transposed)]),
     ("fixed split floors the segment length", [(planner, "fixed_split_plan", _fixed_floor),
                                                (oracle, "fixed_split_plan", _fixed_floor)]),
+    ("e4m3 encode ties away from zero", [(fp8, "encode_e4m3fn", _encode_ties_up),
+                                         (oracle, "encode_e4m3fn", _encode_ties_up)]),
     ("cache writer K channel split transposed",
      [(shuffle, "write_tokens_shuffled", _write_k_transposed),
       (oracle, "write_tokens_shuffled", _write_k_transposed)]),
