@@ -234,24 +234,33 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
  * the shuffled backend's writer places each new token at its slot]. For each
  * token t with slot s = slot_mapping[t] in [0, num_blocks * page_size)
  * (block b = s / page_size, row n = s % page_size) and head h:
- *   k_plane[b, h, c / x, n, c % x] = key[t, h, c]
- *   v_plane[b, h, n / x, d, n % x] = value[t, h, d]
- * x = 16 / elem_bytes. Negative slots (padding) and slots past the cache are
- * skipped. key, value: element codes of the cache type (bf16 or fp8 e4m3fn,
- * written unchanged); token t's [kv_heads, head_dim] row starts key_stride
- * (value_stride) elements after token t-1's. Strides must be multiples of x
- * and at least kv_heads * head_dim; all pointers 16-byte aligned. Slots must be
- * distinct: two tokens at one slot race. Bit-exact byte movement.
- * Errors: EINVAL for NULL pointers, num_tokens < 1, num_blocks < 1,
- * kv_heads < 1, a stride below kv_heads * head_dim or not a multiple of x;
- * EUNSUPPORTED for head_dim != 128, page_size not 16 or 32, elem_bytes not 1
- * or 2. */
+ *   k_plane[b, h, c / x, n, c % x] = K(key[t, h, c])
+ *   v_plane[b, h, n / x, d, n % x] = V(value[t, h, d])
+ * x = 16 / elem_bytes (the cache's element size). Negative slots (padding) and
+ * slots past the cache are skipped. Slots must be distinct: two tokens at one
+ * slot race.
+ *   k_scale = v_scale = NULL: key, value hold element codes of the cache type
+ *     (bf16 or fp8 e4m3fn) and K, V copy them unchanged (bit-exact).
+ *   k_scale, v_scale = device fp32 scalars (fp8 cache only, elem_bytes 1): key,
+ *     value are bf16 and K(v) = e4m3fn(v / k_scale), V(v) = e4m3fn(v / v_scale),
+ *     the division in fp32, rounded to the nearest code with ties to even,
+ *     magnitudes >= 448 saturating to +-448, NaN kept as NaN: the inverse of
+ *     the attention path's value = code * scale.
+ * Token t's [kv_heads, head_dim] input row starts key_stride (value_stride)
+ * input elements after token t-1's; strides must be multiples of
+ * 16 / (input element bytes) and at least kv_heads * head_dim; all pointers
+ * 16-byte aligned.
+ * Errors: EINVAL for NULL pointers, only one scale given, scales with
+ * elem_bytes != 1, num_tokens < 1, num_blocks < 1, kv_heads < 1, a stride
+ * below kv_heads * head_dim or not a multiple of the above; EUNSUPPORTED for
+ * head_dim != 128, page_size not 16 or 32, elem_bytes not 1 or 2. */
 int skv_kv_cache_write(const void* key, const void* value,
                        const int64_t* slot_mapping, int num_tokens,
                        long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks,
                        int kv_heads, int page_size, int head_dim,
-                       int elem_bytes, void* stream);
+                       int elem_bytes, const float* k_scale,
+                       const float* v_scale, void* stream);
 
 /* Static text for a status code. */
 const char* skv_strerror(int status);

@@ -41,7 +41,8 @@ _SIGNATURES = {
     "skv_kv_page_unshuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
                                        _c_int, _p]),
     "skv_kv_cache_write": (_c_int, [_p, _p, _p, _c_int, ctypes.c_longlong, ctypes.c_longlong,
-                                    _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p]),
+                                    _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p,
+                                    _p]),
     "skv_strerror": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -285,20 +286,28 @@ def kv_page_unshuffle(k_plane, v_plane, std_cache=None, block_ids=None, stream=N
     return std_cache
 
 
-def kv_cache_write(key, value, slot_mapping, k_plane, v_plane, stream=None):
-    """Write new tokens (key, value [T, H, D], the cache's element type; token
-    rows may be strided) into the shuffled planes at slot_mapping (int64 [T];
-    negative = padding). Returns the planes."""
+def kv_cache_write(key, value, slot_mapping, k_plane, v_plane, k_scale=None, v_scale=None,
+                   stream=None):
+    """Write new tokens (key, value [T, H, D]; token rows may be strided) into
+    the shuffled planes at slot_mapping (int64 [T]; negative = padding).
+    Without scales key/value are in the cache's element type and copied; with
+    k_scale/v_scale (fp32 [1] device tensors) they are bf16 and quantised into
+    an fp8 cache. Returns the planes."""
     B, H, D, N, e = _planes(k_plane, v_plane)
+    in_e = 2 if k_scale is not None else e
     for t, n in ((key, "key"), (value, "value")):
         if not t.is_cuda or t.dim() != 3 or t.shape[1:] != (H, D):
             raise ValueError(f"{n}: expected a device tensor [T, {H}, {D}]")
-        if t.stride(2) != 1 or t.stride(1) != D or t.element_size() != e:
-            raise ValueError(f"{n}: heads and channels must be dense, element size {e}")
+        if t.stride(2) != 1 or t.stride(1) != D or t.element_size() != in_e:
+            raise ValueError(f"{n}: heads and channels must be dense, element size {in_e}")
     _need(slot_mapping, torch.int64, "slot_mapping", key.shape[0])
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        if t is not None:
+            _need(t, torch.float32, n, 1)
     T = key.shape[0]
     st = load().skv_kv_cache_write(_ptr(key), _ptr(value), _ptr(slot_mapping), T,
                                    key.stride(0), value.stride(0), _ptr(k_plane),
-                                   _ptr(v_plane), B, H, N, D, e, _stream(stream))
+                                   _ptr(v_plane), B, H, N, D, e, _ptr(k_scale),
+                                   _ptr(v_scale), _stream(stream))
     _check(st, "skv_kv_cache_write")
     return k_plane, v_plane

@@ -167,15 +167,17 @@ int skv_kv_cache_write(const void* key, const void* value,
                        long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks,
                        int kv_heads, int page_size, int head_dim,
-                       int elem_bytes, void* stream) {
+                       int elem_bytes, const float* k_scale,
+                       const float* v_scale, void* stream) {
   int st = skv::check_cache_write_args(key, value, slot_mapping, num_tokens,
                                        key_stride, value_stride, k_plane, v_plane,
                                        num_blocks, kv_heads, page_size, head_dim,
-                                       elem_bytes);
+                                       elem_bytes, k_scale, v_scale);
   if (st != SKV_OK) return st;
   return skv::launch_cache_write(key, value, slot_mapping, num_tokens, key_stride,
                                  value_stride, k_plane, v_plane, num_blocks,
-                                 kv_heads, page_size, elem_bytes, stream);
+                                 kv_heads, page_size, elem_bytes, k_scale, v_scale,
+                                 stream);
 }
 
 const char* skv_strerror(int status) {

@@ -15,7 +15,11 @@
 // 16-byte chunk, so a token's V row scatters: lane l writes channels 2l and
 // 2l+1 (e bytes each) at stride x*e. Tokens of one block write disjoint bytes,
 // so concurrent waves need no ordering. Decode steps write few tokens; the
-// kernel is launch-bound, not bandwidth-bound.
+// kernel is launch-bound, not bandwidth-bound. With per-tensor scales, bf16
+// rows are quantised into an fp8 cache on the way (the RFC leaves the fp8
+// writer's scale handling to its own treatment; the reading here is
+// code = e4m3fn(value / scale), the inverse of the attention path's
+// value = code * scale).
 #include <hip/hip_runtime.h>
 
 #include "skv.h"
@@ -72,12 +76,87 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
   }
 }
 
+// fp32 -> OCP e4m3fn code: round to nearest, ties to even; magnitudes at or
+// above 448 (infinity included) saturate to +-448; NaN stays NaN; the sign of
+// zero is kept. Integer rounding of the fp32 mantissa for the normal range
+// (>= 2^-6); below it the code counts 2^-9 steps, so v * 512 (exact) is
+// rounded to an integer, half to even.
+__device__ __forceinline__ uint32_t e4m3fn_rne_sat(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7fu;
+  if (a >= 0x43e00000u) return sign | 0x7eu;            // 448.0f
+  const uint32_t e = a >> 23;
+  if (e >= 121u) {                                      // 2^-6: first normal e4m3fn exponent
+    const uint32_t m = a & 0x7fffffu;
+    uint32_t q = m >> 20;
+    const uint32_t rem = m & 0xfffffu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+    return sign | (((e - 120u) << 3) + q);              // a carry moves into the exponent
+  }
+  return sign | static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+}
+
+// bf16 K/V rows quantised into an fp8 cache: code = e4m3fn(value / scale),
+// the division in fp32. Same placement as cache_write_kernel<1, kN>.
+template <int kN>
+__global__ __launch_bounds__(kThreads) void cache_write_quant_kernel(
+    const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
+    const int64_t* __restrict__ slots, int num_tokens, long long key_stride,
+    long long value_stride, uint8_t* __restrict__ kp, uint8_t* __restrict__ vp,
+    int kv_heads, long long num_slots, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  constexpr int kX = 16;
+  constexpr int kKChunks = kD / 16;
+  constexpr size_t kPlane = static_cast<size_t>(kN) * kD;
+  const int lane = threadIdx.x & 63;
+  const long long unit = static_cast<long long>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (unit >= static_cast<long long>(num_tokens) * kv_heads) return;   // wave-uniform
+  const int t = static_cast<int>(unit / kv_heads);
+  const int h = static_cast<int>(unit % kv_heads);
+  const long long slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const long long b = slot / kN;
+  const int n = static_cast<int>(slot % kN);
+  const size_t head = static_cast<size_t>(b) * kv_heads + h;
+  const uint16_t* krow = key + t * key_stride + static_cast<long long>(h) * kD;
+  const uint16_t* vrow = value + t * value_stride + static_cast<long long>(h) * kD;
+  const float ks = *k_scale, vs = *v_scale;
+  if (lane < kKChunks) {
+    // 16 channels -> one 16-byte K chunk
+    const uint4 lo = reinterpret_cast<const uint4*>(krow + 16 * lane)[0];
+    const uint4 hi = reinterpret_cast<const uint4*>(krow + 16 * lane)[1];
+    const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = w[2 * q], bb = w[2 * q + 1];
+      c[q] = e4m3fn_rne_sat(__uint_as_float(a << 16) / ks) |
+             (e4m3fn_rne_sat(__uint_as_float(a & 0xffff0000u) / ks) << 8) |
+             (e4m3fn_rne_sat(__uint_as_float(bb << 16) / ks) << 16) |
+             (e4m3fn_rne_sat(__uint_as_float(bb & 0xffff0000u) / ks) << 24);
+    }
+    *reinterpret_cast<uint4*>(kp + head * kPlane + (static_cast<size_t>(lane) * kN + n) * 16) =
+        make_uint4(c[0], c[1], c[2], c[3]);
+  }
+  const size_t vbase = static_cast<size_t>(n / kX) * kD * kX + n % kX;
+  const int d = 2 * lane;
+  const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + d);
+  uint8_t* vdst = vp + head * kPlane;
+  vdst[vbase + static_cast<size_t>(d) * kX] =
+      static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w << 16) / vs));
+  vdst[vbase + static_cast<size_t>(d + 1) * kX] =
+      static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w & 0xffff0000u) / vs));
+}
+
 }  // namespace
 
 int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
                        int num_tokens, long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int page_size, int elem_bytes, void* stream) {
+                       int page_size, int elem_bytes, const float* k_scale,
+                       const float* v_scale, void* stream) {
   const long long units = static_cast<long long>(num_tokens) * kv_heads;
   const long long blocks = (units + kWaves - 1) / kWaves;
   if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
@@ -88,6 +167,19 @@ int launch_cache_write(const void* key, const void* value, const int64_t* slot_m
   auto kp = static_cast<uint8_t*>(k_plane);
   auto vp = static_cast<uint8_t*>(v_plane);
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (k_scale) {
+    auto kq = static_cast<const uint16_t*>(key);
+    auto vq = static_cast<const uint16_t*>(value);
+    if (page_size == 32)
+      hipLaunchKernelGGL((cache_write_quant_kernel<32>), grid, block, 0, st, kq, vq,
+                         slot_mapping, num_tokens, key_stride, value_stride, kp, vp,
+                         kv_heads, num_slots, k_scale, v_scale);
+    else
+      hipLaunchKernelGGL((cache_write_quant_kernel<16>), grid, block, 0, st, kq, vq,
+                         slot_mapping, num_tokens, key_stride, value_stride, kp, vp,
+                         kv_heads, num_slots, k_scale, v_scale);
+    return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+  }
 #define SKV_W(E, N)                                                                  \
   hipLaunchKernelGGL((cache_write_kernel<E, N>), grid, block, 0, st, k, v, slot_mapping, \
                      num_tokens, key_stride, value_stride, kp, vp, kv_heads, num_slots)

@@ -49,7 +49,8 @@ int check_cache_write_args(const void* key, const void* value, const void* slots
                            int num_tokens, long long key_stride,
                            long long value_stride, const void* k_plane,
                            const void* v_plane, int num_blocks, int kv_heads,
-                           int page_size, int head_dim, int elem_bytes);
+                           int page_size, int head_dim, int elem_bytes,
+                           const void* k_scale, const void* v_scale);
 
 // Segments per sequence of the fixed split: max(1, min(seg_max,
 // pow2floor(num_cus / (bs * kv_heads)))).
@@ -108,7 +109,8 @@ int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
 int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
                        int num_tokens, long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int page_size, int elem_bytes, void* stream);
+                       int page_size, int elem_bytes, const float* k_scale,
+                       const float* v_scale, void* stream);
 
 }  // namespace skv
 

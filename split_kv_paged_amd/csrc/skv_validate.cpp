@@ -90,15 +90,18 @@ int check_cache_write_args(const void* key, const void* value, const void* slots
                            int num_tokens, long long key_stride,
                            long long value_stride, const void* k_plane,
                            const void* v_plane, int num_blocks, int kv_heads,
-                           int page_size, int head_dim, int elem_bytes) {
+                           int page_size, int head_dim, int elem_bytes,
+                           const void* k_scale, const void* v_scale) {
   if (!key || !value || !slots || !k_plane || !v_plane) return SKV_EINVAL;
+  if ((k_scale == nullptr) != (v_scale == nullptr)) return SKV_EINVAL;
+  if (k_scale && elem_bytes != 1) return SKV_EINVAL;   // quantising needs an fp8 cache
   if (num_tokens < 1 || num_blocks < 1 || kv_heads < 1 || page_size < 1 ||
       head_dim < 1)
     return SKV_EINVAL;
   if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   const long long row = static_cast<long long>(kv_heads) * head_dim;
-  const int x = 16 / elem_bytes;
+  const int x = 16 / (k_scale ? 2 : elem_bytes);       // input rows: bf16 when quantising
   if (key_stride < row || value_stride < row) return SKV_EINVAL;
   if (key_stride % x != 0 || value_stride % x != 0) return SKV_EINVAL;
   return SKV_OK;

@@ -165,11 +165,12 @@ def test_unshuffle_errors(kw, code):
 
 
 def _write(**kw):
-    a = dict(k=P, v=P, slots=P, T=4, ks=256, vs=256, kp=P, vp=P, nb=8, h=2, ps=16, hd=128, e=2)
+    a = dict(k=P, v=P, slots=P, T=4, ks=256, vs=256, kp=P, vp=P, nb=8, h=2, ps=16, hd=128, e=2,
+             ksc=None, vsc=None)
     a.update(kw)
     return skv.load().skv_kv_cache_write(a["k"], a["v"], a["slots"], a["T"], a["ks"], a["vs"],
                                          a["kp"], a["vp"], a["nb"], a["h"], a["ps"], a["hd"],
-                                         a["e"], None)
+                                         a["e"], a["ksc"], a["vsc"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -177,6 +178,9 @@ def _write(**kw):
     (dict(vp=None), 1), (dict(T=0), 1), (dict(nb=0), 1), (dict(h=0), 1),
     (dict(ks=255), 1), (dict(vs=128), 1), (dict(ks=260), 1),       # below H*D / not a multiple of x
     (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(ksc=P), 1), (dict(vsc=P), 1),                  # one scale without the other
+    (dict(ksc=P, vsc=P), 1),                              # quantising needs an fp8 cache
+    (dict(ksc=P, vsc=P, e=1, ks=260), 1),                 # bf16 input rows: multiple of 8
 ])
 def test_cache_write_errors(kw, code):
     assert _write(**kw) == code
