@@ -13,11 +13,15 @@ namespace skv {
 
 int launch_segments_mfma(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
                          hipStream_t st);
-int launch_segments_valu(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
-                         hipStream_t st);
+int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st);
 
-// Rows at or below this go to the VALU kernel; above it, 16-row MFMA tiles.
-constexpr int kValuMaxRows = 8;
+// bf16 KV with at most this many rows goes to the vector-ALU kernel; the rest
+// to 16-row matrix-core tiles. Measured on MI355X (balanced 32 x 60k batches):
+// at 1-4 bf16 rows both kernels stream at 5.6-6.0 TB/s; at 5-8 rows the
+// vector ALU's rows x 128 fp32 FMAs per token, and for fp8 at any row count the
+// widening of every K and V element, make it compute-bound (1.7-3.4 TB/s)
+// where a partly filled MFMA tile still streams at 5.3-5.9 TB/s.
+constexpr int kValuMaxRows = 4;
 
 int launch_segments(const AttnArgs& a, void* stream) {
   SegParams sp;
@@ -55,8 +59,8 @@ int launch_segments(const AttnArgs& a, void* stream) {
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
   const int rows = sp.G * a.max_q;
   auto st = static_cast<hipStream_t>(stream);
-  if (rows <= kValuMaxRows)
-    return launch_segments_valu(sp, e, shuf, rows, static_cast<int>(grid), st);
+  if (e == 2 && rows <= kValuMaxRows)
+    return launch_segments_valu(sp, shuf, static_cast<int>(grid), st);
   return launch_segments_mfma(sp, e, shuf, rows, static_cast<int>(grid), st);
 }
 

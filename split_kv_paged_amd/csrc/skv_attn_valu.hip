@@ -1,5 +1,5 @@
-// Segment attention, vector-ALU variant (query rows = GQA group x query tokens
-// <= 8: too few to fill a 16-row matrix-core tile).
+// Segment attention, vector-ALU variant: bf16 KV with at most 4 query rows
+// (GQA group x query tokens), too few to fill a 16-row matrix-core tile.
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Motivation and Modifications: one work-group per
@@ -8,13 +8,16 @@
 // list and leaves on -1.
 //
 // MI355X design:
-//  * 4 wave64s; wave w takes pages w, w+4, ... of the segment and computes all
-//    query rows of each, so no wave needs another's data: each wave streams
-//    its pages through a private LDS ring of NS pages with direct-to-LDS DMA
+//  * NW wave64s (8 for standard pages, 4 for shuffled planes; measured); wave
+//    w takes pages w, w+NW, ... of the segment and computes all query rows of
+//    each, so no wave needs another's data: each wave streams its pages
+//    through a private LDS ring (128 KB / NW) with direct-to-LDS DMA
 //    (global_load_lds_dwordx4, issued from inline asm) and waits only on its
-//    own vmcnt — there is no barrier in the main loop. Page ids are read
-//    through the constant address space (scalar loads), so waiting on them
-//    never drains the DMA queue.
+//    own vmcnt — there is no barrier in the main loop. Two waves per SIMD hide
+//    each other's LDS and DPP latencies; the shuffled layout's two planes
+//    prefer the deeper four-page ring of four waves. Page ids are read through
+//    the constant address space (scalar loads), so waiting on them never
+//    drains the DMA queue.
 //  * LDS tiles are laid out for the readers: K chunk-major ([16-byte chunk]
 //    [token]) so a quad of lanes per token reads its 16-byte chunks
 //    conflict-free; standard V row-major (one token's channel chunks per
@@ -26,31 +29,32 @@
 //  * p.V, standard pages: lane (token phase, channel chunk) accumulates in
 //    fp32 with p from a per-wave LDS buffer; shuffled pages: a lane owns two
 //    channels and takes v_dot2 over token pairs with bf16 p.
-//  * fp8 e4m3fn codes are widened exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8)
-//    or fp32 (v_cvt_pk_f32_fp8); k_scale folds into the score scale and
-//    v_scale into the output.
 //  * Masked scores are forced to -inf and V of tokens past the segment end is
 //    zeroed, so page-tail poison (even NaN) never reaches the accumulator.
+//  * fp8 KV and 5..8 rows go to the matrix-core variant: there the vector
+//    ALU's widening and rows x 128 fp32 FMAs per token cannot keep up with
+//    HBM, while a partly filled 16-row MFMA tile can (measured).
 #include "skv_attn_common.h"
 #include "skv.h"
 
 namespace skv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 constexpr int kD = kHeadDim;
-constexpr int kRingPerWave = 32 * 1024;
+constexpr int kRows = 4;                       // query rows per work-group (padded)
+constexpr int kHalf = kPageSize * kD * 2;      // a page's K (or V) half, bf16
+constexpr int kPage = 2 * kHalf;
+constexpr int kInstrPerPage = kPage / 1024;    // DMA instructions per page
+constexpr int kStdRow = 2 * kD * 2;            // one standard token row
+constexpr int kStdTile = kPageSize * kStdRow;  // one (block, head) standard tile
 
-template <int E>
+template <int NW>
 struct VRing {
-  static constexpr int kHalf = kPageSize * kD * E;            // a page's K (or V) half
-  static constexpr int kPage = 2 * kHalf;
-  static constexpr int kNS = kRingPerWave / kPage;             // pages in a wave's ring
-  static constexpr int kInstrPerPage = kPage / 1024;           // DMA instructions per page
+  static constexpr int kBytes = 128 * 1024 / NW;   // this wave's ring
+  static constexpr int kNS = kBytes / kPage;       // pages in it
+  static_assert(kNS >= 2, "ring needs two pages");
   static_assert((kNS - 2) * kInstrPerPage <= 63, "vmcnt range");
-  static constexpr int kStdTile = kPageSize * 2 * kD * E;
-  static constexpr int kStdRow = 2 * kD * E;
+  static_assert(kRows * kD * 4 <= kBytes, "the wave's output slot fits its ring");
 };
 
 template <int N>
@@ -80,31 +84,30 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
 // One page (this wave's) into its ring slot: K half chunk-major
 // [c][token][16 B]; V half row-major [token][channels] (standard) or the
 // plane as is (shuffled).
-template <int E, bool SHUF>
+template <bool SHUF>
 __device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it, int pid,
                                            uint8_t* slot, int lane) {
-  using R = VRing<E>;
   const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
-  const uint8_t* ktile = p.kv_a + head * (SHUF ? R::kHalf : R::kStdTile);
-  const uint8_t* vtile = SHUF ? p.kv_b + head * R::kHalf : ktile;
+  const uint8_t* ktile = p.kv_a + head * (SHUF ? kHalf : kStdTile);
+  const uint8_t* vtile = SHUF ? p.kv_b + head * kHalf : ktile;
 #pragma unroll
-  for (int i = 0; i < R::kHalf / 1024; ++i) {
+  for (int i = 0; i < kHalf / 1024; ++i) {
     const int c = 4 * i + (lane >> 4), tau = lane & 15;
     const size_t off = SHUF ? static_cast<size_t>(i * 64 + lane) * 16
-                            : static_cast<size_t>(tau) * R::kStdRow + c * 16;
+                            : static_cast<size_t>(tau) * kStdRow + c * 16;
     dma16(ktile + off, slot + i * 1024);
   }
 #pragma unroll
-  for (int i = 0; i < R::kHalf / 1024; ++i) {
+  for (int i = 0; i < kHalf / 1024; ++i) {
     size_t off;
     if constexpr (SHUF) {
       off = static_cast<size_t>(i * 64 + lane) * 16;
     } else {
-      constexpr int kCpr = kD * E / 16;                  // chunks per V row
+      constexpr int kCpr = kD * 2 / 16;                  // chunks per V row
       const int tau = i * (64 / kCpr) + lane / kCpr, c = lane % kCpr;
-      off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
+      off = static_cast<size_t>(tau) * kStdRow + kD * 2 + c * 16;
     }
-    dma16(vtile + off, slot + R::kHalf + i * 1024);
+    dma16(vtile + off, slot + kHalf + i * 1024);
   }
 }
 
@@ -117,17 +120,18 @@ __device__ __forceinline__ float max_over_tokens(float v) {
   return v;
 }
 
-template <int E, bool SHUF, int RM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <bool SHUF, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_valu_kernel(SegParams p) {
-  using R = VRing<E>;
+  using R = VRing<NW>;
   constexpr int kNS = R::kNS;
+  constexpr int kThreads = 64 * NW;
+  constexpr int RM = kRows;
   constexpr int kPBytes = SHUF ? RM * 16 * 2 : 16 * RM * 4;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[kWaves][kRingPerWave];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[kWaves][kPBytes];
-  __shared__ __attribute__((aligned(16))) float oslot[kWaves][RM][kD];
-  __shared__ float sm_m[kWaves][RM];
-  __shared__ float sm_l[kWaves][RM];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[NW][kPBytes];
+  __shared__ float sm_m[NW][RM];
+  __shared__ float sm_l[NW][RM];
 
   const SegItem it = decode_item(p);
   write_fixed_counts(p, it);
@@ -137,16 +141,11 @@ void seg_valu_kernel(SegParams p) {
   const int tq = lane >> 2, qq = lane & 3;
   const int seg_page0 = it.seg_start >> 4;
   const int seg_pages = (it.seg_end - it.seg_start + 15) >> 4;
-  const int np = seg_pages > wave ? (seg_pages - wave + kWaves - 1) / kWaves : 0;
+  const int np = seg_pages > wave ? (seg_pages - wave + NW - 1) / NW : 0;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
-  float sm_scale = kScoreScaleLog2;
-  float out_scale = 1.f;
-  if constexpr (E == 1) {
-    sm_scale *= p.k_scale[0];
-    out_scale = p.v_scale[0];
-  }
+  const float sm_scale = kScoreScaleLog2;
 
   // Q rows (bf16 pairs) for this lane's 32 channels; consumed before any DMA
   uint4 qr[RM][4];
@@ -159,11 +158,8 @@ void seg_valu_kernel(SegParams p) {
     const int h = it.g * p.G + (okr ? r % p.G : 0);
     const uint16_t* q = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // E==2: chunk 4u+qq -> channels 32u + 8qq; E==1: chunk 4(u/2)+qq, half u%2
-      const int ch = E == 2 ? 32 * u + 8 * qq : 64 * (u >> 1) + 16 * qq + 8 * (u & 1);
-      qr[r][u] = *reinterpret_cast<const uint4*>(q + ch);   // padding rows read row 0
-    }
+    for (int u = 0; u < 4; ++u)          // chunk 4u+qq -> channels 32u + 8qq
+      qr[r][u] = *reinterpret_cast<const uint4*>(q + 32 * u + 8 * qq);   // padding rows read row 0
   }
 #pragma unroll
   for (int r = 0; r < RM; ++r)
@@ -174,14 +170,14 @@ void seg_valu_kernel(SegParams p) {
     }
 
   uint8_t* wring = ring[wave];
-  // page ids: this wave's k-th page is seg page wave + 4k
-  auto pid_of = [&](int k) { return ptab[wave + kWaves * k]; };
+  // page ids: this wave's k-th page is seg page wave + NW k
+  auto pid_of = [&](int k) { return ptab[wave + NW * k]; };
 #pragma unroll
   for (int k = 0; k < kNS - 1; ++k)
-    if (k < np) issue_page<E, SHUF>(p, it, pid_of(k), wring + k * R::kPage, lane);
+    if (k < np) issue_page<SHUF>(p, it, pid_of(k), wring + k * kPage, lane);
   int pid_next = kNS - 1 < np ? pid_of(kNS - 1) : 0;
 
-  constexpr int kAcc = SHUF ? 2 : (E == 2 ? 8 : 16);
+  constexpr int kAcc = SHUF ? 2 : 8;
   float acc[RM][kAcc];
   float m[RM], l[RM];
 #pragma unroll
@@ -194,31 +190,22 @@ void seg_valu_kernel(SegParams p) {
   uint8_t* pw = pbuf[wave];
 
   for (int k = 0; k < np; ++k) {
-    wait_vmcnt_pages<R::kInstrPerPage, kNS - 2>(min(kNS - 2, np - 1 - k));
+    wait_vmcnt_pages<kInstrPerPage, kNS - 2>(min(kNS - 2, np - 1 - k));
     if (k + kNS - 1 < np) {
-      issue_page<E, SHUF>(p, it, pid_next, wring + ((k + kNS - 1) % kNS) * R::kPage, lane);
+      issue_page<SHUF>(p, it, pid_next, wring + ((k + kNS - 1) % kNS) * kPage, lane);
       if (k + kNS < np) pid_next = pid_of(k + kNS);
     }
-    const uint8_t* sK = wring + (k % kNS) * R::kPage;
-    const uint8_t* sV = sK + R::kHalf;
-    const int tok0 = it.seg_start + 16 * (wave + kWaves * k);
+    const uint8_t* sK = wring + (k % kNS) * kPage;
+    const uint8_t* sV = sK + kHalf;
+    const int tok0 = it.seg_start + 16 * (wave + NW * k);
     const int vend = it.seg_end - tok0;        // tokens of this page before the end
     const bool tail = vend < 16;
 
     // ---- scores: token tq, this lane's quarter of the channels ----
     uint4 kw[4];
-    if constexpr (E == 2) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        kw[u] = *reinterpret_cast<const uint4*>(sK + u * 1024 + (16 * qq + tq) * 16);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint4 c = *reinterpret_cast<const uint4*>(sK + u * 1024 + (16 * qq + tq) * 16);
-        kw[2 * u] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
-        kw[2 * u + 1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
-      }
-    }
+    for (int u = 0; u < 4; ++u)
+      kw[u] = *reinterpret_cast<const uint4*>(sK + u * 1024 + (16 * qq + tq) * 16);
     float s[RM];
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
@@ -254,11 +241,9 @@ void seg_valu_kernel(SegParams p) {
     if constexpr (!SHUF) {
       if (qq == 0) {                           // p[tau][r] fp32
         float* dst = reinterpret_cast<float*>(pw) + tq * RM;
-#pragma unroll
-        for (int r4 = 0; r4 < RM; r4 += 4)
-          *reinterpret_cast<float4*>(dst + r4) = make_float4(s[r4], s[r4 + 1], s[r4 + 2], s[r4 + 3]);
+        *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
       }
-    } else {                                   // p[r][tau] bf16; quarter qq: rows qq, qq+4
+    } else {                                   // p[r][tau] bf16; quarter qq: row qq
 #pragma unroll
       for (int r = 0; r < RM; ++r)
         if ((r & 3) == qq)
@@ -270,39 +255,25 @@ void seg_valu_kernel(SegParams p) {
 
     // ---- o += p.V ----
     if constexpr (!SHUF) {
-      constexpr int kCh = kD * E / 16;        // chunks per V row: 16 / 8
-      constexpr int kPh = 64 / kCh;           // token phases: 4 / 8
+      constexpr int kCh = kD * 2 / 16;        // chunks per V row
+      constexpr int kPh = 64 / kCh;           // token phases
       const int tp = lane / kCh, c = lane % kCh;
 #pragma unroll
       for (int u = 0; u < 16 / kPh; ++u) {
         const int tau = tp + kPh * u;
-        uint4 v = *reinterpret_cast<const uint4*>(sV + tau * (kD * E) + c * 16);
+        uint4 v = *reinterpret_cast<const uint4*>(sV + tau * (kD * 2) + c * 16);
         if (tail && tau >= vend) v = make_uint4(0, 0, 0, 0);
-        float x[kAcc];
-        if constexpr (E == 2) {
-          x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
-          x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
-        } else {
-          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+        const float x[kAcc] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                               bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float4 pv = *reinterpret_cast<const float4*>(
+            reinterpret_cast<const float*>(pw) + tau * RM);
+        const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[q2]), false);
-            const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(wv[q2]), true);
-            x[4 * q2] = a[0]; x[4 * q2 + 1] = a[1]; x[4 * q2 + 2] = b[0]; x[4 * q2 + 3] = b[1];
-          }
-        }
-        const float* pr = reinterpret_cast<const float*>(pw) + tau * RM;
+        for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-        for (int r4 = 0; r4 < RM; r4 += 4) {
-          const float4 pv = *reinterpret_cast<const float4*>(pr + r4);
-          const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-            for (int a = 0; a < kAcc; ++a) acc[r4 + rr][a] += pp[rr] * x[a];
-        }
+          for (int a = 0; a < kAcc; ++a) acc[rr][a] += pp[rr] * x[a];
       }
-    } else if constexpr (E == 2) {
+    } else {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         uint4 vv[2];
@@ -333,44 +304,15 @@ void seg_valu_kernel(SegParams p) {
           }
         }
       }
-    } else {
-      uint4 vb[2][2];                          // [h][half]: 16 tokens as bf16 pairs
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint4 c = *reinterpret_cast<const uint4*>(sV + (lane + 64 * h) * 16);
-        if (tail) {
-          uint32_t w[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-          for (int b = 0; b < 16; ++b)
-            if (b >= vend) w[b >> 2] &= ~(0xffu << (8 * (b & 3)));
-          c = make_uint4(w[0], w[1], w[2], w[3]);
-        }
-        vb[h][0] = fp8x8_to_bf16x8(make_uint2(c.x, c.y));
-        vb[h][1] = fp8x8_to_bf16x8(make_uint2(c.z, c.w));
-      }
-#pragma unroll
-      for (int r = 0; r < RM; ++r) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const uint4 pp = *reinterpret_cast<const uint4*>(pw + (r * 16 + 8 * half) * 2);
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float a = acc[r][h];
-            a = dot2_bf16(vb[h][half].x, pp.x, a);
-            a = dot2_bf16(vb[h][half].y, pp.y, a);
-            a = dot2_bf16(vb[h][half].z, pp.z, a);
-            a = dot2_bf16(vb[h][half].w, pp.w, a);
-            acc[r][h] = a;
-          }
-        }
-      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 
-  // ---- per-wave totals ----
+  // ---- per-wave totals into the wave's own ring, now idle ----
+  wait_vmcnt<0>();
+  float(*oslot)[kD] = reinterpret_cast<float(*)[kD]>(wring);   // [RM][kD]
 #pragma unroll
   for (int r = 0; r < RM; ++r) {
     float v = l[r];                            // identical within a quad: sum over tq only
@@ -381,7 +323,7 @@ void seg_valu_kernel(SegParams p) {
     l[r] = v;
   }
   if constexpr (!SHUF) {
-    constexpr int kCh = kD * E / 16;
+    constexpr int kCh = kD * 2 / 16;
     const int tp = lane / kCh, c = lane % kCh;
 #pragma unroll
     for (int r = 0; r < RM; ++r)
@@ -395,13 +337,13 @@ void seg_valu_kernel(SegParams p) {
 #pragma unroll
       for (int r = 0; r < RM; ++r)
 #pragma unroll
-        for (int a = 0; a < kAcc; ++a) oslot[wave][r][c * kAcc + a] = acc[r][a];
+        for (int a = 0; a < kAcc; ++a) oslot[r][c * kAcc + a] = acc[r][a];
     }
   } else {
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
-      oslot[wave][r][lane] = acc[r][0];
-      oslot[wave][r][lane + 64] = acc[r][1];
+      oslot[r][lane] = acc[r][0];
+      oslot[r][lane + 64] = acc[r][1];
     }
   }
   if (lane == 0) {
@@ -411,7 +353,6 @@ void seg_valu_kernel(SegParams p) {
       sm_l[wave][r] = l[r];
     }
   }
-  wait_vmcnt<0>();
   __syncthreads();
 
   // ---- merge waves: thread -> (row, channel) elements ----
@@ -420,41 +361,32 @@ void seg_valu_kernel(SegParams p) {
     if (r >= it.rows) continue;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][r]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][r]);
     const float mu = M == -INFINITY ? 0.f : M;
     float Ls = 0.f, o = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float f = fast_exp2(sm_m[w][r] - mu);
       Ls += sm_l[w][r] * f;
-      o += oslot[w][r][d] * f;
+      o += reinterpret_cast<const float(*)[kD]>(ring[w])[r][d] * f;
     }
     const int t = it.c0 + r / p.G;
     const int h = it.g * p.G + r % p.G;
     const size_t prow = (static_cast<size_t>(t) * p.Hq + h) * p.seg_max + it.seg;
     const bool any = Ls > 0.f;
-    p.part_o[prow * kD + d] = any ? o * (out_scale / Ls) : 0.f;
+    p.part_o[prow * kD + d] = any ? o / Ls : 0.f;
     if (d == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
   }
 }
 
-template <int E, bool SHUF>
-int launch_valu_e(const SegParams& sp, int rows, int grid, hipStream_t st) {
-  if (rows <= 4)
-    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 4>), dim3(grid), dim3(kThreads), 0, st, sp);
-  else
-    hipLaunchKernelGGL((seg_valu_kernel<E, SHUF, 8>), dim3(grid), dim3(kThreads), 0, st, sp);
-  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
-}
-
 }  // namespace
 
-int launch_segments_valu(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
-                         hipStream_t st) {
-  if (e == 2) return shuf ? launch_valu_e<2, true>(sp, max_rows, grid, st)
-                          : launch_valu_e<2, false>(sp, max_rows, grid, st);
-  return shuf ? launch_valu_e<1, true>(sp, max_rows, grid, st)
-              : launch_valu_e<1, false>(sp, max_rows, grid, st);
+int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
+  if (shuf)
+    hipLaunchKernelGGL((seg_valu_kernel<true, 4>), dim3(grid), dim3(64 * 4), 0, st, sp);
+  else
+    hipLaunchKernelGGL((seg_valu_kernel<false, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
 }  // namespace skv

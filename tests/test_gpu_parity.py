@@ -120,10 +120,15 @@ CASES = [
     # name, seq_lens, q_lens, Hq, Hkv, dtype, layout, causal, num_cus, seg_max
     ("tiny_std", [37, 100], [1, 1], 8, 2, "bf16", "standard", 1, 256, 64),
     ("tiny_shuf", [37, 100], [1, 1], 8, 2, "bf16", "shuffled", 1, 256, 64),
-    ("valu8_ragged", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "standard", 1, 64, 8),
-    ("valu8_shuf", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "shuffled", 1, 64, 8),
-    ("valu_fp8_std", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "standard", 1, 40, 16),
-    ("valu_fp8_shuf", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "shuffled", 1, 40, 16),
+    ("rows8_ragged", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "standard", 1, 64, 8),
+    ("rows8_shuf", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "bf16", "shuffled", 1, 64, 8),
+    ("fp8_rows4_std", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "standard", 1, 40, 16),
+    ("fp8_rows4_shuf", [3, 77, 513, 2049], [1, 1, 1, 1], 16, 4, "fp8", "shuffled", 1, 40, 16),
+    ("valu_g1_q1", [7, 300, 5000, 33, 0], [1, 1, 1, 1, 1], 2, 2, "bf16", "standard", 1, 64, 16),
+    ("valu_g1_q3", [50, 700, 3, 129], [3, 3, 2, 1], 2, 2, "bf16", "standard", 1, 32, 64),
+    ("valu_g2_q2_shuf", [1, 17, 999, 4096], [2, 1, 2, 2], 4, 2, "bf16", "shuffled", 1, 32, 64),
+    ("valu_g4_noncausal", [100, 2000, 16], [1, 1, 1], 8, 2, "bf16", "standard", 0, 256, 64),
+    ("valu_g4_shuf_tails", [15, 31, 33, 1023], [1, 1, 1, 1], 32, 8, "bf16", "shuffled", 1, 128, 64),
     ("mfma1_g16_q1", [0, 1, 5, 17, 4000, 2333], [1, 1, 1, 1, 1, 1], 32, 2, "bf16", "standard", 1, 256, 64),
     ("mfma2_g8_q4", [1, 5, 17, 900, 3000], [4, 3, 2, 4, 1], 16, 2, "bf16", "standard", 1, 32, 64),
     ("mfma4_g16_q4", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "bf16", "standard", 1, 64, 64),
@@ -185,7 +190,12 @@ def test_fixed_split_matches_oracle(spec):
     assert r["lse_err"] <= 1e-3, r
 
 
-@pytest.mark.parametrize("spec", [CASES[2], CASES[8], CASES[12]], ids=lambda c: c[0])
+_BY = {c[0]: c for c in CASES}
+
+
+@pytest.mark.parametrize("spec", [_BY[n] for n in ("rows8_ragged", "mfma4_g16_q4", "mfma_fp8_std",
+                                                   "valu_g1_q3", "valu_g4_shuf_tails")],
+                         ids=lambda c: c[0])
 def test_nan_poison_does_not_leak(spec):
     a = run_hip(_mk(*spec, poison="finite"))
     b = run_hip(_mk(*spec, poison="nan"))
@@ -193,7 +203,8 @@ def test_nan_poison_does_not_leak(spec):
     assert np.all(np.isfinite(b["out"]))
 
 
-@pytest.mark.parametrize("spec", [CASES[1], CASES[9]], ids=lambda c: c[0])
+@pytest.mark.parametrize("spec", [_BY[n] for n in ("tiny_shuf", "mfma4_g16_q4_shuf",
+                                                   "valu_g1_q1")], ids=lambda c: c[0])
 def test_deterministic(spec):
     case = _mk(*spec)
     a = run_hip(case)
