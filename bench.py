@@ -189,6 +189,35 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         reduce_us=red_us, attn_us_per_call=call_us, step_us=step_us, wall_s=wall,
         kv_tb_s=kvb / call_us / 1e6, frac_of_hbm_peak=kvb / call_us / 1e3 / HBM_PEAK_GBS,
         segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
+    # the same attention call captured once in a HIP graph and replayed, as a
+    # serving loop runs decode steps: launch gaps between segment and reduce go
+    def attn_call():
+        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
+                         case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
+        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
+                         seg_max=cfg.seg_max, out=out)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(st)
+    with torch.cuda.stream(side):
+        attn_call()
+    st.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        attn_call()
+    for _ in range(warmup):
+        graph.replay()
+    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        gev[i][0].record(st)
+        graph.replay()
+        gev[i][1].record(st)
+    torch.cuda.synchronize()
+    res["graph_us_per_call"] = sum(e[0].elapsed_time(e[1]) for e in gev) * 1e3 / steps
+    res["graph_kv_tb_s"] = kvb / res["graph_us_per_call"] / 1e6
+    del graph
+
     # the fixed split on the same batch (no plan; the segment kernel writes the
     # per-token counts): the pages' A/B comparison, on these kernels
     def fixed_call(ev=None):
@@ -316,6 +345,8 @@ def main():
         "breakdown_us": {k: round(head[k], 2) for k in
                          ("plan_us", "segment_us", "segment_us_median", "segment_us_p10",
                           "segment_us_p90", "reduce_us", "step_us")},
+        "graph_replay": {"us_per_call": round(head["graph_us_per_call"], 2),
+                         "kv_tb_s": round(head["graph_kv_tb_s"], 4)},
         "fixed_split": {"us_per_call": round(head["fixed_split_us_per_call"], 2),
                         "kv_tb_s": round(head["fixed_split_kv_tb_s"], 4),
                         "segments_per_seq": head["fixed_split_segments"]},
