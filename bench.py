@@ -46,7 +46,7 @@ def _args():
 
 
 # the sources the segment-attention kernels are compiled from
-SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_valu.hip",
+SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip", "skv_attn_valu.hip",
                    "skv_attn_common.h", "skv_internal.h")
 
 

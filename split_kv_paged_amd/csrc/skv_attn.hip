@@ -14,6 +14,8 @@ namespace skv {
 int launch_segments_mfma(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
                          hipStream_t st);
 int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st);
+int launch_segments_mfma_priv(const SegParams& sp, bool shuf, int max_rows, int grid,
+                              hipStream_t st);
 
 // bf16 KV with at most this many rows goes to the vector-ALU kernel; the rest
 // to 16-row matrix-core tiles. Measured on MI355X (balanced 32 x 60k batches):
@@ -61,6 +63,8 @@ int launch_segments(const AttnArgs& a, void* stream) {
   auto st = static_cast<hipStream_t>(stream);
   if (e == 2 && rows <= kValuMaxRows)
     return launch_segments_valu(sp, shuf, static_cast<int>(grid), st);
+  if (e == 1)       // fp8: private per-wave rings, K and V widened once per block
+    return launch_segments_mfma_priv(sp, shuf, rows, static_cast<int>(grid), st);
   return launch_segments_mfma(sp, e, shuf, rows, static_cast<int>(grid), st);
 }
 

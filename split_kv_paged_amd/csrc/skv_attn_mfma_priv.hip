@@ -1,0 +1,370 @@
+// Segment attention, matrix-core variant with private per-wave rings (fp8 KV,
+// query rows = GQA group x query tokens, padded to 16-row tiles).
+//
+// sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
+// for dynamic workload", Motivation and Modifications: one work-group per
+// (segment, sequence, kv head) computes softmax(q.K^T/sqrt(d)).V of all the
+// sequence's query rows for that kv head over the segment's pages and writes a
+// per-segment partial; the work-group decodes (seq, seg) from the work list.
+//
+// MI355X design. With a skewed batch the plan leaves only some CUs streaming
+// the longest segments, so what one work-group can pull through a CU sets the
+// layer time. A shared ring with a barrier per stage runs every wave through
+// the same serial chain (wait, LDS, widen, MFMA, softmax, MFMA) in lockstep;
+// a bare DMA ring of the same depth streams about twice as fast. Here:
+//  * Each of NW waves owns the 32-token blocks w, w + NW, ... of the segment
+//    and streams them through a private LDS ring of NP block slots (direct-
+//    to-LDS DMA issued from inline asm, waits on its own vmcnt only): no
+//    barrier in the main loop, so the waves drift apart and one wave's MFMA or
+//    VALU work overlaps another's waits.
+//  * A wave computes every 16-row query tile (NRT of them) of its block, so
+//    each K and V element is widened from fp8 once (v_cvt_scalef32_pk_bf16_fp8,
+//    exact) and read from LDS once.
+//  * Block layout in LDS as in the shared-ring variant: K chunk-major per page
+//    (operand lanes read contiguous 16-byte chunks), V chunk-major for the
+//    transposing byte read (ds_read_b64_tr_b8), or the shuffled V plane as is.
+//  * Scores transposed per page, S^T = K.Q^T, with v_mfma_f32_16x16x32_bf16;
+//    online softmax in the exp2 domain per tile, lazy rescale; masked scores
+//    -inf and V past the segment end zeroed (page-tail poison never leaks).
+//  * At the end the waves' (max, sum, O) are merged through LDS, each wave
+//    taking a share of the (row tile, channel tile) pairs.
+#include "skv_attn_common.h"
+#include "skv.h"
+
+namespace skv {
+namespace {
+
+constexpr int kD = kHeadDim;
+constexpr int kE = 1;                                   // fp8 elements
+constexpr int kUnitBytes = kPageSize * kD * kE;         // one page's K (or V) half
+constexpr int kUnitInstr = kUnitBytes / 1024;           // DMA instructions per unit
+constexpr int kBlockBytes = 4 * kUnitBytes;             // 2 pages x (K, V)
+constexpr int kBlockInstr = 4 * kUnitInstr;
+constexpr int kStdTile = kPageSize * 2 * kD * kE;       // standard (block, head)
+constexpr int kStdRow = 2 * kD * kE;
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
+
+template <int NW, int NRT>
+struct PRing {
+  static constexpr int kBytes = 128 * 1024 / NW;        // one wave's ring
+  static constexpr int kNP = kBytes / kBlockBytes;      // block slots
+  static_assert(kNP >= 2, "two block slots per wave");
+  static_assert((kNP - 1) * kBlockInstr <= 63, "vmcnt range");
+  // merge scratch: every wave's O^T tiles, in the (then idle) rings
+  static_assert(NW * NRT * 8 * 64 * 16 <= NW * kBytes, "merge scratch fits");
+};
+
+template <int N>
+__device__ __forceinline__ void pwait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int STEP, int MAXK>
+__device__ __forceinline__ void pwait_blocks(int k) {
+  // wait until at most k blocks' worth (k * STEP instructions) remain in flight
+  if constexpr (MAXK >= 6) { if (k >= 6) { pwait_vmcnt<6 * STEP>(); return; } }
+  if constexpr (MAXK >= 5) { if (k == 5) { pwait_vmcnt<5 * STEP>(); return; } }
+  if constexpr (MAXK >= 4) { if (k == 4) { pwait_vmcnt<4 * STEP>(); return; } }
+  if constexpr (MAXK >= 3) { if (k == 3) { pwait_vmcnt<3 * STEP>(); return; } }
+  if constexpr (MAXK >= 2) { if (k == 2) { pwait_vmcnt<2 * STEP>(); return; } }
+  if constexpr (MAXK >= 1) { if (k == 1) { pwait_vmcnt<1 * STEP>(); return; } }
+  pwait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void pdma16(const uint8_t* g, uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// One 32-token block (pages pid0, pid1) into a slot: unit u = (page u/2, K if
+// u even, V if odd) at slot + u * kUnitBytes; the same lane -> chunk maps as
+// the shared-ring variant.
+template <bool SHUF>
+__device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& it, int pid0,
+                                            int pid1, uint8_t* slot, int lane) {
+  const int r16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const size_t head = static_cast<size_t>(u < 2 ? pid0 : pid1) * p.Hkv + it.g;
+    uint8_t* dst = slot + u * kUnitBytes;
+    if ((u & 1) == 0) {
+      const uint8_t* tile = p.kv_a + head * (SHUF ? kUnitBytes : kStdTile);
+#pragma unroll
+      for (int i = 0; i < kUnitInstr; ++i) {
+        const size_t off = SHUF ? (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16
+                                : static_cast<size_t>(r16) * kStdRow + 64 * i + 16 * j4;
+        pdma16(tile + off, dst + i * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kUnitInstr; ++i) {
+        size_t off;
+        if constexpr (SHUF) {
+          off = static_cast<size_t>(i * 64 + lane) * 16;          // plane copied as is
+        } else {
+          const int c = 4 * i + (lane >> 4), tau = lane & 15;     // [chunk c][token tau][16 B]
+          off = static_cast<size_t>(tau) * kStdRow + kD * kE + c * 16;
+        }
+        const uint8_t* base = SHUF ? p.kv_b + head * kUnitBytes : p.kv_a + head * kStdTile;
+        pdma16(base + off, dst + i * 1024);
+      }
+    }
+  }
+}
+
+template <bool SHUF, int NRT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void seg_mfma_priv_kernel(SegParams p) {
+  using R = PRing<NW, NRT>;
+  constexpr int kNP = R::kNP;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
+  __shared__ float sm_m[NW][NRT][16];
+  __shared__ float sm_l[NW][NRT][16];
+
+  const SegItem it = decode_item(p);
+  write_fixed_counts(p, it);
+  if (!it.valid) return;                                          // work-group uniform
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const int ntok = it.seg_end - it.seg_start;
+  const int nblk = (ntok + 31) >> 5;
+  const int seg_pages = (ntok + 15) >> 4;
+  const int nb = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;   // this wave's blocks
+  const int seg_page0 = it.seg_start >> 4;
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+  const float sm_scale = kScoreScaleLog2 * p.k_scale[0];
+  const float out_scale = p.v_scale[0];
+
+  // ---- Q rows of every tile (B operand of S^T = K.Q^T) ----
+  bf16x8_t qb[NRT][4];
+  int lim[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    const int n = 16 * t + r16;
+    lim[t] = row_limit(it, n, p.G, p.causal);
+    const bool ok = n < it.rows;
+    const int tq = it.c0 + (ok ? n / p.G : 0);
+    const int h = it.g * p.G + (ok ? n % p.G : 0);
+    const uint16_t* qr = p.q + (static_cast<size_t>(tq) * p.Hq + h) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int ch = 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
+      qb[t][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + ch));   // padding rows read row 0
+    }
+  }
+  // consume Q before any DMA is in flight (a later wait for it would drain the ring)
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      asm volatile("" : "+v"(qb[t][kk]));
+      if (16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+
+  uint8_t* wring = ring[wave];
+  // pages of this wave's k-th block (block wave + NW k); pages past the end
+  // read the segment's first page (masked and zeroed; keeps vmcnt exact)
+  auto pids = [&](int k, int& a, int& b) {
+    const int pg = 2 * (wave + NW * k);
+    a = ptab[pg < seg_pages ? pg : 0];
+    b = ptab[pg + 1 < seg_pages ? pg + 1 : 0];
+  };
+#pragma unroll
+  for (int k = 0; k < kNP - 1; ++k) {
+    if (k < nb) {
+      int a, b;
+      pids(k, a, b);
+      issue_block<SHUF>(p, it, a, b, wring + k * kBlockBytes, lane);
+    }
+  }
+
+  f32x4_t oacc[NRT][8];
+  float m[NRT], l[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // per-lane part of the transposing byte-read address in the chunk-major V tile
+  const int vtr_off = (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;
+
+  for (int k = 0; k < nb; ++k) {
+    if (k + kNP - 1 < nb) {                     // slot of block k-1, consumed last iteration
+      int a, b;
+      pids(k + kNP - 1, a, b);
+      issue_block<SHUF>(p, it, a, b, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
+    }
+    pwait_blocks<kBlockInstr, kNP - 1>(min(kNP - 1, nb - 1 - k));   // block k landed
+    const uint8_t* slot = wring + (k % kNP) * kBlockBytes;
+    const uint8_t* kU[2] = {slot, slot + 2 * kUnitBytes};
+    const uint8_t* vU[2] = {slot + kUnitBytes, slot + 3 * kUnitBytes};
+    const int tok0 = it.seg_start + 32 * (wave + NW * k);
+
+    // ---- S^T per page, every tile ----
+    f32x4_t sacc[NRT][2];
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      bf16x8_t kop[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint4 c = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
+        kop[2 * u] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.x, c.y)));
+        kop[2 * u + 1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.z, c.w)));
+      }
+#pragma unroll
+      for (int t = 0; t < NRT; ++t) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[t][kk], acc, 0, 0, 0);
+        sacc[t][pg] = acc;
+      }
+    }
+
+    // ---- online softmax per tile (row n = 16t + r16; 8 tokens per lane) ----
+    bf16x8_t pb[NRT];
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      float s[8];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
+        const float v = sacc[t][e >> 2][e & 3] * sm_scale;
+        s[e] = pos < lim[t] ? v : -INFINITY;
+        bm = fmaxf(bm, s[e]);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m[t], bm);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      if (__builtin_amdgcn_ballot_w64(mn != m[t]) != 0) {  // some row max moved
+        const float alpha = fast_exp2(m[t] - mu);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[t][dt] *= alpha;
+        m[t] = mn;
+      }
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
+        l[t] += a + b;
+        pk[e >> 1] = pack_bf16x2(a, b);
+      }
+      pb[t] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+    }
+
+    // ---- O^T += V^T.P^T, V widened once for every tile ----
+    const bool tail = tok0 + 32 > it.seg_end;
+    const int vend = it.seg_end - tok0;
+    const uint8_t* vU8 = vU[r16 >> 3];           // lanes 0-7 of a group read page 0
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + r16;
+      uint32_t w[4];
+      if constexpr (SHUF) {
+        const uint32_t a = *reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4);
+        const uint32_t b = *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4);
+        const uint4 c = fp8x8_to_bf16x8(make_uint2(a, b));
+        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+      } else {
+        // in each 16-lane group, lane i receives byte i%8 of the 8 bytes read
+        // by lane 2k + i/8: the block's 8 tokens of channel 16dt + i
+        const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32_t*)(
+                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256));
+        const uint4 c = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
+        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+      }
+      if (tail) {                    // zero V of tokens past the segment end
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
+          w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
+        }
+      }
+      const bf16x8_t vop = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+#pragma unroll
+      for (int t = 0; t < NRT; ++t)
+        oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
+    }
+  }
+
+  // ---- this wave's totals; then merge the waves through LDS ----
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
+  pwait_vmcnt<0>();
+  __syncthreads();                               // every ring is idle: reuse it
+  f32x4_t* oslot = reinterpret_cast<f32x4_t*>(&ring[0][0]);   // [w][t][dt][lane]
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oslot[((wave * NRT + t) * 8 + dt) * 64 + lane] = oacc[t][dt];
+  if (j4 == 0) {
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      sm_m[wave][t][r16] = m[t];
+      sm_l[wave][t][r16] = l[t];
+    }
+  }
+  __syncthreads();
+  for (int pair = wave; pair < NRT * 8; pair += NW) {     // (tile, channel tile) pairs
+    const int t = pair >> 3, dt = pair & 7;
+    const int n = 16 * t + r16;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float Ls = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm_m[w][t][r16] - mu);
+      Ls += sm_l[w][t][r16] * f;
+      o += oslot[((w * NRT + t) * 8 + dt) * 64 + lane] * f;
+    }
+    if (n >= it.rows) continue;
+    const int tq = it.c0 + n / p.G;
+    const int h = it.g * p.G + n % p.G;
+    const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
+    const bool any = Ls > 0.f;
+    const float inv = any ? out_scale / Ls : 0.f;
+    *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
+    if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
+  }
+}
+
+template <bool SHUF>
+int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
+  // 8 waves (two per SIMD) up to two row tiles; four row tiles need the
+  // registers and merge scratch of 4 waves
+  if (nrt <= 1)
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 1, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  else if (nrt <= 2)
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 2, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  else
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 4, 4>), dim3(grid), dim3(64 * 4), 0, st, sp);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+}  // namespace
+
+int launch_segments_mfma_priv(const SegParams& sp, bool shuf, int max_rows, int grid,
+                              hipStream_t st) {
+  const int nrt = (max_rows + 15) / 16;
+  return shuf ? launch_priv<true>(sp, nrt, grid, st) : launch_priv<false>(sp, nrt, grid, st);
+}
+
+}  // namespace skv
