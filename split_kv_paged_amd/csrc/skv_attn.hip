@@ -11,19 +11,24 @@
 
 namespace skv {
 
-int launch_segments_mfma(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
-                         hipStream_t st);
+int launch_segments_mfma(const SegParams& sp, bool shuf, int grid, hipStream_t st);
 int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st);
-int launch_segments_mfma_priv(const SegParams& sp, bool shuf, int max_rows, int grid,
+int launch_segments_mfma_priv(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
                               hipStream_t st);
 
-// bf16 KV with at most this many rows goes to the vector-ALU kernel; the rest
-// to 16-row matrix-core tiles. Measured on MI355X (balanced 32 x 60k batches):
-// at 1-4 bf16 rows both kernels stream at 5.6-6.0 TB/s; at 5-8 rows the
-// vector ALU's rows x 128 fp32 FMAs per token, and for fp8 at any row count the
-// widening of every K and V element, make it compute-bound (1.7-3.4 TB/s)
-// where a partly filled MFMA tile still streams at 5.3-5.9 TB/s.
+// Which kernel runs, by element type and query rows (GQA group x max query
+// tokens); measured on MI355X:
+//  * bf16, <= 4 rows: the vector-ALU kernel (5.6-6.0 TB/s; at 5+ rows its
+//    rows x 128 fp32 FMAs per token make it compute-bound);
+//  * bf16, 5-32 rows, and fp8 at any row count: matrix cores on private
+//    per-wave rings (no barrier in the loop; fp8 K/V widened once), which a
+//    single work-group streams ~35-42 GB/s through a CU against ~24-30 GB/s
+//    for a shared ring: that is what skewed batches, with part of the CUs
+//    idle, need;
+//  * bf16, 33-64 rows: matrix cores on a ring shared by 8 waves (four row
+//    tiles per block do not fit two waves per SIMD in private form).
 constexpr int kValuMaxRows = 4;
+constexpr int kPrivMaxRowsBf16 = 32;
 
 int launch_segments(const AttnArgs& a, void* stream) {
   SegParams sp;
@@ -63,9 +68,9 @@ int launch_segments(const AttnArgs& a, void* stream) {
   auto st = static_cast<hipStream_t>(stream);
   if (e == 2 && rows <= kValuMaxRows)
     return launch_segments_valu(sp, shuf, static_cast<int>(grid), st);
-  if (e == 1)       // fp8: private per-wave rings, K and V widened once per block
-    return launch_segments_mfma_priv(sp, shuf, rows, static_cast<int>(grid), st);
-  return launch_segments_mfma(sp, e, shuf, rows, static_cast<int>(grid), st);
+  if (e == 1 || rows <= kPrivMaxRowsBf16)
+    return launch_segments_mfma_priv(sp, e, shuf, rows, static_cast<int>(grid), st);
+  return launch_segments_mfma(sp, shuf, static_cast<int>(grid), st);
 }
 
 }  // namespace skv

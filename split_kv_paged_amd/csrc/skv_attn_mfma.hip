@@ -1,5 +1,6 @@
-// Segment attention, matrix-core variant (query rows = GQA group x query
-// tokens >= 9, padded to 16-row tiles).
+// Segment attention, matrix-core variant on a ring shared by all waves, used
+// for bf16 KV with 33-64 query rows (GQA group x query tokens, four 16-row
+// tiles); the kernel itself is generic in the element type and tile count.
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Motivation and Modifications: one work-group per
@@ -450,29 +451,18 @@ void seg_mfma_kernel(SegParams p) {
   if (j4 == 0) p.part_lse[prow] = any ? (M + fast_log2(Ls)) * kLn2 : -INFINITY;
 }
 
-template <int E, bool SHUF>
-int launch_mfma_e(const SegParams& sp, int nrt, int grid, hipStream_t st) {
-  if (nrt <= 1)
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 1>), dim3(grid),
-                       dim3(64 * Ring<E, 1>::kWaves), 0, st, sp);
-  else if (nrt <= 2)
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 2>), dim3(grid),
-                       dim3(64 * Ring<E, 2>::kWaves), 0, st, sp);
-  else
-    hipLaunchKernelGGL((seg_mfma_kernel<E, SHUF, 4>), dim3(grid),
-                       dim3(64 * Ring<E, 4>::kWaves), 0, st, sp);
-  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
-}
-
 }  // namespace
 
-int launch_segments_mfma(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
-                         hipStream_t st) {
-  const int nrt = (max_rows + 15) / 16;
-  if (e == 2) return shuf ? launch_mfma_e<2, true>(sp, nrt, grid, st)
-                          : launch_mfma_e<2, false>(sp, nrt, grid, st);
-  return shuf ? launch_mfma_e<1, true>(sp, nrt, grid, st)
-              : launch_mfma_e<1, false>(sp, nrt, grid, st);
+// bf16 KV with 33-64 rows (four row tiles); the other cases run on the
+// private-ring variants
+int launch_segments_mfma(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
+  if (shuf)
+    hipLaunchKernelGGL((seg_mfma_kernel<2, true, 4>), dim3(grid),
+                       dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
+  else
+    hipLaunchKernelGGL((seg_mfma_kernel<2, false, 4>), dim3(grid),
+                       dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
 }  // namespace skv

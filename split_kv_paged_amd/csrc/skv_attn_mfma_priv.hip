@@ -1,5 +1,6 @@
-// Segment attention, matrix-core variant with private per-wave rings (fp8 KV,
-// query rows = GQA group x query tokens, padded to 16-row tiles).
+// Segment attention, matrix-core variants with private per-wave rings: fp8 KV
+// (32-token block slots) and bf16 KV with up to 32 rows (16-token page slots);
+// query rows = GQA group x query tokens, padded to 16-row tiles.
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Motivation and Modifications: one work-group per
@@ -346,6 +347,247 @@ void seg_mfma_priv_kernel(SegParams p) {
   }
 }
 
+// ---- bf16 KV: a 32-token block is 16 KB, so the private slots are pages ----
+//
+// One 16-token page (K 4 KB, V 4 KB) per slot. Scores per page as above; P.V
+// with v_mfma_f32_16x16x16bf16_1k over the page's 16 tokens: the score MFMA's
+// C layout already holds 4 tokens of one row per lane (the B operand), and the
+// transposing 16-bit read of the chunk-major V tile gives each lane 4 tokens of
+// one channel (the A operand).
+constexpr int kHalf2 = kPageSize * kD * 2;              // a bf16 page's K (or V) half
+constexpr int kPage2 = 2 * kHalf2;
+constexpr int kPageInstr2 = kPage2 / 1024;
+constexpr int kStdTile2 = kPageSize * 2 * kD * 2;
+constexpr int kStdRow2 = 2 * kD * 2;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+template <int NW, int NRT>
+struct PRing2 {
+  static constexpr int kBytes = 128 * 1024 / NW;
+  static constexpr int kNP = kBytes / kPage2;
+  static_assert(kNP >= 2, "two page slots per wave");
+  static_assert((kNP - 1) * kPageInstr2 <= 63, "vmcnt range");
+  static_assert(NW * NRT * 8 * 64 * 16 <= NW * kBytes, "merge scratch fits");
+};
+
+// one page into a slot: K chunk-major for the operand lanes, V in the
+// chunk-pair-major tile of the transposing read ([pair][token][32 B]), or the
+// shuffled planes as they are
+template <bool SHUF>
+__device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& it, int pid,
+                                            uint8_t* slot, int lane) {
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
+  const uint8_t* ktile = p.kv_a + head * (SHUF ? kHalf2 : kStdTile2);
+#pragma unroll
+  for (int i = 0; i < kHalf2 / 1024; ++i) {
+    const size_t off = SHUF ? (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16
+                            : static_cast<size_t>(r16) * kStdRow2 + (32 * i + 8 * j4) * 2;
+    pdma16(ktile + off, slot + i * 1024);
+  }
+  const uint8_t* vbase = SHUF ? p.kv_b + head * kHalf2 : p.kv_a + head * kStdTile2;
+#pragma unroll
+  for (int i = 0; i < kHalf2 / 1024; ++i) {
+    size_t off;
+    if constexpr (SHUF) {
+      off = static_cast<size_t>(i * 64 + lane) * 16;
+    } else {
+      const int u = 2 * i + (lane >> 5), tau = (lane >> 1) & 15, c = 2 * u + (lane & 1);
+      off = static_cast<size_t>(tau) * kStdRow2 + kD * 2 + c * 16;
+    }
+    pdma16(vbase + off, slot + kHalf2 + i * 1024);
+  }
+}
+
+template <bool SHUF, int NRT, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+void seg_mfma_priv2_kernel(SegParams p) {
+  using R = PRing2<NW, NRT>;
+  constexpr int kNP = R::kNP;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
+  __shared__ float sm_m[NW][NRT][16];
+  __shared__ float sm_l[NW][NRT][16];
+
+  const SegItem it = decode_item(p);
+  write_fixed_counts(p, it);
+  if (!it.valid) return;                                          // work-group uniform
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, j4 = lane >> 4;
+  const int seg_pages = (it.seg_end - it.seg_start + 15) >> 4;
+  const int np = seg_pages > wave ? (seg_pages - wave + NW - 1) / NW : 0;   // this wave's pages
+  const int seg_page0 = it.seg_start >> 4;
+  const __attribute__((address_space(4))) int32_t* ptab =
+      (const __attribute__((address_space(4))) int32_t*)(
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+  const float sm_scale = kScoreScaleLog2;
+
+  bf16x8_t qb[NRT][4];
+  int lim[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    const int n = 16 * t + r16;
+    lim[t] = row_limit(it, n, p.G, p.causal);
+    const bool ok = n < it.rows;
+    const int tq = it.c0 + (ok ? n / p.G : 0);
+    const int h = it.g * p.G + (ok ? n % p.G : 0);
+    const uint16_t* qr = p.q + (static_cast<size_t>(tq) * p.Hq + h) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qb[t][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + 32 * kk + 8 * j4));
+  }
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      asm volatile("" : "+v"(qb[t][kk]));
+      if (16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    }
+
+  uint8_t* wring = ring[wave];
+  auto pid_of = [&](int k) { return ptab[wave + NW * k]; };       // page wave + NW k
+#pragma unroll
+  for (int k = 0; k < kNP - 1; ++k)
+    if (k < np) issue_page2<SHUF>(p, it, pid_of(k), wring + k * kPage2, lane);
+
+  f32x4_t oacc[NRT][8];
+  float m[NRT], l[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    m[t] = -INFINITY;
+    l[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // transposing 16-bit read: in each 16-lane group lane i receives element i%4
+  // of the 8 bytes read by lane 4k + i/4; lane j reads token 4*j4 + j/4,
+  // channels 16dt + 4(j%4) .. +3, so lane i gets tokens 4*j4 .. +3 of channel
+  // 16dt + i (512 contiguous bytes per channel tile)
+  const int vtr_off = (4 * j4 + (r16 >> 2)) * 32 + ((r16 >> 1) & 1) * 16 + (r16 & 1) * 8;
+
+  for (int k = 0; k < np; ++k) {
+    if (k + kNP - 1 < np)                       // slot of page k-1, consumed last iteration
+      issue_page2<SHUF>(p, it, pid_of(k + kNP - 1), wring + ((k + kNP - 1) % kNP) * kPage2,
+                        lane);
+    pwait_blocks<kPageInstr2, kNP - 1>(min(kNP - 1, np - 1 - k));   // page k landed
+    const uint8_t* sK = wring + (k % kNP) * kPage2;
+    const uint8_t* sV = sK + kHalf2;
+    const int tok0 = it.seg_start + 16 * (wave + NW * k);
+
+    // ---- S^T of the page, every tile ----
+    bf16x8_t kop[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sK + kk * 1024 + lane * 16));
+    v4i16_t pb[NRT];
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[t][kk], acc, 0, 0, 0);
+      // online softmax: this lane holds tokens 4*j4 .. +3 of row 16t + r16
+      float s[4];
+      float bm = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = acc[e] * sm_scale;
+        s[e] = tok0 + 4 * j4 + e < lim[t] ? v : -INFINITY;
+        bm = fmaxf(bm, s[e]);
+      }
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m[t], bm);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      if (__builtin_amdgcn_ballot_w64(mn != m[t]) != 0) {  // some row max moved
+        const float alpha = fast_exp2(m[t] - mu);
+        l[t] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) oacc[t][dt] *= alpha;
+        m[t] = mn;
+      }
+      const float a0 = fast_exp2(s[0] - mu), a1 = fast_exp2(s[1] - mu);
+      const float a2 = fast_exp2(s[2] - mu), a3 = fast_exp2(s[3] - mu);
+      l[t] += (a0 + a1) + (a2 + a3);
+      pb[t] = __builtin_bit_cast(v4i16_t, make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)));
+    }
+
+    // ---- O^T += V^T.P^T over the page's 16 tokens ----
+    const int vend = it.seg_end - tok0;          // tokens of the page before the end
+    const bool tail = vend < 16;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 w;
+      if constexpr (SHUF) {
+        // V plane [N/x][D][x]: channel d's 16-byte chunk of token group g holds
+        // tokens 8g .. 8g+7; this lane needs tokens 4*j4 .. +3
+        const int d = 16 * dt + r16;
+        w = *reinterpret_cast<const uint2*>(sV + ((j4 >> 1) * kD + d) * 16 + (j4 & 1) * 8);
+      } else {
+        const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16_t*)(
+                (__attribute__((address_space(3))) uint8_t*)(sV) + vtr_off + dt * 512));
+        w = __builtin_bit_cast(uint2, v);
+      }
+      if (tail) {                    // zero V of tokens past the segment end
+        const int rel0 = vend - 4 * j4, rel1 = rel0 - 2;
+        w.x = rel0 <= 0 ? 0u : (rel0 == 1 ? (w.x & 0xffffu) : w.x);
+        w.y = rel1 <= 0 ? 0u : (rel1 == 1 ? (w.y & 0xffffu) : w.y);
+      }
+      const v4i16_t vop = __builtin_bit_cast(v4i16_t, w);
+#pragma unroll
+      for (int t = 0; t < NRT; ++t)
+        oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb[t], oacc[t][dt], 0, 0, 0);
+    }
+  }
+
+  // ---- this wave's totals; then merge the waves through LDS ----
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
+  pwait_vmcnt<0>();
+  __syncthreads();                               // every ring is idle: reuse it
+  f32x4_t* oslot = reinterpret_cast<f32x4_t*>(&ring[0][0]);   // [w][t][dt][lane]
+#pragma unroll
+  for (int t = 0; t < NRT; ++t)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oslot[((wave * NRT + t) * 8 + dt) * 64 + lane] = oacc[t][dt];
+  if (j4 == 0) {
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      sm_m[wave][t][r16] = m[t];
+      sm_l[wave][t][r16] = l[t];
+    }
+  }
+  __syncthreads();
+  for (int pair = wave; pair < NRT * 8; pair += NW) {     // (tile, channel tile) pairs
+    const int t = pair >> 3, dt = pair & 7;
+    const int n = 16 * t + r16;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
+    const float mu = M == -INFINITY ? 0.f : M;
+    float Ls = 0.f;
+    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float f = fast_exp2(sm_m[w][t][r16] - mu);
+      Ls += sm_l[w][t][r16] * f;
+      o += oslot[((w * NRT + t) * 8 + dt) * 64 + lane] * f;
+    }
+    if (n >= it.rows) continue;
+    const int tq = it.c0 + n / p.G;
+    const int h = it.g * p.G + n % p.G;
+    const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
+    const bool any = Ls > 0.f;
+    const float inv = any ? 1.f / Ls : 0.f;
+    *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
+    if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
+  }
+}
+
 template <bool SHUF>
 int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   // 8 waves (two per SIMD) up to two row tiles; four row tiles need the
@@ -359,11 +601,24 @@ int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
+// bf16 with up to two row tiles (four would not fit two waves per SIMD)
+template <bool SHUF>
+int launch_priv2(const SegParams& sp, int nrt, int grid, hipStream_t st) {
+  if (nrt > 2) return SKV_EUNSUPPORTED;
+  if (nrt <= 1)
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 1, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  else
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 2, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
 }  // namespace
 
-int launch_segments_mfma_priv(const SegParams& sp, bool shuf, int max_rows, int grid,
+int launch_segments_mfma_priv(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
                               hipStream_t st) {
   const int nrt = (max_rows + 15) / 16;
+  if (e == 2)
+    return shuf ? launch_priv2<true>(sp, nrt, grid, st) : launch_priv2<false>(sp, nrt, grid, st);
   return shuf ? launch_priv<true>(sp, nrt, grid, st) : launch_priv<false>(sp, nrt, grid, st);
 }
 

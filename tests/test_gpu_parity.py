@@ -129,6 +129,9 @@ CASES = [
     ("valu_g2_q2_shuf", [1, 17, 999, 4096], [2, 1, 2, 2], 4, 2, "bf16", "shuffled", 1, 32, 64),
     ("valu_g4_noncausal", [100, 2000, 16], [1, 1, 1], 8, 2, "bf16", "standard", 0, 256, 64),
     ("valu_g4_shuf_tails", [15, 31, 33, 1023], [1, 1, 1, 1], 32, 8, "bf16", "shuffled", 1, 128, 64),
+    ("bf16_rows32_shuf", [3, 40, 777, 2500], [4, 2, 4, 3], 16, 2, "bf16", "shuffled", 1, 32, 64),
+    ("fp8_rows64_std", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "standard", 1, 64, 64),
+    ("fp8_rows64_shuf", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "shuffled", 1, 64, 64),
     ("mfma1_g16_q1", [0, 1, 5, 17, 4000, 2333], [1, 1, 1, 1, 1, 1], 32, 2, "bf16", "standard", 1, 256, 64),
     ("mfma2_g8_q4", [1, 5, 17, 900, 3000], [4, 3, 2, 4, 1], 16, 2, "bf16", "standard", 1, 32, 64),
     ("mfma4_g16_q4", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "bf16", "standard", 1, 64, 64),
