@@ -51,8 +51,7 @@ struct PRing {
   static constexpr int kNP = kBytes / kBlockBytes;      // block slots
   static_assert(kNP >= 2, "two block slots per wave");
   static_assert((kNP - 1) * kBlockInstr <= 63, "vmcnt range");
-  // merge scratch: every wave's O^T tiles, in the (then idle) rings
-  static_assert(NW * NRT * 8 * 64 * 16 <= NW * kBytes, "merge scratch fits");
+  static_assert(NW * 8 * 64 * 16 <= NW * kBytes, "a row tile's merge scratch fits");
 };
 
 template <int N>
@@ -112,6 +111,72 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
         const uint8_t* base = SHUF ? p.kv_b + head * kUnitBytes : p.kv_a + head * kStdTile;
         pdma16(base + off, dst + i * 1024);
       }
+    }
+  }
+}
+
+// The NW waves' partial states of each 16-row tile (row max m, row sum l and
+// O^T, each relative to the wave's own max) are merged through LDS and the
+// segment partial is written: every wave takes a share of the (row tile,
+// channel tile) pairs. The idle rings hold the O^T tiles, as many tiles per
+// round as fit (rounds are separated by barriers).
+template <int NW, int NRT>
+__device__ __forceinline__ void merge_and_write(const SegParams& p, const SegItem& it,
+                                                uint8_t* scratch, int scratch_bytes,
+                                                float (*sm_m)[NRT][16], float (*sm_l)[NRT][16],
+                                                f32x4_t (&oacc)[NRT][8], float (&m)[NRT],
+                                                float (&l)[NRT], float out_scale, int wave,
+                                                int lane) {
+  constexpr int kTileBytes = NW * 8 * 64 * 16;          // one row tile's O^T of every wave
+  const int tpr = scratch_bytes / kTileBytes;            // tiles per round (>= 1)
+  const int r16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
+  if (j4 == 0) {
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      sm_m[wave][t][r16] = m[t];
+      sm_l[wave][t][r16] = l[t];
+    }
+  }
+  f32x4_t* oslot = reinterpret_cast<f32x4_t*>(scratch);   // [tile in round][w][dt][lane]
+  for (int t0 = 0; t0 < NRT; t0 += tpr) {
+    __syncthreads();                 // rings idle / previous round's reads done
+#pragma unroll
+    for (int t = 0; t < NRT; ++t)
+      if (t >= t0 && t < t0 + tpr) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          oslot[(((t - t0) * NW + wave) * 8 + dt) * 64 + lane] = oacc[t][dt];
+      }
+    __syncthreads();
+    const int tn = min(tpr, NRT - t0);
+    for (int pair = wave; pair < tn * 8; pair += NW) {    // (tile, channel tile) pairs
+      const int tt = pair >> 3, dt = pair & 7, t = t0 + tt;
+      const int n = 16 * t + r16;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
+      const float mu = M == -INFINITY ? 0.f : M;
+      float Ls = 0.f;
+      f32x4_t o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = fast_exp2(sm_m[w][t][r16] - mu);
+        Ls += sm_l[w][t][r16] * f;
+        o += oslot[((tt * NW + w) * 8 + dt) * 64 + lane] * f;
+      }
+      if (n >= it.rows) continue;
+      const int tq = it.c0 + n / p.G;
+      const int h = it.g * p.G + n % p.G;
+      const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
+      const bool any = Ls > 0.f;
+      const float inv = any ? out_scale / Ls : 0.f;
+      *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
+      if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -300,51 +365,10 @@ void seg_mfma_priv_kernel(SegParams p) {
     }
   }
 
-  // ---- this wave's totals; then merge the waves through LDS ----
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
-  }
+  // ---- merge the waves' partial states; write the segment partial ----
   pwait_vmcnt<0>();
-  __syncthreads();                               // every ring is idle: reuse it
-  f32x4_t* oslot = reinterpret_cast<f32x4_t*>(&ring[0][0]);   // [w][t][dt][lane]
-#pragma unroll
-  for (int t = 0; t < NRT; ++t)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oslot[((wave * NRT + t) * 8 + dt) * 64 + lane] = oacc[t][dt];
-  if (j4 == 0) {
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      sm_m[wave][t][r16] = m[t];
-      sm_l[wave][t][r16] = l[t];
-    }
-  }
-  __syncthreads();
-  for (int pair = wave; pair < NRT * 8; pair += NW) {     // (tile, channel tile) pairs
-    const int t = pair >> 3, dt = pair & 7;
-    const int n = 16 * t + r16;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
-    const float mu = M == -INFINITY ? 0.f : M;
-    float Ls = 0.f;
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(sm_m[w][t][r16] - mu);
-      Ls += sm_l[w][t][r16] * f;
-      o += oslot[((w * NRT + t) * 8 + dt) * 64 + lane] * f;
-    }
-    if (n >= it.rows) continue;
-    const int tq = it.c0 + n / p.G;
-    const int h = it.g * p.G + n % p.G;
-    const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
-    const bool any = Ls > 0.f;
-    const float inv = any ? out_scale / Ls : 0.f;
-    *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
-    if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
-  }
+  merge_and_write<NW, NRT>(p, it, &ring[0][0], NW * R::kBytes, sm_m, sm_l, oacc, m, l,
+                           out_scale, wave, lane);
 }
 
 // ---- bf16 KV: a 32-token block is 16 KB, so the private slots are pages ----
@@ -367,7 +391,7 @@ struct PRing2 {
   static constexpr int kNP = kBytes / kPage2;
   static_assert(kNP >= 2, "two page slots per wave");
   static_assert((kNP - 1) * kPageInstr2 <= 63, "vmcnt range");
-  static_assert(NW * NRT * 8 * 64 * 16 <= NW * kBytes, "merge scratch fits");
+  static_assert(NW * 8 * 64 * 16 <= NW * kBytes, "a row tile's merge scratch fits");
 };
 
 // one page into a slot: K chunk-major for the operand lanes, V in the
@@ -541,51 +565,10 @@ void seg_mfma_priv2_kernel(SegParams p) {
     }
   }
 
-  // ---- this wave's totals; then merge the waves through LDS ----
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
-  }
+  // ---- merge the waves' partial states; write the segment partial ----
   pwait_vmcnt<0>();
-  __syncthreads();                               // every ring is idle: reuse it
-  f32x4_t* oslot = reinterpret_cast<f32x4_t*>(&ring[0][0]);   // [w][t][dt][lane]
-#pragma unroll
-  for (int t = 0; t < NRT; ++t)
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) oslot[((wave * NRT + t) * 8 + dt) * 64 + lane] = oacc[t][dt];
-  if (j4 == 0) {
-#pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      sm_m[wave][t][r16] = m[t];
-      sm_l[wave][t][r16] = l[t];
-    }
-  }
-  __syncthreads();
-  for (int pair = wave; pair < NRT * 8; pair += NW) {     // (tile, channel tile) pairs
-    const int t = pair >> 3, dt = pair & 7;
-    const int n = 16 * t + r16;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
-    const float mu = M == -INFINITY ? 0.f : M;
-    float Ls = 0.f;
-    f32x4_t o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float f = fast_exp2(sm_m[w][t][r16] - mu);
-      Ls += sm_l[w][t][r16] * f;
-      o += oslot[((w * NRT + t) * 8 + dt) * 64 + lane] * f;
-    }
-    if (n >= it.rows) continue;
-    const int tq = it.c0 + n / p.G;
-    const int h = it.g * p.G + n % p.G;
-    const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
-    const bool any = Ls > 0.f;
-    const float inv = any ? 1.f / Ls : 0.f;
-    *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
-    if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
-  }
+  merge_and_write<NW, NRT>(p, it, &ring[0][0], NW * R::kBytes, sm_m, sm_l, oacc, m, l,
+                           1.f, wave, lane);
 }
 
 template <bool SHUF>
