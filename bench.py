@@ -12,7 +12,8 @@ own, as is the in-place conversion of the same pool received as byte halves
 
 Prints ONE JSON line (rank 0). Default workload: the uniform verify batch
 (bs=16 x 119k tokens, 4 query tokens, 32/2 heads, bf16). `--all` adds the other
-workloads to the line under "workloads".
+workloads to the line under "workloads", among them the uniform and agentic
+batches with an fp8 cache, the element type of the split-KV PR's own table.
 """
 import argparse
 import hashlib
@@ -366,7 +367,7 @@ def main():
         line["repack"] = repack
     if a.all:
         wl = []
-        for c in configs.CONFIGS:
+        for c in configs.CONFIGS + configs.EXTRA:
             if c.name == cfg.name:
                 continue
             r = time_workload(c, a.steps, a.warmup, torch, skv, gen)

@@ -25,8 +25,13 @@
 //    (operand lanes read contiguous 16-byte chunks), V chunk-major for the
 //    transposing byte read (ds_read_b64_tr_b8), or the shuffled V plane as is.
 //  * Scores transposed per page, S^T = K.Q^T, with v_mfma_f32_16x16x32_bf16;
-//    online softmax in the exp2 domain per tile, lazy rescale; masked scores
-//    -inf and V past the segment end zeroed (page-tail poison never leaks).
+//    online softmax in the exp2 domain per tile (the scale folded into one fma
+//    before exp2). The running row max moves only when a block's scores rise
+//    2^8 above it, so most blocks need no cross-lane max and no rescale; blocks
+//    that every row sees in full skip the masks. Masked scores are -inf and V
+//    past the segment end is zeroed (page-tail poison never leaks).
+//  * fp8 with four row tiles (64 rows) keeps two waves per SIMD by reading Q
+//    from LDS instead of holding it in registers.
 //  * At the end the waves' (max, sum, O) are merged through LDS, each wave
 //    taking a share of the (row tile, channel tile) pairs.
 #include "skv_attn_common.h"
@@ -181,14 +186,26 @@ __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegIte
   }
 }
 
+// Online softmax of a private-ring wave, per 16-row tile and lane (row
+// 16t + r16): m is the running row max in the log2 domain (-inf before any
+// visible key) and the offset every exponential of the row uses (0 while m is
+// -inf). A block whose raw scores all stay below thr = (m + kSlackLog2) / c
+// keeps m: its weights are then at most 2^kSlackLog2, which bf16 and the fp32
+// sums carry without loss of relative precision, so the row max is exchanged
+// across lanes (and O rescaled) only when some row's scores rise that far.
+constexpr float kSlackLog2 = 8.f;
+
 template <bool SHUF, int NRT, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_mfma_priv_kernel(SegParams p) {
   using R = PRing<NW, NRT>;
   constexpr int kNP = R::kNP;
+  // four row tiles at two waves per SIMD: Q is read from LDS, not held in registers
+  constexpr bool kQLds = NRT >= 4;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
   __shared__ float sm_m[NW][NRT][16];
   __shared__ float sm_l[NW][NRT][16];
+  __shared__ uint4 qs[kQLds ? NRT * 4 * 64 : 1];
 
   const SegItem it = decode_item(p);
   write_fixed_counts(p, it);
@@ -204,34 +221,54 @@ void seg_mfma_priv_kernel(SegParams p) {
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
-  const float sm_scale = kScoreScaleLog2 * p.k_scale[0];
+  // scores enter exp2 as fma(raw, c, -m) with c > 0: a negative K scale is
+  // moved into Q's sign (exact), a zero one becomes the least normal float
+  const float ks = p.k_scale[0];
+  const float c = fmaxf(fabsf(ks) * kScoreScaleLog2, 1.17549435e-38f);
+  const float inv_c = 1.f / c;
+  const uint32_t qflip = ks < 0.f ? 0x80008000u : 0u;
   const float out_scale = p.v_scale[0];
+  // every row sees at least the keys below lim_min (row 0 is the most restricted)
+  const int lim_min = row_limit(it, 0, p.G, p.causal);
 
   // ---- Q rows of every tile (B operand of S^T = K.Q^T) ----
-  bf16x8_t qb[NRT][4];
-  int lim[NRT];
-#pragma unroll
-  for (int t = 0; t < NRT; ++t) {
+  auto load_q = [&](int t, int kk) -> uint4 {
     const int n = 16 * t + r16;
-    lim[t] = row_limit(it, n, p.G, p.causal);
     const bool ok = n < it.rows;
     const int tq = it.c0 + (ok ? n / p.G : 0);
     const int h = it.g * p.G + (ok ? n % p.G : 0);
     const uint16_t* qr = p.q + (static_cast<size_t>(tq) * p.Hq + h) * kD;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
-      qb[t][kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + ch));   // padding rows read row 0
+    const int ch = 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
+    return *reinterpret_cast<const uint4*>(qr + ch);             // padding rows read row 0
+  };
+  auto fix_q = [&](int t, uint4 v) -> uint4 {
+    if (16 * t + r16 >= it.rows) return make_uint4(0, 0, 0, 0);
+    return make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
+  };
+  bf16x8_t qb[kQLds ? 1 : NRT][4];
+  if constexpr (kQLds) {
+    for (int i = wave; i < NRT * 4; i += NW) {
+      const int t = i >> 2, kk = i & 3;
+      qs[i * 64 + lane] = fix_q(t, load_q(t, kk));
     }
+    __syncthreads();                           // before any DMA is in flight
+  } else {
+#pragma unroll
+    for (int t = 0; t < NRT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qb[t][kk] = as_bf16x8(load_q(t, kk));
+    // consume Q before any DMA is in flight (a later wait for it would drain the ring)
+#pragma unroll
+    for (int t = 0; t < NRT; ++t)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        asm volatile("" : "+v"(qb[t][kk]));
+        qb[t][kk] = as_bf16x8(fix_q(t, __builtin_bit_cast(uint4, qb[t][kk])));
+      }
   }
-  // consume Q before any DMA is in flight (a later wait for it would drain the ring)
+  int lim[NRT];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      asm volatile("" : "+v"(qb[t][kk]));
-      if (16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
+  for (int t = 0; t < NRT; ++t) lim[t] = row_limit(it, 16 * t + r16, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
   // pages of this wave's k-th block (block wave + NW k); pages past the end
@@ -251,10 +288,11 @@ void seg_mfma_priv_kernel(SegParams p) {
   }
 
   f32x4_t oacc[NRT][8];
-  float m[NRT], l[NRT];
+  float m[NRT], thr[NRT], l[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
     m[t] = -INFINITY;
+    thr[t] = -INFINITY;
     l[t] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -273,25 +311,35 @@ void seg_mfma_priv_kernel(SegParams p) {
     const uint8_t* kU[2] = {slot, slot + 2 * kUnitBytes};
     const uint8_t* vU[2] = {slot + kUnitBytes, slot + 3 * kUnitBytes};
     const int tok0 = it.seg_start + 32 * (wave + NW * k);
+    // wave-uniform: does any key of this block lie past some row's limit?
+    const bool masked = tok0 + 32 > lim_min;
 
-    // ---- S^T per page, every tile ----
+    // ---- S^T per page, every tile; independent MFMAs back to back ----
     f32x4_t sacc[NRT][2];
 #pragma unroll
-    for (int pg = 0; pg < 2; ++pg) {
-      bf16x8_t kop[4];
+    for (int t = 0; t < NRT; ++t) sacc[t][0] = sacc[t][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint4 c = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
-        kop[2 * u] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.x, c.y)));
-        kop[2 * u + 1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.z, c.w)));
+    for (int u = 0; u < 2; ++u) {
+      bf16x8_t kop[2][2];
+#pragma unroll
+      for (int pg = 0; pg < 2; ++pg) {
+        const uint4 cw = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
+        kop[pg][0] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cw.x, cw.y)));
+        kop[pg][1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cw.z, cw.w)));
       }
 #pragma unroll
-      for (int t = 0; t < NRT; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int kk = 2 * u + k2;
+        bf16x8_t qo[NRT];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[t][kk], acc, 0, 0, 0);
-        sacc[t][pg] = acc;
+        for (int t = 0; t < NRT; ++t)
+          qo[t] = kQLds ? as_bf16x8(qs[(t * 4 + kk) * 64 + lane]) : qb[kQLds ? 0 : t][kk];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+          for (int t = 0; t < NRT; ++t)
+            sacc[t][pg] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pg][k2], qo[t], sacc[t][pg], 0, 0, 0);
       }
     }
 
@@ -300,29 +348,35 @@ void seg_mfma_priv_kernel(SegParams p) {
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
       float s[8];
-      float bm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
-        const float v = sacc[t][e >> 2][e & 3] * sm_scale;
-        s[e] = pos < lim[t] ? v : -INFINITY;
-        bm = fmaxf(bm, s[e]);
+      for (int e = 0; e < 8; ++e) s[e] = sacc[t][e >> 2][e & 3];
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
+          s[e] = pos < lim[t] ? s[e] : -INFINITY;
+        }
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m[t], bm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      if (__builtin_amdgcn_ballot_w64(mn != m[t]) != 0) {  // some row max moved
-        const float alpha = fast_exp2(m[t] - mu);
+      float lm = s[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) lm = fmaxf(lm, s[e]);
+      if (__builtin_amdgcn_ballot_w64(lm > thr[t]) != 0) {   // some row max must move
+        float bm = lm == -INFINITY ? -INFINITY : lm * c;
+        bm = fmaxf(bm, __shfl_xor(bm, 16));
+        bm = fmaxf(bm, __shfl_xor(bm, 32));
+        const float mn = fmaxf(m[t], bm);
+        const float alpha = fast_exp2(m[t] - (mn == -INFINITY ? 0.f : mn));
         l[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[t][dt] *= alpha;
         m[t] = mn;
+        thr[t] = mn == -INFINITY ? -INFINITY : (mn + kSlackLog2) * inv_c;
       }
+      const float mu = m[t] == -INFINITY ? 0.f : m[t];
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
+        const float a = fast_exp2(fmaf(s[e], c, -mu)), b = fast_exp2(fmaf(s[e + 1], c, -mu));
         l[t] += a + b;
         pk[e >> 1] = pack_bf16x2(a, b);
       }
@@ -330,8 +384,8 @@ void seg_mfma_priv_kernel(SegParams p) {
     }
 
     // ---- O^T += V^T.P^T, V widened once for every tile ----
-    const bool tail = tok0 + 32 > it.seg_end;
     const int vend = it.seg_end - tok0;
+    const bool tail = masked && vend < 32;
     const uint8_t* vU8 = vU[r16 >> 3];           // lanes 0-7 of a group read page 0
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -340,16 +394,16 @@ void seg_mfma_priv_kernel(SegParams p) {
       if constexpr (SHUF) {
         const uint32_t a = *reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4);
         const uint32_t b = *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4);
-        const uint4 c = fp8x8_to_bf16x8(make_uint2(a, b));
-        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+        const uint4 cw = fp8x8_to_bf16x8(make_uint2(a, b));
+        w[0] = cw.x; w[1] = cw.y; w[2] = cw.z; w[3] = cw.w;
       } else {
         // in each 16-lane group, lane i receives byte i%8 of the 8 bytes read
         // by lane 2k + i/8: the block's 8 tokens of channel 16dt + i
         const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) v2i32_t*)(
                 (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256));
-        const uint4 c = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
-        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
+        const uint4 cw = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
+        w[0] = cw.x; w[1] = cw.y; w[2] = cw.z; w[3] = cw.w;
       }
       if (tail) {                    // zero V of tokens past the segment end
 #pragma unroll
@@ -580,7 +634,7 @@ int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   else if (nrt <= 2)
     hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 2, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 4, 4>), dim3(grid), dim3(64 * 4), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 4, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

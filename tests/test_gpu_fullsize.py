@@ -43,6 +43,8 @@ SAMPLES = {
     "agentic_skew": [0, 1, 2, 3, 4, 5, 19],
     "fp8_kv": [0, 15, 16, 29, 48, 63],
     "shuffled_decode": [0, 64, 127],
+    "uniform_verify_fp8": [0, 15],
+    "agentic_skew_fp8": [0, 3, 4, 19],
 }
 
 

@@ -84,4 +84,17 @@ SHUFFLED_DECODE = Config("shuffled_decode", [8192] * 128, [1] * 128, 32, 8,
                          note="bs=128 x 8k, q=1, 32/8 heads, bf16, standard pages repacked")
 
 CONFIGS = [TINY, UNIFORM_VERIFY, AGENTIC_SKEW, FP8_KV, SHUFFLED_DECODE]
-BY_NAME = {c.name: c for c in CONFIGS}
+
+# The split-KV PR's own MI355X kernel table (Benchmarking and Profiling: the
+# 16 x 119k uniform verify and the bs 20 / 2.32M-token agentic verify) counts
+# one byte per KV element, i.e. an fp8 cache. The same two batches with e4m3fn
+# KV (the fp8 workload's scales) give like-for-like figures beside that table.
+UNIFORM_VERIFY_FP8 = Config("uniform_verify_fp8", [119_000] * 16, [4] * 16, 32, 2,
+                            kv_dtype="fp8", k_scale=0.0173, v_scale=0.0211, seed=6,
+                            note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), e4m3fn KV")
+AGENTIC_SKEW_FP8 = Config("agentic_skew_fp8", SKEW_LENS, SKEW_Q, 32, 2, kv_dtype="fp8",
+                          k_scale=0.0173, v_scale=0.0211, seed=7,
+                          note="bs=20, 2.32M tokens, lognormal + {0,1,5,17,248k}, q 1..4, "
+                               "e4m3fn KV")
+EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8]
+BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
