@@ -314,6 +314,29 @@ void seg_mfma_priv_kernel(SegParams p) {
     // wave-uniform: does any key of this block lie past some row's limit?
     const bool masked = tok0 + 32 > lim_min;
 
+    // ---- V chunks of the block: up to two row tiles, every LDS read is issued
+    // before the score MFMAs, so its latency hides behind the MFMAs and the
+    // softmax; four row tiles (no registers to spare) read them in the P.V loop ----
+    uint2 vraw[8];
+    auto read_v1 = [&](int dt) -> uint2 {
+      if constexpr (SHUF) {
+        const int d = 16 * dt + r16;
+        return make_uint2(*reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4),
+                          *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4));
+      } else {
+        // in each 16-lane group, lane i receives byte i%8 of the 8 bytes read
+        // by lane 2k + i/8: the block's 8 tokens of channel 16dt + i
+        const uint8_t* vU8 = vU[r16 >> 3];       // lanes 0-7 of a group read page 0
+        return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) v2i32_t*)(
+                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256)));
+      }
+    };
+    if constexpr (!kQLds) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) vraw[dt] = read_v1(dt);
+    }
+
     // ---- S^T per page, every tile; independent MFMAs back to back ----
     f32x4_t sacc[NRT][2];
 #pragma unroll
@@ -384,38 +407,31 @@ void seg_mfma_priv_kernel(SegParams p) {
     }
 
     // ---- O^T += V^T.P^T, V widened once for every tile ----
+    // lane bytes 0-3 hold tokens 4 j4 .. +3 of the block, bytes 4-7 tokens 16 + 4 j4 .. +3
+    auto pv = [&](uint32_t m0, uint32_t m1) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 vr = kQLds ? read_v1(dt) : vraw[dt];
+        const uint4 cw = fp8x8_to_bf16x8(make_uint2(vr.x & m0, vr.y & m1));
+        const bf16x8_t vop = as_bf16x8(cw);
+#pragma unroll
+        for (int t = 0; t < NRT; ++t)
+          oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
+      }
+    };
+    // V of tokens past the segment end is zeroed (byte masks of the lane's tokens)
     const int vend = it.seg_end - tok0;
-    const bool tail = masked && vend < 32;
-    const uint8_t* vU8 = vU[r16 >> 3];           // lanes 0-7 of a group read page 0
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const int d = 16 * dt + r16;
-      uint32_t w[4];
-      if constexpr (SHUF) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4);
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4);
-        const uint4 cw = fp8x8_to_bf16x8(make_uint2(a, b));
-        w[0] = cw.x; w[1] = cw.y; w[2] = cw.z; w[3] = cw.w;
-      } else {
-        // in each 16-lane group, lane i receives byte i%8 of the 8 bytes read
-        // by lane 2k + i/8: the block's 8 tokens of channel 16dt + i
-        const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i32_t*)(
-                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256));
-        const uint4 cw = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
-        w[0] = cw.x; w[1] = cw.y; w[2] = cw.z; w[3] = cw.w;
-      }
-      if (tail) {                    // zero V of tokens past the segment end
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
-          w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
-        }
-      }
-      const bf16x8_t vop = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-#pragma unroll
-      for (int t = 0; t < NRT; ++t)
-        oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
+    auto keep = [&](int first) -> uint32_t {     // tokens first .. first+3
+      const int n = vend - first;
+      return n <= 0 ? 0u : (n >= 4 ? 0xffffffffu : (0xffffffffu >> (32 - 8 * n)));
+    };
+    if constexpr (kQLds) {
+      pv(keep(4 * j4), keep(16 + 4 * j4));
+    } else {
+      if (masked && vend < 32)
+        pv(keep(4 * j4), keep(16 + 4 * j4));
+      else
+        pv(0xffffffffu, 0xffffffffu);
     }
   }
 
