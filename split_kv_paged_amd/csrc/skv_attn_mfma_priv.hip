@@ -84,38 +84,52 @@ __device__ __forceinline__ void pdma16(const uint8_t* g, uint8_t* lds_uniform) {
                :: "v"(g), "s"(lds) : "memory", "m0");
 }
 
-// One 32-token block (pages pid0, pid1) into a slot: unit u = (page u/2, K if
-// u even, V if odd) at slot + u * kUnitBytes; the same lane -> chunk maps as
-// the shared-ring variant.
+// Standard pages in a slot: page pg's (block, head) tile is copied whole, 16
+// token rows of 256 B (K 128 B, then V 128 B), each DMA instruction taking 4
+// consecutive rows, i.e. 1 KB of contiguous HBM. Within a row the sixteen
+// 16-byte chunks are stored XOR-swizzled by token and page, so the K operand
+// reads (16 tokens of one chunk) and the transposing V reads (4 tokens of two
+// pages) spread over all LDS banks.
+__device__ __forceinline__ int std_chunk_pos(int tau, int q, int pg) {
+  return q ^ tau ^ (pg << 3);
+}
+
+// One 32-token block (pages pid0, pid1) into a slot. Standard pages: page pg
+// at slot + pg * 4 KB as above. Shuffled planes: unit u = (page u/2, K if u
+// even, V if odd) at slot + u * kUnitBytes, the K plane's 16-token chunk rows
+// and the V plane copied as they are.
 template <bool SHUF>
 __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& it, int pid0,
                                             int pid1, uint8_t* slot, int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
+  if constexpr (!SHUF) {
+#pragma unroll
+    for (int pg = 0; pg < 2; ++pg) {
+      const uint8_t* tile =
+          p.kv_a + (static_cast<size_t>(pg == 0 ? pid0 : pid1) * p.Hkv + it.g) * kStdTile;
+#pragma unroll
+      for (int i = 0; i < kStdTile / 1024; ++i) {
+        const int row = 4 * i + j4;                               // lane -> (row, position r16)
+        const int q = std_chunk_pos(row, r16, pg);                // the chunk stored there
+        pdma16(tile + row * kStdRow + q * 16, slot + pg * kStdTile + i * 1024);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const size_t head = static_cast<size_t>(u < 2 ? pid0 : pid1) * p.Hkv + it.g;
     uint8_t* dst = slot + u * kUnitBytes;
     if ((u & 1) == 0) {
-      const uint8_t* tile = p.kv_a + head * (SHUF ? kUnitBytes : kStdTile);
+      const uint8_t* tile = p.kv_a + head * kUnitBytes;
 #pragma unroll
-      for (int i = 0; i < kUnitInstr; ++i) {
-        const size_t off = SHUF ? (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16
-                                : static_cast<size_t>(r16) * kStdRow + 64 * i + 16 * j4;
-        pdma16(tile + off, dst + i * 1024);
-      }
+      for (int i = 0; i < kUnitInstr; ++i)
+        pdma16(tile + (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16, dst + i * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kUnitInstr; ++i) {
-        size_t off;
-        if constexpr (SHUF) {
-          off = static_cast<size_t>(i * 64 + lane) * 16;          // plane copied as is
-        } else {
-          const int c = 4 * i + (lane >> 4), tau = lane & 15;     // [chunk c][token tau][16 B]
-          off = static_cast<size_t>(tau) * kStdRow + kD * kE + c * 16;
-        }
-        const uint8_t* base = SHUF ? p.kv_b + head * kUnitBytes : p.kv_a + head * kStdTile;
-        pdma16(base + off, dst + i * 1024);
-      }
+      for (int i = 0; i < kUnitInstr; ++i)    // plane copied as is
+        pdma16(p.kv_b + head * kUnitBytes + static_cast<size_t>(i * 64 + lane) * 16,
+               dst + i * 1024);
     }
   }
 }
@@ -297,8 +311,9 @@ void seg_mfma_priv_kernel(SegParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  // per-lane part of the transposing byte-read address in the chunk-major V tile
-  const int vtr_off = (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;
+  // token of the transposing V reads: in each 16-lane group, lane i receives
+  // byte i%8 of the 8 bytes read by lane 2k + i/8, i.e. 8 tokens of one channel
+  const int vtau = 4 * j4 + ((r16 >> 1) & 3);
 
   for (int k = 0; k < nb; ++k) {
     if (k + kNP - 1 < nb) {                     // slot of block k-1, consumed last iteration
@@ -324,12 +339,13 @@ void seg_mfma_priv_kernel(SegParams p) {
         return make_uint2(*reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4),
                           *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4));
       } else {
-        // in each 16-lane group, lane i receives byte i%8 of the 8 bytes read
-        // by lane 2k + i/8: the block's 8 tokens of channel 16dt + i
-        const uint8_t* vU8 = vU[r16 >> 3];       // lanes 0-7 of a group read page 0
+        // lanes 0-7 of a group read page 0, lanes 8-15 page 1; token vtau,
+        // channel chunk 8 + dt, byte half r16 & 1
+        const int pgv = r16 >> 3;
         return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
             (__attribute__((address_space(3))) v2i32_t*)(
-                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256)));
+                (__attribute__((address_space(3))) uint8_t*)(slot) + pgv * kStdTile +
+                vtau * kStdRow + std_chunk_pos(vtau, 8 + dt, pgv) * 16 + (r16 & 1) * 8)));
       }
     };
     if constexpr (!kQLds) {
@@ -346,7 +362,9 @@ void seg_mfma_priv_kernel(SegParams p) {
       bf16x8_t kop[2][2];
 #pragma unroll
       for (int pg = 0; pg < 2; ++pg) {
-        const uint4 cw = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
+        const uint4 cw = *reinterpret_cast<const uint4*>(
+            SHUF ? kU[pg] + u * 1024 + lane * 16
+                 : slot + pg * kStdTile + r16 * kStdRow + std_chunk_pos(r16, 4 * u + j4, pg) * 16);
         kop[pg][0] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cw.x, cw.y)));
         kop[pg][1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(cw.z, cw.w)));
       }
