@@ -251,3 +251,49 @@ def test_fixed_split_equals_unsplit_and_counts_match():
     assert list(nseg) == tok
     out, _ = _oracle(cfg, case)
     np.testing.assert_allclose(so, out, rtol=1e-12, atol=1e-13)
+
+
+def _as_32_token_pages(case16, cfg16):
+    """The same tokens re-stored in 32-token pages: page j of sequence i holds
+    its tokens 32j .. 32j + 31, taken from the 16-token pages 2j and 2j + 1;
+    blocks are numbered in order, the slots past a sequence's end hold zeros."""
+    raw = gen.raw_kv(case16)
+    table16 = case16.page_table.numpy()
+    lens = case16.seq_lens.numpy()
+    H, D2 = raw.shape[1], raw.shape[3]
+    n32 = [-(-int(L) // 32) for L in lens]
+    pool = sum(n32) + 1
+    kv32 = np.zeros((pool, H, 32, D2), dtype=raw.dtype)
+    table32 = np.full((len(lens), max(max(n32), 1)), pool - 1, dtype=np.int32)
+    b = 0
+    for i, L in enumerate(lens):
+        for j in range(n32[i]):
+            for half in range(2):
+                p16 = 2 * j + half
+                if 16 * p16 < L:
+                    kv32[b, :, 16 * half:16 * half + 16] = raw[table16[i, p16]]
+            table32[i, j] = b
+            b += 1
+    return kv32, table32
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_32_token_pages_equal_16_token_pages(kv_dtype):
+    """Attention over a 32-token-page cache, standard and shuffled, equals
+    attention over the same tokens in 16-token pages: the gathered K and V rows
+    are the same values (the standard gather bit for bit)."""
+    cfg, case = _case([0, 1, 15, 16, 17, 31, 32, 33, 100, 257], [1, 2, 1, 3, 4, 1, 2, 4, 3, 2],
+                      kv_dtype=kv_dtype, seed=21)
+    want_o, want_l = _oracle(cfg, case)
+    kv32, table32 = _as_32_token_pages(case, cfg)
+    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    args = (case.seq_lens.numpy(), case.cu_seqlens_q.numpy(), cfg.kv_heads, 32, cfg.causal,
+            cfg.k_scale, cfg.v_scale)
+    o, l = oracle.decode_attention(q, kv32, cfg.kv_dtype, table32, *args)
+    assert np.array_equal(o, want_o) and np.array_equal(l, want_l)
+    planes = oracle.shuffle_blocks(kv32)
+    assert planes[0].shape[-2:] == (32, 16 // (2 if kv_dtype == "bf16" else 1))
+    o2, l2 = oracle.decode_attention(q, None, cfg.kv_dtype, table32, *args, planes=planes)
+    # same gathered values; only BLAS summation order may differ with memory layout
+    np.testing.assert_allclose(o2, want_o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l2, want_l, rtol=1e-15)

@@ -57,8 +57,9 @@ def _brute_force_T(pages, cap, seg_max):
     return best if best is not None else upper
 
 
-def test_brute_force_and_invariants_random():
-    rng = np.random.default_rng(11)
+@pytest.mark.parametrize("P", [16, 32])
+def test_brute_force_and_invariants_random(P):
+    rng = np.random.default_rng(11 + P)
     for trial in range(300):
         bs = int(rng.integers(1, 9))
         lens = [int(v) for v in rng.integers(0, 400, size=bs)]
@@ -69,8 +70,8 @@ def test_brute_force_and_invariants_random():
         ncu = int(rng.integers(1, 40))
         smax = int(rng.integers(1, 9))
         causal = int(rng.integers(0, 2))
-        plan, tok = oracle.plan_segments(lens, _cu(ql), kvh, 16, ncu, smax, causal)
-        pages = [-(-L // 16) for L in lens]
+        plan, tok = oracle.plan_segments(lens, _cu(ql), kvh, P, ncu, smax, causal)
+        pages = [-(-L // P) for L in lens]
         cap = ncu // kvh
         T = plan[0]
         assert T == _brute_force_T(pages, cap, smax)
@@ -98,8 +99,8 @@ def test_brute_force_and_invariants_random():
                 assert tok[t] <= max(smax, 1)
                 vis = min(max(lens[i] - ql[i] + j + 1, 0), lens[i]) if causal else lens[i]
                 # the count covers the visible keys and no segment beyond them
-                assert tok[t] * T * 16 >= vis
-                assert (tok[t] - 1) * T * 16 < vis or tok[t] == 0
+                assert tok[t] * T * P >= vis
+                assert (tok[t] - 1) * T * P < vis or tok[t] == 0
                 t += 1
 
 
@@ -189,3 +190,13 @@ def test_uniform_fixed_split_equals_planned():
     S, seg_pages, ftok = oracle.fixed_split_plan(cfg.seq_lens, cu, cfg.kv_heads, 16,
                                                  cfg.num_cus, cfg.seg_max, 1)
     assert S == 8 and set(seg_pages) == {plan[0]} and ftok == tok
+
+
+def test_hand_derived_32_token_pages():
+    """num_CUs 8, kv_heads 2 (cap 4), L {160, 16, 0}, one query each, 32-token
+    pages: page counts {5, 1, 0}; T = 1 needs 6 > 4 segments, T = 2 needs
+    3 + 1 = 4, so T = 2 with items (0,0) (0,1) (0,2) (1,0); the counts are
+    ceil(vis / 64) = {3, 1, 0}."""
+    plan, tok = oracle.plan_segments([160, 16, 0], [0, 1, 2, 3], 2, 32, 8, 64, 1)
+    assert plan == [2, 0, 1, 2, 65536]
+    assert tok == [3, 1, 0]
