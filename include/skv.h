@@ -31,9 +31,10 @@
  *
  * Element types: Q and the output are bf16 (IEEE binary32 upper half). KV is
  * bf16 or OCP e4m3fn fp8 (kv_dtype 1) with per-tensor fp32 dequant scales.
- * Supported geometry: head_dim 128; page_size 16 for the planner and
- * attention, 16 or 32 for the page repacks and the cache writer; 1..4 query
- * tokens per sequence, (q_heads / kv_heads) * max_q <= 64.
+ * Supported geometry: head_dim 128; page_size 16 or 32 tokens for every
+ * entry point (the RFC's decoder scope: 16- or 32-token pages; the split-KV
+ * PR's kernels use 16); 1..4 query tokens per sequence,
+ * (q_heads / kv_heads) * max_q <= 64.
  */
 #ifndef SKV_H_
 #define SKV_H_
@@ -88,7 +89,7 @@ size_t skv_workspace_bytes(int total_q, int q_heads, int head_dim, int seg_max);
  * One single-work-group launch; integer arithmetic only.
  * Errors: EINVAL for NULL pointers, bs < 1, bs >= 32768, total_q < 1,
  * kv_heads < 1, num_cus < 1, seg_max outside [1, 65535]; EUNSUPPORTED for
- * page_size != 16. */
+ * page_size other than 16 or 32. */
 int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                    int total_q, int kv_heads, int page_size, int num_cus,
                    int seg_max, int causal, int32_t* plan, int32_t* tok_nseg,
@@ -136,7 +137,7 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
  * scales present for bf16 or missing for fp8, kv_b NULL for SHUFFLED or
  * non-NULL for STANDARD, pt_stride < 1, an unknown layout or dtype;
- * EUNSUPPORTED for head_dim != 128, page_size != 16, max_q > 4,
+ * EUNSUPPORTED for head_dim != 128, page_size other than 16 or 32, max_q > 4,
  * (q_heads/kv_heads) * max_q > 64. */
 int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           int layout, int kv_dtype, const int32_t* page_table,

@@ -10,7 +10,8 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
                              int kv_dtype, const int32_t* page_table, int pt_stride,
                              const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                              int total_q, int max_q, int q_heads, int kv_heads,
-                             const float* k_scale, const float* v_scale, int causal,
+                             int page_size, const float* k_scale, const float* v_scale,
+                             int causal,
                              const int32_t* plan, int32_t* tok_nseg, int num_cus,
                              int seg_max, float* part_o, float* part_lse) {
   skv::AttnArgs a;
@@ -28,6 +29,7 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
   a.max_q = max_q;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
+  a.page_size = page_size;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.causal = causal ? 1 : 0;
@@ -62,7 +64,7 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
   int st = skv::check_plan_args(seq_lens, cu_seqlens_q, bs, total_q, kv_heads,
                                 page_size, num_cus, seg_max, plan, tok_nseg);
   if (st != SKV_OK) return st;
-  return skv::launch_plan(seq_lens, cu_seqlens_q, bs, total_q, kv_heads,
+  return skv::launch_plan(seq_lens, cu_seqlens_q, bs, total_q, kv_heads, page_size,
                           num_cus, seg_max, causal ? 1 : 0, plan, tok_nseg,
                           stream);
 }
@@ -84,7 +86,7 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
   if (st != SKV_OK) return st;
   return skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                              pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
-                                             max_q, q_heads, kv_heads, k_scale, v_scale,
+                                             max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
                                              causal, plan, tok_nseg, num_cus, seg_max,
                                              part_o, part_lse),
                               stream);
@@ -108,7 +110,7 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
   if (st != SKV_OK) return st;
   st = skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                            pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
-                                           max_q, q_heads, kv_heads, k_scale, v_scale,
+                                           max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
                                            causal, plan, tok_nseg, num_cus, seg_max,
                                            part_o, part_lse),
                             stream);

@@ -52,6 +52,7 @@ int launch_segments(const AttnArgs& a, void* stream) {
   sp.causal = a.causal;
   sp.tok_out = nullptr;
   sp.fixed_S = 0;
+  sp.page_shift = page_shift_of(a.page_size);
   long long grid;
   if (a.plan) {
     grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) * a.kv_heads;

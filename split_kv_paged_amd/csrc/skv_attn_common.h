@@ -30,6 +30,7 @@ struct SegParams {
   int32_t* tok_out;           // fixed split: per-token segment counts written here
   int pt_stride, bs, Hq, Hkv, G, seg_max, causal;
   int fixed_S;                // 0: planned split (plan); > 0: fixed split, S per sequence
+  int page_shift;             // log2(tokens per page): 4 or 5
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -106,9 +107,10 @@ __device__ __forceinline__ SegItem decode_fixed(const SegParams& p) {
   it.c0 = p.cu_q[it.seq];
   it.qn = p.cu_q[it.seq + 1] - it.c0;
   it.rows = p.G * it.qn;
-  const int pages = it.L <= 0 ? 0 : (it.L >> 4) + ((it.L & 15) != 0);
+  const int sh = p.page_shift;
+  const int pages = it.L <= 0 ? 0 : (it.L >> sh) + ((it.L & ((1 << sh) - 1)) != 0);
   it.seg_pages = pages == 0 ? 1 : 1 + (pages - 1) / p.fixed_S;
-  const long long seg_tokens = static_cast<long long>(it.seg_pages) * kPageSize;
+  const long long seg_tokens = static_cast<long long>(it.seg_pages) << sh;
   const long long s0 = it.seg * seg_tokens;
   if (s0 >= it.L || it.qn <= 0) return it;
   const long long s1 = s0 + seg_tokens;
@@ -129,7 +131,7 @@ __device__ __forceinline__ void write_fixed_counts(const SegParams& p, const Seg
     vis = it.L - it.qn + j + 1;
     vis = vis < 0 ? 0 : (vis > it.L ? it.L : vis);
   }
-  const long long seg_tokens = static_cast<long long>(it.seg_pages) * kPageSize;
+  const long long seg_tokens = static_cast<long long>(it.seg_pages) << p.page_shift;
   p.tok_out[it.c0 + j] = vis <= 0 ? 0 : static_cast<int>(1 + (vis - 1) / seg_tokens);
 }
 
@@ -149,13 +151,52 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   it.c0 = p.cu_q[it.seq];
   it.qn = p.cu_q[it.seq + 1] - it.c0;
   it.rows = p.G * it.qn;
-  const long long s0 = static_cast<long long>(it.seg) * T * kPageSize;
+  const long long s0 = (static_cast<long long>(it.seg) * T) << p.page_shift;
   if (s0 >= it.L || it.qn <= 0) return it;
-  const long long s1 = s0 + T * kPageSize;
+  const long long s1 = s0 + (T << p.page_shift);
   it.seg_start = static_cast<int>(s0);
   it.seg_end = static_cast<int>(s1 < it.L ? s1 : it.L);
   it.valid = 1;
   return it;
+}
+
+// Pages hold 16 or 32 tokens; the kernels stream 16-token sub-pages (a
+// 32-token page holds two: its tokens 0-15 and 16-31). Sub-page v of a
+// sequence (its tokens 16v .. 16v + 15) lies in page table entry v >> (shift
+// - 4), as sub-page v & 1 of a 32-token page.
+__device__ __forceinline__ int sub_of(const SegParams& p, int v) {
+  return v & ((1 << (p.page_shift - 4)) - 1);
+}
+
+// Addresses of one sub-page of kv head g in page pid, element size E bytes.
+//  * Standard pages [blocks, Hkv, P, 2D]: k (== v) is the sub-page's first
+//    token row; the rows of its 16 tokens follow contiguously (each K, then V).
+//  * Shuffled planes K [blocks, Hkv, D/x, P, x], V [blocks, Hkv, P/x, D, x]:
+//    k is the sub-page's first token in the K plane's chunk row 0 (chunk row c
+//    at k + c * kplane_row_bytes); v is the sub-page's 16 / x token groups of
+//    the V plane, laid out exactly as a 16-token page's V plane.
+struct SubPageAddr {
+  const uint8_t* k;
+  const uint8_t* v;
+};
+
+template <int E, bool SHUF>
+__device__ __forceinline__ SubPageAddr sub_page(const SegParams& p, int g, int pid, int sub) {
+  const size_t head = static_cast<size_t>(pid) * p.Hkv + g;
+  constexpr size_t kHalf16 = static_cast<size_t>(kPageSize) * kHeadDim * E;   // 16 tokens' K or V
+  if constexpr (SHUF) {
+    const size_t plane = (head * kHalf16) << (p.page_shift - 4);
+    return {p.kv_a + plane + static_cast<size_t>(sub) * kPageSize * 16,
+            p.kv_b + plane + static_cast<size_t>(sub) * kHalf16};
+  } else {
+    const uint8_t* t = p.kv_a + (((head << (p.page_shift - 4)) + sub) * 2 * kHalf16);
+    return {t, t};
+  }
+}
+
+// bytes between consecutive 16-byte chunk rows of a K-plane tile: P tokens x 16 B
+__device__ __forceinline__ int kplane_row_bytes(const SegParams& p) {
+  return 16 << p.page_shift;
 }
 
 // Last key (exclusive) row n may see inside the segment: the bottom-right

@@ -110,31 +110,34 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
                :: "v"(g), "s"(lds) : "memory", "m0");
 }
 
-// Issue this wave's DMA units of one stage. Unit u of the stage is (page u/2,
-// K half if u even, V half if odd); wave w issues units [w*UPW, (w+1)*UPW).
-// Pages past the segment end are read from the segment's first page (same
-// instruction count keeps vmcnt exact; their tokens are masked and zeroed).
+// Issue this wave's DMA units of one stage. Unit u of the stage is (16-token
+// sub-page u/2, K half if u even, V half if odd); wave w issues units
+// [w*UPW, (w+1)*UPW). v0 is the stage's first sub-page in the sequence.
+// Sub-pages past the segment end are read from the segment's first sub-page
+// (same instruction count keeps vmcnt exact; their tokens are masked and
+// zeroed).
 template <int E, bool SHUF, int NRT>
 __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& it,
-                                            const int* pids, uint8_t* slot, int wave,
-                                            int lane) {
+                                            const int* pids, const int* subs, uint8_t* slot,
+                                            int wave, int lane) {
   using R = Ring<E, NRT>;
   const int r16 = lane & 15, j4 = lane >> 4;
+  const int krow = kplane_row_bytes(p);
 #pragma unroll
   for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
     const int u = wave * R::kUnitsPerWave + uw;
     const int pg = u >> 1;
     const bool vhalf = u & 1;
-    const size_t head = static_cast<size_t>(pids[uw]) * p.Hkv + it.g;
+    const SubPageAddr a = sub_page<E, SHUF>(p, it.g, pids[uw], subs[uw]);
     uint8_t* dst = slot + (2 * pg + (vhalf ? 1 : 0)) * R::kUnitBytes;
     if (!vhalf) {
-      const uint8_t* tile = p.kv_a + head * (SHUF ? R::kUnitBytes : R::kStdTile);
+      const uint8_t* tile = a.k;
 #pragma unroll
       for (int i = 0; i < R::kUnitInstr; ++i) {
         // lane reads the 16 bytes compute-lane `lane` needs for k-step i
         size_t off;
         if constexpr (SHUF) {
-          off = (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16;
+          off = static_cast<size_t>(4 * i + j4) * krow + r16 * 16;
         } else {
           const int byte = E == 2 ? (32 * i + 8 * j4) * 2 : 64 * i + 16 * j4;
           off = static_cast<size_t>(r16) * R::kStdRow + byte;
@@ -161,9 +164,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
           }
           off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
         }
-        const uint8_t* base = SHUF ? p.kv_b + head * R::kUnitBytes
-                                   : p.kv_a + head * R::kStdTile;
-        dma16(base + off, dst + i * 1024);
+        dma16(a.v + off, dst + i * 1024);
       }
     }
   }
@@ -201,7 +202,7 @@ void seg_mfma_kernel(SegParams p) {
   // waiting on them never waits on the vector-memory (DMA) queue
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
-          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   float sm_scale = kScoreScaleLog2;
   float out_scale = 1.f;
   if constexpr (E == 1) {
@@ -209,12 +210,21 @@ void seg_mfma_kernel(SegParams p) {
     out_scale = p.v_scale[0];
   }
 
-  // page ids of this wave's units for a stage (pages past the end -> first page)
+  // page ids and sub-pages of this wave's units for a stage (sub-pages past
+  // the end -> the segment's first)
+  const int psh = p.page_shift - 4;
   auto load_pids = [&](int st, int* out) {
 #pragma unroll
     for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
       const int pg = st * R::kPages + ((wave * R::kUnitsPerWave + uw) >> 1);
-      out[uw] = ptab[pg < seg_pages ? pg : 0];
+      out[uw] = ptab[(seg_page0 + (pg < seg_pages ? pg : 0)) >> psh];
+    }
+  };
+  auto stage_subs = [&](int st, int* out) {
+#pragma unroll
+    for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
+      const int pg = st * R::kPages + ((wave * R::kUnitsPerWave + uw) >> 1);
+      out[uw] = sub_of(p, seg_page0 + (pg < seg_pages ? pg : 0));
     }
   };
 
@@ -246,9 +256,10 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
   for (int s = 0; s < kNS - 1; ++s) {
     if (s < nst) {
-      int pids[R::kUnitsPerWave];
+      int pids[R::kUnitsPerWave], subs[R::kUnitsPerWave];
       load_pids(s, pids);
-      issue_stage<E, SHUF, NRT>(p, it, pids, ring + s * R::kStageBytes, wave, lane);
+      stage_subs(s, subs);
+      issue_stage<E, SHUF, NRT>(p, it, pids, subs, ring + s * R::kStageBytes, wave, lane);
     }
   }
   if (kNS - 1 < nst) load_pids(kNS - 1, pid_next);
@@ -266,8 +277,10 @@ void seg_mfma_kernel(SegParams p) {
     }
     barrier_keep_loads();
     if (i + kNS - 1 < nst) {
-      issue_stage<E, SHUF, NRT>(p, it, pid_next, ring + ((i + kNS - 1) % kNS) * R::kStageBytes,
-                                wave, lane);
+      int subs[R::kUnitsPerWave];
+      stage_subs(i + kNS - 1, subs);
+      issue_stage<E, SHUF, NRT>(p, it, pid_next, subs,
+                                ring + ((i + kNS - 1) % kNS) * R::kStageBytes, wave, lane);
       if (i + kNS < nst) load_pids(i + kNS, pid_next);
     }
     if (!active) continue;

@@ -100,13 +100,15 @@ __device__ __forceinline__ int std_chunk_pos(int tau, int q, int pg) {
 // and the V plane copied as they are.
 template <bool SHUF>
 __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& it, int pid0,
-                                            int pid1, uint8_t* slot, int lane) {
+                                            int sub0, int pid1, int sub1, uint8_t* slot,
+                                            int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
+  const SubPageAddr sp[2] = {sub_page<kE, SHUF>(p, it.g, pid0, sub0),
+                             sub_page<kE, SHUF>(p, it.g, pid1, sub1)};
   if constexpr (!SHUF) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
-      const uint8_t* tile =
-          p.kv_a + (static_cast<size_t>(pg == 0 ? pid0 : pid1) * p.Hkv + it.g) * kStdTile;
+      const uint8_t* tile = sp[pg].k;
 #pragma unroll
       for (int i = 0; i < kStdTile / 1024; ++i) {
         const int row = 4 * i + j4;                               // lane -> (row, position r16)
@@ -116,20 +118,18 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
     }
     return;
   }
+  const int krow = kplane_row_bytes(p);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const size_t head = static_cast<size_t>(u < 2 ? pid0 : pid1) * p.Hkv + it.g;
     uint8_t* dst = slot + u * kUnitBytes;
     if ((u & 1) == 0) {
-      const uint8_t* tile = p.kv_a + head * kUnitBytes;
 #pragma unroll
       for (int i = 0; i < kUnitInstr; ++i)
-        pdma16(tile + (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16, dst + i * 1024);
+        pdma16(sp[u >> 1].k + static_cast<size_t>(4 * i + j4) * krow + r16 * 16, dst + i * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < kUnitInstr; ++i)    // plane copied as is
-        pdma16(p.kv_b + head * kUnitBytes + static_cast<size_t>(i * 64 + lane) * 16,
-               dst + i * 1024);
+      for (int i = 0; i < kUnitInstr; ++i)    // the sub-page's V plane as is
+        pdma16(sp[u >> 1].v + static_cast<size_t>(i * 64 + lane) * 16, dst + i * 1024);
     }
   }
 }
@@ -231,10 +231,11 @@ void seg_mfma_priv_kernel(SegParams p) {
   const int nblk = (ntok + 31) >> 5;
   const int seg_pages = (ntok + 15) >> 4;
   const int nb = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;   // this wave's blocks
-  const int seg_page0 = it.seg_start >> 4;
+  const int seg_page0 = it.seg_start >> 4;          // first 16-token sub-page
+  const int psh = p.page_shift - 4;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
-          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   // scores enter exp2 as fma(raw, c, -m) with c > 0: a negative K scale is
   // moved into Q's sign (exact), a zero one becomes the least normal float
   const float ks = p.k_scale[0];
@@ -287,17 +288,21 @@ void seg_mfma_priv_kernel(SegParams p) {
   uint8_t* wring = ring[wave];
   // pages of this wave's k-th block (block wave + NW k); pages past the end
   // read the segment's first page (masked and zeroed; keeps vmcnt exact)
-  auto pids = [&](int k, int& a, int& b) {
+  auto pids = [&](int k, int& a, int& sa, int& b, int& sb) {
     const int pg = 2 * (wave + NW * k);
-    a = ptab[pg < seg_pages ? pg : 0];
-    b = ptab[pg + 1 < seg_pages ? pg + 1 : 0];
+    const int va = seg_page0 + (pg < seg_pages ? pg : 0);
+    const int vb = seg_page0 + (pg + 1 < seg_pages ? pg + 1 : 0);
+    a = ptab[va >> psh];
+    b = ptab[vb >> psh];
+    sa = sub_of(p, va);
+    sb = sub_of(p, vb);
   };
 #pragma unroll
   for (int k = 0; k < kNP - 1; ++k) {
     if (k < nb) {
-      int a, b;
-      pids(k, a, b);
-      issue_block<SHUF>(p, it, a, b, wring + k * kBlockBytes, lane);
+      int a, sa, b, sb;
+      pids(k, a, sa, b, sb);
+      issue_block<SHUF>(p, it, a, sa, b, sb, wring + k * kBlockBytes, lane);
     }
   }
 
@@ -317,9 +322,9 @@ void seg_mfma_priv_kernel(SegParams p) {
 
   for (int k = 0; k < nb; ++k) {
     if (k + kNP - 1 < nb) {                     // slot of block k-1, consumed last iteration
-      int a, b;
-      pids(k + kNP - 1, a, b);
-      issue_block<SHUF>(p, it, a, b, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
+      int a, sa, b, sb;
+      pids(k + kNP - 1, a, sa, b, sb);
+      issue_block<SHUF>(p, it, a, sa, b, sb, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
     }
     pwait_blocks<kBlockInstr, kNP - 1>(min(kNP - 1, nb - 1 - k));   // block k landed
     const uint8_t* slot = wring + (k % kNP) * kBlockBytes;
@@ -487,17 +492,18 @@ struct PRing2 {
 // shuffled planes as they are
 template <bool SHUF>
 __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& it, int pid,
-                                            uint8_t* slot, int lane) {
+                                            int sub, uint8_t* slot, int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
-  const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
-  const uint8_t* ktile = p.kv_a + head * (SHUF ? kHalf2 : kStdTile2);
+  const SubPageAddr sp = sub_page<2, SHUF>(p, it.g, pid, sub);
+  const uint8_t* ktile = sp.k;
+  const int krow = kplane_row_bytes(p);
 #pragma unroll
   for (int i = 0; i < kHalf2 / 1024; ++i) {
-    const size_t off = SHUF ? (static_cast<size_t>(4 * i + j4) * kPageSize + r16) * 16
+    const size_t off = SHUF ? static_cast<size_t>(4 * i + j4) * krow + r16 * 16
                             : static_cast<size_t>(r16) * kStdRow2 + (32 * i + 8 * j4) * 2;
     pdma16(ktile + off, slot + i * 1024);
   }
-  const uint8_t* vbase = SHUF ? p.kv_b + head * kHalf2 : p.kv_a + head * kStdTile2;
+  const uint8_t* vbase = sp.v;
 #pragma unroll
   for (int i = 0; i < kHalf2 / 1024; ++i) {
     size_t off;
@@ -528,10 +534,11 @@ void seg_mfma_priv2_kernel(SegParams p) {
   const int r16 = lane & 15, j4 = lane >> 4;
   const int seg_pages = (it.seg_end - it.seg_start + 15) >> 4;
   const int np = seg_pages > wave ? (seg_pages - wave + NW - 1) / NW : 0;   // this wave's pages
-  const int seg_page0 = it.seg_start >> 4;
+  const int seg_page0 = it.seg_start >> 4;          // first 16-token sub-page
+  const int psh = p.page_shift - 4;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
-          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   const float sm_scale = kScoreScaleLog2;
 
   bf16x8_t qb[NRT][4];
@@ -557,10 +564,12 @@ void seg_mfma_priv2_kernel(SegParams p) {
     }
 
   uint8_t* wring = ring[wave];
-  auto pid_of = [&](int k) { return ptab[wave + NW * k]; };       // page wave + NW k
+  // this wave's k-th sub-page is the segment's sub-page wave + NW k
+  auto vpage = [&](int k) { return seg_page0 + wave + NW * k; };
+  auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
 #pragma unroll
   for (int k = 0; k < kNP - 1; ++k)
-    if (k < np) issue_page2<SHUF>(p, it, pid_of(k), wring + k * kPage2, lane);
+    if (k < np) issue_page2<SHUF>(p, it, pid_of(k), sub_of(p, vpage(k)), wring + k * kPage2, lane);
 
   f32x4_t oacc[NRT][8];
   float m[NRT], l[NRT];
@@ -579,7 +588,8 @@ void seg_mfma_priv2_kernel(SegParams p) {
 
   for (int k = 0; k < np; ++k) {
     if (k + kNP - 1 < np)                       // slot of page k-1, consumed last iteration
-      issue_page2<SHUF>(p, it, pid_of(k + kNP - 1), wring + ((k + kNP - 1) % kNP) * kPage2,
+      issue_page2<SHUF>(p, it, pid_of(k + kNP - 1), sub_of(p, vpage(k + kNP - 1)),
+                        wring + ((k + kNP - 1) % kNP) * kPage2,
                         lane);
     pwait_blocks<kPageInstr2, kNP - 1>(min(kNP - 1, np - 1 - k));   // page k landed
     const uint8_t* sK = wring + (k % kNP) * kPage2;

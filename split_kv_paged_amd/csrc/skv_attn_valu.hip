@@ -81,19 +81,20 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
                :: "v"(g), "s"(lds) : "memory", "m0");
 }
 
-// One page (this wave's) into its ring slot: K half chunk-major
+// One 16-token sub-page (this wave's) into its ring slot: K half chunk-major
 // [c][token][16 B]; V half row-major [token][channels] (standard) or the
-// plane as is (shuffled).
+// plane's sub-page as is (shuffled).
 template <bool SHUF>
 __device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it, int pid,
-                                           uint8_t* slot, int lane) {
-  const size_t head = static_cast<size_t>(pid) * p.Hkv + it.g;
-  const uint8_t* ktile = p.kv_a + head * (SHUF ? kHalf : kStdTile);
-  const uint8_t* vtile = SHUF ? p.kv_b + head * kHalf : ktile;
+                                           int sub, uint8_t* slot, int lane) {
+  const SubPageAddr a = sub_page<2, SHUF>(p, it.g, pid, sub);
+  const uint8_t* ktile = a.k;
+  const uint8_t* vtile = a.v;
+  const int krow = kplane_row_bytes(p);
 #pragma unroll
   for (int i = 0; i < kHalf / 1024; ++i) {
     const int c = 4 * i + (lane >> 4), tau = lane & 15;
-    const size_t off = SHUF ? static_cast<size_t>(i * 64 + lane) * 16
+    const size_t off = SHUF ? static_cast<size_t>(c) * krow + tau * 16
                             : static_cast<size_t>(tau) * kStdRow + c * 16;
     dma16(ktile + off, slot + i * 1024);
   }
@@ -144,7 +145,8 @@ void seg_valu_kernel(SegParams p) {
   const int np = seg_pages > wave ? (seg_pages - wave + NW - 1) / NW : 0;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
-          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride + seg_page0);
+          p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
+  const int psh = p.page_shift - 4;
   const float sm_scale = kScoreScaleLog2;
 
   // Q rows (bf16 pairs) for this lane's 32 channels; consumed before any DMA
@@ -170,11 +172,12 @@ void seg_valu_kernel(SegParams p) {
     }
 
   uint8_t* wring = ring[wave];
-  // page ids: this wave's k-th page is seg page wave + NW k
-  auto pid_of = [&](int k) { return ptab[wave + NW * k]; };
+  // page ids: this wave's k-th sub-page is the segment's sub-page wave + NW k
+  auto vpage = [&](int k) { return seg_page0 + wave + NW * k; };
+  auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
 #pragma unroll
   for (int k = 0; k < kNS - 1; ++k)
-    if (k < np) issue_page<SHUF>(p, it, pid_of(k), wring + k * kPage, lane);
+    if (k < np) issue_page<SHUF>(p, it, pid_of(k), sub_of(p, vpage(k)), wring + k * kPage, lane);
   int pid_next = kNS - 1 < np ? pid_of(kNS - 1) : 0;
 
   constexpr int kAcc = SHUF ? 2 : 8;
@@ -192,7 +195,8 @@ void seg_valu_kernel(SegParams p) {
   for (int k = 0; k < np; ++k) {
     wait_vmcnt_pages<kInstrPerPage, kNS - 2>(min(kNS - 2, np - 1 - k));
     if (k + kNS - 1 < np) {
-      issue_page<SHUF>(p, it, pid_next, wring + ((k + kNS - 1) % kNS) * kPage, lane);
+      issue_page<SHUF>(p, it, pid_next, sub_of(p, vpage(k + kNS - 1)),
+                       wring + ((k + kNS - 1) % kNS) * kPage, lane);
       if (k + kNS < np) pid_next = pid_of(k + kNS);
     }
     const uint8_t* sK = wring + (k % kNS) * kPage;

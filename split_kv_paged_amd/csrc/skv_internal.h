@@ -17,9 +17,10 @@ constexpr int kMaxBs = 32767;    // seq << 16 stays a non-negative int32
 constexpr int kMaxSegMax = 65535;
 constexpr int kMaxConvertBytes = 128 * 1024;   // one block staged in LDS
 
-// page sizes of the repack entry points (shuffle, conversion, writer); the
-// attention path uses 16-token pages
+// page sizes of every entry point: 16- or 32-token pages (the attention
+// kernels stream 16-token sub-pages; a 32-token page holds two)
 inline bool repack_page_size_ok(int page_size) { return page_size == 16 || page_size == 32; }
+inline int page_shift_of(int page_size) { return page_size == 32 ? 5 : 4; }   // log2
 
 // ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
 int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
@@ -78,6 +79,7 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* cu_seqlens_q;
   int bs, total_q, max_q, q_heads, kv_heads;
+  int page_size;             // 16 or 32 tokens
   const float* k_scale;
   const float* v_scale;
   int causal;
@@ -91,7 +93,7 @@ struct AttnArgs {
 };
 
 int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
-                int total_q, int kv_heads, int num_cus, int seg_max,
+                int total_q, int kv_heads, int page_size, int num_cus, int seg_max,
                 int causal, int32_t* plan, int32_t* tok_nseg, void* stream);
 int launch_segments(const AttnArgs& a, void* stream);
 int launch_reduce(const float* part_o, const float* part_lse,

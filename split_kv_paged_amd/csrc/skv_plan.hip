@@ -30,9 +30,10 @@ constexpr int kPlanThreads = 1024;
 constexpr int kWaves = kPlanThreads / 64;
 constexpr int kSmallBs = 32;         // candidate search up to this batch size
 
-__device__ __forceinline__ int pages_of(int L) {
-  // ceil(L / 16) without forming L + 15 (L may be close to INT_MAX)
-  return L <= 0 ? 0 : (L >> 4) + ((L & 15) != 0);
+__device__ __forceinline__ int pages_of(int L, int sh) {
+  // ceil(L / 2^sh) (pages of 16 or 32 tokens) without forming L + 2^sh - 1
+  // (L may be close to INT_MAX)
+  return L <= 0 ? 0 : (L >> sh) + ((L & ((1 << sh) - 1)) != 0);
 }
 
 __device__ __forceinline__ int ceil_div_pos(int a, int b) {
@@ -83,7 +84,7 @@ __device__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ cu_q,
-    int bs, int kv_heads, int num_cus, int seg_max, int causal,
+    int bs, int kv_heads, int page_shift, int num_cus, int seg_max, int causal,
     int32_t* __restrict__ plan, int32_t* __restrict__ tok_nseg) {
   __shared__ long long red_s[kWaves];
   __shared__ int red_m[kWaves];
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   long long tot = 0;
   int mx = 0, nonempty = 0;
   for (int i = tid; i < bs; i += kPlanThreads) {
-    const int n = pages_of(seq_lens[i]);
+    const int n = pages_of(seq_lens[i], page_shift);
     if (bs <= kSmallBs) pages_lds[i] = n;
     mx = max(mx, n);
     tot += n;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
         long long sum = 0;
         int m = 0;
         for (int i = tid; i < bs; i += kPlanThreads) {
-          const int c = ceil_div_pos(pages_of(seq_lens[i]), t);
+          const int c = ceil_div_pos(pages_of(seq_lens[i], page_shift), t);
           sum += c;
           m = max(m, c);
         }
@@ -193,19 +194,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   const int chunk = (bs + kPlanThreads - 1) / kPlanThreads;
   const int i0 = min(bs, tid * chunk), i1 = min(bs, i0 + chunk);
   int local = 0;
-  for (int i = i0; i < i1; ++i) local += ceil_div_pos(pages_of(seq_lens[i]), T);
+  for (int i = i0; i < i1; ++i) local += ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
   int total;
   int pos = block_exclusive_scan(local, wave_tot, total);
   for (int i = i0; i < i1; ++i) {
-    const int ns = ceil_div_pos(pages_of(seq_lens[i]), T);
+    const int ns = ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
     for (int s = 0; s < ns; ++s) plan[1 + pos + s] = (i << 16) | s;
     pos += ns;
   }
   for (int k = total + tid; k < width; k += kPlanThreads) plan[1 + k] = -1;
   if (tid == 0) plan[0] = T;
 
-  // per-token segment counts: ceil(visible / (T * 16)), in 64-bit
-  const long long seg_tokens = static_cast<long long>(T) * kPageSize;
+  // per-token segment counts: ceil(visible / (T * page_size)), in 64-bit
+  const long long seg_tokens = static_cast<long long>(T) << page_shift;
   for (int i = tid; i < bs; i += kPlanThreads) {
     const int L = seq_lens[i];
     const int c0 = cu_q[i], qn = cu_q[i + 1] - c0;
@@ -223,12 +224,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
 }  // namespace
 
 int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
-                int total_q, int kv_heads, int num_cus, int seg_max,
+                int total_q, int kv_heads, int page_size, int num_cus, int seg_max,
                 int causal, int32_t* plan, int32_t* tok_nseg, void* stream) {
   (void)total_q;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0,
                      static_cast<hipStream_t>(stream), seq_lens, cu_seqlens_q,
-                     bs, kv_heads, num_cus, seg_max, causal, plan, tok_nseg);
+                     bs, kv_heads, page_shift_of(page_size), num_cus, seg_max, causal,
+                     plan, tok_nseg);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

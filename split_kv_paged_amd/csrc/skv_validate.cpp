@@ -13,7 +13,7 @@ int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
   if (bs < 1 || bs > kMaxBs || total_q < 1 || kv_heads < 1 || num_cus < 1)
     return SKV_EINVAL;
   if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
-  if (page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (!repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
 
@@ -44,7 +44,7 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
   if (q_heads % kv_heads != 0) return SKV_EINVAL;
   if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
   if (max_q < 1) return SKV_EINVAL;
-  if (head_dim != kHeadDim || page_size != kPageSize) return SKV_EUNSUPPORTED;
+  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (max_q > kMaxQ) return SKV_EUNSUPPORTED;
   if ((q_heads / kv_heads) * max_q > kMaxRows) return SKV_EUNSUPPORTED;
   return SKV_OK;

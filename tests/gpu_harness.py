@@ -33,7 +33,8 @@ def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_ma
         tok = torch.full((cfg.total_q,), -7, dtype=torch.int32, device=case.q.device)
     else:
         plan, tok = skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q,
-                                   cfg.kv_heads, num_cus, seg_max, causal)
+                                   cfg.kv_heads, num_cus, seg_max, causal,
+                                   page_size=cfg.page_size)
     if layout == "shuffled" and planes is None:
         planes = skv.kv_page_shuffle(case.kv)
     rows = cfg.total_q * cfg.q_heads * seg_max
@@ -46,7 +47,8 @@ def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_ma
         case.q, kv_a, kv_b, case.page_table, case.seq_lens, case.cu_seqlens_q, plan, tok,
         kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=num_cus, seg_max=seg_max,
         kv_dtype=cfg.kv_dtype, layout=layout, k_scale=case.k_scale, v_scale=case.v_scale,
-        causal=causal, part_o=part_o, part_lse=part_lse, out_lse=out_lse)
+        causal=causal, part_o=part_o, part_lse=part_lse, out_lse=out_lse,
+        page_size=cfg.page_size)
     torch.cuda.synchronize()
     return dict(plan=None if plan is None else plan.cpu().numpy().tolist(),
                 tok=tok.cpu().numpy().tolist(),

@@ -58,7 +58,7 @@ def _plan(**kw):
     (dict(seq_lens=None), 1), (dict(cu=None), 1), (dict(plan=None), 1), (dict(tok=None), 1),
     (dict(bs=0), 1), (dict(bs=32768), 1), (dict(total_q=0), 1), (dict(kv_heads=0), 1),
     (dict(num_cus=0), 1), (dict(seg_max=0), 1), (dict(seg_max=65536), 1),
-    (dict(page_size=32), 2),
+    (dict(page_size=64), 2), (dict(page_size=8), 2),
 ])
 def test_plan_build_errors(kw, code):
     assert _plan(**kw) == code
@@ -93,7 +93,7 @@ def _attn(**kw):
     (dict(q_heads=12, kv_heads=8), 1), (dict(bs=0), 1), (dict(bs=40000), 1),
     (dict(total_q=0), 1), (dict(max_q=0), 1), (dict(seg_max=0), 1), (dict(seg_max=70000), 1),
     (dict(pt_stride=0), 1), (dict(num_cus=0), 1), (dict(kv_heads=0), 1),
-    (dict(head_dim=64), 2), (dict(page_size=32), 2), (dict(max_q=5), 2),
+    (dict(head_dim=64), 2), (dict(page_size=64), 2), (dict(page_size=24), 2), (dict(max_q=5), 2),
     (dict(q_heads=32, kv_heads=2, max_q=8), 2),           # rows 128 > 64 (max_q checked first)
     (dict(q_heads=64, kv_heads=2, max_q=3), 2),           # rows 96 > 64
 ])

@@ -62,16 +62,17 @@ def test_cache_write_bit_exact(e, H, N):
     assert np.array_equal(_host(vp, e), wv)
 
 
+@pytest.mark.parametrize("P", [16, 32])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_decode_step_writes_then_attends(dtype):
+def test_decode_step_writes_then_attends(dtype, P):
     """A verify step: each sequence's last q tokens are written into the
     shuffled cache through their slots, then attention reads them. Against the
     oracle writing the same tokens into standard pages."""
-    say("write+attend", dtype)
+    say("write+attend", dtype, P)
     base = configs.FP8_KV if dtype == "fp8" else configs.TINY
     lens, ql = [40, 300, 17, 1000, 2], [2, 4, 1, 3, 1]
     cfg = gen.small_config(base, lens, ql, q_heads=16, kv_heads=2, layout="shuffled",
-                           num_cus=64, seg_max=16, seed=21)
+                           num_cus=64, seg_max=16, seed=21, page_size=P)
     case = gen.make_case(cfg, DEV)
     e = 2 if dtype == "bf16" else 1
     H = cfg.kv_heads
@@ -79,7 +80,7 @@ def test_decode_step_writes_then_attends(dtype):
     slots = []
     for i, (L, q) in enumerate(zip(lens, ql)):
         for pos in range(L - q, L):
-            slots.append(int(table[i, pos // PAGE]) * PAGE + pos % PAGE)
+            slots.append(int(table[i, pos // P]) * P + pos % P)
     slots = np.array(slots, dtype=np.int64)
     T = len(slots)
     # new K/V codes: copies of other real tokens' rows (unit-scale values of the
@@ -92,7 +93,7 @@ def test_decode_step_writes_then_attends(dtype):
     for w in range(2):
         for t in range(T):
             i, pos = real[pick[w, t]]
-            row = std0[int(table[i, pos // PAGE]), :, pos % PAGE]
+            row = std0[int(table[i, pos // P]), :, pos % P]
             kv_new[w, t] = row[:, :D] if w == 0 else row[:, D:]
     kp, vp = skv.kv_page_shuffle(case.kv)
     key = _dev(kv_new[0], e).view(T, H, D)
@@ -101,23 +102,23 @@ def test_decode_step_writes_then_attends(dtype):
         key, val = key.view(torch.bfloat16), val.view(torch.bfloat16)
     skv.kv_cache_write(key, val, torch.as_tensor(slots, device=DEV), kp, vp)
     plan, tok = skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, H,
-                               cfg.num_cus, cfg.seg_max, cfg.causal)
+                               cfg.num_cus, cfg.seg_max, cfg.causal, page_size=P)
     out_lse = torch.empty((cfg.total_q, cfg.q_heads), dtype=torch.float32, device=DEV)
     out, _ = skv.paged_decode_attn(case.q, kp, vp, case.page_table, case.seq_lens,
                                    case.cu_seqlens_q, plan, tok, kv_heads=H, max_q=cfg.max_q,
                                    num_cus=cfg.num_cus, seg_max=cfg.seg_max,
                                    kv_dtype=dtype, layout="shuffled", k_scale=case.k_scale,
-                                   v_scale=case.v_scale, out_lse=out_lse)
+                                   v_scale=case.v_scale, out_lse=out_lse, page_size=P)
     torch.cuda.synchronize()
     # oracle: the same tokens written into the standard pages
     std = oracle.write_tokens_standard(std0, kv_new[0], kv_new[1], slots)
     q = oracle.decode_bf16(gen.raw_u16(case.q))
     ref_out, ref_lse = oracle.decode_attention(
         q, std, dtype, table, case.seq_lens.cpu().numpy(), case.cu_seqlens_q.cpu().numpy(),
-        H, PAGE, cfg.causal, cfg.k_scale, cfg.v_scale)
+        H, P, cfg.causal, cfg.k_scale, cfg.v_scale)
     r = compare(out.float().cpu().numpy().astype(np.float64),
                 out_lse.cpu().numpy().astype(np.float64), ref_out, ref_lse, dtype)
-    say("write+attend", dtype, r)
+    say("write+attend", dtype, P, r)
     assert r["max_abs"] <= TOL[dtype], r
     assert r["lse_err"] <= 1e-3, r
 

@@ -145,10 +145,12 @@ CASES = [
 ]
 
 
-def _mk(name, lens, ql, hq, hkv, dt, layout, causal, ncu, smax, seed=5, poison="finite"):
+def _mk(name, lens, ql, hq, hkv, dt, layout, causal, ncu, smax, seed=5, poison="finite",
+        page_size=16):
     base = configs.FP8_KV if dt == "fp8" else configs.TINY
     cfg = gen.small_config(base, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
-                           causal=causal, num_cus=ncu, seg_max=smax, seed=seed)
+                           causal=causal, num_cus=ncu, seg_max=smax, seed=seed,
+                           page_size=page_size)
     return gen.make_case(cfg, DEV, poison=poison)
 
 
@@ -164,6 +166,67 @@ def test_attention_matches_oracle(spec):
     say(spec[0], r)
     assert r["max_abs"] <= r["tol"], r
     assert r["lse_err"] <= 1e-3, r
+
+
+# 32-token pages (the kernels stream 16-token sub-pages): every kernel variant,
+# both layouts, lengths around sub-page and page boundaries
+P32_CASES = [
+    ("p32_valu_std", [1, 15, 16, 17, 31, 32, 33, 1000], [1] * 8, 8, 2, "bf16", "standard", 1, 64, 64),
+    ("p32_valu_shuf", [33, 4097, 64, 2], [1, 1, 1, 1], 8, 2, "bf16", "shuffled", 1, 32, 64),
+    ("p32_valu_q3", [50, 700, 3, 129], [3, 3, 2, 1], 2, 2, "bf16", "standard", 1, 32, 64),
+    ("p32_bf16_rows16", [5, 17, 900, 3000], [2, 1, 2, 2], 16, 2, "bf16", "standard", 1, 32, 64),
+    ("p32_bf16_rows32_shuf", [3, 40, 777, 2500], [4, 2, 4, 3], 16, 2, "bf16", "shuffled", 1, 32, 64),
+    ("p32_bf16_rows64", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "bf16", "standard", 1, 64, 64),
+    ("p32_bf16_rows64_shuf", [31, 33, 2049, 777], [4, 4, 3, 4], 32, 2, "bf16", "shuffled", 0, 64, 64),
+    ("p32_fp8_rows8", [3, 77, 513, 2049], [1, 2, 1, 1], 16, 4, "fp8", "standard", 1, 40, 16),
+    ("p32_fp8_rows8_shuf", [3, 77, 513, 2049], [1, 2, 1, 1], 16, 4, "fp8", "shuffled", 1, 40, 16),
+    ("p32_fp8_rows32", [1, 8, 700, 4100], [4, 1, 3, 2], 16, 2, "fp8", "standard", 1, 64, 64),
+    ("p32_fp8_rows64", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "standard", 1, 64, 64),
+    ("p32_fp8_rows64_shuf", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "shuffled", 1, 64, 64),
+    ("p32_infeasible", [100, 200, 300, 400, 500], [1, 2, 3, 4, 1], 8, 4, "bf16", "standard", 1, 8, 64),
+]
+
+
+@pytest.mark.parametrize("spec", P32_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("fixed", [False, True], ids=["planned", "fixed"])
+def test_32_token_pages_match_oracle(spec, fixed):
+    say("p32", spec[0], "fixed" if fixed else "planned")
+    case = _mk(*spec, page_size=32)
+    cfg = case.cfg
+    hip = run_hip(case, fixed=fixed)
+    if fixed:
+        _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                                 cfg.kv_heads, 32, cfg.num_cus, cfg.seg_max,
+                                                 cfg.causal)
+        assert hip["tok"] == want_tok
+    else:
+        wp, wt = oracle_plan(case)
+        assert hip["plan"] == wp and hip["tok"] == wt
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, cfg.kv_dtype)
+    say(spec[0], r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3, r
+
+
+def test_plan_bit_exact_fuzz_32_token_pages():
+    rng = np.random.default_rng(2032)
+    for trial in range(60):
+        bs = int(rng.integers(1, 301))
+        lens = rng.integers(0, 300_001 if trial % 3 == 0 else 3000, size=bs)
+        lens[rng.random(bs) < 0.1] = 0
+        ql = rng.integers(1, 5, size=bs)
+        kvh = int(rng.choice([1, 2, 4, 8]))
+        ncu = int(rng.integers(4, 305))
+        smax = int(rng.integers(1, 65))
+        causal = int(rng.integers(0, 2))
+        cu_h = np.array(_cu(ql.tolist()), dtype=np.int32)
+        plan, tok = skv.plan_build(torch.as_tensor(lens.astype(np.int32), device=DEV),
+                                   torch.as_tensor(cu_h, device=DEV), int(cu_h[-1]), kvh, ncu,
+                                   smax, causal, page_size=32)
+        wp, wt = oracle.plan_segments(lens.tolist(), cu_h, kvh, 32, ncu, smax, causal)
+        assert plan.cpu().tolist() == wp, (trial, bs, kvh, ncu, smax)
+        assert tok.cpu().tolist() == wt, trial
 
 
 FIXED_CASES = CASES + [
