@@ -84,6 +84,16 @@ __device__ __forceinline__ void pdma16(const uint8_t* g, uint8_t* lds_uniform) {
                :: "v"(g), "s"(lds) : "memory", "m0");
 }
 
+// The same DMA from a wave-uniform base (held in SGPRs) plus a 32-bit
+// per-lane byte offset: half the VGPRs of a 64-bit per-lane address.
+__device__ __forceinline__ void pdma16s(const uint8_t* base_uniform, uint32_t off,
+                                        uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
+}
+
 // Standard pages in a slot: page pg's (block, head) tile is copied whole, 16
 // token rows of 256 B (K 128 B, then V 128 B), each DMA instruction taking 4
 // consecutive rows, i.e. 1 KB of contiguous HBM. Within a row the sixteen
@@ -113,7 +123,7 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
       for (int i = 0; i < kStdTile / 1024; ++i) {
         const int row = 4 * i + j4;                               // lane -> (row, position r16)
         const int q = std_chunk_pos(row, r16, pg);                // the chunk stored there
-        pdma16(tile + row * kStdRow + q * 16, slot + pg * kStdTile + i * 1024);
+        pdma16s(tile, row * kStdRow + q * 16, slot + pg * kStdTile + i * 1024);
       }
     }
     return;
@@ -125,11 +135,11 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
     if ((u & 1) == 0) {
 #pragma unroll
       for (int i = 0; i < kUnitInstr; ++i)
-        pdma16(sp[u >> 1].k + static_cast<size_t>(4 * i + j4) * krow + r16 * 16, dst + i * 1024);
+        pdma16s(sp[u >> 1].k, (4 * i + j4) * krow + r16 * 16, dst + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < kUnitInstr; ++i)    // the sub-page's V plane as is
-        pdma16(sp[u >> 1].v + static_cast<size_t>(i * 64 + lane) * 16, dst + i * 1024);
+        pdma16s(sp[u >> 1].v, (i * 64 + lane) * 16, dst + i * 1024);
     }
   }
 }
@@ -333,6 +343,44 @@ void seg_mfma_priv_kernel(SegParams p) {
     const int tok0 = it.seg_start + 32 * (wave + NW * k);
     // wave-uniform: does any key of this block lie past some row's limit?
     const bool masked = tok0 + 32 > lim_min;
+    // the segment's last block: V of its tokens past the segment end is zeroed
+    // in the slot before any read, so page-tail poison (even NaN) times a zero
+    // weight never reaches O
+    const int vend = it.seg_end - tok0;
+    if (vend < 32) {
+      // lane index recomputed here (not hoisted into the loop's live registers)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      if constexpr (SHUF) {
+        // V plane units: channel d's 16-byte chunk holds the page's 16 tokens
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pg = r >> 1, d = 2 * ln + (r & 1);
+          const int n = min(max(vend - 16 * pg, 0), 16);   // tokens kept in this page
+          if (n < 16) {
+            uint4* ch = reinterpret_cast<uint4*>(const_cast<uint8_t*>(vU[pg]) + d * 16);
+            uint4 v = *ch;
+            auto keep = [&](int b0) -> uint32_t {           // bytes b0 .. b0+3
+              const int kb = n - b0;
+              return kb <= 0 ? 0u : (kb >= 4 ? 0xffffffffu : (0xffffffffu >> (32 - 8 * kb)));
+            };
+            v.x &= keep(0); v.y &= keep(4); v.z &= keep(8); v.w &= keep(12);
+            *ch = v;
+          }
+        }
+      } else {
+        // standard pages: token rows 16 pg + tau, V chunks 8 .. 15, 16 bytes each
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int pair = 64 * r + ln, tok = pair >> 3, cq = 8 + (pair & 7);
+          const int pg = tok >> 4, tau = tok & 15;
+          if (tok >= vend)
+            *reinterpret_cast<uint4*>(const_cast<uint8_t*>(slot) + pg * kStdTile + tau * kStdRow +
+                                      std_chunk_pos(tau, cq, pg) * 16) = make_uint4(0, 0, 0, 0);
+        }
+      }
+      asm volatile("" ::: "memory");
+    }
 
     // ---- V chunks of the block: up to two row tiles, every LDS read is issued
     // before the score MFMAs, so its latency hides behind the MFMAs and the
@@ -418,7 +466,7 @@ void seg_mfma_priv_kernel(SegParams p) {
         m[t] = mn;
         thr[t] = mn == -INFINITY ? -INFINITY : (mn + kSlackLog2) * inv_c;
       }
-      const float mu = m[t] == -INFINITY ? 0.f : m[t];
+      const float mu = m[t] == -INFINITY ? 0.f : m[t];   // the exp2 offset
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -430,31 +478,12 @@ void seg_mfma_priv_kernel(SegParams p) {
     }
 
     // ---- O^T += V^T.P^T, V widened once for every tile ----
-    // lane bytes 0-3 hold tokens 4 j4 .. +3 of the block, bytes 4-7 tokens 16 + 4 j4 .. +3
-    auto pv = [&](uint32_t m0, uint32_t m1) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const uint2 vr = kQLds ? read_v1(dt) : vraw[dt];
-        const uint4 cw = fp8x8_to_bf16x8(make_uint2(vr.x & m0, vr.y & m1));
-        const bf16x8_t vop = as_bf16x8(cw);
+    for (int dt = 0; dt < 8; ++dt) {
+      const bf16x8_t vop = as_bf16x8(fp8x8_to_bf16x8(kQLds ? read_v1(dt) : vraw[dt]));
 #pragma unroll
-        for (int t = 0; t < NRT; ++t)
-          oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
-      }
-    };
-    // V of tokens past the segment end is zeroed (byte masks of the lane's tokens)
-    const int vend = it.seg_end - tok0;
-    auto keep = [&](int first) -> uint32_t {     // tokens first .. first+3
-      const int n = vend - first;
-      return n <= 0 ? 0u : (n >= 4 ? 0xffffffffu : (0xffffffffu >> (32 - 8 * n)));
-    };
-    if constexpr (kQLds) {
-      pv(keep(4 * j4), keep(16 + 4 * j4));
-    } else {
-      if (masked && vend < 32)
-        pv(keep(4 * j4), keep(16 + 4 * j4));
-      else
-        pv(0xffffffffu, 0xffffffffu);
+      for (int t = 0; t < NRT; ++t)
+        oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
     }
   }
 

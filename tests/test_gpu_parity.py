@@ -308,11 +308,26 @@ def test_fp8_negative_k_scale(spec):
 
 
 @pytest.mark.parametrize("spec", [_BY[n] for n in ("rows8_ragged", "mfma4_g16_q4", "mfma_fp8_std",
+                                                   "mfma_fp8_shuf", "fp8_rows64_std",
+                                                   "fp8_rows64_shuf", "fp8_rows4_shuf",
                                                    "valu_g1_q3", "valu_g4_shuf_tails")],
                          ids=lambda c: c[0])
 def test_nan_poison_does_not_leak(spec):
     a = run_hip(_mk(*spec, poison="finite"))
     b = run_hip(_mk(*spec, poison="nan"))
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.all(np.isfinite(b["out"]))
+
+
+_BY32 = {c[0]: c for c in P32_CASES}
+
+
+@pytest.mark.parametrize("spec", [_BY32[n] for n in ("p32_valu_std", "p32_bf16_rows32_shuf",
+                                                     "p32_bf16_rows64", "p32_fp8_rows8_shuf",
+                                                     "p32_fp8_rows64")], ids=lambda c: c[0])
+def test_nan_poison_does_not_leak_32_token_pages(spec):
+    a = run_hip(_mk(*spec, poison="finite", page_size=32))
+    b = run_hip(_mk(*spec, poison="nan", page_size=32))
     assert np.array_equal(a["out_bits"], b["out_bits"])
     assert np.all(np.isfinite(b["out"]))
 
