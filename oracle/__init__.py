@@ -19,10 +19,11 @@ Sources, cited by page title and section throughout:
          checks (Accuracy Tests).
   [OCP]  the OCP 8-bit floating point specification (E4M3 encoding), for the
          fp8 KV codes the RFC names in Proposed Change ("e4m3fn").
+  [IEEE] IEEE 754 binary16, for the FP16 pages in the RFC's scope.
 
 Modules:
-  fp8        element decode (bf16 bits, e4m3fn codes) and the
-             rounding of values to e4m3fn codes                 -- pinned
+  fp8        element decode (bf16 and fp16 bits, e4m3fn codes) and
+             the rounding of values to e4m3fn codes             -- pinned
   attention  page gather + unsplit fp64 attention               -- pinned
   planner    length-aware segment planner, fixed split          -- pinned
   merge      per-segment partials and log-sum-exp merge         -- pinned
@@ -33,8 +34,8 @@ Every function is pinned by tests under tests/test_oracle_*.py against values
 the pages print, closed forms, invariants, brute force or an independent
 library routine; none is "parity unpinned".
 """
-from .fp8 import (decode_bf16, decode_e4m3fn, e4m3fn_value, decode_kv, encode_e4m3fn,
-                  quantize_e4m3fn)
+from .fp8 import (decode_bf16, decode_fp16, decode_q, fp16_value, decode_e4m3fn,
+                  e4m3fn_value, decode_kv, encode_e4m3fn, quantize_e4m3fn)
 from .attention import (gather_standard, gather_shuffled, visible_keys,
                         attend_one, decode_attention)
 from .planner import plan_segments, fixed_split_segments, fixed_split_plan, pow2floor
@@ -44,8 +45,8 @@ from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
                       write_tokens_shuffled)
 
 __all__ = [
-    "decode_bf16", "decode_e4m3fn", "e4m3fn_value", "decode_kv", "encode_e4m3fn",
-    "quantize_e4m3fn",
+    "decode_bf16", "decode_fp16", "decode_q", "fp16_value", "decode_e4m3fn",
+    "e4m3fn_value", "decode_kv", "encode_e4m3fn", "quantize_e4m3fn",
     "gather_standard", "gather_shuffled", "visible_keys", "attend_one",
     "decode_attention", "plan_segments", "fixed_split_segments", "fixed_split_plan",
     "pow2floor",

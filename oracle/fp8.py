@@ -1,6 +1,9 @@
 """Element decode for the oracle (test infrastructure; see oracle/__init__.py).
 
 bf16: the upper half of an IEEE fp32 word, so widening is exact.
+fp16 [IEEE 754 binary16; the RFC's decoder scope is BF16/FP16]: 1 sign bit,
+5 exponent bits (bias 15), 10 mantissa bits; exponent 0 is subnormal
+(M/1024 * 2^-14); exponent 31 is infinity (M = 0) or NaN.
 e4m3fn [OCP E4M3; the RFC's Proposed Change names this OCP format as distinct
 from MI300's e4m3fnuz]: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits;
 exponent 0 is subnormal (M/8 * 2^-6); exponent 15 with mantissa 7 is NaN and
@@ -15,6 +18,33 @@ def decode_bf16(bits) -> np.ndarray:
     """uint16 bf16 bit patterns -> float64 (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def fp16_value(code: int) -> float:
+    """Value of one IEEE binary16 pattern, from the bit-field definition."""
+    code = int(code) & 0xFFFF
+    sign = -1.0 if code & 0x8000 else 1.0
+    exp = (code >> 10) & 0x1F
+    man = code & 0x3FF
+    if exp == 0x1F:
+        return sign * math.inf if man == 0 else math.nan
+    if exp == 0:
+        return sign * (man / 1024.0) * 2.0 ** -14
+    return sign * (1.0 + man / 1024.0) * 2.0 ** (exp - 15)
+
+
+_FP16 = np.array([fp16_value(c) for c in range(1 << 16)], dtype=np.float64)
+
+
+def decode_fp16(bits) -> np.ndarray:
+    """uint16 binary16 bit patterns -> float64 (exact)."""
+    return _FP16[np.asarray(bits, dtype=np.uint16)]
+
+
+def decode_q(bits, kv_dtype: str) -> np.ndarray:
+    """Query bit patterns -> float64: fp16 queries go with an fp16 cache, bf16
+    queries with a bf16 or fp8 cache."""
+    return decode_fp16(bits) if kv_dtype == "fp16" else decode_bf16(bits)
 
 
 def e4m3fn_value(code: int) -> float:
@@ -46,6 +76,8 @@ def decode_kv(raw, kv_dtype: str, scale=None) -> np.ndarray:
     """
     if kv_dtype == "bf16":
         return decode_bf16(raw)
+    if kv_dtype == "fp16":
+        return decode_fp16(raw)
     if kv_dtype == "fp8":
         v = decode_e4m3fn(raw)
         return v if scale is None else v * float(scale)

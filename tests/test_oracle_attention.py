@@ -10,14 +10,14 @@ from workloads import configs, gen
 
 
 def _case(seq_lens, q_lens, q_heads=8, kv_heads=2, kv_dtype="bf16", seed=7, **kw):
-    base = configs.TINY if kv_dtype == "bf16" else configs.FP8_KV
+    base = configs.FP8_KV if kv_dtype == "fp8" else configs.TINY
     cfg = gen.small_config(base, seq_lens, q_lens, q_heads=q_heads, kv_heads=kv_heads,
-                           seed=seed, **kw)
+                           seed=seed, kv_dtype=kv_dtype, **kw)
     return cfg, gen.make_case(cfg, "cpu")
 
 
 def _oracle(cfg, case, planes=None, rows=None, causal=None):
-    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    q = oracle.decode_q(gen.raw_u16(case.q), cfg.kv_dtype)
     kv = None if planes is not None else gen.raw_kv(case)
     return oracle.decode_attention(
         q, kv, cfg.kv_dtype, case.page_table.numpy(), case.seq_lens.numpy(),
@@ -87,14 +87,15 @@ def test_scale_and_sign_against_exp_loops():
     assert lse == pytest.approx(m + math.log(tot), rel=1e-14)
 
 
-@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp16"])
 def test_batch_matches_torch_sdpa_fp64(kv_dtype):
     """Independent library routine: torch SDPA in float64 on gathered tensors,
     with the bottom-right causal mask and grouped heads expanded by hand."""
     lens, ql = [37, 100, 16, 1, 5], [1, 4, 3, 2, 4]
     cfg, case = _case(lens, ql, q_heads=8, kv_heads=2, kv_dtype=kv_dtype)
     out, lse = _oracle(cfg, case)
-    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    q = torch.from_numpy(gen.raw_u16(case.q).view(np.int16)).view(
+        torch.float16 if kv_dtype == "fp16" else torch.bfloat16).double().numpy()
     kv = gen.raw_kv(case)
     G = cfg.q_heads // cfg.kv_heads
     cu = case.cu_seqlens_q.numpy()

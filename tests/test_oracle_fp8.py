@@ -114,3 +114,27 @@ def test_quantize_divides_in_fp32():
     for xi, bi in zip(x, back):
         t = float(np.float32(xi) / np.float32(scale))
         assert abs(bi - t) == np.min(np.abs(table - t))
+
+
+def test_fp16_points_from_the_bit_fields():
+    """Hand-derived binary16 values: 1.0, -2.0, the largest finite, the least
+    normal and subnormal, 1/3 rounded, infinities, NaN and -0."""
+    pts = {0x3C00: 1.0, 0xC000: -2.0, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14,
+           0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24, 0x3555: 1365 / 4096,
+           0x7C00: math.inf, 0xFC00: -math.inf}
+    for code, want in pts.items():
+        assert oracle.fp16_value(code) == want, hex(code)
+    assert math.isnan(oracle.fp16_value(0x7E00)) and math.isnan(oracle.fp16_value(0x7C01))
+    z = oracle.fp16_value(0x8000)
+    assert z == 0.0 and math.copysign(1.0, z) == -1.0
+
+
+def test_fp16_decode_matches_numpy_all_codes():
+    """Independent library routine: numpy's float16 widened to float64."""
+    codes = np.arange(1 << 16, dtype=np.uint16)
+    got = oracle.decode_fp16(codes)
+    want = codes.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(oracle.decode_kv(codes, "fp16"), got, equal_nan=True)

@@ -9,9 +9,9 @@ Recipe (per config, seed = config.seed):
   * metadata from numpy PCG64 default_rng(seed), drawn in this order: physical
     block permutation of a pool of sum(ceil(L_i/P)) + extra_blocks blocks;
   * values from a torch.Generator seeded with `seed` on the target device:
-    Q ~ N(0,1) rounded to bf16 (RNE); K and V ~ N(0,1), rounded to bf16, or
-    divided by the per-tensor scale and rounded to e4m3fn with saturation to
-    +-448 for fp8;
+    Q ~ N(0,1) rounded to bf16 (RNE; fp16 with an fp16 cache); K and V ~ N(0,1),
+    rounded to bf16 or fp16, or divided by the per-tensor scale and rounded to
+    e4m3fn with saturation to +-448 for fp8;
   * page-tail slots (token slots >= L_i mod P of a sequence's last page), the
     unused pool blocks and page-table entries past a sequence's last page hold
     poison (a large finite value by default, NaN in strict mode); the latter
@@ -27,6 +27,7 @@ import torch
 from .configs import Config
 
 POISON_BF16 = {"finite": 0x46EA, "nan": 0x7FC0}   # 29952.0 and a quiet NaN
+POISON_FP16 = {"finite": 0x7800, "nan": 0x7E00}   # 32768.0 and a quiet NaN
 POISON_FP8 = {"finite": 0x7E, "nan": 0x7F}        # 448.0 and the e4m3fn NaN
 
 
@@ -76,14 +77,14 @@ def layout_metadata(cfg: Config):
 
 
 def _fill_values(shape, gen, device, dtype, scale, chunk_rows=2048):
-    out = torch.empty(shape, dtype=torch.bfloat16 if dtype == "bf16" else torch.uint8,
-                      device=device)
+    out = torch.empty(shape, dtype={"bf16": torch.bfloat16, "fp16": torch.float16}.get(
+        dtype, torch.uint8), device=device)
     for s in range(0, shape[0], chunk_rows):
         e = min(shape[0], s + chunk_rows)
         x = torch.randn((e - s,) + tuple(shape[1:]), generator=gen, device=device,
                         dtype=torch.float32)
-        if dtype == "bf16":
-            out[s:e] = x.to(torch.bfloat16)
+        if dtype in ("bf16", "fp16"):
+            out[s:e] = x.to(out.dtype)
         else:
             y = (x / scale).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn)
             out[s:e] = y.view(torch.uint8)
@@ -95,19 +96,20 @@ def make_case(cfg: Config, device="cpu", poison="finite") -> Case:
     gen = torch.Generator(device=device)
     gen.manual_seed(cfg.seed)
     D, P, Hkv = cfg.head_dim, cfg.page_size, cfg.kv_heads
+    qdt = torch.float16 if cfg.kv_dtype == "fp16" else torch.bfloat16
     q = torch.randn((cfg.total_q, cfg.q_heads, D), generator=gen, device=device,
-                    dtype=torch.float32).to(torch.bfloat16)
+                    dtype=torch.float32).to(qdt)
     shape = (meta["pool"], Hkv, P, 2 * D)
-    if cfg.kv_dtype == "bf16":
-        kv = _fill_values(shape, gen, device, "bf16", None)
+    if cfg.kv_dtype in ("bf16", "fp16"):
+        kv = _fill_values(shape, gen, device, cfg.kv_dtype, None)
     else:
         # K and V share one draw stream but use their own per-tensor scale
         kv = torch.empty(shape, dtype=torch.uint8, device=device)
         kv[..., :D] = _fill_values(shape[:-1] + (D,), gen, device, "fp8", cfg.k_scale)
         kv[..., D:] = _fill_values(shape[:-1] + (D,), gen, device, "fp8", cfg.v_scale)
     if poison != "none":
-        raw = kv.view(torch.int16) if cfg.kv_dtype == "bf16" else kv
-        pv = POISON_BF16[poison] if cfg.kv_dtype == "bf16" else POISON_FP8[poison]
+        raw = kv.view(torch.int16) if cfg.kv_dtype != "fp8" else kv
+        pv = {"bf16": POISON_BF16, "fp16": POISON_FP16, "fp8": POISON_FP8}[cfg.kv_dtype][poison]
         if pv >= 0x8000:
             pv -= 0x10000
         if len(meta["unused"]):
@@ -144,4 +146,4 @@ def raw_u8(t: torch.Tensor) -> np.ndarray:
 
 
 def raw_kv(case: Case) -> np.ndarray:
-    return raw_u16(case.kv) if case.cfg.kv_dtype == "bf16" else raw_u8(case.kv)
+    return raw_u8(case.kv) if case.cfg.kv_dtype == "fp8" else raw_u16(case.kv)
