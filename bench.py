@@ -143,7 +143,9 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
     rows = cfg.total_q * cfg.q_heads * cfg.seg_max
     part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
     part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
-    out = torch.empty((cfg.total_q, cfg.q_heads, cfg.head_dim), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((cfg.total_q, cfg.q_heads, cfg.head_dim), dtype=skv.io_dtype(cfg.kv_dtype),
+                      device=dev)
+    odt = "fp16" if cfg.kv_dtype == "fp16" else "bf16"
     plan = torch.empty(skv.plan_words(cfg.bs, cfg.kv_heads, cfg.num_cus), dtype=torch.int32,
                        device=dev)
     tok = torch.empty(cfg.total_q, dtype=torch.int32, device=dev)
@@ -163,7 +165,7 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         if ev:
             ev[2].record(st)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out)
+                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
         if ev:
             ev[3].record(st)
 
@@ -196,7 +198,7 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                          case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out)
+                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
 
     side = torch.cuda.Stream()
     side.wait_stream(st)
@@ -227,7 +229,7 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                          case.cu_seqlens_q, None, tok, part_o=part_o, part_lse=part_lse, **kw)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out)
+                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
         if ev:
             ev[1].record(st)
 
@@ -333,7 +335,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.kv_dtype == "bf16" else "fp8-e4m3fn",
+        "dtype": {"bf16": "bf16", "fp16": "fp16", "fp8": "fp8-e4m3fn"}[cfg.kv_dtype],
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: {cfg.note}", "bs": cfg.bs,
                    "total_kv_tokens": int(sum(cfg.seq_lens)), "q_heads": cfg.q_heads,

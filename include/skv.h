@@ -29,8 +29,10 @@
  *   - Device data must satisfy the stated contract (lengths, page ids,
  *     cu_seqlens_q); a violation is undefined behaviour and is not detected.
  *
- * Element types: Q and the output are bf16 (IEEE binary32 upper half). KV is
- * bf16 or OCP e4m3fn fp8 (kv_dtype 1) with per-tensor fp32 dequant scales.
+ * Element types: KV is bf16 (IEEE binary32 upper half), OCP e4m3fn fp8
+ * (kv_dtype 1) with per-tensor fp32 dequant scales, or IEEE binary16 fp16
+ * (kv_dtype 2; the RFC's decoder scope is BF16/FP16). Q and the output are
+ * fp16 with an fp16 cache and bf16 otherwise.
  * Supported geometry: head_dim 128; page_size 16 or 32 tokens for every
  * entry point (the RFC's decoder scope: 16- or 32-token pages; the split-KV
  * PR's kernels use 16); 1..4 query tokens per sequence,
@@ -54,7 +56,7 @@ enum skv_status {
 };
 
 enum skv_layout { SKV_LAYOUT_STANDARD = 0, SKV_LAYOUT_SHUFFLED = 1 };
-enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1 };
+enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1, SKV_KV_FP16 = 2 };
 enum skv_convert_dir { SKV_TO_SHUFFLED = 0, SKV_TO_STANDARD = 1 };
 
 /* Number of int32 words of a plan: 1 + max(num_cus / kv_heads, bs).
@@ -98,28 +100,28 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
 /* Paged decode/verify attention: the segment kernel, then the split reduce
  * [PR, Motivation and Modifications].
  *
- * q            bf16 [total_q, q_heads, head_dim]
+ * q            [total_q, q_heads, head_dim], fp16 for SKV_KV_FP16, else bf16
  * kv_a, kv_b   layout STANDARD: kv_a = pages [num_blocks, kv_heads, page_size,
  *              2 * head_dim] (per token: K channels then V channels), kv_b NULL;
  *              layout SHUFFLED: kv_a = K plane [num_blocks, kv_heads,
  *              head_dim/x, page_size, x], kv_b = V plane [num_blocks, kv_heads,
  *              page_size/x, head_dim, x], x = 16 / element bytes [RFC, Background]
- * kv_dtype     SKV_KV_BF16 or SKV_KV_FP8_E4M3FN
+ * kv_dtype     SKV_KV_BF16, SKV_KV_FP8_E4M3FN or SKV_KV_FP16
  * page_table   int32 [bs, pt_stride]; entry [i, p] is the block holding tokens
- *              [16p, 16p + 16) of sequence i; entries at p >= ceil(L_i/16) are
- *              never read
+ *              [p * page_size, (p + 1) * page_size) of sequence i; entries at
+ *              p >= ceil(L_i / page_size) are never read
  * seq_lens, cu_seqlens_q, bs, total_q   as for skv_plan_build
  * max_q        an upper bound of the query tokens of any sequence (1..4)
  * q_heads, kv_heads   grouped-query heads: q head h reads kv head h / (q_heads/kv_heads)
  * k_scale, v_scale    device fp32 scalars: required for fp8 (dequantized value =
- *              code value * scale), NULL for bf16
+ *              code value * scale), NULL for bf16 and fp16
  * causal       1: bottom-right causal mask as in skv_plan_build; 0: all L keys
  * plan, tok_nseg      from skv_plan_build with the same bs, kv_heads, num_cus,
  *              seg_max, causal and page_size (planned split). plan NULL selects
  *              the FIXED split [PR, Motivation; Modifications: bs == 1 runs it
  *              without a plan]: every sequence gets S = max(1, min(seg_max,
  *              pow2floor(num_cus / (bs * kv_heads)))) segments of
- *              ceil(ceil(L_i/16) / S) pages (trailing ones empty when a sequence
+ *              ceil(ceil(L_i/page_size) / S) pages (trailing ones empty when a sequence
  *              has fewer than S pages), one work-group per (sequence, segment,
  *              kv head); no plan launch is needed, and the segment kernel
  *              WRITES tok_nseg[t] = ceil(visible_t / segment tokens) for the
@@ -129,13 +131,13 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  *              softmax-normalized output), part_lse fp32 [total_q, q_heads,
  *              seg_max] (natural-log sum-exp); entries s >= tok_nseg[t] are
  *              unspecified
- * out          bf16 [total_q, q_heads, head_dim], round-to-nearest-even;
+ * out          [total_q, q_heads, head_dim], the type of q, round to nearest even;
  *              a token that sees no key gets zeros
  * out_lse      fp32 [total_q, q_heads] or NULL; -inf where no key is visible
  * Scale: softmax(q.k / sqrt(head_dim)).
  * Errors: EINVAL for NULL required pointers, non-positive sizes, q_heads not a
  * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
- * scales present for bf16 or missing for fp8, kv_b NULL for SHUFFLED or
+ * scales present for bf16/fp16 or missing for fp8, kv_b NULL for SHUFFLED or
  * non-NULL for STANDARD, pt_stride < 1, an unknown layout or dtype;
  * EUNSUPPORTED for head_dim != 128, page_size other than 16 or 32, max_q > 4,
  * (q_heads/kv_heads) * max_q > 64. */
@@ -170,14 +172,15 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
  * lse = M + ln sum_s exp(lse_s - M), out = sum_s exp(lse_s - lse) * o_s.
  * tok_nseg[t] == 0 gives zeros and lse -inf. Values of tok_nseg[t] above
  * seg_max are clamped to seg_max.
- * Layouts as for skv_paged_decode_attn; out bf16 [total_q, q_heads, head_dim];
+ * Layouts as for skv_paged_decode_attn; out [total_q, q_heads, head_dim] of
+ * out_dtype (SKV_KV_BF16: bf16, SKV_KV_FP16: fp16; round to nearest even);
  * out_lse may be NULL.
  * Errors: EINVAL for NULL required pointers, non-positive sizes, seg_max
- * outside [1, 65535]; EUNSUPPORTED for head_dim != 128. */
+ * outside [1, 65535], another out_dtype; EUNSUPPORTED for head_dim != 128. */
 int skv_split_reduce(const float* part_o, const float* part_lse,
                      const int32_t* tok_nseg, int total_q, int q_heads,
-                     int head_dim, int seg_max, void* out, float* out_lse,
-                     void* stream);
+                     int head_dim, int seg_max, int out_dtype, void* out,
+                     float* out_lse, void* stream);
 
 /* Standard -> shuffled page repack [RFC, Background and Proposed Change §4].
  * For each listed block b (block_ids int32 [num_blocks]; NULL = blocks

@@ -5,11 +5,11 @@ include/skv.h); this package only binds it. Build with
 `python -m split_kv_paged_amd.build`.
 """
 from ._lib import (CONVERT_DIR, EXPORTED, KV_DTYPE, LAYOUT, LIB_PATH, SkvError,
-                   kv_cache_write, kv_page_convert, kv_page_shuffle, kv_page_unshuffle,
-                   load, paged_decode_attn, plan_build, plan_words, segment_attn, split_reduce,
+                   io_dtype, kv_cache_write, kv_page_convert, kv_page_shuffle,
+                   kv_page_unshuffle, load, paged_decode_attn, plan_build, plan_words, segment_attn, split_reduce,
                    strerror, workspace_bytes)
 
 __all__ = ["CONVERT_DIR", "EXPORTED", "KV_DTYPE", "LAYOUT", "LIB_PATH", "SkvError",
-           "kv_cache_write", "kv_page_convert", "kv_page_shuffle", "kv_page_unshuffle",
+           "io_dtype", "kv_cache_write", "kv_page_convert", "kv_page_shuffle", "kv_page_unshuffle",
            "load", "paged_decode_attn", "plan_build", "plan_words", "segment_attn", "split_reduce",
            "strerror", "workspace_bytes"]

@@ -16,7 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libskv.so")
 SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_ELAUNCH = 0, 1, 2, 3
 LAYOUT = {"standard": 0, "shuffled": 1}
 CONVERT_DIR = {"to_shuffled": 0, "to_standard": 1}
-KV_DTYPE = {"bf16": 0, "fp8": 1}
+KV_DTYPE = {"bf16": 0, "fp8": 1, "fp16": 2}
+
+
+def io_dtype(kv_dtype):
+    """torch dtype of q and of the output: fp16 with an fp16 cache, else bf16."""
+    return torch.float16 if kv_dtype == "fp16" else torch.bfloat16
 
 _c_int, _c_sz, _p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
@@ -33,7 +38,8 @@ _SIGNATURES = {
                                   _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                   _c_int, _p, _p, _c_int, _p, _p, _c_int, _c_int,
                                   _p, _p, _p]),
-    "skv_split_reduce": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _p, _p, _p]),
+    "skv_split_reduce": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p,
+                                  _p]),
     "skv_kv_page_shuffle": (_c_int, [_p, _p, _p, _p, _c_int, _c_int, _c_int, _c_int,
                                      _c_int, _p]),
     "skv_kv_page_convert": (_c_int, [_p, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -136,7 +142,8 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
                       layout="standard", k_scale=None, v_scale=None, causal=1,
                       part_o=None, part_lse=None, out=None, out_lse=None,
                       page_size=16, stream=None):
-    """Enqueue segment attention + split reduce; returns (out bf16, out_lse or None).
+    """Enqueue segment attention + split reduce; returns (out, out_lse or None);
+    q and out are fp16 with kv_dtype="fp16", else bf16.
 
     plan=None selects the fixed split (no plan launch); tok_nseg is then
     written by the segment kernel (allocated when None)."""
@@ -150,10 +157,11 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
         part_o = torch.empty(rows * head_dim, dtype=torch.float32, device=dev)
     if part_lse is None:
         part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
+    iot = io_dtype(kv_dtype)
     if out is None:
-        out = torch.empty((total_q, q_heads, head_dim), dtype=torch.bfloat16, device=dev)
-    _need(q, torch.bfloat16, "q")
-    _need(out, torch.bfloat16, "out", total_q * q_heads * head_dim)
+        out = torch.empty((total_q, q_heads, head_dim), dtype=iot, device=dev)
+    _need(q, iot, "q")
+    _need(out, iot, "out", total_q * q_heads * head_dim)
     _need(part_o, torch.float32, "part_o", rows * head_dim)
     _need(part_lse, torch.float32, "part_lse", rows)
     _need(page_table, torch.int32, "page_table")
@@ -186,7 +194,7 @@ def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_ns
     if plan is None and tok_nseg is None:
         tok_nseg = torch.empty(total_q, dtype=torch.int32, device=q.device)
     rows = total_q * q_heads * seg_max
-    _need(q, torch.bfloat16, "q")
+    _need(q, io_dtype(kv_dtype), "q")
     _need(part_o, torch.float32, "part_o", rows * head_dim)
     _need(part_lse, torch.float32, "part_lse", rows)
     _need(page_table, torch.int32, "page_table")
@@ -204,18 +212,20 @@ def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_ns
 
 
 def split_reduce(part_o, part_lse, tok_nseg, *, total_q, q_heads, seg_max, head_dim=128,
-                 out=None, out_lse=None, stream=None):
+                 out=None, out_lse=None, out_dtype="bf16", stream=None):
+    """LSE merge of the partials; out bf16 (out_dtype "bf16") or fp16 ("fp16")."""
     dev = part_o.device
+    iot = io_dtype(out_dtype)
     if out is None:
-        out = torch.empty((total_q, q_heads, head_dim), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((total_q, q_heads, head_dim), dtype=iot, device=dev)
     rows = total_q * q_heads * seg_max
     _need(part_o, torch.float32, "part_o", rows * head_dim)
     _need(part_lse, torch.float32, "part_lse", rows)
     _need(tok_nseg, torch.int32, "tok_nseg", total_q)
-    _need(out, torch.bfloat16, "out", total_q * q_heads * head_dim)
+    _need(out, iot, "out", total_q * q_heads * head_dim)
     st = load().skv_split_reduce(_ptr(part_o), _ptr(part_lse), _ptr(tok_nseg), total_q,
-                                 q_heads, head_dim, seg_max, _ptr(out), _ptr(out_lse),
-                                 _stream(stream))
+                                 q_heads, head_dim, seg_max, KV_DTYPE[out_dtype], _ptr(out),
+                                 _ptr(out_lse), _stream(stream))
     _check(st, "skv_split_reduce")
     return out, out_lse
 

@@ -116,18 +116,18 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                             stream);
   if (st != SKV_OK) return st;
   return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads,
-                            seg_max, out, out_lse, stream);
+                            seg_max, kv_dtype == SKV_KV_FP16, out, out_lse, stream);
 }
 
 int skv_split_reduce(const float* part_o, const float* part_lse,
                      const int32_t* tok_nseg, int total_q, int q_heads,
-                     int head_dim, int seg_max, void* out, float* out_lse,
-                     void* stream) {
+                     int head_dim, int seg_max, int out_dtype, void* out,
+                     float* out_lse, void* stream) {
   int st = skv::check_reduce_args(part_o, part_lse, tok_nseg, total_q, q_heads,
-                                  head_dim, seg_max, out);
+                                  head_dim, seg_max, out_dtype, out);
   if (st != SKV_OK) return st;
   return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads,
-                            seg_max, out, out_lse, stream);
+                            seg_max, out_dtype == SKV_KV_FP16, out, out_lse, stream);
 }
 
 int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,

@@ -11,9 +11,10 @@
 
 namespace skv {
 
-int launch_segments_mfma(const SegParams& sp, bool shuf, int grid, hipStream_t st);
-int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st);
-int launch_segments_mfma_priv(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
+int launch_segments_mfma(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st);
+int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st);
+int launch_segments_mfma_priv(const SegParams& sp, int e, bool f16, bool shuf, int max_rows,
+                              int grid,
                               hipStream_t st);
 
 // Which kernel runs, by element type and query rows (GQA group x max query
@@ -27,6 +28,7 @@ int launch_segments_mfma_priv(const SegParams& sp, int e, bool shuf, int max_row
 //    idle, need;
 //  * bf16, 33-64 rows: matrix cores on a ring shared by 8 waves (four row
 //    tiles per block do not fit two waves per SIMD in private form).
+// fp16 KV (with fp16 Q) takes the bf16 routes with the fp16 instructions.
 constexpr int kValuMaxRows = 4;
 constexpr int kPrivMaxRowsBf16 = 32;
 
@@ -64,14 +66,15 @@ int launch_segments(const AttnArgs& a, void* stream) {
   }
   if (grid > 0x7fffffffLL) return SKV_EUNSUPPORTED;
   const int e = a.kv_dtype == SKV_KV_FP8_E4M3FN ? 1 : 2;
+  const bool f16 = a.kv_dtype == SKV_KV_FP16;      // fp16 Q and KV (else bf16 Q)
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
   const int rows = sp.G * a.max_q;
   auto st = static_cast<hipStream_t>(stream);
   if (e == 2 && rows <= kValuMaxRows)
-    return launch_segments_valu(sp, shuf, static_cast<int>(grid), st);
+    return launch_segments_valu(sp, shuf, f16, static_cast<int>(grid), st);
   if (e == 1 || rows <= kPrivMaxRowsBf16)
-    return launch_segments_mfma_priv(sp, e, shuf, rows, static_cast<int>(grid), st);
-  return launch_segments_mfma(sp, shuf, static_cast<int>(grid), st);
+    return launch_segments_mfma_priv(sp, e, f16, shuf, rows, static_cast<int>(grid), st);
+  return launch_segments_mfma(sp, shuf, f16, static_cast<int>(grid), st);
 }
 
 }  // namespace skv

@@ -69,6 +69,67 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 w) {
   return make_uint4(a.x, a.y, b.x, b.y);
 }
 
+// ---- the 16-bit element type of Q, K, V and P: bf16, or IEEE fp16 (F16) with
+// an fp16 cache. Operands travel as raw 16-bit patterns; these helpers pick
+// the instruction. ----
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// D(16x16) += A(16x32) B(32x16), fp32 accumulate
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma_k32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x16) B(16x16), fp32 accumulate
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma_k16(i16x4_t a, i16x4_t b, f32x4_t c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// two fp32 -> a packed pair, round to nearest even
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  if constexpr (F16) {
+    const f16x2_t v = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
+}
+
+// a.x * b.x + a.y * b.y + c over packed pairs, fp32 accumulate
+template <bool F16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  c, false);
+  else
+    return dot2_bf16(a, b, c);
+}
+
+// the low / high element of a packed pair, widened exactly to fp32
+template <bool F16>
+__device__ __forceinline__ float elem_lo(uint32_t w) {
+  if constexpr (F16) return static_cast<float>(__builtin_bit_cast(f16x2_t, w).x);
+  else return bf16_lo(w);
+}
+template <bool F16>
+__device__ __forceinline__ float elem_hi(uint32_t w) {
+  if constexpr (F16) return static_cast<float>(__builtin_bit_cast(f16x2_t, w).y);
+  else return bf16_hi(w);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));

@@ -170,7 +170,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
   }
 }
 
-template <int E, bool SHUF, int NRT>
+template <int E, bool SHUF, int NRT, bool F16>
 __global__ __launch_bounds__((64 * Ring<E, NRT>::kWaves))
 __attribute__((amdgpu_waves_per_eu((Ring<E, NRT>::kWaves / 4), (Ring<E, NRT>::kWaves / 4))))
 void seg_mfma_kernel(SegParams p) {
@@ -312,7 +312,7 @@ void seg_mfma_kernel(SegParams p) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[kk], acc, 0, 0, 0);
+        acc = mfma_k32<F16>(kop[kk], qb[kk], acc);
       sacc[pg] = acc;
     }
 
@@ -342,7 +342,7 @@ void seg_mfma_kernel(SegParams p) {
     for (int e = 0; e < 8; e += 2) {
       const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
       l += a + b;
-      pk[e >> 1] = pack_bf16x2(a, b);
+      pk[e >> 1] = pack2<F16>(a, b);
     }
     const bf16x8_t pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
@@ -403,8 +403,7 @@ void seg_mfma_kernel(SegParams p) {
           w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
         }
       }
-      oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, oacc[dt], 0, 0, 0);
+      oacc[dt] = mfma_k32<F16>(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, oacc[dt]);
     }
   }
 
@@ -466,16 +465,21 @@ void seg_mfma_kernel(SegParams p) {
 
 }  // namespace
 
-// bf16 KV with 33-64 rows (four row tiles); the other cases run on the
-// private-ring variants
-int launch_segments_mfma(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
+template <bool F16>
+int launch_shared(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
   if (shuf)
-    hipLaunchKernelGGL((seg_mfma_kernel<2, true, 4>), dim3(grid),
+    hipLaunchKernelGGL((seg_mfma_kernel<2, true, 4, F16>), dim3(grid),
                        dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_mfma_kernel<2, false, 4>), dim3(grid),
+    hipLaunchKernelGGL((seg_mfma_kernel<2, false, 4, F16>), dim3(grid),
                        dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+// bf16 or fp16 KV with 33-64 rows (four row tiles); the other cases run on the
+// private-ring variants
+int launch_segments_mfma(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st) {
+  return f16 ? launch_shared<true>(sp, shuf, grid, st) : launch_shared<false>(sp, shuf, grid, st);
 }
 
 }  // namespace skv

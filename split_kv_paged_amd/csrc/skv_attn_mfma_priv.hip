@@ -1,5 +1,6 @@
 // Segment attention, matrix-core variants with private per-wave rings: fp8 KV
-// (32-token block slots) and bf16 KV with up to 32 rows (16-token page slots);
+// (32-token block slots) and bf16 or fp16 KV with up to 32 rows (16-token page
+// slots);
 // query rows = GQA group x query tokens, padded to 16-row tiles.
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
@@ -505,7 +506,7 @@ constexpr int kPage2 = 2 * kHalf2;
 constexpr int kPageInstr2 = kPage2 / 1024;
 constexpr int kStdTile2 = kPageSize * 2 * kD * 2;
 constexpr int kStdRow2 = 2 * kD * 2;
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef i16x4_t v4i16_t;
 
 template <int NW, int NRT>
 struct PRing2 {
@@ -546,7 +547,7 @@ __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& i
   }
 }
 
-template <bool SHUF, int NRT, int NW>
+template <bool SHUF, int NRT, int NW, bool F16>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_mfma_priv2_kernel(SegParams p) {
   using R = PRing2<NW, NRT>;
@@ -636,7 +637,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[kk], qb[t][kk], acc, 0, 0, 0);
+        acc = mfma_k32<F16>(kop[kk], qb[t][kk], acc);
       // online softmax: this lane holds tokens 4*j4 .. +3 of row 16t + r16
       float s[4];
       float bm = -INFINITY;
@@ -660,7 +661,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
       const float a0 = fast_exp2(s[0] - mu), a1 = fast_exp2(s[1] - mu);
       const float a2 = fast_exp2(s[2] - mu), a3 = fast_exp2(s[3] - mu);
       l[t] += (a0 + a1) + (a2 + a3);
-      pb[t] = __builtin_bit_cast(v4i16_t, make_uint2(pack_bf16x2(a0, a1), pack_bf16x2(a2, a3)));
+      pb[t] = __builtin_bit_cast(v4i16_t, make_uint2(pack2<F16>(a0, a1), pack2<F16>(a2, a3)));
     }
 
     // ---- O^T += V^T.P^T over the page's 16 tokens ----
@@ -688,7 +689,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
       const v4i16_t vop = __builtin_bit_cast(v4i16_t, w);
 #pragma unroll
       for (int t = 0; t < NRT; ++t)
-        oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pb[t], oacc[t][dt], 0, 0, 0);
+        oacc[t][dt] = mfma_k16<F16>(vop, pb[t], oacc[t][dt]);
     }
   }
 
@@ -711,24 +712,31 @@ int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
-// bf16 with up to two row tiles (four would not fit two waves per SIMD)
-template <bool SHUF>
-int launch_priv2(const SegParams& sp, int nrt, int grid, hipStream_t st) {
+// bf16 or fp16 with up to two row tiles (four would not fit two waves per SIMD)
+template <bool SHUF, bool F16>
+int launch_priv2_t(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   if (nrt > 2) return SKV_EUNSUPPORTED;
   if (nrt <= 1)
-    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 1, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 1, 8, F16>), dim3(grid), dim3(64 * 8), 0, st,
+                       sp);
   else
-    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 2, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 2, 8, F16>), dim3(grid), dim3(64 * 8), 0, st,
+                       sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
 }  // namespace
 
-int launch_segments_mfma_priv(const SegParams& sp, int e, bool shuf, int max_rows, int grid,
-                              hipStream_t st) {
+int launch_segments_mfma_priv(const SegParams& sp, int e, bool f16, bool shuf, int max_rows,
+                              int grid, hipStream_t st) {
   const int nrt = (max_rows + 15) / 16;
-  if (e == 2)
-    return shuf ? launch_priv2<true>(sp, nrt, grid, st) : launch_priv2<false>(sp, nrt, grid, st);
+  if (e == 2) {
+    if (f16)
+      return shuf ? launch_priv2_t<true, true>(sp, nrt, grid, st)
+                  : launch_priv2_t<false, true>(sp, nrt, grid, st);
+    return shuf ? launch_priv2_t<true, false>(sp, nrt, grid, st)
+                : launch_priv2_t<false, false>(sp, nrt, grid, st);
+  }
   return shuf ? launch_priv<true>(sp, nrt, grid, st) : launch_priv<false>(sp, nrt, grid, st);
 }
 

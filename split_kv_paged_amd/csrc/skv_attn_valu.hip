@@ -1,5 +1,6 @@
-// Segment attention, vector-ALU variant: bf16 KV with at most 4 query rows
-// (GQA group x query tokens), too few to fill a 16-row matrix-core tile.
+// Segment attention, vector-ALU variant: bf16 or fp16 KV (F16: fp16 Q and
+// KV) with at most 4 query rows (GQA group x query tokens), too few to fill a
+// 16-row matrix-core tile.
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Motivation and Modifications: one work-group per
@@ -121,7 +122,7 @@ __device__ __forceinline__ float max_over_tokens(float v) {
   return v;
 }
 
-template <bool SHUF, int NW>
+template <bool SHUF, int NW, bool F16>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_valu_kernel(SegParams p) {
   using R = VRing<NW>;
@@ -216,10 +217,10 @@ void seg_valu_kernel(SegParams p) {
       float a = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        a = dot2_bf16(kw[u].x, qr[r][u].x, a);
-        a = dot2_bf16(kw[u].y, qr[r][u].y, a);
-        a = dot2_bf16(kw[u].z, qr[r][u].z, a);
-        a = dot2_bf16(kw[u].w, qr[r][u].w, a);
+        a = dot2<F16>(kw[u].x, qr[r][u].x, a);
+        a = dot2<F16>(kw[u].y, qr[r][u].y, a);
+        a = dot2<F16>(kw[u].z, qr[r][u].z, a);
+        a = dot2<F16>(kw[u].w, qr[r][u].w, a);
       }
       a += dpp<kDppQuadXor1>(a);
       a += dpp<kDppQuadXor2>(a);
@@ -247,11 +248,15 @@ void seg_valu_kernel(SegParams p) {
         float* dst = reinterpret_cast<float*>(pw) + tq * RM;
         *reinterpret_cast<float4*>(dst) = make_float4(s[0], s[1], s[2], s[3]);
       }
-    } else {                                   // p[r][tau] bf16; quarter qq: row qq
+    } else {                                   // p[r][tau] 16-bit; quarter qq: row qq
 #pragma unroll
       for (int r = 0; r < RM; ++r)
-        if ((r & 3) == qq)
-          *reinterpret_cast<__bf16*>(pw + (r * 16 + tq) * 2) = static_cast<__bf16>(s[r]);
+        if ((r & 3) == qq) {
+          if constexpr (F16)
+            *reinterpret_cast<_Float16*>(pw + (r * 16 + tq) * 2) = static_cast<_Float16>(s[r]);
+          else
+            *reinterpret_cast<__bf16*>(pw + (r * 16 + tq) * 2) = static_cast<__bf16>(s[r]);
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -267,8 +272,9 @@ void seg_valu_kernel(SegParams p) {
         const int tau = tp + kPh * u;
         uint4 v = *reinterpret_cast<const uint4*>(sV + tau * (kD * 2) + c * 16);
         if (tail && tau >= vend) v = make_uint4(0, 0, 0, 0);
-        const float x[kAcc] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                               bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float x[kAcc] = {elem_lo<F16>(v.x), elem_hi<F16>(v.x), elem_lo<F16>(v.y),
+                               elem_hi<F16>(v.y), elem_lo<F16>(v.z), elem_hi<F16>(v.z),
+                               elem_lo<F16>(v.w), elem_hi<F16>(v.w)};
         const float4 pv = *reinterpret_cast<const float4*>(
             reinterpret_cast<const float*>(pw) + tau * RM);
         const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
@@ -300,10 +306,10 @@ void seg_valu_kernel(SegParams p) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             float a = acc[r][h];
-            a = dot2_bf16(vv[h].x, pp.x, a);
-            a = dot2_bf16(vv[h].y, pp.y, a);
-            a = dot2_bf16(vv[h].z, pp.z, a);
-            a = dot2_bf16(vv[h].w, pp.w, a);
+            a = dot2<F16>(vv[h].x, pp.x, a);
+            a = dot2<F16>(vv[h].y, pp.y, a);
+            a = dot2<F16>(vv[h].z, pp.z, a);
+            a = dot2<F16>(vv[h].w, pp.w, a);
             acc[r][h] = a;
           }
         }
@@ -385,12 +391,17 @@ void seg_valu_kernel(SegParams p) {
 
 }  // namespace
 
-int launch_segments_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
+template <bool F16>
+int launch_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
   if (shuf)
-    hipLaunchKernelGGL((seg_valu_kernel<true, 4>), dim3(grid), dim3(64 * 4), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16>), dim3(grid), dim3(64 * 4), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_valu_kernel<false, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<false, 8, F16>), dim3(grid), dim3(64 * 8), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st) {
+  return f16 ? launch_valu<true>(sp, shuf, grid, st) : launch_valu<false>(sp, shuf, grid, st);
 }
 
 }  // namespace skv

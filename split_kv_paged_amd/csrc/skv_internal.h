@@ -37,7 +37,7 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     const void* out);
 int check_reduce_args(const void* part_o, const void* part_lse,
                       const void* tok_nseg, int total_q, int q_heads,
-                      int head_dim, int seg_max, const void* out);
+                      int head_dim, int seg_max, int out_dtype, const void* out);
 int check_shuffle_args(const void* std_cache, const void* k_plane,
                        const void* v_plane, int num_blocks, int kv_heads,
                        int page_size, int head_dim, int elem_bytes);
@@ -98,7 +98,7 @@ int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
 int launch_segments(const AttnArgs& a, void* stream);
 int launch_reduce(const float* part_o, const float* part_lse,
                   const int32_t* tok_nseg, int total_q, int q_heads,
-                  int seg_max, void* out, float* out_lse, void* stream);
+                  int seg_max, bool out_f16, void* out, float* out_lse, void* stream);
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
                    int page_size, int elem_bytes, void* stream);

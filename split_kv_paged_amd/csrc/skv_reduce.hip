@@ -9,7 +9,7 @@
 //
 // MI355X design: one wave64 per (token, q head); lane l owns channels 2l and
 // 2l+1 (float2 loads, 512 contiguous bytes per segment); the segment weights
-// are formed in fp32 registers, the output rounded to bf16 (RNE). Traffic is
+// are formed in fp32 registers, the output rounded to bf16 or fp16 (RNE). Traffic is
 // tiny next to the KV stream, so this kernel is latency-, not
 // bandwidth-, shaped.
 #include <hip/hip_runtime.h>
@@ -32,6 +32,7 @@ __device__ __forceinline__ unsigned short f32_to_bf16_rne(float f) {
   return static_cast<unsigned short>(u >> 16);
 }
 
+template <bool F16>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
     const int32_t* __restrict__ tok_nseg, int total_q, int q_heads, int seg_max,
@@ -109,8 +110,15 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
       }
     }
   }
-  const unsigned int packed = static_cast<unsigned int>(f32_to_bf16_rne(acc.x)) |
-                              (static_cast<unsigned int>(f32_to_bf16_rne(acc.y)) << 16);
+  unsigned int packed;
+  if constexpr (F16) {      // v_cvt_pk_f16_f32: round to nearest even, overflow to inf
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    const f16x2_t h = {static_cast<_Float16>(acc.x), static_cast<_Float16>(acc.y)};
+    packed = __builtin_bit_cast(unsigned int, h);
+  } else {
+    packed = static_cast<unsigned int>(f32_to_bf16_rne(acc.x)) |
+             (static_cast<unsigned int>(f32_to_bf16_rne(acc.y)) << 16);
+  }
   reinterpret_cast<unsigned int*>(out + row * kHeadDim)[lane] = packed;
   if (out_lse && lane == 0) out_lse[row] = lse;
 }
@@ -119,14 +127,20 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
 
 int launch_reduce(const float* part_o, const float* part_lse,
                   const int32_t* tok_nseg, int total_q, int q_heads,
-                  int seg_max, void* out, float* out_lse, void* stream) {
+                  int seg_max, bool out_f16, void* out, float* out_lse, void* stream) {
   const long long rows = static_cast<long long>(total_q) * q_heads;
   const long long blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
-  hipLaunchKernelGGL(reduce_kernel, dim3(static_cast<unsigned>(blocks)),
-                     dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream),
-                     part_o, part_lse, tok_nseg, total_q, q_heads, seg_max,
-                     static_cast<unsigned short*>(out), out_lse);
+  if (out_f16)
+    hipLaunchKernelGGL(reduce_kernel<true>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream),
+                       part_o, part_lse, tok_nseg, total_q, q_heads, seg_max,
+                       static_cast<unsigned short*>(out), out_lse);
+  else
+    hipLaunchKernelGGL(reduce_kernel<false>, dim3(static_cast<unsigned>(blocks)),
+                       dim3(kReduceThreads), 0, static_cast<hipStream_t>(stream),
+                       part_o, part_lse, tok_nseg, total_q, q_heads, seg_max,
+                       static_cast<unsigned short*>(out), out_lse);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 

@@ -32,7 +32,7 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
     return SKV_EINVAL;
   if (layout != SKV_LAYOUT_STANDARD && layout != SKV_LAYOUT_SHUFFLED)
     return SKV_EINVAL;
-  if (kv_dtype != SKV_KV_BF16 && kv_dtype != SKV_KV_FP8_E4M3FN)
+  if (kv_dtype != SKV_KV_BF16 && kv_dtype != SKV_KV_FP8_E4M3FN && kv_dtype != SKV_KV_FP16)
     return SKV_EINVAL;
   if ((layout == SKV_LAYOUT_SHUFFLED) != (kv_b != nullptr)) return SKV_EINVAL;
   const bool fp8 = kv_dtype == SKV_KV_FP8_E4M3FN;
@@ -52,8 +52,9 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
 
 int check_reduce_args(const void* part_o, const void* part_lse,
                       const void* tok_nseg, int total_q, int q_heads,
-                      int head_dim, int seg_max, const void* out) {
+                      int head_dim, int seg_max, int out_dtype, const void* out) {
   if (!part_o || !part_lse || !tok_nseg || !out) return SKV_EINVAL;
+  if (out_dtype != SKV_KV_BF16 && out_dtype != SKV_KV_FP16) return SKV_EINVAL;
   if (total_q < 1 || q_heads < 1 || head_dim < 1) return SKV_EINVAL;
   if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
   if (head_dim != kHeadDim) return SKV_EUNSUPPORTED;

@@ -84,12 +84,13 @@ def _attn(**kw):
     (dict(plan=None, tok=None), 1),                       # the fixed split writes tok_nseg
     (dict(plan=None, head_dim=64), 2),
     (dict(seq_lens=None), 1), (dict(cu=None), 1),
-    (dict(layout=2), 1), (dict(kv_dtype=2), 1),
+    (dict(layout=2), 1), (dict(kv_dtype=3), 1), (dict(kv_dtype=-1), 1),
     (dict(layout=1), 1),                                  # shuffled needs the V plane
     (dict(kv_b=P), 1),                                    # standard takes no V plane
     (dict(kv_dtype=1), 1),                                # fp8 needs scales
     (dict(k_scale=P, v_scale=P), 1),                      # bf16 takes none
     (dict(kv_dtype=1, k_scale=P), 1),
+    (dict(kv_dtype=2, k_scale=P, v_scale=P), 1),          # fp16 takes none
     (dict(q_heads=12, kv_heads=8), 1), (dict(bs=0), 1), (dict(bs=40000), 1),
     (dict(total_q=0), 1), (dict(max_q=0), 1), (dict(seg_max=0), 1), (dict(seg_max=70000), 1),
     (dict(pt_stride=0), 1), (dict(num_cus=0), 1), (dict(kv_heads=0), 1),
@@ -102,16 +103,17 @@ def test_attn_errors(kw, code):
 
 
 def _reduce(**kw):
-    a = dict(po=P, pl=P, tok=P, total_q=2, q_heads=8, head_dim=128, seg_max=64, out=P)
+    a = dict(po=P, pl=P, tok=P, total_q=2, q_heads=8, head_dim=128, seg_max=64, odt=0, out=P)
     a.update(kw)
     return skv.load().skv_split_reduce(a["po"], a["pl"], a["tok"], a["total_q"], a["q_heads"],
-                                       a["head_dim"], a["seg_max"], a["out"], None, None)
+                                       a["head_dim"], a["seg_max"], a["odt"], a["out"], None,
+                                       None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(po=None), 1), (dict(pl=None), 1), (dict(tok=None), 1), (dict(out=None), 1),
     (dict(total_q=0), 1), (dict(q_heads=0), 1), (dict(seg_max=0), 1), (dict(seg_max=65536), 1),
-    (dict(head_dim=64), 2),
+    (dict(head_dim=64), 2), (dict(odt=1), 1), (dict(odt=3), 1), (dict(odt=-1), 1),
 ])
 def test_reduce_errors(kw, code):
     assert _reduce(**kw) == code

@@ -150,7 +150,7 @@ def _mk(name, lens, ql, hq, hkv, dt, layout, causal, ncu, smax, seed=5, poison="
     base = configs.FP8_KV if dt == "fp8" else configs.TINY
     cfg = gen.small_config(base, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
                            causal=causal, num_cus=ncu, seg_max=smax, seed=seed,
-                           page_size=page_size)
+                           page_size=page_size, kv_dtype=dt)
     return gen.make_case(cfg, DEV, poison=poison)
 
 
@@ -227,6 +227,71 @@ def test_plan_bit_exact_fuzz_32_token_pages():
         wp, wt = oracle.plan_segments(lens.tolist(), cu_h, kvh, 32, ncu, smax, causal)
         assert plan.cpu().tolist() == wp, (trial, bs, kvh, ncu, smax)
         assert tok.cpu().tolist() == wt, trial
+
+
+# fp16 Q and KV: every 16-bit kernel route (vector ALU up to 4 rows, private
+# rings up to 32, shared ring up to 64), both layouts
+FP16_CASES = [
+    ("f16_valu_std", [7, 300, 5000, 33, 0], [1, 1, 1, 1, 1], 2, 2, "fp16", "standard", 1, 64, 16),
+    ("f16_valu_q3", [50, 700, 3, 129], [3, 3, 2, 1], 2, 2, "fp16", "standard", 1, 32, 64),
+    ("f16_valu_shuf_tails", [15, 31, 33, 1023], [1, 1, 1, 1], 32, 8, "fp16", "shuffled", 1, 128, 64),
+    ("f16_rows8_ragged", [1, 5, 17, 300, 1000], [2, 2, 1, 2, 2], 8, 2, "fp16", "standard", 1, 64, 8),
+    ("f16_rows32_shuf", [3, 40, 777, 2500], [4, 2, 4, 3], 16, 2, "fp16", "shuffled", 1, 32, 64),
+    ("f16_rows64", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "fp16", "standard", 1, 64, 64),
+    ("f16_rows64_shuf", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "fp16", "shuffled", 1, 64, 64),
+    ("f16_noncausal", [3, 60, 2000], [4, 4, 4], 32, 2, "fp16", "standard", 0, 48, 64),
+]
+
+
+@pytest.mark.parametrize("spec", FP16_CASES, ids=lambda c: c[0])
+@pytest.mark.parametrize("fixed", [False, True], ids=["planned", "fixed"])
+@pytest.mark.parametrize("page_size", [16, 32])
+def test_fp16_matches_oracle(spec, fixed, page_size):
+    say("fp16", spec[0], fixed, page_size)
+    case = _mk(*spec, page_size=page_size)
+    cfg = case.cfg
+    hip = run_hip(case, fixed=fixed)
+    if fixed:
+        _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                                 cfg.kv_heads, page_size, cfg.num_cus,
+                                                 cfg.seg_max, cfg.causal)
+        assert hip["tok"] == want_tok
+    else:
+        wp, wt = oracle_plan(case)
+        assert hip["plan"] == wp and hip["tok"] == wt
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, cfg.kv_dtype)
+    say(spec[0], r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3, r
+
+
+@pytest.mark.parametrize("qmul", [6.0, 24.0])
+@pytest.mark.parametrize("spec", [c for c in FP16_CASES if c[0] in ("f16_valu_q3", "f16_rows8_ragged",
+                                                                    "f16_rows64")],
+                         ids=lambda c: c[0])
+def test_fp16_sharp_scores_match_oracle(spec, qmul):
+    """fp16 weights underflow below 2^-24 where bf16 ones would not: sharp
+    scores check that this changes nothing beyond the bar."""
+    case = _mk(*spec)
+    case.q.copy_((case.q.float() * qmul).to(torch.float16))
+    hip = run_hip(case)
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, "fp16")
+    say(spec[0], qmul, r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["lse_err"] <= 1e-3 * max(1.0, float(np.abs(ref_lse[np.isfinite(ref_lse)]).max())), r
+
+
+@pytest.mark.parametrize("spec", [c for c in FP16_CASES if c[0] in ("f16_valu_shuf_tails",
+                                                                    "f16_rows8_ragged",
+                                                                    "f16_rows64_shuf")],
+                         ids=lambda c: c[0])
+def test_fp16_nan_poison_does_not_leak(spec):
+    a = run_hip(_mk(*spec, poison="finite"))
+    b = run_hip(_mk(*spec, poison="nan"))
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.all(np.isfinite(b["out"]))
 
 
 FIXED_CASES = CASES + [
@@ -362,8 +427,9 @@ def test_fp8_codes_decode_exactly():
             assert np.array_equal(hip["out"][i, h], want[i]), (i, h)
 
 
+@pytest.mark.parametrize("out_dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("smax", [7, 64, 100])
-def test_split_reduce_alone(smax):
+def test_split_reduce_alone(smax, out_dtype):
     """Both merge paths: up to 64 segments (one per lane) and more."""
     rng = np.random.default_rng(3 + smax)
     total_q, hq, D = 9, 4, 128
@@ -376,9 +442,10 @@ def test_split_reduce_alone(smax):
     out, lse = skv.split_reduce(torch.as_tensor(po.reshape(-1), device=DEV),
                                 torch.as_tensor(pl.reshape(-1), device=DEV),
                                 torch.as_tensor(nseg, device=DEV), total_q=total_q,
-                                q_heads=hq, seg_max=smax,
+                                q_heads=hq, seg_max=smax, out_dtype=out_dtype,
                                 out_lse=torch.empty(total_q * hq, device=DEV))
     torch.cuda.synchronize()
+    assert out.dtype == (torch.float16 if out_dtype == "fp16" else torch.bfloat16)
     out = out.float().cpu().numpy()
     lse = lse.cpu().numpy().reshape(total_q, hq)
     for t in range(total_q):

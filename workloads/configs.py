@@ -38,7 +38,7 @@ class Config:
     kv_heads: int
     head_dim: int = 128
     page_size: int = 16
-    kv_dtype: str = "bf16"          # "bf16" or "fp8" (OCP e4m3fn codes)
+    kv_dtype: str = "bf16"          # "bf16", "fp16" or "fp8" (OCP e4m3fn codes)
     layout: str = "standard"        # "standard" [H,N,2D] or "shuffled" planes
     num_cus: int = 256
     seg_max: int = 64
@@ -96,5 +96,10 @@ AGENTIC_SKEW_FP8 = Config("agentic_skew_fp8", SKEW_LENS, SKEW_Q, 32, 2, kv_dtype
                           k_scale=0.0173, v_scale=0.0211, seed=7,
                           note="bs=20, 2.32M tokens, lognormal + {0,1,5,17,248k}, q 1..4, "
                                "e4m3fn KV")
-EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8]
+# the uniform verify batch with an fp16 cache and fp16 queries (the RFC's
+# decoder scope is BF16/FP16)
+UNIFORM_VERIFY_FP16 = Config("uniform_verify_fp16", [119_000] * 16, [4] * 16, 32, 2,
+                             kv_dtype="fp16", seed=8,
+                             note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), fp16 Q and KV")
+EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, UNIFORM_VERIFY_FP16]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
