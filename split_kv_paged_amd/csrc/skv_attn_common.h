@@ -221,12 +221,14 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   return it;
 }
 
-// Pages hold 16 or 32 tokens; the kernels stream 16-token sub-pages (a
-// 32-token page holds two: its tokens 0-15 and 16-31). Sub-page v of a
-// sequence (its tokens 16v .. 16v + 15) lies in page table entry v >> (shift
-// - 4), as sub-page v & 1 of a 32-token page.
-__device__ __forceinline__ int sub_of(const SegParams& p, int v) {
-  return v & ((1 << (p.page_shift - 4)) - 1);
+// Pages hold 16 or 32 tokens (PSH = log2 of the page size, a template
+// argument of every attention kernel); the kernels stream 16-token sub-pages
+// (a 32-token page holds two: its tokens 0-15 and 16-31). Sub-page v of a
+// sequence (its tokens 16v .. 16v + 15) lies in page-table entry v >> (PSH - 4),
+// as sub-page v & 1 of a 32-token page.
+template <int PSH>
+__device__ __forceinline__ int sub_of(int v) {
+  return v & ((1 << (PSH - 4)) - 1);
 }
 
 // Addresses of one sub-page of kv head g in page pid, element size E bytes.
@@ -241,23 +243,24 @@ struct SubPageAddr {
   const uint8_t* v;
 };
 
-template <int E, bool SHUF>
+template <int E, bool SHUF, int PSH>
 __device__ __forceinline__ SubPageAddr sub_page(const SegParams& p, int g, int pid, int sub) {
   const size_t head = static_cast<size_t>(pid) * p.Hkv + g;
   constexpr size_t kHalf16 = static_cast<size_t>(kPageSize) * kHeadDim * E;   // 16 tokens' K or V
   if constexpr (SHUF) {
-    const size_t plane = (head * kHalf16) << (p.page_shift - 4);
+    const size_t plane = (head * kHalf16) << (PSH - 4);
     return {p.kv_a + plane + static_cast<size_t>(sub) * kPageSize * 16,
             p.kv_b + plane + static_cast<size_t>(sub) * kHalf16};
   } else {
-    const uint8_t* t = p.kv_a + (((head << (p.page_shift - 4)) + sub) * 2 * kHalf16);
+    const uint8_t* t = p.kv_a + (((head << (PSH - 4)) + sub) * 2 * kHalf16);
     return {t, t};
   }
 }
 
 // bytes between consecutive 16-byte chunk rows of a K-plane tile: P tokens x 16 B
-__device__ __forceinline__ int kplane_row_bytes(const SegParams& p) {
-  return 16 << p.page_shift;
+template <int PSH>
+constexpr int kplane_row_bytes() {
+  return 16 << PSH;
 }
 
 // Last key (exclusive) row n may see inside the segment: the bottom-right

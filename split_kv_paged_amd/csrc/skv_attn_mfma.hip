@@ -116,19 +116,19 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
 // Sub-pages past the segment end are read from the segment's first sub-page
 // (same instruction count keeps vmcnt exact; their tokens are masked and
 // zeroed).
-template <int E, bool SHUF, int NRT>
+template <int E, bool SHUF, int NRT, int PSH>
 __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& it,
                                             const int* pids, const int* subs, uint8_t* slot,
                                             int wave, int lane) {
   using R = Ring<E, NRT>;
   const int r16 = lane & 15, j4 = lane >> 4;
-  const int krow = kplane_row_bytes(p);
+  const int krow = kplane_row_bytes<PSH>();
 #pragma unroll
   for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
     const int u = wave * R::kUnitsPerWave + uw;
     const int pg = u >> 1;
     const bool vhalf = u & 1;
-    const SubPageAddr a = sub_page<E, SHUF>(p, it.g, pids[uw], subs[uw]);
+    const SubPageAddr a = sub_page<E, SHUF, PSH>(p, it.g, pids[uw], subs[uw]);
     uint8_t* dst = slot + (2 * pg + (vhalf ? 1 : 0)) * R::kUnitBytes;
     if (!vhalf) {
       const uint8_t* tile = a.k;
@@ -170,7 +170,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
   }
 }
 
-template <int E, bool SHUF, int NRT, bool F16>
+template <int E, bool SHUF, int NRT, bool F16, int PSH>
 __global__ __launch_bounds__((64 * Ring<E, NRT>::kWaves))
 __attribute__((amdgpu_waves_per_eu((Ring<E, NRT>::kWaves / 4), (Ring<E, NRT>::kWaves / 4))))
 void seg_mfma_kernel(SegParams p) {
@@ -212,7 +212,7 @@ void seg_mfma_kernel(SegParams p) {
 
   // page ids and sub-pages of this wave's units for a stage (sub-pages past
   // the end -> the segment's first)
-  const int psh = p.page_shift - 4;
+  constexpr int psh = PSH - 4;
   auto load_pids = [&](int st, int* out) {
 #pragma unroll
     for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
@@ -224,7 +224,7 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
     for (int uw = 0; uw < R::kUnitsPerWave; ++uw) {
       const int pg = st * R::kPages + ((wave * R::kUnitsPerWave + uw) >> 1);
-      out[uw] = sub_of(p, seg_page0 + (pg < seg_pages ? pg : 0));
+      out[uw] = sub_of<PSH>(seg_page0 + (pg < seg_pages ? pg : 0));
     }
   };
 
@@ -259,7 +259,7 @@ void seg_mfma_kernel(SegParams p) {
       int pids[R::kUnitsPerWave], subs[R::kUnitsPerWave];
       load_pids(s, pids);
       stage_subs(s, subs);
-      issue_stage<E, SHUF, NRT>(p, it, pids, subs, ring + s * R::kStageBytes, wave, lane);
+      issue_stage<E, SHUF, NRT, PSH>(p, it, pids, subs, ring + s * R::kStageBytes, wave, lane);
     }
   }
   if (kNS - 1 < nst) load_pids(kNS - 1, pid_next);
@@ -279,7 +279,7 @@ void seg_mfma_kernel(SegParams p) {
     if (i + kNS - 1 < nst) {
       int subs[R::kUnitsPerWave];
       stage_subs(i + kNS - 1, subs);
-      issue_stage<E, SHUF, NRT>(p, it, pid_next, subs,
+      issue_stage<E, SHUF, NRT, PSH>(p, it, pid_next, subs,
                                 ring + ((i + kNS - 1) % kNS) * R::kStageBytes, wave, lane);
       if (i + kNS < nst) load_pids(i + kNS, pid_next);
     }
@@ -465,13 +465,13 @@ void seg_mfma_kernel(SegParams p) {
 
 }  // namespace
 
-template <bool F16>
+template <bool F16, int PSH>
 int launch_shared(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
   if (shuf)
-    hipLaunchKernelGGL((seg_mfma_kernel<2, true, 4, F16>), dim3(grid),
+    hipLaunchKernelGGL((seg_mfma_kernel<2, true, 4, F16, PSH>), dim3(grid),
                        dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_mfma_kernel<2, false, 4, F16>), dim3(grid),
+    hipLaunchKernelGGL((seg_mfma_kernel<2, false, 4, F16, PSH>), dim3(grid),
                        dim3(64 * Ring<2, 4>::kWaves), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
@@ -479,7 +479,9 @@ int launch_shared(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
 // bf16 or fp16 KV with 33-64 rows (four row tiles); the other cases run on the
 // private-ring variants
 int launch_segments_mfma(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st) {
-  return f16 ? launch_shared<true>(sp, shuf, grid, st) : launch_shared<false>(sp, shuf, grid, st);
+  if (sp.page_shift == 5)
+    return f16 ? launch_shared<true, 5>(sp, shuf, grid, st) : launch_shared<false, 5>(sp, shuf, grid, st);
+  return f16 ? launch_shared<true, 4>(sp, shuf, grid, st) : launch_shared<false, 4>(sp, shuf, grid, st);
 }
 
 }  // namespace skv

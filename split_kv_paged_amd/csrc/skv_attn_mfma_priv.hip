@@ -109,13 +109,13 @@ __device__ __forceinline__ int std_chunk_pos(int tau, int q, int pg) {
 // at slot + pg * 4 KB as above. Shuffled planes: unit u = (page u/2, K if u
 // even, V if odd) at slot + u * kUnitBytes, the K plane's 16-token chunk rows
 // and the V plane copied as they are.
-template <bool SHUF>
+template <bool SHUF, int PSH>
 __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& it, int pid0,
                                             int sub0, int pid1, int sub1, uint8_t* slot,
                                             int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
-  const SubPageAddr sp[2] = {sub_page<kE, SHUF>(p, it.g, pid0, sub0),
-                             sub_page<kE, SHUF>(p, it.g, pid1, sub1)};
+  const SubPageAddr sp[2] = {sub_page<kE, SHUF, PSH>(p, it.g, pid0, sub0),
+                             sub_page<kE, SHUF, PSH>(p, it.g, pid1, sub1)};
   if constexpr (!SHUF) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
@@ -129,7 +129,7 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
     }
     return;
   }
-  const int krow = kplane_row_bytes(p);
+  const int krow = kplane_row_bytes<PSH>();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     uint8_t* dst = slot + u * kUnitBytes;
@@ -220,7 +220,7 @@ __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegIte
 // across lanes (and O rescaled) only when some row's scores rise that far.
 constexpr float kSlackLog2 = 8.f;
 
-template <bool SHUF, int NRT, int NW>
+template <bool SHUF, int NRT, int NW, int PSH>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_mfma_priv_kernel(SegParams p) {
   using R = PRing<NW, NRT>;
@@ -243,7 +243,7 @@ void seg_mfma_priv_kernel(SegParams p) {
   const int seg_pages = (ntok + 15) >> 4;
   const int nb = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;   // this wave's blocks
   const int seg_page0 = it.seg_start >> 4;          // first 16-token sub-page
-  const int psh = p.page_shift - 4;
+  constexpr int psh = PSH - 4;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
@@ -305,15 +305,15 @@ void seg_mfma_priv_kernel(SegParams p) {
     const int vb = seg_page0 + (pg + 1 < seg_pages ? pg + 1 : 0);
     a = ptab[va >> psh];
     b = ptab[vb >> psh];
-    sa = sub_of(p, va);
-    sb = sub_of(p, vb);
+    sa = sub_of<PSH>(va);
+    sb = sub_of<PSH>(vb);
   };
 #pragma unroll
   for (int k = 0; k < kNP - 1; ++k) {
     if (k < nb) {
       int a, sa, b, sb;
       pids(k, a, sa, b, sb);
-      issue_block<SHUF>(p, it, a, sa, b, sb, wring + k * kBlockBytes, lane);
+      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + k * kBlockBytes, lane);
     }
   }
 
@@ -335,7 +335,7 @@ void seg_mfma_priv_kernel(SegParams p) {
     if (k + kNP - 1 < nb) {                     // slot of block k-1, consumed last iteration
       int a, sa, b, sb;
       pids(k + kNP - 1, a, sa, b, sb);
-      issue_block<SHUF>(p, it, a, sa, b, sb, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
+      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
     }
     pwait_blocks<kBlockInstr, kNP - 1>(min(kNP - 1, nb - 1 - k));   // block k landed
     const uint8_t* slot = wring + (k % kNP) * kBlockBytes;
@@ -520,13 +520,13 @@ struct PRing2 {
 // one page into a slot: K chunk-major for the operand lanes, V in the
 // chunk-pair-major tile of the transposing read ([pair][token][32 B]), or the
 // shuffled planes as they are
-template <bool SHUF>
+template <bool SHUF, int PSH>
 __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& it, int pid,
                                             int sub, uint8_t* slot, int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
-  const SubPageAddr sp = sub_page<2, SHUF>(p, it.g, pid, sub);
+  const SubPageAddr sp = sub_page<2, SHUF, PSH>(p, it.g, pid, sub);
   const uint8_t* ktile = sp.k;
-  const int krow = kplane_row_bytes(p);
+  const int krow = kplane_row_bytes<PSH>();
 #pragma unroll
   for (int i = 0; i < kHalf2 / 1024; ++i) {
     const size_t off = SHUF ? static_cast<size_t>(4 * i + j4) * krow + r16 * 16
@@ -547,7 +547,7 @@ __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& i
   }
 }
 
-template <bool SHUF, int NRT, int NW, bool F16>
+template <bool SHUF, int NRT, int NW, bool F16, int PSH>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_mfma_priv2_kernel(SegParams p) {
   using R = PRing2<NW, NRT>;
@@ -565,7 +565,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
   const int seg_pages = (it.seg_end - it.seg_start + 15) >> 4;
   const int np = seg_pages > wave ? (seg_pages - wave + NW - 1) / NW : 0;   // this wave's pages
   const int seg_page0 = it.seg_start >> 4;          // first 16-token sub-page
-  const int psh = p.page_shift - 4;
+  constexpr int psh = PSH - 4;
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
@@ -599,7 +599,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
   auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
 #pragma unroll
   for (int k = 0; k < kNP - 1; ++k)
-    if (k < np) issue_page2<SHUF>(p, it, pid_of(k), sub_of(p, vpage(k)), wring + k * kPage2, lane);
+    if (k < np) issue_page2<SHUF, PSH>(p, it, pid_of(k), sub_of<PSH>(vpage(k)), wring + k * kPage2, lane);
 
   f32x4_t oacc[NRT][8];
   float m[NRT], l[NRT];
@@ -618,7 +618,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
 
   for (int k = 0; k < np; ++k) {
     if (k + kNP - 1 < np)                       // slot of page k-1, consumed last iteration
-      issue_page2<SHUF>(p, it, pid_of(k + kNP - 1), sub_of(p, vpage(k + kNP - 1)),
+      issue_page2<SHUF, PSH>(p, it, pid_of(k + kNP - 1), sub_of<PSH>(vpage(k + kNP - 1)),
                         wring + ((k + kNP - 1) % kNP) * kPage2,
                         lane);
     pwait_blocks<kPageInstr2, kNP - 1>(min(kNP - 1, np - 1 - k));   // page k landed
@@ -699,30 +699,45 @@ void seg_mfma_priv2_kernel(SegParams p) {
                            1.f, wave, lane);
 }
 
-template <bool SHUF>
+template <bool SHUF, int PSH>
 int launch_priv(const SegParams& sp, int nrt, int grid, hipStream_t st) {
-  // 8 waves (two per SIMD) up to two row tiles; four row tiles need the
-  // registers and merge scratch of 4 waves
+  // 8 waves (two per SIMD) at every row count; four row tiles read Q from LDS
   if (nrt <= 1)
-    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 1, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 1, 8, PSH>), dim3(grid), dim3(64 * 8), 0, st,
+                       sp);
   else if (nrt <= 2)
-    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 2, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 2, 8, PSH>), dim3(grid), dim3(64 * 8), 0, st,
+                       sp);
   else
-    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 4, 8>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_mfma_priv_kernel<SHUF, 4, 8, PSH>), dim3(grid), dim3(64 * 8), 0, st,
+                       sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
 // bf16 or fp16 with up to two row tiles (four would not fit two waves per SIMD)
-template <bool SHUF, bool F16>
+template <bool SHUF, bool F16, int PSH>
 int launch_priv2_t(const SegParams& sp, int nrt, int grid, hipStream_t st) {
   if (nrt > 2) return SKV_EUNSUPPORTED;
   if (nrt <= 1)
-    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 1, 8, F16>), dim3(grid), dim3(64 * 8), 0, st,
-                       sp);
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 1, 8, F16, PSH>), dim3(grid), dim3(64 * 8), 0,
+                       st, sp);
   else
-    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 2, 8, F16>), dim3(grid), dim3(64 * 8), 0, st,
-                       sp);
+    hipLaunchKernelGGL((seg_mfma_priv2_kernel<SHUF, 2, 8, F16, PSH>), dim3(grid), dim3(64 * 8), 0,
+                       st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+template <int PSH>
+int launch_priv_all(const SegParams& sp, int e, bool f16, bool shuf, int nrt, int grid,
+                    hipStream_t st) {
+  if (e == 2) {
+    if (f16)
+      return shuf ? launch_priv2_t<true, true, PSH>(sp, nrt, grid, st)
+                  : launch_priv2_t<false, true, PSH>(sp, nrt, grid, st);
+    return shuf ? launch_priv2_t<true, false, PSH>(sp, nrt, grid, st)
+                : launch_priv2_t<false, false, PSH>(sp, nrt, grid, st);
+  }
+  return shuf ? launch_priv<true, PSH>(sp, nrt, grid, st) : launch_priv<false, PSH>(sp, nrt, grid, st);
 }
 
 }  // namespace
@@ -730,14 +745,8 @@ int launch_priv2_t(const SegParams& sp, int nrt, int grid, hipStream_t st) {
 int launch_segments_mfma_priv(const SegParams& sp, int e, bool f16, bool shuf, int max_rows,
                               int grid, hipStream_t st) {
   const int nrt = (max_rows + 15) / 16;
-  if (e == 2) {
-    if (f16)
-      return shuf ? launch_priv2_t<true, true>(sp, nrt, grid, st)
-                  : launch_priv2_t<false, true>(sp, nrt, grid, st);
-    return shuf ? launch_priv2_t<true, false>(sp, nrt, grid, st)
-                : launch_priv2_t<false, false>(sp, nrt, grid, st);
-  }
-  return shuf ? launch_priv<true>(sp, nrt, grid, st) : launch_priv<false>(sp, nrt, grid, st);
+  return sp.page_shift == 5 ? launch_priv_all<5>(sp, e, f16, shuf, nrt, grid, st)
+                            : launch_priv_all<4>(sp, e, f16, shuf, nrt, grid, st);
 }
 
 }  // namespace skv

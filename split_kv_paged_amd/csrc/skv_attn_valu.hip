@@ -85,13 +85,13 @@ __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
 // One 16-token sub-page (this wave's) into its ring slot: K half chunk-major
 // [c][token][16 B]; V half row-major [token][channels] (standard) or the
 // plane's sub-page as is (shuffled).
-template <bool SHUF>
+template <bool SHUF, int PSH>
 __device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it, int pid,
                                            int sub, uint8_t* slot, int lane) {
-  const SubPageAddr a = sub_page<2, SHUF>(p, it.g, pid, sub);
+  const SubPageAddr a = sub_page<2, SHUF, PSH>(p, it.g, pid, sub);
   const uint8_t* ktile = a.k;
   const uint8_t* vtile = a.v;
-  const int krow = kplane_row_bytes(p);
+  const int krow = kplane_row_bytes<PSH>();
 #pragma unroll
   for (int i = 0; i < kHalf / 1024; ++i) {
     const int c = 4 * i + (lane >> 4), tau = lane & 15;
@@ -122,7 +122,7 @@ __device__ __forceinline__ float max_over_tokens(float v) {
   return v;
 }
 
-template <bool SHUF, int NW, bool F16>
+template <bool SHUF, int NW, bool F16, int PSH>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void seg_valu_kernel(SegParams p) {
   using R = VRing<NW>;
@@ -147,7 +147,7 @@ void seg_valu_kernel(SegParams p) {
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
-  const int psh = p.page_shift - 4;
+  constexpr int psh = PSH - 4;
   const float sm_scale = kScoreScaleLog2;
 
   // Q rows (bf16 pairs) for this lane's 32 channels; consumed before any DMA
@@ -178,7 +178,7 @@ void seg_valu_kernel(SegParams p) {
   auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
 #pragma unroll
   for (int k = 0; k < kNS - 1; ++k)
-    if (k < np) issue_page<SHUF>(p, it, pid_of(k), sub_of(p, vpage(k)), wring + k * kPage, lane);
+    if (k < np) issue_page<SHUF, PSH>(p, it, pid_of(k), sub_of<PSH>(vpage(k)), wring + k * kPage, lane);
   int pid_next = kNS - 1 < np ? pid_of(kNS - 1) : 0;
 
   constexpr int kAcc = SHUF ? 2 : 8;
@@ -196,7 +196,7 @@ void seg_valu_kernel(SegParams p) {
   for (int k = 0; k < np; ++k) {
     wait_vmcnt_pages<kInstrPerPage, kNS - 2>(min(kNS - 2, np - 1 - k));
     if (k + kNS - 1 < np) {
-      issue_page<SHUF>(p, it, pid_next, sub_of(p, vpage(k + kNS - 1)),
+      issue_page<SHUF, PSH>(p, it, pid_next, sub_of<PSH>(vpage(k + kNS - 1)),
                        wring + ((k + kNS - 1) % kNS) * kPage, lane);
       if (k + kNS < np) pid_next = pid_of(k + kNS);
     }
@@ -391,17 +391,19 @@ void seg_valu_kernel(SegParams p) {
 
 }  // namespace
 
-template <bool F16>
+template <bool F16, int PSH>
 int launch_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
   if (shuf)
-    hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16>), dim3(grid), dim3(64 * 4), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16, PSH>), dim3(grid), dim3(64 * 4), 0, st, sp);
   else
-    hipLaunchKernelGGL((seg_valu_kernel<false, 8, F16>), dim3(grid), dim3(64 * 8), 0, st, sp);
+    hipLaunchKernelGGL((seg_valu_kernel<false, 8, F16, PSH>), dim3(grid), dim3(64 * 8), 0, st, sp);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
 int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st) {
-  return f16 ? launch_valu<true>(sp, shuf, grid, st) : launch_valu<false>(sp, shuf, grid, st);
+  if (sp.page_shift == 5)
+    return f16 ? launch_valu<true, 5>(sp, shuf, grid, st) : launch_valu<false, 5>(sp, shuf, grid, st);
+  return f16 ? launch_valu<true, 4>(sp, shuf, grid, st) : launch_valu<false, 4>(sp, shuf, grid, st);
 }
 
 }  // namespace skv
