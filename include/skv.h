@@ -56,6 +56,9 @@ enum skv_status {
 };
 
 enum skv_layout { SKV_LAYOUT_STANDARD = 0, SKV_LAYOUT_SHUFFLED = 1 };
+/* Flags of the attention entry points. */
+enum skv_attn_flags { SKV_ATTN_DETERMINISTIC = 1 };
+
 enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1, SKV_KV_FP16 = 2 };
 enum skv_convert_dir { SKV_TO_SHUFFLED = 0, SKV_TO_STANDARD = 1 };
 
@@ -134,11 +137,20 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  * out          [total_q, q_heads, head_dim], the type of q, round to nearest even;
  *              a token that sees no key gets zeros
  * out_lse      fp32 [total_q, q_heads] or NULL; -inf where no key is visible
+ * flags        0 or SKV_ATTN_DETERMINISTIC. With 0 and fp8 KV, the waves of
+ *              a work-group take the segment's 32-token blocks in the order
+ *              they claim them at run time, so they finish together; each
+ *              wave's fp32 sums then run in an order that depends on timing,
+ *              and results for identical inputs agree to rounding, not bit
+ *              for bit. SKV_ATTN_DETERMINISTIC fixes the order (wave w takes
+ *              blocks w, w + waves, ...): bit-identical results for identical
+ *              inputs, 2-3% slower on fp8 KV. bf16 and fp16 KV always run in
+ *              the fixed order.
  * Scale: softmax(q.k / sqrt(head_dim)).
  * Errors: EINVAL for NULL required pointers, non-positive sizes, q_heads not a
  * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
  * scales present for bf16/fp16 or missing for fp8, kv_b NULL for SHUFFLED or
- * non-NULL for STANDARD, pt_stride < 1, an unknown layout or dtype;
+ * non-NULL for STANDARD, pt_stride < 1, an unknown layout, dtype or flag;
  * EUNSUPPORTED for head_dim != 128, page_size other than 16 or 32, max_q > 4,
  * (q_heads/kv_heads) * max_q > 64. */
 int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
@@ -150,7 +162,7 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           const float* v_scale, int causal, const int32_t* plan,
                           int32_t* tok_nseg, int num_cus, int seg_max,
                           float* part_o, float* part_lse, void* out,
-                          float* out_lse, void* stream);
+                          float* out_lse, int flags, void* stream);
 
 /* The segment kernel of skv_paged_decode_attn alone: writes the partials
  * (part_o, part_lse) of every (token, q head, segment) that the plan lists
@@ -165,7 +177,7 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
                      int page_size, const float* k_scale, const float* v_scale,
                      int causal, const int32_t* plan, int32_t* tok_nseg,
                      int num_cus, int seg_max, float* part_o, float* part_lse,
-                     void* stream);
+                     int flags, void* stream);
 
 /* Split reduce alone [PR, Modifications]: for every (t, h), merges the first
  * tok_nseg[t] partials by log-sum-exp: M = max_s lse_s,

@@ -13,8 +13,9 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
                              int page_size, const float* k_scale, const float* v_scale,
                              int causal,
                              const int32_t* plan, int32_t* tok_nseg, int num_cus,
-                             int seg_max, float* part_o, float* part_lse) {
+                             int seg_max, float* part_o, float* part_lse, int flags) {
   skv::AttnArgs a;
+  a.flags = flags;
   a.q = q;
   a.kv_a = kv_a;
   a.kv_b = kv_b;
@@ -76,19 +77,19 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
                      int page_size, const float* k_scale, const float* v_scale,
                      int causal, const int32_t* plan, int32_t* tok_nseg,
                      int num_cus, int seg_max, float* part_o, float* part_lse,
-                     void* stream) {
+                     int flags, void* stream) {
   // `out` is not used by this call; pass a non-NULL stand-in to the shared check
   int st = skv::check_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                 pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
                                 max_q, q_heads, kv_heads, head_dim, page_size,
                                 k_scale, v_scale, plan, tok_nseg, num_cus,
-                                seg_max, part_o, part_lse, part_o);
+                                seg_max, part_o, part_lse, part_o, flags);
   if (st != SKV_OK) return st;
   return skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                              pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
                                              max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
                                              causal, plan, tok_nseg, num_cus, seg_max,
-                                             part_o, part_lse),
+                                             part_o, part_lse, flags),
                               stream);
 }
 
@@ -101,18 +102,18 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           const float* v_scale, int causal, const int32_t* plan,
                           int32_t* tok_nseg, int num_cus, int seg_max,
                           float* part_o, float* part_lse, void* out,
-                          float* out_lse, void* stream) {
+                          float* out_lse, int flags, void* stream) {
   int st = skv::check_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                 pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
                                 max_q, q_heads, kv_heads, head_dim, page_size,
                                 k_scale, v_scale, plan, tok_nseg, num_cus,
-                                seg_max, part_o, part_lse, out);
+                                seg_max, part_o, part_lse, out, flags);
   if (st != SKV_OK) return st;
   st = skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                            pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
                                            max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
                                            causal, plan, tok_nseg, num_cus, seg_max,
-                                           part_o, part_lse),
+                                           part_o, part_lse, flags),
                             stream);
   if (st != SKV_OK) return st;
   return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads,

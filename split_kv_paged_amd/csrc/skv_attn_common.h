@@ -31,6 +31,7 @@ struct SegParams {
   int pt_stride, bs, Hq, Hkv, G, seg_max, causal;
   int fixed_S;                // 0: planned split (plan); > 0: fixed split, S per sequence
   int page_shift;             // log2(tokens per page): 4 or 5
+  int claim;                  // 1: waves claim their units at run time; 0: fixed order
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -219,6 +220,24 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   it.seg_end = static_cast<int>(s1 < it.L ? s1 : it.L);
   it.valid = 1;
   return it;
+}
+
+// The next unit (32-token block of the segment) a wave of the fp8
+// private-ring kernel streams after unit cur. Fixed order: wave w takes units
+// w, w + NW, w + 2 NW, ... Claimed (p.claim): the next unit not yet taken,
+// from a work-group counter in LDS that starts at NW (units 0 .. NW-1 go to
+// waves 0 .. NW-1). The waves of a CU do not progress at one rate (each waits
+// on its own DMA), so with a fixed share the work-group waits for its slowest
+// wave; with claimed units they all finish within about one unit. Returns a
+// wave-uniform value; once it reaches the unit count, every later one does.
+// (The 16-bit private-ring and vector-ALU kernels keep the fixed order: claims
+// gained nothing there, and cost 5% where one wave per SIMD waits on them.)
+template <int NW>
+__device__ __forceinline__ int next_unit(const SegParams& p, int cur, int* counter, int lane) {
+  if (!p.claim) return cur + NW;
+  int u = 0;
+  if (lane == 0) u = atomicAdd(counter, 1);
+  return __builtin_amdgcn_readfirstlane(u);
 }
 
 // Pages hold 16 or 32 tokens (PSH = log2 of the page size, a template

@@ -231,6 +231,8 @@ void seg_mfma_priv_kernel(SegParams p) {
   __shared__ float sm_m[NW][NRT][16];
   __shared__ float sm_l[NW][NRT][16];
   __shared__ uint4 qs[kQLds ? NRT * 4 * 64 : 1];
+  __shared__ int next_blk;                   // next_unit's counter
+  static_assert(kNP == 2, "one block in flight while another is computed");
 
   const SegItem it = decode_item(p);
   write_fixed_counts(p, it);
@@ -241,7 +243,6 @@ void seg_mfma_priv_kernel(SegParams p) {
   const int ntok = it.seg_end - it.seg_start;
   const int nblk = (ntok + 31) >> 5;
   const int seg_pages = (ntok + 15) >> 4;
-  const int nb = nblk > wave ? (nblk - wave + NW - 1) / NW : 0;   // this wave's blocks
   const int seg_page0 = it.seg_start >> 4;          // first 16-token sub-page
   constexpr int psh = PSH - 4;
   const __attribute__((address_space(4))) int32_t* ptab =
@@ -277,7 +278,6 @@ void seg_mfma_priv_kernel(SegParams p) {
       const int t = i >> 2, kk = i & 3;
       qs[i * 64 + lane] = fix_q(t, load_q(t, kk));
     }
-    __syncthreads();                           // before any DMA is in flight
   } else {
 #pragma unroll
     for (int t = 0; t < NRT; ++t)
@@ -292,15 +292,17 @@ void seg_mfma_priv_kernel(SegParams p) {
         qb[t][kk] = as_bf16x8(fix_q(t, __builtin_bit_cast(uint4, qb[t][kk])));
       }
   }
+  if (threadIdx.x == 0) next_blk = NW;
+  __syncthreads();                             // before any DMA is in flight
   int lim[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) lim[t] = row_limit(it, 16 * t + r16, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
-  // pages of this wave's k-th block (block wave + NW k); pages past the end
-  // read the segment's first page (masked and zeroed; keeps vmcnt exact)
-  auto pids = [&](int k, int& a, int& sa, int& b, int& sb) {
-    const int pg = 2 * (wave + NW * k);
+  // pages of block bi of the segment; pages past the end read the segment's
+  // first page (masked and zeroed; keeps vmcnt exact)
+  auto pids = [&](int bi, int& a, int& sa, int& b, int& sb) {
+    const int pg = 2 * bi;
     const int va = seg_page0 + (pg < seg_pages ? pg : 0);
     const int vb = seg_page0 + (pg + 1 < seg_pages ? pg + 1 : 0);
     a = ptab[va >> psh];
@@ -308,13 +310,11 @@ void seg_mfma_priv_kernel(SegParams p) {
     sa = sub_of<PSH>(va);
     sb = sub_of<PSH>(vb);
   };
-#pragma unroll
-  for (int k = 0; k < kNP - 1; ++k) {
-    if (k < nb) {
-      int a, sa, b, sb;
-      pids(k, a, sa, b, sb);
-      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + k * kBlockBytes, lane);
-    }
+  int cur = wave;                              // this wave's block (next_unit order)
+  if (cur < nblk) {
+    int a, sa, b, sb;
+    pids(cur, a, sa, b, sb);
+    issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring, lane);
   }
 
   f32x4_t oacc[NRT][8];
@@ -331,17 +331,20 @@ void seg_mfma_priv_kernel(SegParams p) {
   // byte i%8 of the 8 bytes read by lane 2k + i/8, i.e. 8 tokens of one channel
   const int vtau = 4 * j4 + ((r16 >> 1) & 3);
 
-  for (int k = 0; k < nb; ++k) {
-    if (k + kNP - 1 < nb) {                     // slot of block k-1, consumed last iteration
+  for (int k = 0; cur < nblk; ++k) {
+    const int nxt = next_unit<NW>(p, cur, &next_blk, lane);
+    if (nxt < nblk) {                           // into the slot consumed last iteration
       int a, sa, b, sb;
-      pids(k + kNP - 1, a, sa, b, sb);
-      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + ((k + kNP - 1) % kNP) * kBlockBytes, lane);
+      pids(nxt, a, sa, b, sb);
+      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + ((k + 1) & 1) * kBlockBytes, lane);
+      pwait_vmcnt<kBlockInstr>();               // block cur landed
+    } else {
+      pwait_vmcnt<0>();
     }
-    pwait_blocks<kBlockInstr, kNP - 1>(min(kNP - 1, nb - 1 - k));   // block k landed
-    const uint8_t* slot = wring + (k % kNP) * kBlockBytes;
+    const uint8_t* slot = wring + (k & 1) * kBlockBytes;
     const uint8_t* kU[2] = {slot, slot + 2 * kUnitBytes};
     const uint8_t* vU[2] = {slot + kUnitBytes, slot + 3 * kUnitBytes};
-    const int tok0 = it.seg_start + 32 * (wave + NW * k);
+    const int tok0 = it.seg_start + 32 * cur;
     // wave-uniform: does any key of this block lie past some row's limit?
     const bool masked = tok0 + 32 > lim_min;
     // the segment's last block: V of its tokens past the segment end is zeroed
@@ -486,6 +489,7 @@ void seg_mfma_priv_kernel(SegParams p) {
       for (int t = 0; t < NRT; ++t)
         oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
     }
+    cur = nxt;
   }
 
   // ---- merge the waves' partial states; write the segment partial ----

@@ -34,7 +34,7 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     const void* k_scale, const void* v_scale,
                     const void* plan, const void* tok_nseg, int num_cus,
                     int seg_max, const void* part_o, const void* part_lse,
-                    const void* out);
+                    const void* out, int flags);
 int check_reduce_args(const void* part_o, const void* part_lse,
                       const void* tok_nseg, int total_q, int q_heads,
                       int head_dim, int seg_max, int out_dtype, const void* out);
@@ -90,6 +90,7 @@ struct AttnArgs {
   float* part_lse;
   void* out;
   float* out_lse;
+  int flags;                 // SKV_ATTN_DETERMINISTIC or 0
 };
 
 int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,

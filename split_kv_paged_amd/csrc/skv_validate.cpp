@@ -25,7 +25,8 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     const void* k_scale, const void* v_scale,
                     const void* plan, const void* tok_nseg, int num_cus,
                     int seg_max, const void* part_o, const void* part_lse,
-                    const void* out) {
+                    const void* out, int flags) {
+  if (flags & ~SKV_ATTN_DETERMINISTIC) return SKV_EINVAL;
   (void)plan;   // NULL selects the fixed split
   if (!q || !kv_a || !page_table || !seq_lens || !cu_seqlens_q || !tok_nseg ||
       !part_o || !part_lse || !out)

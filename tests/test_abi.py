@@ -68,14 +68,14 @@ def _attn(**kw):
     a = dict(q=P, kv_a=P, kv_b=None, layout=0, kv_dtype=0, pt=P, pt_stride=8, seq_lens=P,
              cu=P, bs=2, total_q=2, max_q=1, q_heads=8, kv_heads=2, head_dim=128,
              page_size=16, k_scale=None, v_scale=None, causal=1, plan=P, tok=P,
-             num_cus=256, seg_max=64, part_o=P, part_lse=P, out=P, out_lse=None)
+             num_cus=256, seg_max=64, part_o=P, part_lse=P, out=P, out_lse=None, flags=0)
     a.update(kw)
     return skv.load().skv_paged_decode_attn(
         a["q"], a["kv_a"], a["kv_b"], a["layout"], a["kv_dtype"], a["pt"], a["pt_stride"],
         a["seq_lens"], a["cu"], a["bs"], a["total_q"], a["max_q"], a["q_heads"],
         a["kv_heads"], a["head_dim"], a["page_size"], a["k_scale"], a["v_scale"],
         a["causal"], a["plan"], a["tok"], a["num_cus"], a["seg_max"], a["part_o"],
-        a["part_lse"], a["out"], a["out_lse"], None)
+        a["part_lse"], a["out"], a["out_lse"], a["flags"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -97,9 +97,17 @@ def _attn(**kw):
     (dict(head_dim=64), 2), (dict(page_size=64), 2), (dict(page_size=24), 2), (dict(max_q=5), 2),
     (dict(q_heads=32, kv_heads=2, max_q=8), 2),           # rows 128 > 64 (max_q checked first)
     (dict(q_heads=64, kv_heads=2, max_q=3), 2),           # rows 96 > 64
+    (dict(flags=2), 1), (dict(flags=-1), 1), (dict(flags=3), 1),
 ])
 def test_attn_errors(kw, code):
     assert _attn(**kw) == code
+
+
+@pytest.mark.parametrize("flags,code", [(2, 1), (-1, 1), (4, 1), (1 << 30, 1)])
+def test_segment_attn_flag_errors(flags, code):
+    st = skv.load().skv_segment_attn(P, P, None, 0, 0, P, 8, P, P, 2, 2, 1, 8, 2, 128, 16, None,
+                                     None, 1, P, P, 256, 64, P, P, flags, None)
+    assert st == code
 
 
 def _reduce(**kw):

@@ -2,7 +2,8 @@
 so a forward can be captured into a HIP graph. A captured plan + attention
 (planned and fixed split) + shuffle + conversion + cache write, replayed
 several times with eager work and synchronisations between replays, must give
-the eager results bit for bit on every replay."""
+the eager results bit for bit on every replay (attention in its deterministic
+order; the default order, captured too, agrees to rounding)."""
 import numpy as np
 import pytest
 import torch
@@ -57,7 +58,8 @@ def test_graph_replays_match_eager(dtype, layout):
     vnew = case.kv[:4, :, 0, 128:].contiguous()
     kw = dict(kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=cfg.num_cus,
               seg_max=cfg.seg_max, kv_dtype=dtype, layout=layout, k_scale=case.k_scale,
-              v_scale=case.v_scale, causal=cfg.causal)
+              v_scale=case.v_scale, causal=cfg.causal, deterministic=True)
+    cout = torch.zeros_like(out)          # claimed units (the default order): to rounding
 
     def forward():                        # library calls only: nothing else is captured
         skv.kv_page_shuffle(case.kv, kp, vp)
@@ -72,6 +74,9 @@ def test_graph_replays_match_eager(dtype, layout):
         skv.paged_decode_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                               case.cu_seqlens_q, None, ftok, part_o=part_o, part_lse=part_lse,
                               out=fout, **kw)
+        skv.paged_decode_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
+                              case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse,
+                              out=cout, **dict(kw, deterministic=False))
 
     def restore_halves():                 # eager, before every run
         kh.copy_(kh0)
@@ -98,7 +103,7 @@ def test_graph_replays_match_eager(dtype, layout):
         forward()
     names = ["plan", "tok", "ftok", "out", "fout", "lse", "kh", "vh", "kp", "vp"]
     for rep in range(4):
-        for t in (plan, tok, ftok, out, fout, lse, kp, vp):   # eager work between replays
+        for t in (plan, tok, ftok, out, fout, lse, kp, vp, cout):   # eager work between replays
             t.zero_()
         restore_halves()
         torch.cuda.synchronize()
@@ -107,4 +112,6 @@ def test_graph_replays_match_eager(dtype, layout):
         got = snap()
         for n, a, b in zip(names, got, want):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (rep, n)
+        d = (cout.float() - want[3].float()).abs().max().item()
+        assert d <= (2e-2 if dtype == "fp8" else 1e-2), (rep, d)
     assert np.all(np.isfinite(out.float().cpu().numpy()))
