@@ -229,25 +229,24 @@ void seg_mfma_kernel(SegParams p) {
   };
 
   // ---- Q rows of this wave's tile (B operand of S^T = K.Q^T) ----
+  // Q comes through the same LDS DMA, into the ring's last stage (not used
+  // before the first iteration issues into it), ahead of the prologue's
+  // stages: its latency overlaps theirs, and the wait for it below counts
+  // only on the DMAs issued after it (vector-memory loads complete in order).
+  // Wave w's 4 KB: piece kk at + kk * 1 KB, lane l's 16 bytes at + l * 16.
+  static_assert(kWaves * 4096 <= R::kStageBytes && kNS >= 2, "Q fits the last stage");
+  uint8_t* qstage = ring + (kNS - 1) * R::kStageBytes + wave * 4096;
   const int n = 16 * rt + r16;
   const int lim = row_limit(it, n, p.G, p.causal);
-  bf16x8_t qb[4];
+  const bool qok = active && n < it.rows;
   {
-    const bool ok = active && n < it.rows;
-    const int t = it.c0 + (ok ? n / p.G : 0);
-    const int h = it.g * p.G + (ok ? n % p.G : 0);
+    const int t = it.c0 + (qok ? n / p.G : 0);
+    const int h = it.g * p.G + (qok ? n % p.G : 0);
     const uint16_t* qr = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ch = E == 2 ? 32 * kk + 8 * j4 : 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
-      qb[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(qr + ch));   // padding rows read row 0
-    }
-    // consume Q here, before any DMA is in flight: otherwise the compiler's
-    // wait for these loads lands inside the loop and drains the DMA ring
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      asm volatile("" : "+v"(qb[kk]));
-      if (!ok) qb[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      dma16(reinterpret_cast<const uint8_t*>(qr + ch), qstage + kk * 1024);  // padding rows read row 0
     }
   }
 
@@ -263,6 +262,19 @@ void seg_mfma_kernel(SegParams p) {
     }
   }
   if (kNS - 1 < nst) load_pids(kNS - 1, pid_next);
+  // Q landed once at most the prologue's stages remain in flight; each wave
+  // reads back its own pieces (written by its own DMA) before the first
+  // barrier, after which the last stage is refilled
+  wait_vmcnt_stages<R::kInstrPerWave, kNS - 1>(min(kNS - 1, nst));
+  bf16x8_t qb[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qb[kk] = *reinterpret_cast<const bf16x8_t*>(qstage + kk * 1024 + lane * 16);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    if (!qok) qb[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    asm volatile("" : "+v"(qb[kk]));           // the reads complete here
+  }
 
   f32x4_t oacc[8];
 #pragma unroll

@@ -57,7 +57,6 @@ struct PRing {
   static constexpr int kNP = kBytes / kBlockBytes;      // block slots
   static_assert(kNP >= 2, "two block slots per wave");
   static_assert((kNP - 1) * kBlockInstr <= 63, "vmcnt range");
-  static_assert(NW * 8 * 64 * 16 <= NW * kBytes, "a row tile's merge scratch fits");
 };
 
 template <int N>
@@ -145,20 +144,24 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
   }
 }
 
-// The NW waves' partial states of each 16-row tile (row max m, row sum l and
-// O^T, each relative to the wave's own max) are merged through LDS and the
-// segment partial is written: every wave takes a share of the (row tile,
-// channel tile) pairs. The idle rings hold the O^T tiles, as many tiles per
-// round as fit (rounds are separated by barriers).
-template <int NW, int NRT>
+// The NW = 8 waves' partial states of each 16-row tile (row max m, row sum l
+// and O^T, each relative to the wave's own max) are merged through LDS and the
+// segment partial is written. The idle rings hold the O^T tiles, as many row
+// tiles per round as fit (rounds are separated by barriers); in each round
+// wave w merges channel tile w of every row tile, reading the eight waves'
+// 16-byte pieces and the row statistics (stored wave-minor: two 16-byte
+// reads) with all loads in flight at once.
+template <int NW, int NRT, int SCRATCH>
 __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegItem& it,
-                                                uint8_t* scratch, int scratch_bytes,
-                                                float (*sm_m)[NRT][16], float (*sm_l)[NRT][16],
+                                                uint8_t* scratch, float (*sm_m)[16][NW],
+                                                float (*sm_l)[16][NW],
                                                 f32x4_t (&oacc)[NRT][8], float (&m)[NRT],
                                                 float (&l)[NRT], float out_scale, int wave,
                                                 int lane) {
+  static_assert(NW == 8, "wave w merges channel tile w");
   constexpr int kTileBytes = NW * 8 * 64 * 16;          // one row tile's O^T of every wave
-  const int tpr = scratch_bytes / kTileBytes;            // tiles per round (>= 1)
+  constexpr int kTpr = SCRATCH / kTileBytes;             // row tiles per round
+  static_assert(kTpr >= 1, "a row tile's merge scratch fits");
   const int r16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
@@ -168,45 +171,58 @@ __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegIte
   if (j4 == 0) {
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
-      sm_m[wave][t][r16] = m[t];
-      sm_l[wave][t][r16] = l[t];
+      sm_m[t][r16][wave] = m[t];
+      sm_l[t][r16][wave] = l[t];
     }
   }
   f32x4_t* oslot = reinterpret_cast<f32x4_t*>(scratch);   // [tile in round][w][dt][lane]
-  for (int t0 = 0; t0 < NRT; t0 += tpr) {
+#pragma unroll
+  for (int t0 = 0; t0 < NRT; t0 += kTpr) {
     __syncthreads();                 // rings idle / previous round's reads done
 #pragma unroll
-    for (int t = 0; t < NRT; ++t)
-      if (t >= t0 && t < t0 + tpr) {
+    for (int tt = 0; tt < kTpr; ++tt)
+      if (t0 + tt < NRT) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          oslot[(((t - t0) * NW + wave) * 8 + dt) * 64 + lane] = oacc[t][dt];
+          oslot[((tt * NW + wave) * 8 + dt) * 64 + lane] = oacc[t0 + tt][dt];
       }
     __syncthreads();
-    const int tn = min(tpr, NRT - t0);
-    for (int pair = wave; pair < tn * 8; pair += NW) {    // (tile, channel tile) pairs
-      const int tt = pair >> 3, dt = pair & 7, t = t0 + tt;
-      const int n = 16 * t + r16;
-      float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) M = fmaxf(M, sm_m[w][t][r16]);
+    for (int tt = 0; tt < kTpr; ++tt) {
+      const int t = t0 + tt;
+      if (t >= NRT) break;
+      const float4 ma = *reinterpret_cast<const float4*>(&sm_m[t][r16][0]);
+      const float4 mb = *reinterpret_cast<const float4*>(&sm_m[t][r16][4]);
+      const float4 la = *reinterpret_cast<const float4*>(&sm_l[t][r16][0]);
+      const float4 lb = *reinterpret_cast<const float4*>(&sm_l[t][r16][4]);
+      f32x4_t ow[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) ow[w] = oslot[((tt * NW + w) * 8 + wave) * 64 + lane];
+      const float mw[NW] = {ma.x, ma.y, ma.z, ma.w, mb.x, mb.y, mb.z, mb.w};
+      const float lw[NW] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+      float M = mw[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, mw[w]);
       const float mu = M == -INFINITY ? 0.f : M;
       float Ls = 0.f;
       f32x4_t o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float f = fast_exp2(sm_m[w][t][r16] - mu);
-        Ls += sm_l[w][t][r16] * f;
-        o += oslot[((tt * NW + w) * 8 + dt) * 64 + lane] * f;
+        const float f = fast_exp2(mw[w] - mu);
+        Ls += lw[w] * f;
+        o += ow[w] * f;
       }
-      if (n >= it.rows) continue;
-      const int tq = it.c0 + n / p.G;
-      const int h = it.g * p.G + n % p.G;
-      const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
-      const bool any = Ls > 0.f;
-      const float inv = any ? out_scale / Ls : 0.f;
-      *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * dt + 4 * j4) = o * inv;
-      if (dt == 0 && j4 == 0) p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
+      const int n = 16 * t + r16;
+      if (n < it.rows) {
+        const int tq = it.c0 + n / p.G;
+        const int h = it.g * p.G + n % p.G;
+        const size_t prow = (static_cast<size_t>(tq) * p.Hq + h) * p.seg_max + it.seg;
+        const bool any = Ls > 0.f;
+        const float inv = any ? out_scale / Ls : 0.f;
+        *reinterpret_cast<f32x4_t*>(p.part_o + prow * kD + 16 * wave + 4 * j4) = o * inv;
+        if (wave == 0 && j4 == 0)
+          p.part_lse[prow] = any ? (mu + fast_log2(Ls)) * kLn2 : -INFINITY;
+      }
     }
   }
 }
@@ -228,8 +244,8 @@ void seg_mfma_priv_kernel(SegParams p) {
   // four row tiles at two waves per SIMD: Q is read from LDS, not held in registers
   constexpr bool kQLds = NRT >= 4;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
-  __shared__ float sm_m[NW][NRT][16];
-  __shared__ float sm_l[NW][NRT][16];
+  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW];
+  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW];
   __shared__ uint4 qs[kQLds ? NRT * 4 * 64 : 1];
   __shared__ int next_blk;                   // next_unit's counter
   static_assert(kNP == 2, "one block in flight while another is computed");
@@ -258,6 +274,28 @@ void seg_mfma_priv_kernel(SegParams p) {
   // every row sees at least the keys below lim_min (row 0 is the most restricted)
   const int lim_min = row_limit(it, 0, p.G, p.causal);
 
+  uint8_t* wring = ring[wave];
+  // pages of block bi of the segment; pages past the end read the segment's
+  // first page (masked and zeroed; keeps vmcnt exact)
+  auto pids = [&](int bi, int& a, int& sa, int& b, int& sb) {
+    const int pg = 2 * bi;
+    const int va = seg_page0 + (pg < seg_pages ? pg : 0);
+    const int vb = seg_page0 + (pg + 1 < seg_pages ? pg + 1 : 0);
+    a = ptab[va >> psh];
+    b = ptab[vb >> psh];
+    sa = sub_of<PSH>(va);
+    sb = sub_of<PSH>(vb);
+  };
+  // the first block is issued before Q is loaded, so the two latencies
+  // overlap (the first wait for Q also waits for this DMA; nothing else
+  // is in flight yet)
+  int cur = wave;                              // this wave's block (next_unit order)
+  if (cur < nblk) {
+    int a, sa, b, sb;
+    pids(cur, a, sa, b, sb);
+    issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring, lane);
+  }
+
   // ---- Q rows of every tile (B operand of S^T = K.Q^T) ----
   auto load_q = [&](int t, int kk) -> uint4 {
     const int n = 16 * t + r16;
@@ -274,16 +312,26 @@ void seg_mfma_priv_kernel(SegParams p) {
   };
   bf16x8_t qb[kQLds ? 1 : NRT][4];
   if constexpr (kQLds) {
-    for (int i = wave; i < NRT * 4; i += NW) {
-      const int t = i >> 2, kk = i & 3;
-      qs[i * 64 + lane] = fix_q(t, load_q(t, kk));
+    // this wave's pieces i = wave + NW k: every load in flight before one wait
+    constexpr int kQPer = (NRT * 4 + NW - 1) / NW;
+    uint4 qv[kQPer];
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = wave + NW * k;
+      if (i < NRT * 4) qv[k] = load_q(i >> 2, i & 3);
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = wave + NW * k;
+      if (i < NRT * 4) qs[i * 64 + lane] = fix_q(i >> 2, qv[k]);
     }
   } else {
 #pragma unroll
     for (int t = 0; t < NRT; ++t)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qb[t][kk] = as_bf16x8(load_q(t, kk));
-    // consume Q before any DMA is in flight (a later wait for it would drain the ring)
+    // consume Q here, while only the first block is in flight (a later wait
+    // for it would drain the ring)
 #pragma unroll
     for (int t = 0; t < NRT; ++t)
 #pragma unroll
@@ -293,29 +341,10 @@ void seg_mfma_priv_kernel(SegParams p) {
       }
   }
   if (threadIdx.x == 0) next_blk = NW;
-  __syncthreads();                             // before any DMA is in flight
+  __syncthreads();                             // Q staged, the claim counter set
   int lim[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) lim[t] = row_limit(it, 16 * t + r16, p.G, p.causal);
-
-  uint8_t* wring = ring[wave];
-  // pages of block bi of the segment; pages past the end read the segment's
-  // first page (masked and zeroed; keeps vmcnt exact)
-  auto pids = [&](int bi, int& a, int& sa, int& b, int& sb) {
-    const int pg = 2 * bi;
-    const int va = seg_page0 + (pg < seg_pages ? pg : 0);
-    const int vb = seg_page0 + (pg + 1 < seg_pages ? pg + 1 : 0);
-    a = ptab[va >> psh];
-    b = ptab[vb >> psh];
-    sa = sub_of<PSH>(va);
-    sb = sub_of<PSH>(vb);
-  };
-  int cur = wave;                              // this wave's block (next_unit order)
-  if (cur < nblk) {
-    int a, sa, b, sb;
-    pids(cur, a, sa, b, sb);
-    issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring, lane);
-  }
 
   f32x4_t oacc[NRT][8];
   float m[NRT], thr[NRT], l[NRT];
@@ -494,8 +523,8 @@ void seg_mfma_priv_kernel(SegParams p) {
 
   // ---- merge the waves' partial states; write the segment partial ----
   pwait_vmcnt<0>();
-  merge_and_write<NW, NRT>(p, it, &ring[0][0], NW * R::kBytes, sm_m, sm_l, oacc, m, l,
-                           out_scale, wave, lane);
+  merge_and_write<NW, NRT, NW * R::kBytes>(p, it, &ring[0][0], sm_m, sm_l, oacc, m, l,
+                                          out_scale, wave, lane);
 }
 
 // ---- bf16 KV: a 32-token block is 16 KB, so the private slots are pages ----
@@ -518,7 +547,6 @@ struct PRing2 {
   static constexpr int kNP = kBytes / kPage2;
   static_assert(kNP >= 2, "two page slots per wave");
   static_assert((kNP - 1) * kPageInstr2 <= 63, "vmcnt range");
-  static_assert(NW * 8 * 64 * 16 <= NW * kBytes, "a row tile's merge scratch fits");
 };
 
 // one page into a slot: K chunk-major for the operand lanes, V in the
@@ -557,8 +585,8 @@ void seg_mfma_priv2_kernel(SegParams p) {
   using R = PRing2<NW, NRT>;
   constexpr int kNP = R::kNP;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
-  __shared__ float sm_m[NW][NRT][16];
-  __shared__ float sm_l[NW][NRT][16];
+  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW];
+  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW];
 
   const SegItem it = decode_item(p);
   write_fixed_counts(p, it);
@@ -574,6 +602,15 @@ void seg_mfma_priv2_kernel(SegParams p) {
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   const float sm_scale = kScoreScaleLog2;
+
+  uint8_t* wring = ring[wave];
+  // this wave's k-th sub-page is the segment's sub-page wave + NW k
+  auto vpage = [&](int k) { return seg_page0 + wave + NW * k; };
+  auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
+  // the first page is issued before Q is loaded, so the two latencies
+  // overlap (the wait for Q also waits for this page; nothing else is in flight)
+  static_assert(kNP == 2, "one page ahead");
+  if (np > 0) issue_page2<SHUF, PSH>(p, it, pid_of(0), sub_of<PSH>(vpage(0)), wring, lane);
 
   bf16x8_t qb[NRT][4];
   int lim[NRT];
@@ -593,17 +630,10 @@ void seg_mfma_priv2_kernel(SegParams p) {
   for (int t = 0; t < NRT; ++t)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      asm volatile("" : "+v"(qb[t][kk]));
+      asm volatile("" : "+v"(qb[t][kk]));        // Q consumed while only page 0 is in flight
       if (16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
 
-  uint8_t* wring = ring[wave];
-  // this wave's k-th sub-page is the segment's sub-page wave + NW k
-  auto vpage = [&](int k) { return seg_page0 + wave + NW * k; };
-  auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
-#pragma unroll
-  for (int k = 0; k < kNP - 1; ++k)
-    if (k < np) issue_page2<SHUF, PSH>(p, it, pid_of(k), sub_of<PSH>(vpage(k)), wring + k * kPage2, lane);
 
   f32x4_t oacc[NRT][8];
   float m[NRT], l[NRT];
@@ -699,8 +729,8 @@ void seg_mfma_priv2_kernel(SegParams p) {
 
   // ---- merge the waves' partial states; write the segment partial ----
   pwait_vmcnt<0>();
-  merge_and_write<NW, NRT>(p, it, &ring[0][0], NW * R::kBytes, sm_m, sm_l, oacc, m, l,
-                           1.f, wave, lane);
+  merge_and_write<NW, NRT, NW * R::kBytes>(p, it, &ring[0][0], sm_m, sm_l, oacc, m, l,
+                                          1.f, wave, lane);
 }
 
 template <bool SHUF, int PSH>

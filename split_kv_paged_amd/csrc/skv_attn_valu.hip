@@ -150,36 +150,50 @@ void seg_valu_kernel(SegParams p) {
   constexpr int psh = PSH - 4;
   const float sm_scale = kScoreScaleLog2;
 
-  // Q rows (bf16 pairs) for this lane's 32 channels; consumed before any DMA
-  uint4 qr[RM][4];
   int lim[RM];
 #pragma unroll
-  for (int r = 0; r < RM; ++r) {
-    lim[r] = row_limit(it, r, p.G, p.causal);
-    const bool okr = r < it.rows;
-    const int t = it.c0 + (okr ? r / p.G : 0);
-    const int h = it.g * p.G + (okr ? r % p.G : 0);
-    const uint16_t* q = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)          // chunk 4u+qq -> channels 32u + 8qq
-      qr[r][u] = *reinterpret_cast<const uint4*>(q + 32 * u + 8 * qq);   // padding rows read row 0
-  }
-#pragma unroll
-  for (int r = 0; r < RM; ++r)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      asm volatile("" : "+v"(qr[r][u].x), "+v"(qr[r][u].y), "+v"(qr[r][u].z), "+v"(qr[r][u].w));
-      if (r >= it.rows) qr[r][u] = make_uint4(0, 0, 0, 0);
-    }
+  for (int r = 0; r < RM; ++r) lim[r] = row_limit(it, r, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
   // page ids: this wave's k-th sub-page is the segment's sub-page wave + NW k
   auto vpage = [&](int k) { return seg_page0 + wave + NW * k; };
   auto pid_of = [&](int k) { return ptab[vpage(k) >> psh]; };
+  // Q rows (RM x 256 bytes) come by one DMA into the ring's last slot (not
+  // used before the first iteration issues into it), ahead of the prologue's
+  // pages, so the latencies overlap; the wait for Q counts only on the DMAs
+  // issued after it (vector-memory loads complete in order). Lane i loads
+  // bytes 16 (i % 16) .. +15 of row i / 16.
+  static_assert(RM * kD * 2 == 64 * 16, "the Q rows are one DMA instruction");
+  static_assert((kNS - 1) * kInstrPerPage <= 63, "vmcnt range");
+  uint8_t* qslot = wring + (kNS - 1) * kPage;
+  {
+    const int r = lane >> 4;
+    const bool okr = r < it.rows;
+    const int t = it.c0 + (okr ? r / p.G : 0);
+    const int h = it.g * p.G + (okr ? r % p.G : 0);
+    dma16(reinterpret_cast<const uint8_t*>(p.q + (static_cast<size_t>(t) * p.Hq + h) * kD +
+                                           (lane & 15) * 8),
+          qslot);                                // padding rows read row 0
+  }
 #pragma unroll
   for (int k = 0; k < kNS - 1; ++k)
     if (k < np) issue_page<SHUF, PSH>(p, it, pid_of(k), sub_of<PSH>(vpage(k)), wring + k * kPage, lane);
   int pid_next = kNS - 1 < np ? pid_of(kNS - 1) : 0;
+  wait_vmcnt_pages<kInstrPerPage, kNS - 1>(min(kNS - 1, np));   // Q landed
+  // Q rows (bf16 pairs) for this lane's 32 channels: chunk 4u+qq of row r
+  uint4 qr[RM][4];
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      qr[r][u] = *reinterpret_cast<const uint4*>(qslot + r * kD * 2 + (4 * u + qq) * 16);
+#pragma unroll
+  for (int r = 0; r < RM; ++r)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (r >= it.rows) qr[r][u] = make_uint4(0, 0, 0, 0);
+      asm volatile("" : "+v"(qr[r][u].x), "+v"(qr[r][u].y), "+v"(qr[r][u].z), "+v"(qr[r][u].w));
+    }
 
   constexpr int kAcc = SHUF ? 2 : 8;
   float acc[RM][kAcc];
