@@ -149,12 +149,13 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
 // segment partial is written. The idle rings hold the O^T tiles, as many row
 // tiles per round as fit (rounds are separated by barriers); in each round
 // wave w merges channel tile w of every row tile, reading the eight waves'
-// 16-byte pieces and the row statistics (stored wave-minor: two 16-byte
-// reads) with all loads in flight at once.
+// 16-byte pieces and the row statistics (stored wave-minor, rows padded to
+// 48 bytes so that the 16 rows' 16-byte reads fall in disjoint LDS banks: two
+// reads per row) with all loads in flight at once.
 template <int NW, int NRT, int SCRATCH>
 __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegItem& it,
-                                                uint8_t* scratch, float (*sm_m)[16][NW],
-                                                float (*sm_l)[16][NW],
+                                                uint8_t* scratch, float (*sm_m)[16][NW + 4],
+                                                float (*sm_l)[16][NW + 4],
                                                 f32x4_t (&oacc)[NRT][8], float (&m)[NRT],
                                                 float (&l)[NRT], float out_scale, int wave,
                                                 int lane) {
@@ -244,8 +245,8 @@ void seg_mfma_priv_kernel(SegParams p) {
   // four row tiles at two waves per SIMD: Q is read from LDS, not held in registers
   constexpr bool kQLds = NRT >= 4;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
-  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW];
-  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW];
+  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW + 4];
+  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW + 4];
   __shared__ uint4 qs[kQLds ? NRT * 4 * 64 : 1];
   __shared__ int next_blk;                   // next_unit's counter
   static_assert(kNP == 2, "one block in flight while another is computed");
@@ -585,8 +586,8 @@ void seg_mfma_priv2_kernel(SegParams p) {
   using R = PRing2<NW, NRT>;
   constexpr int kNP = R::kNP;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NW][R::kBytes];
-  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW];
-  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW];
+  __shared__ __attribute__((aligned(16))) float sm_m[NRT][16][NW + 4];
+  __shared__ __attribute__((aligned(16))) float sm_l[NRT][16][NW + 4];
 
   const SegItem it = decode_item(p);
   write_fixed_counts(p, it);
