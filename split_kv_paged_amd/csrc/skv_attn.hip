@@ -12,7 +12,8 @@
 namespace skv {
 
 int launch_segments_mfma(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st);
-int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st);
+int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, bool dual, int grid,
+                         hipStream_t st);
 int launch_segments_mfma_priv(const SegParams& sp, int e, bool f16, bool shuf, int max_rows,
                               int grid,
                               hipStream_t st);
@@ -71,8 +72,13 @@ int launch_segments(const AttnArgs& a, void* stream) {
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
   const int rows = sp.G * a.max_q;
   auto st = static_cast<hipStream_t>(stream);
+  // more work-groups than CUs: the shuffled vector-ALU kernel (one wave per
+  // SIMD) runs two work-groups per CU with half-size rings, so that one's
+  // prologue and merge overlap the other's streaming instead of leaving the
+  // CU idle between consecutive work-groups (the 8-wave kernels gain nothing)
+  const bool dual = grid > a.num_cus;
   if (e == 2 && rows <= kValuMaxRows)
-    return launch_segments_valu(sp, shuf, f16, static_cast<int>(grid), st);
+    return launch_segments_valu(sp, shuf, f16, dual, static_cast<int>(grid), st);
   if (e == 1 || rows <= kPrivMaxRowsBf16)
     return launch_segments_mfma_priv(sp, e, f16, shuf, rows, static_cast<int>(grid), st);
   return launch_segments_mfma(sp, shuf, f16, static_cast<int>(grid), st);

@@ -49,9 +49,9 @@ constexpr int kInstrPerPage = kPage / 1024;    // DMA instructions per page
 constexpr int kStdRow = 2 * kD * 2;            // one standard token row
 constexpr int kStdTile = kPageSize * kStdRow;  // one (block, head) standard tile
 
-template <int NW>
+template <int NW, int RING_KB>
 struct VRing {
-  static constexpr int kBytes = 128 * 1024 / NW;   // this wave's ring
+  static constexpr int kBytes = RING_KB * 1024 / NW;   // this wave's ring
   static constexpr int kNS = kBytes / kPage;       // pages in it
   static_assert(kNS >= 2, "ring needs two pages");
   static_assert((kNS - 2) * kInstrPerPage <= 63, "vmcnt range");
@@ -122,10 +122,11 @@ __device__ __forceinline__ float max_over_tokens(float v) {
   return v;
 }
 
-template <bool SHUF, int NW, bool F16, int PSH>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+template <bool SHUF, int NW, bool F16, int PSH, int RING_KB>
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(NW * (128 / RING_KB) / 4, NW * (128 / RING_KB) / 4)))
 void seg_valu_kernel(SegParams p) {
-  using R = VRing<NW>;
+  using R = VRing<NW, RING_KB>;
   constexpr int kNS = R::kNS;
   constexpr int kThreads = 64 * NW;
   constexpr int RM = kRows;
@@ -406,18 +407,28 @@ void seg_valu_kernel(SegParams p) {
 }  // namespace
 
 template <bool F16, int PSH>
-int launch_valu(const SegParams& sp, bool shuf, int grid, hipStream_t st) {
-  if (shuf)
-    hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16, PSH>), dim3(grid), dim3(64 * 4), 0, st, sp);
-  else
-    hipLaunchKernelGGL((seg_valu_kernel<false, 8, F16, PSH>), dim3(grid), dim3(64 * 8), 0, st, sp);
+int launch_valu(const SegParams& sp, bool shuf, bool dual, int grid, hipStream_t st) {
+  if (shuf) {
+    if (dual)
+      hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16, PSH, 64>), dim3(grid), dim3(64 * 4), 0, st, sp);
+    else
+      hipLaunchKernelGGL((seg_valu_kernel<true, 4, F16, PSH, 128>), dim3(grid), dim3(64 * 4), 0, st, sp);
+  } else {
+    // standard pages: the 8-wave form streams consecutive work-groups without
+    // a gap measurable against a two-per-CU form (705 against 706 us on a
+    // 128 x 8k decode batch)
+    hipLaunchKernelGGL((seg_valu_kernel<false, 8, F16, PSH, 128>), dim3(grid), dim3(64 * 8), 0, st, sp);
+  }
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
 }
 
-int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, int grid, hipStream_t st) {
+int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, bool dual, int grid,
+                         hipStream_t st) {
   if (sp.page_shift == 5)
-    return f16 ? launch_valu<true, 5>(sp, shuf, grid, st) : launch_valu<false, 5>(sp, shuf, grid, st);
-  return f16 ? launch_valu<true, 4>(sp, shuf, grid, st) : launch_valu<false, 4>(sp, shuf, grid, st);
+    return f16 ? launch_valu<true, 5>(sp, shuf, dual, grid, st)
+               : launch_valu<false, 5>(sp, shuf, dual, grid, st);
+  return f16 ? launch_valu<true, 4>(sp, shuf, dual, grid, st)
+             : launch_valu<false, 4>(sp, shuf, dual, grid, st);
 }
 
 }  // namespace skv

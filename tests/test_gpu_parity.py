@@ -142,6 +142,17 @@ CASES = [
     ("mfma_g4_q3", [33, 1000], [3, 3], 16, 4, "bf16", "standard", 1, 256, 64),
     ("seg_max_binds", [1600, 16, 9999], [2, 4, 3], 16, 2, "bf16", "standard", 1, 512, 3),
     ("infeasible_fallback", [100, 200, 300, 400, 500], [1, 2, 3, 4, 1], 8, 4, "bf16", "standard", 1, 8, 64),
+    # more work-groups than num_cus (more sequences than num_cus / kv_heads): the
+    # two-per-CU forms with half-size rings (4 waves in the private-ring kernels)
+    ("dual_valu_shuf", [1, 17, 300, 999, 64, 5000, 0, 2049], [1] * 8, 8, 2, "bf16", "shuffled", 1, 4, 64),
+    ("dual_valu_std", [1, 17, 300, 999, 64, 5000, 0, 2049], [1] * 8, 8, 2, "bf16", "standard", 1, 4, 64),
+    ("dual_fp8_rows8", [3, 77, 513, 2049, 16, 0, 4000], [1] * 7, 16, 2, "fp8", "standard", 1, 4, 64),
+    ("dual_fp8_rows32_shuf", [3, 77, 513, 2049, 16, 1, 4000], [4, 2, 3, 4, 1, 1, 4], 16, 2, "fp8",
+     "shuffled", 1, 4, 64),
+    ("dual_bf16_rows16_shuf", [5, 300, 2000, 17, 999], [2, 1, 2, 2, 1], 16, 2, "bf16", "shuffled", 1, 4, 64),
+    ("dual_bf16_rows32", [5, 300, 2000, 17, 999], [4, 3, 4, 1, 2], 16, 2, "bf16", "standard", 1, 4, 64),
+    ("dual_bf16_rows32_noncausal", [5, 300, 2000, 17, 999], [4, 3, 4, 1, 2], 16, 2, "bf16", "standard", 0, 4,
+     64),
 ]
 
 
@@ -184,6 +195,9 @@ P32_CASES = [
     ("p32_fp8_rows64", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "standard", 1, 64, 64),
     ("p32_fp8_rows64_shuf", [1, 50, 1500, 333], [4, 4, 3, 2], 32, 2, "fp8", "shuffled", 1, 64, 64),
     ("p32_infeasible", [100, 200, 300, 400, 500], [1, 2, 3, 4, 1], 8, 4, "bf16", "standard", 1, 8, 64),
+    ("p32_dual_valu_shuf", [33, 4097, 64, 2, 1000, 31], [1] * 6, 8, 2, "bf16", "shuffled", 1, 4, 64),
+    ("p32_dual_fp8_rows16", [3, 77, 513, 2049, 33, 4000], [2, 2, 1, 2, 1, 2], 16, 2, "fp8", "standard", 1, 4, 64),
+    ("p32_dual_bf16_rows32_shuf", [3, 40, 777, 2500, 65], [4, 2, 4, 3, 1], 16, 2, "bf16", "shuffled", 1, 4, 64),
 ]
 
 
@@ -240,6 +254,8 @@ FP16_CASES = [
     ("f16_rows64", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "fp16", "standard", 1, 64, 64),
     ("f16_rows64_shuf", [0, 1, 5, 17, 5000, 1234], [4, 4, 4, 2, 4, 3], 32, 2, "fp16", "shuffled", 1, 64, 64),
     ("f16_noncausal", [3, 60, 2000], [4, 4, 4], 32, 2, "fp16", "standard", 0, 48, 64),
+    ("f16_dual_valu_shuf", [1, 17, 300, 999, 64, 5000], [1] * 6, 8, 2, "fp16", "shuffled", 1, 4, 64),
+    ("f16_dual_rows32", [5, 300, 2000, 17, 999], [4, 3, 4, 1, 2], 16, 2, "fp16", "standard", 1, 4, 64),
 ]
 
 
@@ -378,7 +394,8 @@ def test_fp8_negative_k_scale(spec):
 @pytest.mark.parametrize("spec", [_BY[n] for n in ("rows8_ragged", "mfma4_g16_q4", "mfma_fp8_std",
                                                    "mfma_fp8_shuf", "fp8_rows64_std",
                                                    "fp8_rows64_shuf", "fp8_rows4_shuf",
-                                                   "valu_g1_q3", "valu_g4_shuf_tails")],
+                                                   "valu_g1_q3", "valu_g4_shuf_tails", "dual_valu_shuf",
+                                                   "dual_fp8_rows32_shuf", "dual_bf16_rows16_shuf")],
                          ids=lambda c: c[0])
 def test_nan_poison_does_not_leak(spec):
     a = run_hip(_mk(*spec, poison="finite"), deterministic=True)
@@ -405,7 +422,8 @@ def test_nan_poison_does_not_leak_32_token_pages(spec):
 
 
 @pytest.mark.parametrize("spec", [_BY[n] for n in ("tiny_shuf", "mfma4_g16_q4_shuf",
-                                                   "valu_g1_q1")], ids=lambda c: c[0])
+                                                   "valu_g1_q1", "fp8_rows64_std", "dual_fp8_rows8",
+                                                   "dual_bf16_rows16_shuf")], ids=lambda c: c[0])
 def test_deterministic(spec):
     case = _mk(*spec)
     a = run_hip(case, deterministic=True)
