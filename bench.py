@@ -51,12 +51,38 @@ SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip"
                    "skv_attn_common.h", "skv_internal.h")
 
 
+def _code_only(text):
+    """C++ source with comments removed and whitespace collapsed (string and
+    character literals kept), so that editing a comment keeps the hash."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash():
+    """Hash of the segment kernels' code (comments and layout ignored)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "split_kv_paged_amd", "csrc")
     for f in SEGMENT_SOURCES:
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(d, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -14,8 +14,10 @@
 // layer time. A shared ring with a barrier per stage runs every wave through
 // the same serial chain (wait, LDS, widen, MFMA, softmax, MFMA) in lockstep;
 // a bare DMA ring of the same depth streams about twice as fast. Here:
-//  * Each of NW waves owns the 32-token blocks w, w + NW, ... of the segment
-//    and streams them through a private LDS ring of NP block slots (direct-
+//  * Each of NW waves streams 32-token blocks of the segment (fp8: wave w
+//    starts with block w and then claims the next unclaimed block from an LDS
+//    counter, or takes w + NW, w + 2 NW, ... in the deterministic order; 16-bit
+//    KV: pages w, w + NW, ...) through a private LDS ring of NP slots (direct-
 //    to-LDS DMA issued from inline asm, waits on its own vmcnt only): no
 //    barrier in the main loop, so the waves drift apart and one wave's MFMA or
 //    VALU work overlaps another's waits.
@@ -33,8 +35,9 @@
 //    past the segment end is zeroed (page-tail poison never leaks).
 //  * fp8 with four row tiles (64 rows) keeps two waves per SIMD by reading Q
 //    from LDS instead of holding it in registers.
-//  * At the end the waves' (max, sum, O) are merged through LDS, each wave
-//    taking a share of the (row tile, channel tile) pairs.
+//  * The first block is issued before Q is loaded, so the two latencies
+//    overlap. At the end the waves' (max, sum, O) are merged through LDS,
+//    wave w merging channel tile w of every row tile.
 #include "skv_attn_common.h"
 #include "skv.h"
 

@@ -12,7 +12,9 @@
 //  * NW wave64s (8 for standard pages, 4 for shuffled planes; measured); wave
 //    w takes pages w, w+NW, ... of the segment and computes all query rows of
 //    each, so no wave needs another's data: each wave streams its pages
-//    through a private LDS ring (128 KB / NW) with direct-to-LDS DMA
+//    through a private LDS ring (128 KB / NW; 64 KB / NW for the shuffled
+//    form when the launch has more work-groups than CUs, two per CU) with
+//    direct-to-LDS DMA
 //    (global_load_lds_dwordx4, issued from inline asm) and waits only on its
 //    own vmcnt — there is no barrier in the main loop. Two waves per SIMD hide
 //    each other's LDS and DPP latencies; the shuffled layout's two planes
