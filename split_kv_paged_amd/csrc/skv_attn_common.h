@@ -222,6 +222,43 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   return it;
 }
 
+// 16 bytes per lane, global -> LDS at lds_base + lane * 16 (lds_base
+// wave-uniform): global_load_lds_dwordx4, issued from inline asm so that the
+// only waits on it are the kernels' explicit vmcnt waits (the compiler would
+// otherwise drain every DMA in flight before each LDS read).
+// NT: the non-temporal (streaming) cache policy. Every KV byte is read once, by
+// one work-group, and streamed reads reach markedly more of the HBM peak (a
+// plain read kernel: 7.1 against 6.0-6.3 TB/s). It is used where each
+// instruction covers whole 128-byte lines; where an instruction gathers half
+// lines (16 token rows x 64 bytes), the default policy lets L2 serve the other
+// half to the next instruction, and the streaming policy was slower there.
+template <bool NT>
+__device__ __forceinline__ void dma16_lds(const void* g, uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :: "v"(g), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(g), "s"(lds) : "memory", "m0");
+}
+
+// The same from a wave-uniform base (held in SGPRs) plus a 32-bit per-lane
+// byte offset: half the VGPRs of a 64-bit per-lane address.
+template <bool NT>
+__device__ __forceinline__ void dma16_lds_s(const uint8_t* base_uniform, uint32_t off,
+                                            uint8_t* lds_uniform) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
+}
+
 // The next unit (32-token block of the segment) a wave of the fp8
 // private-ring kernel streams after unit cur. Fixed order: wave w takes units
 // w, w + NW, w + 2 NW, ... Claimed (p.claim): the next unit not yet taken,

@@ -99,16 +99,14 @@ __device__ __forceinline__ void wait_vmcnt_stages(int k) {
   wait_vmcnt<0>();
 }
 
-// 16 bytes per lane, global -> LDS at lds_base + lane * 16 (lds_base uniform).
-// Issued from inline asm so that the only waits on it are the explicit
-// per-stage vmcnt waits (the compiler would otherwise drain every in-flight
-// DMA before each LDS read).
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
-  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
-}
+
+// bf16 standard pages in LDS: a page is its 16 token rows of 512 bytes (K
+// channels, then V), each row's thirty-two 16-byte chunks XOR-swizzled by
+// token: chunk q of row tau sits at position q ^ 2 tau. The K operand reads
+// (16 tokens of one chunk) and the transposing V reads (4 tokens of two
+// chunks per 16-lane group) then spread over all LDS banks. (An involution:
+// the DMA lane at position p fetches chunk std2_chunk_pos(tau, p).)
+__device__ __forceinline__ int std2_chunk_pos(int tau, int q) { return q ^ (2 * tau); }
 
 // Issue this wave's DMA units of one stage. Unit u of the stage is (16-token
 // sub-page u/2, K half if u even, V half if odd); wave w issues units
@@ -130,6 +128,20 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
     const bool vhalf = u & 1;
     const SubPageAddr a = sub_page<E, SHUF, PSH>(p, it.g, pids[uw], subs[uw]);
     uint8_t* dst = slot + (2 * pg + (vhalf ? 1 : 0)) * R::kUnitBytes;
+    if constexpr (E == 2 && !SHUF) {
+      // bf16 standard pages: unit (page, row half h) = token rows 8h .. 8h+7
+      // (K then V, 512 bytes each), two whole rows (1 KB of contiguous HBM) per
+      // instruction, streamed; chunk q of row tau lands at position
+      // std2_chunk_pos(tau, q) of the row
+      const int h = u & 1;
+#pragma unroll
+      for (int i = 0; i < R::kUnitInstr; ++i) {
+        const int row = 8 * h + 2 * i + (lane >> 5);
+        const int q = std2_chunk_pos(row, lane & 31);          // the chunk stored there
+        dma16_lds<true>(a.k + static_cast<size_t>(row) * R::kStdRow + q * 16, dst + i * 1024);
+      }
+      continue;
+    }
     if (!vhalf) {
       const uint8_t* tile = a.k;
 #pragma unroll
@@ -142,7 +154,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
           const int byte = E == 2 ? (32 * i + 8 * j4) * 2 : 64 * i + 16 * j4;
           off = static_cast<size_t>(r16) * R::kStdRow + byte;
         }
-        dma16(tile + off, dst + i * 1024);
+        dma16_lds<SHUF>(tile + off, dst + i * 1024);   // shuffled: whole lines
       }
     } else {
 #pragma unroll
@@ -164,7 +176,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
           }
           off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
         }
-        dma16(a.v + off, dst + i * 1024);
+        dma16_lds<SHUF>(a.v + off, dst + i * 1024);
       }
     }
   }
@@ -246,7 +258,7 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int ch = E == 2 ? 32 * kk + 8 * j4 : 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
-      dma16(reinterpret_cast<const uint8_t*>(qr + ch), qstage + kk * 1024);  // padding rows read row 0
+      dma16_lds<false>(qr + ch, qstage + kk * 1024);   // padding rows read row 0
     }
   }
 
@@ -309,7 +321,13 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       bf16x8_t kop[4];
-      if constexpr (E == 2) {
+      if constexpr (E == 2 && !SHUF) {
+        // page tile at kU[pg]: chunk 4 kk + j4 of token row r16
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(
+              kU[pg] + r16 * R::kStdRow + std2_chunk_pos(r16, 4 * kk + j4) * 16));
+      } else if constexpr (E == 2) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kU[pg] + kk * 1024 + lane * 16));
@@ -362,8 +380,7 @@ void seg_mfma_kernel(SegParams p) {
     const bool tail = tok0 + 32 > it.seg_end;
     const int vend = it.seg_end - tok0;       // tokens of the block before the end
     // per-lane part of the transposing-read address in the chunk-major V tile
-    const int vtr_off = E == 2 ? (4 * j4 + (r16 >> 2)) * 32 + ((r16 >> 1) & 1) * 16 + (r16 & 1) * 8
-                               : (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;
+    const int vtr_off = (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;   // fp8 tile
     const uint8_t* vU8 = vU[r16 >> 3];        // fp8: lanes 0-7 of a group read page 0
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -385,14 +402,17 @@ void seg_mfma_kernel(SegParams p) {
       } else if constexpr (E == 2) {
         // transposing LDS read: in each 16-lane group, lane i receives element
         // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
-        // token 4*j4 + j/4, channels 16dt + 4(j%4) .. +3 (chunk pair dt of the
-        // chunk-major tile), so lane i ends up with tokens 4*j4 .. 4*j4+3 of
-        // channel 16dt + i. The 64 lanes cover 512 contiguous bytes.
+        // token tau = 4*j4 + j/4, channels 16dt + 4(j%4) .. +3, i.e. half j%2
+        // of V chunk 2dt + (j/2)%2 (row chunk 16 + that, swizzled), so lane i
+        // ends up with tokens 4*j4 .. 4*j4+3 of channel 16dt + i.
+        const int vtau = 4 * j4 + (r16 >> 2);
+        const int vq = 16 + 2 * dt + ((r16 >> 1) & 1);
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
           const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (__attribute__((address_space(3))) v4i16_t*)(
-                  (__attribute__((address_space(3))) uint8_t*)(vU[pg]) + vtr_off + dt * 512));
+                  (__attribute__((address_space(3))) uint8_t*)(kU[pg]) + vtau * R::kStdRow +
+                  std2_chunk_pos(vtau, vq) * 16 + (r16 & 1) * 8));
           const uint2 u = __builtin_bit_cast(uint2, v);
           w[2 * pg] = u.x;
           w[2 * pg + 1] = u.y;

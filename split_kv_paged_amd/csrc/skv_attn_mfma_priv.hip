@@ -80,23 +80,6 @@ __device__ __forceinline__ void pwait_blocks(int k) {
   pwait_vmcnt<0>();
 }
 
-__device__ __forceinline__ void pdma16(const uint8_t* g, uint8_t* lds_uniform) {
-  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
-}
-
-// The same DMA from a wave-uniform base (held in SGPRs) plus a 32-bit
-// per-lane byte offset: half the VGPRs of a 64-bit per-lane address.
-__device__ __forceinline__ void pdma16s(const uint8_t* base_uniform, uint32_t off,
-                                        uint8_t* lds_uniform) {
-  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
-}
-
 // Standard pages in a slot: page pg's (block, head) tile is copied whole, 16
 // token rows of 256 B (K 128 B, then V 128 B), each DMA instruction taking 4
 // consecutive rows, i.e. 1 KB of contiguous HBM. Within a row the sixteen
@@ -126,7 +109,7 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
       for (int i = 0; i < kStdTile / 1024; ++i) {
         const int row = 4 * i + j4;                               // lane -> (row, position r16)
         const int q = std_chunk_pos(row, r16, pg);                // the chunk stored there
-        pdma16s(tile, row * kStdRow + q * 16, slot + pg * kStdTile + i * 1024);
+        dma16_lds_s<true>(tile, row * kStdRow + q * 16, slot + pg * kStdTile + i * 1024);
       }
     }
     return;
@@ -138,11 +121,11 @@ __device__ __forceinline__ void issue_block(const SegParams& p, const SegItem& i
     if ((u & 1) == 0) {
 #pragma unroll
       for (int i = 0; i < kUnitInstr; ++i)
-        pdma16s(sp[u >> 1].k, (4 * i + j4) * krow + r16 * 16, dst + i * 1024);
+        dma16_lds_s<true>(sp[u >> 1].k, (4 * i + j4) * krow + r16 * 16, dst + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < kUnitInstr; ++i)    // the sub-page's V plane as is
-        pdma16s(sp[u >> 1].v, (i * 64 + lane) * 16, dst + i * 1024);
+        dma16_lds_s<true>(sp[u >> 1].v, (i * 64 + lane) * 16, dst + i * 1024);
     }
   }
 }
@@ -567,7 +550,7 @@ __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& i
   for (int i = 0; i < kHalf2 / 1024; ++i) {
     const size_t off = SHUF ? static_cast<size_t>(4 * i + j4) * krow + r16 * 16
                             : static_cast<size_t>(r16) * kStdRow2 + (32 * i + 8 * j4) * 2;
-    pdma16(ktile + off, slot + i * 1024);
+    dma16_lds<SHUF>(ktile + off, slot + i * 1024);   // shuffled: whole lines
   }
   const uint8_t* vbase = sp.v;
 #pragma unroll
@@ -579,7 +562,7 @@ __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& i
       const int u = 2 * i + (lane >> 5), tau = (lane >> 1) & 15, c = 2 * u + (lane & 1);
       off = static_cast<size_t>(tau) * kStdRow2 + kD * 2 + c * 16;
     }
-    pdma16(vbase + off, slot + kHalf2 + i * 1024);
+    dma16_lds<SHUF>(vbase + off, slot + kHalf2 + i * 1024);
   }
 }
 

@@ -77,13 +77,6 @@ __device__ __forceinline__ void wait_vmcnt_pages(int k) {
   wait_vmcnt<0>();
 }
 
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_uniform) {
-  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(g), "s"(lds) : "memory", "m0");
-}
-
 // One 16-token sub-page (this wave's) into its ring slot: K half chunk-major
 // [c][token][16 B]; V half row-major [token][channels] (standard) or the
 // plane's sub-page as is (shuffled).
@@ -99,7 +92,7 @@ __device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it
     const int c = 4 * i + (lane >> 4), tau = lane & 15;
     const size_t off = SHUF ? static_cast<size_t>(c) * krow + tau * 16
                             : static_cast<size_t>(tau) * kStdRow + c * 16;
-    dma16(ktile + off, slot + i * 1024);
+    dma16_lds<SHUF>(ktile + off, slot + i * 1024);   // shuffled: whole lines
   }
 #pragma unroll
   for (int i = 0; i < kHalf / 1024; ++i) {
@@ -111,7 +104,7 @@ __device__ __forceinline__ void issue_page(const SegParams& p, const SegItem& it
       const int tau = i * (64 / kCpr) + lane / kCpr, c = lane % kCpr;
       off = static_cast<size_t>(tau) * kStdRow + kD * 2 + c * 16;
     }
-    dma16(vtile + off, slot + kHalf + i * 1024);
+    dma16_lds<true>(vtile + off, slot + kHalf + i * 1024);   // whole rows or the plane
   }
 }
 
@@ -174,9 +167,8 @@ void seg_valu_kernel(SegParams p) {
     const bool okr = r < it.rows;
     const int t = it.c0 + (okr ? r / p.G : 0);
     const int h = it.g * p.G + (okr ? r % p.G : 0);
-    dma16(reinterpret_cast<const uint8_t*>(p.q + (static_cast<size_t>(t) * p.Hq + h) * kD +
-                                           (lane & 15) * 8),
-          qslot);                                // padding rows read row 0
+    dma16_lds<false>(p.q + (static_cast<size_t>(t) * p.Hq + h) * kD + (lane & 15) * 8,
+                     qslot);                     // padding rows read row 0
   }
 #pragma unroll
   for (int k = 0; k < kNS - 1; ++k)
