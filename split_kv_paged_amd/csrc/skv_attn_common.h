@@ -259,6 +259,15 @@ __device__ __forceinline__ void dma16_lds_s(const uint8_t* base_uniform, uint32_
                  :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
 }
 
+// 16-bit standard pages in LDS (matrix-core kernels): a page is its 16 token
+// rows of 512 bytes (K channels, then V), copied two whole rows per DMA
+// instruction, with each row's thirty-two 16-byte chunks XOR-swizzled by
+// token: chunk q of row tau sits at position q ^ 2 tau. The K operand reads
+// (16 tokens of one chunk) and the transposing V reads (4 tokens of two
+// chunks per 16-lane group) then spread over all LDS banks. (An involution:
+// the DMA lane at position p fetches chunk std2_chunk_pos(tau, p).)
+__device__ __forceinline__ int std2_chunk_pos(int tau, int q) { return q ^ (2 * tau); }
+
 // The next unit (32-token block of the segment) a wave of the fp8
 // private-ring kernel streams after unit cur. Fixed order: wave w takes units
 // w, w + NW, w + 2 NW, ... Claimed (p.claim): the next unit not yet taken,

@@ -100,14 +100,6 @@ __device__ __forceinline__ void wait_vmcnt_stages(int k) {
 }
 
 
-// bf16 standard pages in LDS: a page is its 16 token rows of 512 bytes (K
-// channels, then V), each row's thirty-two 16-byte chunks XOR-swizzled by
-// token: chunk q of row tau sits at position q ^ 2 tau. The K operand reads
-// (16 tokens of one chunk) and the transposing V reads (4 tokens of two
-// chunks per 16-lane group) then spread over all LDS banks. (An involution:
-// the DMA lane at position p fetches chunk std2_chunk_pos(tau, p).)
-__device__ __forceinline__ int std2_chunk_pos(int tau, int q) { return q ^ (2 * tau); }
-
 // Issue this wave's DMA units of one stage. Unit u of the stage is (16-token
 // sub-page u/2, K half if u even, V half if odd); wave w issues units
 // [w*UPW, (w+1)*UPW). v0 is the stage's first sub-page in the sequence.

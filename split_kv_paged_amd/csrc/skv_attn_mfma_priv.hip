@@ -516,15 +516,14 @@ void seg_mfma_priv_kernel(SegParams p) {
 
 // ---- bf16 KV: a 32-token block is 16 KB, so the private slots are pages ----
 //
-// One 16-token page (K 4 KB, V 4 KB) per slot. Scores per page as above; P.V
-// with v_mfma_f32_16x16x16bf16_1k over the page's 16 tokens: the score MFMA's
-// C layout already holds 4 tokens of one row per lane (the B operand), and the
-// transposing 16-bit read of the chunk-major V tile gives each lane 4 tokens of
-// one channel (the A operand).
+// One 16-token page (16 token rows of K then V, 8 KB) per slot. Scores per page
+// as above; P.V with v_mfma_f32_16x16x16bf16_1k over the page's 16 tokens: the
+// score MFMA's C layout already holds 4 tokens of one row per lane (the B
+// operand), and the transposing 16-bit read of the swizzled rows gives each
+// lane 4 tokens of one channel (the A operand).
 constexpr int kHalf2 = kPageSize * kD * 2;              // a bf16 page's K (or V) half
 constexpr int kPage2 = 2 * kHalf2;
 constexpr int kPageInstr2 = kPage2 / 1024;
-constexpr int kStdTile2 = kPageSize * 2 * kD * 2;
 constexpr int kStdRow2 = 2 * kD * 2;
 typedef i16x4_t v4i16_t;
 
@@ -536,34 +535,30 @@ struct PRing2 {
   static_assert((kNP - 1) * kPageInstr2 <= 63, "vmcnt range");
 };
 
-// one page into a slot: K chunk-major for the operand lanes, V in the
-// chunk-pair-major tile of the transposing read ([pair][token][32 B]), or the
-// shuffled planes as they are
+// one page into a slot: standard pages as 16 whole token rows (two per
+// instruction, streamed, chunks swizzled by std2_chunk_pos); the shuffled
+// planes as they are (K plane rows and the V plane are whole lines too)
 template <bool SHUF, int PSH>
 __device__ __forceinline__ void issue_page2(const SegParams& p, const SegItem& it, int pid,
                                             int sub, uint8_t* slot, int lane) {
   const int r16 = lane & 15, j4 = lane >> 4;
   const SubPageAddr sp = sub_page<2, SHUF, PSH>(p, it.g, pid, sub);
-  const uint8_t* ktile = sp.k;
+  if constexpr (!SHUF) {
+#pragma unroll
+    for (int i = 0; i < kPage2 / 1024; ++i) {
+      const int row = 2 * i + (lane >> 5);
+      const int q = std2_chunk_pos(row, lane & 31);          // the chunk stored there
+      dma16_lds<true>(sp.k + static_cast<size_t>(row) * kStdRow2 + q * 16, slot + i * 1024);
+    }
+    return;
+  }
   const int krow = kplane_row_bytes<PSH>();
 #pragma unroll
-  for (int i = 0; i < kHalf2 / 1024; ++i) {
-    const size_t off = SHUF ? static_cast<size_t>(4 * i + j4) * krow + r16 * 16
-                            : static_cast<size_t>(r16) * kStdRow2 + (32 * i + 8 * j4) * 2;
-    dma16_lds<SHUF>(ktile + off, slot + i * 1024);   // shuffled: whole lines
-  }
-  const uint8_t* vbase = sp.v;
+  for (int i = 0; i < kHalf2 / 1024; ++i)
+    dma16_lds<true>(sp.k + static_cast<size_t>(4 * i + j4) * krow + r16 * 16, slot + i * 1024);
 #pragma unroll
-  for (int i = 0; i < kHalf2 / 1024; ++i) {
-    size_t off;
-    if constexpr (SHUF) {
-      off = static_cast<size_t>(i * 64 + lane) * 16;
-    } else {
-      const int u = 2 * i + (lane >> 5), tau = (lane >> 1) & 15, c = 2 * u + (lane & 1);
-      off = static_cast<size_t>(tau) * kStdRow2 + kD * 2 + c * 16;
-    }
-    dma16_lds<SHUF>(vbase + off, slot + kHalf2 + i * 1024);
-  }
+  for (int i = 0; i < kHalf2 / 1024; ++i)
+    dma16_lds<true>(sp.v + static_cast<size_t>(i * 64 + lane) * 16, slot + kHalf2 + i * 1024);
 }
 
 template <bool SHUF, int NRT, int NW, bool F16, int PSH>
@@ -632,10 +627,12 @@ void seg_mfma_priv2_kernel(SegParams p) {
     for (int dt = 0; dt < 8; ++dt) oacc[t][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   // transposing 16-bit read: in each 16-lane group lane i receives element i%4
-  // of the 8 bytes read by lane 4k + i/4; lane j reads token 4*j4 + j/4,
-  // channels 16dt + 4(j%4) .. +3, so lane i gets tokens 4*j4 .. +3 of channel
-  // 16dt + i (512 contiguous bytes per channel tile)
-  const int vtr_off = (4 * j4 + (r16 >> 2)) * 32 + ((r16 >> 1) & 1) * 16 + (r16 & 1) * 8;
+  // of the 8 bytes read by lane 4k + i/4; lane j reads token tau = 4*j4 + j/4,
+  // channels 16dt + 4(j%4) .. +3 (half j%2 of V chunk 2dt + (j/2)%2, at its
+  // swizzled position in the token's row), so lane i gets tokens 4*j4 .. +3 of
+  // channel 16dt + i
+  const int vtr_tau = 4 * j4 + (r16 >> 2);
+  const int vtr_row = vtr_tau * kStdRow2 + (r16 & 1) * 8;
 
   for (int k = 0; k < np; ++k) {
     if (k + kNP - 1 < np)                       // slot of page k-1, consumed last iteration
@@ -651,7 +648,9 @@ void seg_mfma_priv2_kernel(SegParams p) {
     bf16x8_t kop[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(sK + kk * 1024 + lane * 16));
+      kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          SHUF ? sK + kk * 1024 + lane * 16
+               : sK + r16 * kStdRow2 + std2_chunk_pos(r16, 4 * kk + j4) * 16));
     v4i16_t pb[NRT];
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
@@ -699,7 +698,8 @@ void seg_mfma_priv2_kernel(SegParams p) {
       } else {
         const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) v4i16_t*)(
-                (__attribute__((address_space(3))) uint8_t*)(sV) + vtr_off + dt * 512));
+                (__attribute__((address_space(3))) uint8_t*)(sK) + vtr_row +
+                std2_chunk_pos(vtr_tau, 16 + 2 * dt + ((r16 >> 1) & 1)) * 16));
         w = __builtin_bit_cast(uint2, v);
       }
       if (tail) {                    // zero V of tokens past the segment end
