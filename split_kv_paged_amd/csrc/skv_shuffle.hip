@@ -36,6 +36,18 @@ struct ShufGeom {
   static constexpr int kChunks = kTileBytes / 16;     // 16-byte chunks per tile
 };
 
+// Global 16-byte loads and stores with the non-temporal (streaming) cache
+// policy: every byte is read once and written once, and streamed accesses
+// reach markedly more of the HBM bandwidth than the default policy.
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gld16(const uint8_t* p) {
+  const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gst16(uint8_t* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt*>(p));
+}
+
 template <int E, int kN>
 __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ kpl,
@@ -59,7 +71,7 @@ __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
   uint4 buf[G::kChunks / 64];
 #pragma unroll
   for (int k = 0; k < G::kChunks / 64; ++k)
-    buf[k] = reinterpret_cast<const uint4*>(s)[k * 64 + lane];
+    buf[k] = gld16(s + 16 * (k * 64 + lane));
 #pragma unroll
   for (int k = 0; k < G::kChunks / 64; ++k) {
     const int c = k * 64 + lane;
@@ -75,8 +87,7 @@ __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
   for (int k = 0; k < kKChunks / 64; ++k) {
     const int o = k * 64 + lane;
     const int c = o / kN, n = o % kN;
-    reinterpret_cast<uint4*>(kd)[o] =
-        *reinterpret_cast<const uint4*>(t + n * G::kLdsRow + c * 16);
+    gst16(kd + 16 * o, *reinterpret_cast<const uint4*>(t + n * G::kLdsRow + c * 16));
   }
   // 3. V plane: output chunk o = g * D + d holds tokens g*x .. g*x + x - 1 of
   //    V channel d (byte offset D*E + d*E in each row)
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
         w[q] = v;
       }
     }
-    reinterpret_cast<uint4*>(vd)[o] = make_uint4(w[0], w[1], w[2], w[3]);
+    gst16(vd + 16 * o, make_uint4(w[0], w[1], w[2], w[3]));
   }
 }
 
