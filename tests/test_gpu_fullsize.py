@@ -45,6 +45,7 @@ SAMPLES = {
     "shuffled_decode": [0, 64, 127],
     "uniform_verify_fp8": [0, 15],
     "agentic_skew_fp8": [0, 3, 4, 19],
+    "uniform_verify_fp16": [0, 15],
 }
 
 
