@@ -8,7 +8,9 @@ also as a fraction of the 8 TB/s HBM peak. Per-kernel durations come from HIP
 events recorded on the stream the kernels run on. For shuffled-page workloads
 the standard->shuffled repack runs before the timed steps and is timed on its
 own, as is the in-place conversion of the same pool received as byte halves
-(and its inverse).
+(and its inverse). A KV pool much smaller than 2 GiB (the fp8 batches) is
+timed on several copies of itself used in turn, so that no call is served from
+the lines the previous call left in the 256 MB last-level cache.
 
 Prints ONE JSON line (rank 0). Default workload: the uniform verify batch
 (bs=16 x 119k tokens, 4 query tokens, 32/2 heads, bf16). `--all` adds the other
@@ -27,6 +29,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# A KV pool small next to the 256 MB last-level cache is timed on several
+# copies used in turn (together at least this many bytes, at most 8 copies),
+# so that no call reads lines the previous call left in that cache.
+ROTATE_BYTES = 2 << 30
 
 
 def _args():
@@ -166,6 +172,11 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         # restore the planes for the attention steps
         skv.kv_page_shuffle(case.kv, kp, vp)
         kv_a, kv_b = kp, vp
+    pool = sum(t.numel() * t.element_size() for t in (kv_a, kv_b) if t is not None)
+    ncopy = max(1, min(8, -(-ROTATE_BYTES // pool)))
+    kvs = [(kv_a, kv_b)] + [(kv_a.clone(), None if kv_b is None else kv_b.clone())
+                            for _ in range(ncopy - 1)]
+    res["kv_copies"] = ncopy
     rows = cfg.total_q * cfg.q_heads * cfg.seg_max
     part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
     part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
@@ -179,7 +190,8 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
               seg_max=cfg.seg_max, kv_dtype=cfg.kv_dtype, layout=cfg.layout,
               k_scale=case.k_scale, v_scale=case.v_scale, causal=cfg.causal)
 
-    def step(ev=None):
+    def step(ev=None, i=0):
+        kv_a, kv_b = kvs[i % ncopy]
         if ev:
             ev[0].record(st)
         skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, cfg.kv_heads,
@@ -195,13 +207,13 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         if ev:
             ev[3].record(st)
 
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i=i)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        step(evs[i])
+        step(evs[i], i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     plan_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / steps
@@ -220,7 +232,7 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
     # the same attention call captured once in a HIP graph and replayed, as a
     # serving loop runs decode steps: launch gaps between segment and reduce go
-    def attn_call():
+    def attn_call(kv_a, kv_b):
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                          case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
@@ -229,27 +241,30 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
     side = torch.cuda.Stream()
     side.wait_stream(st)
     with torch.cuda.stream(side):
-        attn_call()
+        attn_call(*kvs[0])
     st.wait_stream(side)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        attn_call()
-    for _ in range(warmup):
-        graph.replay()
+    graphs = []
+    for kv in kvs:                     # one graph per KV copy, replayed in turn
+        graphs.append(torch.cuda.CUDAGraph())
+        with torch.cuda.graph(graphs[-1]):
+            attn_call(*kv)
+    for i in range(warmup):
+        graphs[i % ncopy].replay()
     gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         gev[i][0].record(st)
-        graph.replay()
+        graphs[i % ncopy].replay()
         gev[i][1].record(st)
     torch.cuda.synchronize()
     res["graph_us_per_call"] = sum(e[0].elapsed_time(e[1]) for e in gev) * 1e3 / steps
     res["graph_kv_tb_s"] = kvb / res["graph_us_per_call"] / 1e6
-    del graph
+    del graphs
 
     # the fixed split on the same batch (no plan; the segment kernel writes the
     # per-token counts): the pages' A/B comparison, on these kernels
-    def fixed_call(ev=None):
+    def fixed_call(ev=None, i=0):
+        kv_a, kv_b = kvs[i % ncopy]
         if ev:
             ev[0].record(st)
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
@@ -259,16 +274,16 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         if ev:
             ev[1].record(st)
 
-    for _ in range(warmup):
-        fixed_call()
+    for i in range(warmup):
+        fixed_call(i=i)
     fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
-        fixed_call(fev[i])
+        fixed_call(fev[i], i)
     torch.cuda.synchronize()
     fixed_us = sum(e[0].elapsed_time(e[1]) for e in fev) * 1e3 / steps
     res.update(fixed_split_us_per_call=fixed_us, fixed_split_kv_tb_s=kvb / fixed_us / 1e6,
                fixed_split_segments=_fixed_segments(cfg))
-    del case, part_o, part_lse, out
+    del case, part_o, part_lse, out, kvs
     torch.cuda.empty_cache()
     return res
 
@@ -368,7 +383,7 @@ def main():
                    "kv_heads": cfg.kv_heads, "head_dim": cfg.head_dim,
                    "page_size": cfg.page_size, "kv_dtype": cfg.kv_dtype,
                    "layout": cfg.layout, "num_cus": cfg.num_cus, "seg_max": cfg.seg_max,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "kv_copies": head["kv_copies"]},
         "us_per_call": round(head["attn_us_per_call"], 2),
         "frac_of_hbm_peak": round(head["frac_of_hbm_peak"], 4),
         "breakdown_us": {k: round(head[k], 2) for k in
