@@ -54,6 +54,7 @@ def _args():
 
 # the sources the segment-attention kernels are compiled from
 SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip", "skv_attn_valu.hip",
+                   "skv_attn_gd.hip",
                    "skv_attn_common.h", "skv_internal.h")
 
 
@@ -203,7 +204,8 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         if ev:
             ev[2].record(st)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
+                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
+                         out_dtype=odt)
         if ev:
             ev[3].record(st)
 
@@ -236,7 +238,8 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                          case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
+                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
+                         out_dtype=odt)
 
     side = torch.cuda.Stream()
     side.wait_stream(st)
@@ -270,7 +273,8 @@ def time_workload(cfg, steps, warmup, torch, skv, gen):
         skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                          case.cu_seqlens_q, None, tok, part_o=part_o, part_lse=part_lse, **kw)
         skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, out=out, out_dtype=odt)
+                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
+                         out_dtype=odt)
         if ev:
             ev[1].record(st)
 

@@ -33,7 +33,10 @@
  * (kv_dtype 1) with per-tensor fp32 dequant scales, or IEEE binary16 fp16
  * (kv_dtype 2; the RFC's decoder scope is BF16/FP16). Q and the output are
  * fp16 with an fp16 cache and bf16 otherwise.
- * Supported geometry: head_dim 128; page_size 16 or 32 tokens for every
+ * Supported geometry: head_dim 64, 128 or 256 for the plan, attention, split
+ * reduce and shuffle entry points (128 on kernels specialised for it, 64 and
+ * 256 on a generic-width segment kernel), 128 for the in-place conversion,
+ * the unshuffle and the cache writer; page_size 16 or 32 tokens for every
  * entry point (the RFC's decoder scope: 16- or 32-token pages; the split-KV
  * PR's kernels use 16); 1..4 query tokens per sequence,
  * (q_heads / kv_heads) * max_q <= 64.
@@ -151,7 +154,7 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
  * scales present for bf16/fp16 or missing for fp8, kv_b NULL for SHUFFLED or
  * non-NULL for STANDARD, pt_stride < 1, an unknown layout, dtype or flag;
- * EUNSUPPORTED for head_dim != 128, page_size other than 16 or 32, max_q > 4,
+ * EUNSUPPORTED for head_dim not 64, 128 or 256, page_size other than 16 or 32, max_q > 4,
  * (q_heads/kv_heads) * max_q > 64. */
 int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
                           int layout, int kv_dtype, const int32_t* page_table,
@@ -188,7 +191,8 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
  * out_dtype (SKV_KV_BF16: bf16, SKV_KV_FP16: fp16; round to nearest even);
  * out_lse may be NULL.
  * Errors: EINVAL for NULL required pointers, non-positive sizes, seg_max
- * outside [1, 65535], another out_dtype; EUNSUPPORTED for head_dim != 128. */
+ * outside [1, 65535], another out_dtype; EUNSUPPORTED for head_dim not 64, 128
+ * or 256. */
 int skv_split_reduce(const float* part_o, const float* part_lse,
                      const int32_t* tok_nseg, int total_q, int q_heads,
                      int head_dim, int seg_max, int out_dtype, void* out,
@@ -202,8 +206,8 @@ int skv_split_reduce(const float* part_o, const float* part_lse,
  * with x = 16 / elem_bytes. Pure byte movement, bit-exact. Out of place: the
  * source must not overlap the planes. Blocks not listed are left untouched.
  * Errors: EINVAL for NULL required pointers, num_blocks < 1, kv_heads < 1;
- * EUNSUPPORTED for head_dim != 128, page_size not 16 or 32, elem_bytes not 1
- * or 2. */
+ * EUNSUPPORTED for head_dim not 64, 128 or 256, page_size not 16 or 32,
+ * elem_bytes not 1 or 2. */
 int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                         const int32_t* block_ids, int num_blocks, int kv_heads,
                         int page_size, int head_dim, int elem_bytes,

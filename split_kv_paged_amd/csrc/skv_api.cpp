@@ -10,7 +10,8 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
                              int kv_dtype, const int32_t* page_table, int pt_stride,
                              const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                              int total_q, int max_q, int q_heads, int kv_heads,
-                             int page_size, const float* k_scale, const float* v_scale,
+                             int head_dim, int page_size, const float* k_scale,
+                             const float* v_scale,
                              int causal,
                              const int32_t* plan, int32_t* tok_nseg, int num_cus,
                              int seg_max, float* part_o, float* part_lse, int flags) {
@@ -28,6 +29,7 @@ skv::AttnArgs make_attn_args(const void* q, const void* kv_a, const void* kv_b, 
   a.bs = bs;
   a.total_q = total_q;
   a.max_q = max_q;
+  a.head_dim = head_dim;
   a.q_heads = q_heads;
   a.kv_heads = kv_heads;
   a.page_size = page_size;
@@ -87,7 +89,7 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
   if (st != SKV_OK) return st;
   return skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                              pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
-                                             max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
+                                             max_q, q_heads, kv_heads, head_dim, page_size, k_scale, v_scale,
                                              causal, plan, tok_nseg, num_cus, seg_max,
                                              part_o, part_lse, flags),
                               stream);
@@ -111,12 +113,12 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
   if (st != SKV_OK) return st;
   st = skv::launch_segments(make_attn_args(q, kv_a, kv_b, layout, kv_dtype, page_table,
                                            pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
-                                           max_q, q_heads, kv_heads, page_size, k_scale, v_scale,
+                                           max_q, q_heads, kv_heads, head_dim, page_size, k_scale, v_scale,
                                            causal, plan, tok_nseg, num_cus, seg_max,
                                            part_o, part_lse, flags),
                             stream);
   if (st != SKV_OK) return st;
-  return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads,
+  return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads, head_dim,
                             seg_max, kv_dtype == SKV_KV_FP16, out, out_lse, stream);
 }
 
@@ -127,7 +129,7 @@ int skv_split_reduce(const float* part_o, const float* part_lse,
   int st = skv::check_reduce_args(part_o, part_lse, tok_nseg, total_q, q_heads,
                                   head_dim, seg_max, out_dtype, out);
   if (st != SKV_OK) return st;
-  return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads,
+  return skv::launch_reduce(part_o, part_lse, tok_nseg, total_q, q_heads, head_dim,
                             seg_max, out_dtype == SKV_KV_FP16, out, out_lse, stream);
 }
 
@@ -139,7 +141,7 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                                    kv_heads, page_size, head_dim, elem_bytes);
   if (st != SKV_OK) return st;
   return skv::launch_shuffle(std_cache, k_plane, v_plane, block_ids, num_blocks,
-                             kv_heads, page_size, elem_bytes, stream);
+                             kv_heads, page_size, head_dim, elem_bytes, stream);
 }
 
 int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
@@ -157,10 +159,12 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
                           void* std_cache, const int32_t* block_ids,
                           int num_blocks, int kv_heads, int page_size,
                           int head_dim, int elem_bytes, void* stream) {
-  // same argument rules as the forward repack
+  // the forward repack's argument rules; its kernel (the conversion's) is
+  // built for head dim 128 only
   int st = skv::check_shuffle_args(std_cache, k_plane, v_plane, num_blocks,
                                    kv_heads, page_size, head_dim, elem_bytes);
   if (st != SKV_OK) return st;
+  if (head_dim != skv::kHeadDim) return SKV_EUNSUPPORTED;
   return skv::launch_unshuffle(k_plane, v_plane, std_cache, block_ids,
                                num_blocks, kv_heads, page_size, elem_bytes, stream);
 }

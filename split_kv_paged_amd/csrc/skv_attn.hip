@@ -17,6 +17,8 @@ int launch_segments_valu(const SegParams& sp, bool shuf, bool f16, bool dual, in
 int launch_segments_mfma_priv(const SegParams& sp, int e, bool f16, bool shuf, int max_rows,
                               int grid,
                               hipStream_t st);
+int launch_segments_gd(const SegParams& sp, int head_dim, int e, bool f16, bool shuf, int grid,
+                       hipStream_t st);
 
 // Which kernel runs, by element type and query rows (GQA group x max query
 // tokens); measured on MI355X:
@@ -77,6 +79,8 @@ int launch_segments(const AttnArgs& a, void* stream) {
   // prologue and merge overlap the other's streaming instead of leaving the
   // CU idle between consecutive work-groups (the 8-wave kernels gain nothing)
   const bool dual = grid > a.num_cus;
+  if (a.head_dim != kHeadDim)             // 64 or 256: the generic-width kernel
+    return launch_segments_gd(sp, a.head_dim, e, f16, shuf, static_cast<int>(grid), st);
   if (e == 2 && rows <= kValuMaxRows)
     return launch_segments_valu(sp, shuf, f16, dual, static_cast<int>(grid), st);
   if (e == 1 || rows <= kPrivMaxRowsBf16)

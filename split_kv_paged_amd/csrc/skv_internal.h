@@ -22,6 +22,11 @@ constexpr int kMaxConvertBytes = 128 * 1024;   // one block staged in LDS
 inline bool repack_page_size_ok(int page_size) { return page_size == 16 || page_size == 32; }
 inline int page_shift_of(int page_size) { return page_size == 32 ? 5 : 4; }   // log2
 
+// head dims of the attention, reduce and shuffle entry points (128 on the
+// specialised kernels; 64 and 256 on the generic-width segment kernel); the
+// in-place conversion, the unshuffle and the cache writer take 128 only
+inline bool head_dim_ok(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+
 // ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
 int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
                     int total_q, int kv_heads, int page_size, int num_cus,
@@ -79,6 +84,7 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* cu_seqlens_q;
   int bs, total_q, max_q, q_heads, kv_heads;
+  int head_dim;              // 64, 128 or 256
   int page_size;             // 16 or 32 tokens
   const float* k_scale;
   const float* v_scale;
@@ -98,11 +104,11 @@ int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                 int causal, int32_t* plan, int32_t* tok_nseg, void* stream);
 int launch_segments(const AttnArgs& a, void* stream);
 int launch_reduce(const float* part_o, const float* part_lse,
-                  const int32_t* tok_nseg, int total_q, int q_heads,
+                  const int32_t* tok_nseg, int total_q, int q_heads, int head_dim,
                   int seg_max, bool out_f16, void* out, float* out_lse, void* stream);
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
-                   int page_size, int elem_bytes, void* stream);
+                   int page_size, int head_dim, int elem_bytes, void* stream);
 int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
                    int num_blocks, int kv_heads, int page_size, int elem_bytes,
                    int direction, void* stream);

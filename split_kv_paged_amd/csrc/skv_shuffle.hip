@@ -8,7 +8,8 @@
 //
 // MI355X design: one wave64 per (listed block, head); 16- or 32-token pages
 // (the RFC's decoders use both). The wave copies the head's whole standard
-// tile (8 KB bf16 / 4 KB fp8 per 16 tokens) into LDS with coalesced 16-byte
+// tile (16 x 2D elements per 16 tokens: 8 KB bf16 at head dim 128) into LDS
+// with coalesced 16-byte
 // loads (1 KB contiguous per wave instruction), then writes both planes with
 // coalesced 16-byte stores: a K chunk is one 16-byte row chunk moved as a unit;
 // a V chunk gathers x tokens of one channel from LDS. Every HBM byte is read
@@ -24,9 +25,7 @@ namespace {
 
 constexpr int kShufThreads = 256;
 constexpr int kShufWaves = kShufThreads / 64;
-constexpr int kD = kHeadDim;
-
-template <int E, int kN>
+template <int E, int kN, int kD>
 struct ShufGeom {
   static constexpr int kX = 16 / E;                   // elements per 16 bytes
   static constexpr int kRowBytes = 2 * kD * E;        // one standard token row
@@ -48,12 +47,12 @@ __device__ __forceinline__ void gst16(uint8_t* p, uint4 v) {
   __builtin_nontemporal_store(u32x4_nt{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_nt*>(p));
 }
 
-template <int E, int kN>
+template <int E, int kN, int kD>
 __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
     const uint8_t* __restrict__ src, uint8_t* __restrict__ kpl,
     uint8_t* __restrict__ vpl, const int32_t* __restrict__ block_ids,
     int num_units, int kv_heads) {
-  using G = ShufGeom<E, kN>;
+  using G = ShufGeom<E, kN, kD>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kShufWaves][kN * G::kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int unit = blockIdx.x * kShufWaves + wave;
@@ -115,26 +114,39 @@ __global__ __launch_bounds__(kShufThreads) void shuffle_kernel(
   }
 }
 
-template <int kN>
+template <int kN, int kD>
 int launch_shuffle_n(const uint8_t* s, uint8_t* k, uint8_t* v, const int32_t* block_ids,
                      long long units, int kv_heads, int elem_bytes, hipStream_t st) {
   const long long blocks = (units + kShufWaves - 1) / kShufWaves;
   if (elem_bytes == 2)
-    hipLaunchKernelGGL((shuffle_kernel<2, kN>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((shuffle_kernel<2, kN, kD>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kShufThreads), 0, st, s, k, v, block_ids,
                        static_cast<int>(units), kv_heads);
   else
-    hipLaunchKernelGGL((shuffle_kernel<1, kN>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((shuffle_kernel<1, kN, kD>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kShufThreads), 0, st, s, k, v, block_ids,
                        static_cast<int>(units), kv_heads);
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+template <int kN>
+int launch_shuffle_d(const uint8_t* s, uint8_t* k, uint8_t* v, const int32_t* block_ids,
+                     long long units, int kv_heads, int head_dim, int elem_bytes,
+                     hipStream_t st) {
+  if (head_dim == 64)
+    return launch_shuffle_n<kN, 64>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
+  if (head_dim == 256)
+    return launch_shuffle_n<kN, 256>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
+  if (head_dim == kHeadDim)
+    return launch_shuffle_n<kN, kHeadDim>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
+  return SKV_EUNSUPPORTED;
 }
 
 }  // namespace
 
 int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
-                   int page_size, int elem_bytes, void* stream) {
+                   int page_size, int head_dim, int elem_bytes, void* stream) {
   const long long units = static_cast<long long>(num_blocks) * kv_heads;
   if (units > 0x7fffffffLL) return SKV_EUNSUPPORTED;
   auto st = static_cast<hipStream_t>(stream);
@@ -142,8 +154,8 @@ int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
   auto k = static_cast<uint8_t*>(k_plane);
   auto v = static_cast<uint8_t*>(v_plane);
   if (page_size == 32)
-    return launch_shuffle_n<32>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
-  return launch_shuffle_n<16>(s, k, v, block_ids, units, kv_heads, elem_bytes, st);
+    return launch_shuffle_d<32>(s, k, v, block_ids, units, kv_heads, head_dim, elem_bytes, st);
+  return launch_shuffle_d<16>(s, k, v, block_ids, units, kv_heads, head_dim, elem_bytes, st);
 }
 
 }  // namespace skv

@@ -45,7 +45,7 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
   if (q_heads % kv_heads != 0) return SKV_EINVAL;
   if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
   if (max_q < 1) return SKV_EINVAL;
-  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (max_q > kMaxQ) return SKV_EUNSUPPORTED;
   if ((q_heads / kv_heads) * max_q > kMaxRows) return SKV_EUNSUPPORTED;
   return SKV_OK;
@@ -58,7 +58,7 @@ int check_reduce_args(const void* part_o, const void* part_lse,
   if (out_dtype != SKV_KV_BF16 && out_dtype != SKV_KV_FP16) return SKV_EINVAL;
   if (total_q < 1 || q_heads < 1 || head_dim < 1) return SKV_EINVAL;
   if (seg_max < 1 || seg_max > kMaxSegMax) return SKV_EINVAL;
-  if (head_dim != kHeadDim) return SKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim)) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }
 
@@ -68,7 +68,7 @@ int check_shuffle_args(const void* std_cache, const void* k_plane,
   if (!std_cache || !k_plane || !v_plane) return SKV_EINVAL;
   if (num_blocks < 1 || kv_heads < 1 || page_size < 1 || head_dim < 1)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   return SKV_OK;
 }

@@ -82,7 +82,7 @@ def _attn(**kw):
     (dict(q=None), 1), (dict(kv_a=None), 1), (dict(pt=None), 1),
     (dict(tok=None), 1), (dict(part_o=None), 1), (dict(part_lse=None), 1), (dict(out=None), 1),
     (dict(plan=None, tok=None), 1),                       # the fixed split writes tok_nseg
-    (dict(plan=None, head_dim=64), 2),
+    (dict(plan=None, head_dim=96), 2),
     (dict(seq_lens=None), 1), (dict(cu=None), 1),
     (dict(layout=2), 1), (dict(kv_dtype=3), 1), (dict(kv_dtype=-1), 1),
     (dict(layout=1), 1),                                  # shuffled needs the V plane
@@ -94,7 +94,8 @@ def _attn(**kw):
     (dict(q_heads=12, kv_heads=8), 1), (dict(bs=0), 1), (dict(bs=40000), 1),
     (dict(total_q=0), 1), (dict(max_q=0), 1), (dict(seg_max=0), 1), (dict(seg_max=70000), 1),
     (dict(pt_stride=0), 1), (dict(num_cus=0), 1), (dict(kv_heads=0), 1),
-    (dict(head_dim=64), 2), (dict(page_size=64), 2), (dict(page_size=24), 2), (dict(max_q=5), 2),
+    (dict(head_dim=96), 2), (dict(head_dim=512), 2), (dict(head_dim=32), 2),
+    (dict(page_size=64), 2), (dict(page_size=24), 2), (dict(max_q=5), 2),
     (dict(q_heads=32, kv_heads=2, max_q=8), 2),           # rows 128 > 64 (max_q checked first)
     (dict(q_heads=64, kv_heads=2, max_q=3), 2),           # rows 96 > 64
     (dict(flags=2), 1), (dict(flags=-1), 1), (dict(flags=3), 1),
@@ -121,7 +122,7 @@ def _reduce(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(po=None), 1), (dict(pl=None), 1), (dict(tok=None), 1), (dict(out=None), 1),
     (dict(total_q=0), 1), (dict(q_heads=0), 1), (dict(seg_max=0), 1), (dict(seg_max=65536), 1),
-    (dict(head_dim=64), 2), (dict(odt=1), 1), (dict(odt=3), 1), (dict(odt=-1), 1),
+    (dict(head_dim=96), 2), (dict(head_dim=512), 2), (dict(odt=1), 1), (dict(odt=3), 1), (dict(odt=-1), 1),
 ])
 def test_reduce_errors(kw, code):
     assert _reduce(**kw) == code
@@ -136,7 +137,7 @@ def _shuffle(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(src=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
-    (dict(hd=64), 2), (dict(ps=64), 2), (dict(ps=8), 2), (dict(e=4), 2),
+    (dict(hd=96), 2), (dict(hd=512), 2), (dict(ps=64), 2), (dict(ps=8), 2), (dict(e=4), 2),
 ])
 def test_shuffle_errors(kw, code):
     assert _shuffle(**kw) == code

@@ -46,6 +46,8 @@ SAMPLES = {
     "uniform_verify_fp8": [0, 15],
     "agentic_skew_fp8": [0, 3, 4, 19],
     "uniform_verify_fp16": [0, 15],
+    "uniform_verify_d64": [0, 15],
+    "uniform_verify_d256": [0, 15],
 }
 
 

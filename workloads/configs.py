@@ -101,5 +101,13 @@ AGENTIC_SKEW_FP8 = Config("agentic_skew_fp8", SKEW_LENS, SKEW_Q, 32, 2, kv_dtype
 UNIFORM_VERIFY_FP16 = Config("uniform_verify_fp16", [119_000] * 16, [4] * 16, 32, 2,
                              kv_dtype="fp16", seed=8,
                              note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), fp16 Q and KV")
-EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, UNIFORM_VERIFY_FP16]
+# the uniform verify batch at head dims 64 and 256 (the generic-width kernel)
+UNIFORM_VERIFY_D64 = Config("uniform_verify_d64", [119_000] * 16, [4] * 16, 32, 2,
+                            head_dim=64, seed=9,
+                            note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), head dim 64, bf16")
+UNIFORM_VERIFY_D256 = Config("uniform_verify_d256", [119_000] * 16, [4] * 16, 32, 2,
+                             head_dim=256, seed=10,
+                             note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), head dim 256, bf16")
+EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64,
+         UNIFORM_VERIFY_D256]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
