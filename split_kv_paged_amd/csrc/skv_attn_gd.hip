@@ -293,48 +293,67 @@ void seg_gd_kernel(SegParams p) {
       continue;
     }
 
-    for (int b = grp; b < R::kBlocks; b += R::kGroups) {
-      const int tok0 = it.seg_start + i * R::kStageTok + 32 * b;
-      if (tok0 >= it.seg_end) break;
-      const uint8_t* sub[2] = {slot + (2 * b) * R::kSubBytes, slot + (2 * b + 1) * R::kSubBytes};
+    // NJ of this group's blocks at once (a 64-token step when the stage
+    // holds four or more blocks): twice the independent work between the
+    // dependent steps (scores, row max across lanes, exponentials, P.V), and
+    // one row-max update per 64 tokens
+    constexpr int NJ = R::kBlocks >= 2 * R::kGroups ? 2 : 1;
+    for (int b0 = grp; b0 < R::kBlocks; b0 += NJ * R::kGroups) {
+      int tokb[NJ];
+      const uint8_t* sub[NJ][2];
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+        const int b = b0 + jb * R::kGroups;
+        tokb[jb] = it.seg_start + i * R::kStageTok + 32 * b;
+        sub[jb][0] = slot + (2 * b) * R::kSubBytes;
+        sub[jb][1] = slot + (2 * b + 1) * R::kSubBytes;
+      }
+      if (tokb[0] >= it.seg_end) break;
 
       // ---- S^T per sub-page: lane holds tokens 4j4..4j4+3 of row r16 ----
-      f32x4_t sacc[2];
+      f32x4_t sacc[NJ][2];
 #pragma unroll
-      for (int pg = 0; pg < 2; ++pg) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int jb = 0; jb < NJ; ++jb) {
 #pragma unroll
-        for (int kk = 0; kk < kKS; ++kk) {
-          bf16x8_t kop;
-          if constexpr (SHUF && E == 2) {
-            kop = as_bf16x8(*reinterpret_cast<const uint4*>(sub[pg] + (4 * kk + j4) * 256 + r16 * 16));
-          } else if constexpr (SHUF) {
-            const uint2 c = *reinterpret_cast<const uint2*>(
-                sub[pg] + (2 * kk + (j4 >> 1)) * 256 + r16 * 16 + (j4 & 1) * 8);
-            kop = as_bf16x8(fp8x8_to_bf16x8(c));
-          } else if constexpr (E == 2) {
-            kop = as_bf16x8(*reinterpret_cast<const uint4*>(
-                sub[pg] + r16 * R::kRowBytes + gd_chunk_pos<D, E>(r16, 4 * kk + j4) * 16));
-          } else {
-            const uint2 c = *reinterpret_cast<const uint2*>(
-                sub[pg] + r16 * R::kRowBytes +
-                gd_chunk_pos<D, E>(r16, 2 * kk + (j4 >> 1)) * 16 + (j4 & 1) * 8);
-            kop = as_bf16x8(fp8x8_to_bf16x8(c));
+        for (int pg = 0; pg < 2; ++pg) {
+          const uint8_t* sp = sub[jb][pg];
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < kKS; ++kk) {
+            bf16x8_t kop;
+            if constexpr (SHUF && E == 2) {
+              kop = as_bf16x8(*reinterpret_cast<const uint4*>(sp + (4 * kk + j4) * 256 + r16 * 16));
+            } else if constexpr (SHUF) {
+              const uint2 c = *reinterpret_cast<const uint2*>(
+                  sp + (2 * kk + (j4 >> 1)) * 256 + r16 * 16 + (j4 & 1) * 8);
+              kop = as_bf16x8(fp8x8_to_bf16x8(c));
+            } else if constexpr (E == 2) {
+              kop = as_bf16x8(*reinterpret_cast<const uint4*>(
+                  sp + r16 * R::kRowBytes + gd_chunk_pos<D, E>(r16, 4 * kk + j4) * 16));
+            } else {
+              const uint2 c = *reinterpret_cast<const uint2*>(
+                  sp + r16 * R::kRowBytes +
+                  gd_chunk_pos<D, E>(r16, 2 * kk + (j4 >> 1)) * 16 + (j4 & 1) * 8);
+              kop = as_bf16x8(fp8x8_to_bf16x8(c));
+            }
+            acc = mfma_k32<F16>(kop, qb[kk], acc);
           }
-          acc = mfma_k32<F16>(kop, qb[kk], acc);
+          sacc[jb][pg] = acc;
         }
-        sacc[pg] = acc;
       }
 
-      // ---- online softmax (row n; 8 tokens per lane) ----
-      float s[8];
+      // ---- online softmax (row n; 8 NJ tokens per lane) ----
+      float s[NJ][8];
       float bm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
-        const float v = sacc[e >> 2][e & 3] * sm_scale;
-        s[e] = pos < lim ? v : -INFINITY;
-        bm = fmaxf(bm, s[e]);
+      for (int jb = 0; jb < NJ; ++jb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int pos = tokb[jb] + 16 * (e >> 2) + 4 * j4 + (e & 3);
+          const float v = sacc[jb][e >> 2][e & 3] * sm_scale;
+          s[jb][e] = pos < lim ? v : -INFINITY;
+          bm = fmaxf(bm, s[jb][e]);
+        }
       }
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -347,74 +366,83 @@ void seg_gd_kernel(SegParams p) {
         for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
         m = mn;
       }
-      uint32_t pk[4];
+      bf16x8_t pb[NJ];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float a = fast_exp2(s[e] - mu), c = fast_exp2(s[e + 1] - mu);
-        l += a + c;
-        pk[e >> 1] = pack2<F16>(a, c);
+      for (int jb = 0; jb < NJ; ++jb) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float a = fast_exp2(s[jb][e] - mu), c = fast_exp2(s[jb][e + 1] - mu);
+          l += a + c;
+          pk[e >> 1] = pack2<F16>(a, c);
+        }
+        pb[jb] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
       }
-      const bf16x8_t pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
       // ---- O^T += V^T.P^T; element e: sub-page e/4, token 4j4 + e%4 ----
-      const bool tail = tok0 + 32 > it.seg_end;
-      const int vend = it.seg_end - tok0;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
         const int d = 16 * dt + r16;
-        uint32_t w[4];
-        if constexpr (SHUF && E == 2) {
 #pragma unroll
-          for (int pg = 0; pg < 2; ++pg) {
-            const uint2 v = *reinterpret_cast<const uint2*>(
-                sub[pg] + R::kKBytes + ((j4 >> 1) * D + d) * 16 + (j4 & 1) * 8);
-            w[2 * pg] = v.x;
-            w[2 * pg + 1] = v.y;
-          }
-        } else if constexpr (SHUF) {
-          const uint32_t a = *reinterpret_cast<const uint32_t*>(sub[0] + R::kKBytes + d * 16 + 4 * j4);
-          const uint32_t c = *reinterpret_cast<const uint32_t*>(sub[1] + R::kKBytes + d * 16 + 4 * j4);
-          const uint4 x = fp8x8_to_bf16x8(make_uint2(a, c));
-          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-        } else if constexpr (E == 2) {
-          // transposing read: in each 16-lane group, lane i receives element
-          // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
-          // token 4j4 + j/4, V channels 16dt + 4(j%4) .. +3, so lane i ends up
-          // with tokens 4j4 .. 4j4+3 of channel 16dt + i.
-          const int tau = 4 * j4 + (r16 >> 2);
-          const int q = D / 8 + 2 * dt + ((r16 >> 1) & 1);
+        for (int jb = 0; jb < NJ; ++jb) {
+          uint32_t w[4];
+          if constexpr (SHUF && E == 2) {
 #pragma unroll
-          for (int pg = 0; pg < 2; ++pg) {
-            const v4i16_gd v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16_gd*)(
-                    (__attribute__((address_space(3))) uint8_t*)(sub[pg]) + tau * R::kRowBytes +
-                    gd_chunk_pos<D, E>(tau, q) * 16 + (r16 & 1) * 8));
-            const uint2 u = __builtin_bit_cast(uint2, v);
-            w[2 * pg] = u.x;
-            w[2 * pg + 1] = u.y;
+            for (int pg = 0; pg < 2; ++pg) {
+              const uint2 v = *reinterpret_cast<const uint2*>(
+                  sub[jb][pg] + R::kKBytes + ((j4 >> 1) * D + d) * 16 + (j4 & 1) * 8);
+              w[2 * pg] = v.x;
+              w[2 * pg + 1] = v.y;
+            }
+          } else if constexpr (SHUF) {
+            const uint32_t a =
+                *reinterpret_cast<const uint32_t*>(sub[jb][0] + R::kKBytes + d * 16 + 4 * j4);
+            const uint32_t c =
+                *reinterpret_cast<const uint32_t*>(sub[jb][1] + R::kKBytes + d * 16 + 4 * j4);
+            const uint4 x = fp8x8_to_bf16x8(make_uint2(a, c));
+            w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+          } else if constexpr (E == 2) {
+            // transposing read: in each 16-lane group, lane i receives element
+            // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
+            // token 4j4 + j/4, V channels 16dt + 4(j%4) .. +3, so lane i ends
+            // up with tokens 4j4 .. 4j4+3 of channel 16dt + i.
+            const int tau = 4 * j4 + (r16 >> 2);
+            const int q = D / 8 + 2 * dt + ((r16 >> 1) & 1);
+#pragma unroll
+            for (int pg = 0; pg < 2; ++pg) {
+              const v4i16_gd v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) v4i16_gd*)(
+                      (__attribute__((address_space(3))) uint8_t*)(sub[jb][pg]) +
+                      tau * R::kRowBytes + gd_chunk_pos<D, E>(tau, q) * 16 + (r16 & 1) * 8));
+              const uint2 u = __builtin_bit_cast(uint2, v);
+              w[2 * pg] = u.x;
+              w[2 * pg + 1] = u.y;
+            }
+          } else {
+            // transposing byte read: in each 16-lane group, lane i receives
+            // byte i%8 of the 8 bytes read by lane 2k + i/8 (k = 0..7). Lane j
+            // reads sub-page j/8, token 4j4 + (j/2)%4, V channels 16dt + 8(j%2)
+            // .. +7, so lane i ends up with the block's 8 tokens of channel
+            // 16dt + i.
+            const int tau = 4 * j4 + ((r16 >> 1) & 3);
+            const int q = D / 16 + dt;
+            const v2i32_gd v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i32_gd*)(
+                    (__attribute__((address_space(3))) uint8_t*)(sub[jb][r16 >> 3]) +
+                    tau * R::kRowBytes + gd_chunk_pos<D, E>(tau, q) * 16 + (r16 & 1) * 8));
+            const uint4 x = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
+            w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
           }
-        } else {
-          // transposing byte read: in each 16-lane group, lane i receives byte
-          // i%8 of the 8 bytes read by lane 2k + i/8 (k = 0..7). Lane j reads
-          // sub-page j/8, token 4j4 + (j/2)%4, V channels 16dt + 8(j%2) .. +7,
-          // so lane i ends up with the block's 8 tokens of channel 16dt + i.
-          const int tau = 4 * j4 + ((r16 >> 1) & 3);
-          const int q = D / 16 + dt;
-          const v2i32_gd v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) v2i32_gd*)(
-                  (__attribute__((address_space(3))) uint8_t*)(sub[r16 >> 3]) +
-                  tau * R::kRowBytes + gd_chunk_pos<D, E>(tau, q) * 16 + (r16 & 1) * 8));
-          const uint4 x = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
-          w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+          const int vend = it.seg_end - tokb[jb];
+          if (vend < 32) {               // zero V of tokens past the segment end
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) {
+              const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
+              w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
+            }
+          }
+          oacc[dt] = mfma_k32<F16>(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb[jb], oacc[dt]);
         }
-        if (tail) {                    // zero V of tokens past the segment end
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
-            w[q2] = rel <= 0 ? 0u : (rel == 1 ? (w[q2] & 0xffffu) : w[q2]);
-          }
-        }
-        oacc[dt] = mfma_k32<F16>(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, oacc[dt]);
       }
     }
   }
