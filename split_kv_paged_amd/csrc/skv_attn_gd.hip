@@ -14,12 +14,13 @@
 //    is one block (256-wide 16-bit rows), one 16-token sub-page of it each
 //    (scores and P.V on 16 tokens, the latter on the 16x16x16 instruction).
 //    Two waves share each SIMD and hide each other's latencies; the groups'
-//    states are merged through LDS at the end.
+//    states are merged through LDS at the end. A wave with two or more
+//    blocks per stage takes two per step (64 tokens between row-max updates).
 //  * KV streams through one 128 KB LDS ring shared by the waves, in four
-//    32 KB stages of 32-token blocks, by direct-to-LDS DMA (16 bytes per lane, 1 KB per instruction,
-//    whole cache lines, streaming policy). Each wave waits on its own DMA
-//    count, then one barrier per stage makes every wave's part visible and
-//    frees the slot computed one stage earlier.
+//    32 KB stages of 32-token blocks, by direct-to-LDS DMA (16 bytes per
+//    lane, 1 KB per instruction, whole cache lines, streaming policy). Each
+//    wave waits on its own DMA count, then one barrier per stage makes every
+//    wave's part visible and frees the slot computed one stage earlier.
 //  * Standard pages are copied as their contiguous 16-row tiles; the 16-byte
 //    chunks of each token row are XOR-swizzled by the row's index, so the 16
 //    rows of one K operand read, and the transposing V reads, fall on
