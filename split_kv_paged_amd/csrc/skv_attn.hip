@@ -32,6 +32,7 @@ int launch_segments_gd(const SegParams& sp, int head_dim, int e, bool f16, bool 
 //  * bf16, 33-64 rows: matrix cores on a ring shared by 8 waves (four row
 //    tiles per block do not fit two waves per SIMD in private form).
 // fp16 KV (with fp16 Q) takes the bf16 routes with the fp16 instructions.
+// Head dims 64 and 256 run on the generic-width kernel at every row count.
 constexpr int kValuMaxRows = 4;
 constexpr int kPrivMaxRowsBf16 = 32;
 
