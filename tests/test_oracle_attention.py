@@ -87,12 +87,14 @@ def test_scale_and_sign_against_exp_loops():
     assert lse == pytest.approx(m + math.log(tot), rel=1e-14)
 
 
+@pytest.mark.parametrize("head_dim", [128, 64, 256])
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8", "fp16"])
-def test_batch_matches_torch_sdpa_fp64(kv_dtype):
+def test_batch_matches_torch_sdpa_fp64(kv_dtype, head_dim):
     """Independent library routine: torch SDPA in float64 on gathered tensors,
-    with the bottom-right causal mask and grouped heads expanded by hand."""
+    with the bottom-right causal mask and grouped heads expanded by hand (its
+    default scale 1/sqrt(D) pins the oracle's at every head dim)."""
     lens, ql = [37, 100, 16, 1, 5], [1, 4, 3, 2, 4]
-    cfg, case = _case(lens, ql, q_heads=8, kv_heads=2, kv_dtype=kv_dtype)
+    cfg, case = _case(lens, ql, q_heads=8, kv_heads=2, kv_dtype=kv_dtype, head_dim=head_dim)
     out, lse = _oracle(cfg, case)
     q = torch.from_numpy(gen.raw_u16(case.q).view(np.int16)).view(
         torch.float16 if kv_dtype == "fp16" else torch.bfloat16).double().numpy()

@@ -20,10 +20,10 @@ def test_hand_derived_offsets(case):
     assert case["token"] * 2 * D + ch == case["std_flat"]
 
 
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (3, 1)])
-def test_bijection_and_inverse(H, e, N):
-    D = 128
+def test_bijection_and_inverse(H, e, N, D):
     B = 3
     std = np.arange(B * H * N * 2 * D, dtype=np.uint32).reshape(B, H, N, 2 * D)
     kp, vp = oracle.shuffle_blocks(std, elem_bytes=e)
