@@ -152,7 +152,7 @@ def _convert(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1), (dict(d=2), 1),
-    (dict(d=-1), 1), (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(d=-1), 1), (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
     (dict(h=17), 2), (dict(h=33, e=1), 2),               # block above 128 KiB
     (dict(h=9, ps=32), 2), (dict(h=17, ps=32, e=1), 2),
 ])
@@ -169,7 +169,7 @@ def _unshuffle(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dst=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
-    (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
 ])
 def test_unshuffle_errors(kw, code):
     assert _unshuffle(**kw) == code
@@ -188,7 +188,7 @@ def _write(**kw):
     (dict(k=None), 1), (dict(v=None), 1), (dict(slots=None), 1), (dict(kp=None), 1),
     (dict(vp=None), 1), (dict(T=0), 1), (dict(nb=0), 1), (dict(h=0), 1),
     (dict(ks=255), 1), (dict(vs=128), 1), (dict(ks=260), 1),       # below H*D / not a multiple of x
-    (dict(hd=64), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
     (dict(ksc=P), 1), (dict(vsc=P), 1),                  # one scale without the other
     (dict(ksc=P, vsc=P), 1),                              # quantising needs an fp8 cache
     (dict(ksc=P, vsc=P, e=1, ks=260), 1),                 # bf16 input rows: multiple of 8
