@@ -13,8 +13,10 @@
 //    groups take alternate 32-token blocks of a ring stage, or, where a stage
 //    is one block (256-wide 16-bit rows), one 16-token sub-page of it each
 //    (scores and P.V on 16 tokens, the latter on the 16x16x16 instruction).
-//    Two waves share each SIMD and hide each other's latencies; the groups'
-//    states are merged through LDS at the end. A wave with two or more
+//    Two waves share each SIMD and hide each other's latencies (three at head
+//    dim 64, whose per-byte softmax work is twice that at 128: three groups,
+//    six-block stages, a 144 KB ring for 16-bit rows); the groups' states are
+//    merged through LDS at the end. A wave with two or more
 //    blocks per stage takes two per step (64 tokens between row-max updates).
 //  * KV streams through one 128 KB LDS ring shared by the waves, in four
 //    32 KB stages of 32-token blocks, by direct-to-LDS DMA (16 bytes per
@@ -50,7 +52,10 @@ struct GdRing {
   static constexpr int kSubBytes = kPageSize * 2 * D * E;  // one 16-token sub-page, K and V
   static constexpr int kKBytes = kPageSize * D * E;        // its K part (shuffled planes)
   static constexpr int kBlkBytes = 2 * kSubBytes;          // one 32-token block
-  static constexpr int kBlocks = kGdStageTarget / kBlkBytes > 1 ? kGdStageTarget / kBlkBytes : 1;
+  // head dim 64: three wave groups, two blocks each per stage
+  static constexpr bool kThree = D == 64;
+  static constexpr int kBlocks = kThree ? 6
+                               : (kGdStageTarget / kBlkBytes > 1 ? kGdStageTarget / kBlkBytes : 1);
   static constexpr int kStageBytes = kBlocks * kBlkBytes;
   static constexpr int kStageTok = 32 * kBlocks;
   static constexpr int kInstr = kStageBytes / 1024;        // DMA instructions per stage
@@ -59,13 +64,13 @@ struct GdRing {
   // 16-token sub-page of the block each
   static constexpr bool kSubSplit = kBlocks == 1;
   static_assert(!kSubSplit || E == 2, "one-block stages only for 16-bit elements");
-  static constexpr int kGroups = 2;
+  static constexpr int kGroups = kThree ? 3 : 2;
   static constexpr int kWaves = 4 * kGroups;
   static_assert(kSubBytes % 1024 == 0, "a DMA instruction stays in one sub-page");
   static_assert(kKBytes % 1024 == 0, "a DMA instruction stays in K or in V");
   static_assert(kInstr % kWaves == 0, "every wave issues the same count");
   static constexpr int kInstrPerWave = kInstr / kWaves;
-  static constexpr int kNS0 = kGdRingBudget / kStageBytes;
+  static constexpr int kNS0 = (kThree && E == 2 ? 144 * 1024 : kGdRingBudget) / kStageBytes;
   static constexpr int kNS = kNS0 > 8 ? 8 : kNS0;
   static_assert(kNS >= 3, "ring needs three stages");
   static_assert((kNS - 2) * kInstrPerWave <= 63, "vmcnt range");
@@ -454,29 +459,42 @@ void seg_gd_kernel(SegParams p) {
   l += __shfl_xor(l, 32);
   float M = m, Ls = l;
   {
-    // group 1 hands its (m, l, O^T) to group 0 through the (now idle) ring
-    static_assert(4 * kDT * 1024 + 2 * 4 * 16 * 4 <= kNS * R::kStageBytes, "merge fits");
+    // groups 1 .. G-1 hand their (m, l, O^T) to group 0 through the (now
+    // idle) ring; slot k - 1 for group k
+    constexpr int kG = R::kGroups;
+    constexpr int kOBytes = (kG - 1) * 4 * kDT * 1024;
+    static_assert(kOBytes + 2 * (kG - 1) * 4 * 16 * 4 <= kNS * R::kStageBytes, "merge fits");
     f32x4_t* oslot = reinterpret_cast<f32x4_t*>(ring);
-    float(*sm_m)[16] = reinterpret_cast<float(*)[16]>(ring + 4 * kDT * 1024);
-    float(*sm_l)[16] = reinterpret_cast<float(*)[16]>(ring + 4 * kDT * 1024 + 4 * 16 * 4);
+    float(*sm_m)[16] = reinterpret_cast<float(*)[16]>(ring + kOBytes);
+    float(*sm_l)[16] = reinterpret_cast<float(*)[16]>(ring + kOBytes + (kG - 1) * 4 * 16 * 4);
     __syncthreads();
-    if (grp == 1 && active) {
+    if (grp > 0 && active) {
+      const int slot_k = (grp - 1) * 4 + rt;
       if (j4 == 0) {
-        sm_m[rt][r16] = m;
-        sm_l[rt][r16] = l;
+        sm_m[slot_k][r16] = m;
+        sm_l[slot_k][r16] = l;
       }
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) oslot[(rt * kDT + dt) * 64 + lane] = oacc[dt];
+      for (int dt = 0; dt < kDT; ++dt) oslot[(slot_k * kDT + dt) * 64 + lane] = oacc[dt];
     }
     __syncthreads();
-    if (grp == 1 || !active) return;
-    const float m1 = sm_m[rt][r16];
-    const float mx = fmaxf(m, m1);
-    const float mu = mx == -INFINITY ? 0.f : mx;
-    const float f0 = fast_exp2(m - mu), f1 = fast_exp2(m1 - mu);
-    Ls = l * f0 + sm_l[rt][r16] * f1;
+    if (grp > 0 || !active) return;
+    float mx = m;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt) oacc[dt] = oacc[dt] * f0 + oslot[(rt * kDT + dt) * 64 + lane] * f1;
+    for (int k = 1; k < kG; ++k) mx = fmaxf(mx, sm_m[(k - 1) * 4 + rt][r16]);
+    const float mu = mx == -INFINITY ? 0.f : mx;
+    const float f0 = fast_exp2(m - mu);
+    Ls = l * f0;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= f0;
+#pragma unroll
+    for (int k = 1; k < kG; ++k) {
+      const int slot_k = (k - 1) * 4 + rt;
+      const float f = fast_exp2(sm_m[slot_k][r16] - mu);
+      Ls += sm_l[slot_k][r16] * f;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] += oslot[(slot_k * kDT + dt) * 64 + lane] * f;
+    }
     M = mu;
   }
 
