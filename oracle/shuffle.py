@@ -138,16 +138,19 @@ def revert_to_halves(k_plane, v_plane, block_ids=None, elem_bytes=None):
 # K and V at the slot its slot mapping names (block = slot // N, row = slot % N),
 # straight into the shuffled planes; negative slots mark padding tokens and are
 # skipped. Standard pages take the same token as one row of K then V channels.
+# The pages never index past the cache; a slot at or past num_blocks * N names
+# no row of it and is skipped like padding (reading taken: the write would land
+# outside the cache, so it is dropped rather than wrapped or clamped).
 
 
 def write_tokens_standard(std, key, value, slot_mapping):
-    """std [B, H, N, 2D] with key/value [T, H, D] written at their slots;
-    returns a new array."""
+    """std [B, H, N, 2D] with key/value [T, H, D] written at their slots
+    (slots < 0 or >= B * N skipped); returns a new array."""
     std = np.array(std)
     B, H, N, D2 = std.shape
     D = D2 // 2
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
+        if slot < 0 or slot >= B * N:
             continue
         b, n = divmod(int(slot), N)
         std[b, :, n, :D] = key[t]
@@ -159,14 +162,14 @@ def write_tokens_shuffled(k_plane, v_plane, key, value, slot_mapping):
     """Planes [B, H, D/x, N, x] and [B, H, N/x, D, x] with key/value [T, H, D]
     written at their slots: token n of block b puts K channel c = c1*x + i at
     k_plane[b, h, c1, n, i] and V channel d at v_plane[b, h, n // x, d, n % x].
-    Returns new arrays."""
+    Slots < 0 or >= B * N are skipped. Returns new arrays."""
     kp = np.array(k_plane)
     vp = np.array(v_plane)
     B, H, Dx, N, x = kp.shape
     D = Dx * x
     c = np.arange(D)
     for t, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
-        if slot < 0:
+        if slot < 0 or slot >= B * N:
             continue
         b, n = divmod(int(slot), N)
         for h in range(H):

@@ -21,9 +21,29 @@ def test_hand_derived_slot():
     assert np.count_nonzero(kp2) == H * D and np.count_nonzero(vp2) == H * D
 
 
+@pytest.mark.parametrize("D,e,ch,kidx,vidx", [
+    (256, 2, 201, (25, 5, 1), (0, 201, 5)),      # x = 8: 201 = 25*8 + 1
+    (64, 1, 50, (3, 5, 2), (0, 50, 5)),          # x = 16: 50 = 3*16 + 2
+    (64, 2, 63, (7, 5, 7), (0, 63, 5))])         # x = 8: 63 = 7*8 + 7
+def test_hand_derived_slot_other_head_dims(D, e, ch, kidx, vidx):
+    """Slot 37 is block 2, row 5 (16-token pages) at head dims 64 and 256 too:
+    K channel ch = c1*x + i lands at k_plane[2, h, c1, 5, i] and V channel ch at
+    v_plane[2, h, 5 // x, ch, 5 % x]."""
+    B, H, x = 4, 2, 16 // e
+    kp = np.zeros((B, H, D // x, N, x), np.uint32)
+    vp = np.zeros((B, H, N // x, D, x), np.uint32)
+    key = np.arange(H * D, dtype=np.uint32).reshape(1, H, D) + 1000
+    val = np.arange(H * D, dtype=np.uint32).reshape(1, H, D) + 5000
+    kp2, vp2 = oracle.write_tokens_shuffled(kp, vp, key, val, [37])
+    assert kp2[(2, 1) + kidx] == 1000 + D + ch
+    assert vp2[(2, 1) + vidx] == 5000 + D + ch
+    assert np.count_nonzero(kp2) == H * D and np.count_nonzero(vp2) == H * D
+
+
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (4, 1)])
-def test_equals_standard_write_then_shuffle(H, e, N):
+def test_equals_standard_write_then_shuffle(H, e, N, D):
     """Writing into shuffled planes equals writing into standard pages and then
     shuffling, on a cache that already holds data (untouched rows keep it);
     padding slots (-1) change nothing."""
@@ -48,3 +68,27 @@ def test_equals_standard_write_then_shuffle(H, e, N):
             t = live.get(b * N + n)
             want = std0[b, :, n] if t is None else np.concatenate([key[t], val[t]], axis=-1)
             assert np.array_equal(std1[b, :, n], want)
+
+
+@pytest.mark.parametrize("writer", ["standard", "shuffled"])
+def test_slots_past_the_cache_are_skipped(writer):
+    """Hand case for the reading that a slot at or past num_blocks * N names no
+    row of the cache and is skipped like padding. B = 2 blocks of N = 16 rows:
+    slot 31 is block 1, row 15 (the last row) and is written; slots 32 (one
+    past the end), 47 and 10**9 change nothing, nor does -1."""
+    B, H = 2, 1
+    std0 = np.full((B, H, N, 2 * D), 7, np.uint16)
+    key = np.arange(5 * H * D, dtype=np.uint16).reshape(5, H, D) + 100
+    val = key + 1000
+    slots = np.array([32, 31, 47, 10**9, -1], np.int64)
+    if writer == "standard":
+        got = oracle.write_tokens_standard(std0, key, val, slots)
+    else:
+        kp, vp = oracle.write_tokens_shuffled(*oracle.shuffle_blocks(std0), key, val, slots)
+        got = oracle.unshuffle_blocks(kp, vp)
+    want = std0.copy()
+    want[1, 0, 15, :D] = key[1, 0]                       # token 1 -> block 1, row 15
+    want[1, 0, 15, D:] = val[1, 0]
+    assert np.array_equal(got, want)
+    # exactly one row changed: nothing wrapped to block 0 or clamped to the end
+    assert np.count_nonzero(got != 7) == 2 * D

@@ -8,15 +8,16 @@ from conftest import load_golden
 N, D = 16, 128
 
 
-def _ids(B, H):
+def _ids(B, H, D=D):
     return np.arange(B * H * N * 2 * D, dtype=np.uint32).reshape(B, H, N, 2 * D)
 
 
 @pytest.mark.parametrize("case", load_golden("byte_halves_offsets.json")["cases"],
-                         ids=lambda c: f'H{c["heads"]}e{c["elem_bytes"]}{c["after"]}{c["after_flat"]}')
+                         ids=lambda c: f'H{c["heads"]}e{c["elem_bytes"]}D{c.get("head_dim", D)}'
+                                       f'{c["after"]}{c["after_flat"]}')
 def test_hand_derived_offsets(case):
     H, e = case["heads"], case["elem_bytes"]
-    std = _ids(1, H)
+    std = _ids(1, H, case.get("head_dim", D))
     assert std.reshape(-1)[case["std_flat"]] == case["std_flat"]
     kp0, vp0 = oracle.halves_from_standard(std, elem_bytes=e)
     before = kp0 if case["before"] == "K" else vp0
@@ -39,9 +40,10 @@ def test_halves_are_the_byte_halves(H):
         assert vp[b].tobytes() == raw[len(raw) // 2:]
 
 
+@pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("N", [16, 32])
 @pytest.mark.parametrize("H,e", [(1, 2), (2, 2), (3, 2), (8, 2), (1, 1), (3, 1), (4, 1)])
-def test_matches_out_of_place_shuffle_and_round_trips(H, e, N):
+def test_matches_out_of_place_shuffle_and_round_trips(H, e, N, D):
     B = 5
     std = np.arange(B * H * N * 2 * D, dtype=np.uint32).reshape(B, H, N, 2 * D)
     listed = [3, 0, 4]

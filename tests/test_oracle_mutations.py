@@ -203,6 +203,18 @@ def _write_k_transposed(k_plane, v_plane, key, value, slot_mapping):
     return kp, vp
 
 
+def _write_wraps(k_plane, v_plane, key, value, slot_mapping):
+    B, N = k_plane.shape[0], k_plane.shape[3]
+    wrapped = [s % (B * N) if s >= 0 else s for s in np.asarray(slot_mapping, np.int64)]
+    return TRUE_WRITE(k_plane, v_plane, key, value, wrapped)
+
+
+def _write_std_wraps(std, key, value, slot_mapping):
+    B, N = std.shape[0], std.shape[2]
+    wrapped = [s % (B * N) if s >= 0 else s for s in np.asarray(slot_mapping, np.int64)]
+    return TRUE_WRITE_STD(std, key, value, wrapped)
+
+
 def _encode_ties_up(values):
     v = np.asarray(values, dtype=np.float64)
     pos = fp8._E4M3FN[:0x7F]
@@ -218,6 +230,7 @@ def _encode_ties_up(values):
 
 
 TRUE_WRITE = shuffle.write_tokens_shuffled
+TRUE_WRITE_STD = shuffle.write_tokens_standard
 TRUE_FIXED = planner.fixed_split_plan
 TRUE_HALVES = shuffle.halves_from_standard
 TRUE_GATHER = att.gather_standard
@@ -268,6 +281,11 @@ MUTATIONS = [
     ("cache writer K channel split transposed",
      [(shuffle, "write_tokens_shuffled", _write_k_transposed),
       (oracle, "write_tokens_shuffled", _write_k_transposed)]),
+    ("cache writer wraps slots past the cache",
+     [(shuffle, "write_tokens_shuffled", _write_wraps),
+      (oracle, "write_tokens_shuffled", _write_wraps),
+      (shuffle, "write_tokens_standard", _write_std_wraps),
+      (oracle, "write_tokens_standard", _write_std_wraps)]),
     ("byte halves swapped", [(shuffle, "halves_from_standard", _halves_swapped),
                              (oracle, "halves_from_standard", _halves_swapped)]),
 ]
