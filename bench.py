@@ -5,19 +5,43 @@ in HBM: the length-aware plan (plan_build), the segment kernel and the split
 reduce. The metric is the attention call (segment + reduce): microseconds per
 call and effective KV TB/s = sum_i L_i * kv_heads * 2 * head_dim * bytes / time,
 also as a fraction of the 8 TB/s HBM peak. Per-kernel durations come from HIP
-events recorded on the stream the kernels run on. For shuffled-page workloads
-the standard->shuffled repack runs before the timed steps and is timed on its
-own, as is the in-place conversion of the same pool received as byte halves
-(and its inverse). A KV pool much smaller than 2 GiB (the fp8 batches) is
-timed on several copies of itself used in turn, so that no call is served from
-the lines the previous call left in the 256 MB last-level cache.
+events recorded on the stream the kernels run on.
 
-Prints ONE JSON line (rank 0). Default workload: the uniform verify batch
-(bs=16 x 119k tokens, 4 query tokens, 32/2 heads, bf16). `--all` adds the other
-workloads to the line under "workloads", among them the uniform and agentic
-batches with an fp8 cache, the element type of the split-KV PR's own table.
+Headline (`value`): the skewed agentic verify batch (bs 20, 2.32M tokens,
+ragged 1..4 query tokens, 32/2 heads, bf16), the batch shape of the split-KV
+PR's agentic rows (Benchmarking and Profiling). Every other workload is timed
+the same way and reported under "workloads" in the same JSON line (`--only`
+times the headline alone).
+
+Each workload is timed in three arms: the planned split (plan + segment +
+reduce), the fixed split (no plan; the PR's A/B baseline and its bs == 1
+path) and the planned call replayed from a HIP graph. The arms are
+interleaved: timed step i runs all three, in an order rotated by i, so no arm
+gains or loses from its position. Before the counted warm-up, the planned
+call is repeated until the median duration of its last 20 segment launches is
+within 1% of the 20 before (at least 100 launches, at most --precondition-s
+seconds): after the GPU has been idle, the first ~100 launches run up to 40%
+slower while clocks ramp. That phase is reported under "precondition".
+
+Every KV pool is timed on at least two copies used in turn (more when the
+pool is small: together at least 4 GiB, at most 8 copies), one copy per call
+whatever the arm, so no call reads lines the previous call left in the 256 MB
+last-level cache.
+
+For shuffled-page workloads the standard->shuffled repack, the in-place
+conversion of the same pool received as byte halves (and its inverse) and a
+cache write are timed on their own.
+
+`--summarize DIR` turns the rocprofv3 outputs of one workload (the kernel
+trace and the two HBM counter runs whose commands it prints) into the
+summaries under profiles/.
+
+Prints ONE JSON line.
 """
 import argparse
+import csv
+import collections
+import glob
 import hashlib
 import json
 import os
@@ -29,33 +53,33 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# A KV pool small next to the 256 MB last-level cache is timed on several
-# copies used in turn (together at least this many bytes, at most 8 copies),
-# so that no call reads lines the previous call left in that cache.
-ROTATE_BYTES = 2 << 30
+HEADLINE = "agentic_skew"
+ROTATE_BYTES = 4 << 30          # KV copies used in turn: together at least this
+ARMS = ("planned", "fixed", "graph")
 
 
-def _args():
+def _args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The first ~100 launches after the GPU has been idle run up to 40% slower
-    # (clock/power ramp); 100 warmup steps put the timed region in steady state.
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--config", default="uniform_verify")
-    ap.add_argument("--all", action="store_true", help="also time the other workloads")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--only", action="store_true", help="time the --config workload alone")
+    ap.add_argument("--precondition-s", type=float, default=3.0,
+                    help="cap (seconds) of the clock pre-conditioning phase; 0 skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU-oracle time for the baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
-    return ap.parse_args()
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 outputs in DIR")
+    return ap.parse_args(argv)
 
 
 # the sources the segment-attention kernels are compiled from
 SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip", "skv_attn_valu.hip",
-                   "skv_attn_gd.hip",
-                   "skv_attn_common.h", "skv_internal.h")
+                   "skv_attn_gd.hip", "skv_attn_common.h", "skv_internal.h")
 
 
 def _code_only(text):
@@ -94,7 +118,7 @@ def kernel_source_hash():
 
 
 def traffic_from_profiles(cfg_name, src_hash):
-    """HBM bytes per segment-kernel launch from committed rocprofv3 PMC
+    """HBM bytes per segment-kernel launch from the committed rocprofv3 PMC
     summaries, only if they were taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "segment_traffic.json")
     if not os.path.exists(p):
@@ -107,187 +131,254 @@ def traffic_from_profiles(cfg_name, src_hash):
     return e.get("hbm_bytes_per_launch")
 
 
-def time_workload(cfg, steps, warmup, torch, skv, gen):
-    dev = "cuda:0"
-    case = gen.make_case(cfg, dev)
+def _stats(xs):
+    s = sorted(xs)
+    n = len(s)
+    return {"mean": sum(s) / n, "median": s[n // 2], "p10": s[n // 10], "p90": s[(9 * n) // 10]}
+
+
+def _repack_timings(cfg, case, warmup, torch, skv, dev):
+    """Shuffle, in-place conversion (and back) and one decode step's cache
+    write on the workload's own pool; returns (timings, k_plane, v_plane)."""
     st = torch.cuda.current_stream()
     res = {}
+    kp, vp = skv.kv_page_shuffle(case.kv)
+    for _ in range(max(warmup, 2)):
+        skv.kv_page_shuffle(case.kv, kp, vp)
+    n = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(n):
+        skv.kv_page_shuffle(case.kv, kp, vp)
+    e1.record(st)
+    torch.cuda.synchronize()
+    moved = 2 * case.kv.numel() * case.kv.element_size()
+    res["shuffle_us"] = e0.elapsed_time(e1) * 1e3 / n
+    res["shuffle_gbs"] = moved / res["shuffle_us"] / 1e3
+    B = case.kv.shape[0]
+    flat = case.kv.view(torch.uint8).view(B, -1)
+    hb = flat.shape[1] // 2
+    x = 16 // case.kv.element_size()
+    H, D, P = cfg.kv_heads, cfg.head_dim, cfg.page_size
+    kh = flat[:, :hb].contiguous().view(case.kv.dtype).view(B, H, D // x, P, x)
+    vh = flat[:, hb:].contiguous().view(case.kv.dtype).view(B, H, P // x, D, x)
+    for _ in range(max(warmup, 2)):
+        skv.kv_page_convert(kh, vh)
+        skv.kv_page_convert(kh, vh, direction="to_standard")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    to_s = to_b = 0.0
+    for _ in range(n):
+        ev[0].record(st)
+        skv.kv_page_convert(kh, vh)
+        ev[1].record(st)
+        skv.kv_page_convert(kh, vh, direction="to_standard")
+        ev[2].record(st)
+        torch.cuda.synchronize()
+        to_s += ev[0].elapsed_time(ev[1]) * 1e3 / n
+        to_b += ev[1].elapsed_time(ev[2]) * 1e3 / n
+    res.update(convert_us=to_s, convert_gbs=moved / to_s / 1e3, convert_back_us=to_b,
+               convert_back_gbs=moved / to_b / 1e3)
+    del kh, vh, flat
+    tab = case.page_table
+    last = (case.seq_lens.long() - 1).clamp(min=0)
+    slots = tab.gather(1, (last // P).view(-1, 1).int()).view(-1).long() * P + last % P
+    knew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
+    vnew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
+    for _ in range(5):
+        skv.kv_cache_write(knew, vnew, slots, kp, vp)
+    ev[0].record(st)
+    for _ in range(n):
+        skv.kv_cache_write(knew, vnew, slots, kp, vp)
+    ev[1].record(st)
+    torch.cuda.synchronize()
+    res["cache_write_us"] = ev[0].elapsed_time(ev[1]) * 1e3 / n
+    res["cache_write_tokens"] = cfg.bs
+    skv.kv_page_shuffle(case.kv, kp, vp)     # restore the planes for attention
+    return res, kp, vp
+
+
+def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
+    dev = "cuda:0"
+    st = torch.cuda.current_stream()
+    case = gen.make_case(cfg, dev)
+    res = {"workload": cfg.name, "note": cfg.note}
     kv_a, kv_b = case.kv, None
     if cfg.layout == "shuffled":
-        kp, vp = skv.kv_page_shuffle(case.kv)
-        for _ in range(max(warmup // 5, 2)):
-            skv.kv_page_shuffle(case.kv, kp, vp)
-        n = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        for _ in range(n):
-            skv.kv_page_shuffle(case.kv, kp, vp)
-        e1.record(st)
-        torch.cuda.synchronize()
-        sh_us = e0.elapsed_time(e1) * 1e3 / n
-        moved = 2 * case.kv.numel() * case.kv.element_size()
-        res["shuffle_us"] = sh_us
-        res["shuffle_gbs"] = moved / sh_us / 1e3
-        # in-place conversion of the same pool received as byte halves, and back
-        B = case.kv.shape[0]
-        flat = case.kv.view(torch.uint8).view(B, -1)
-        hb = flat.shape[1] // 2
-        x = 16 // case.kv.element_size()
-        H, D = cfg.kv_heads, cfg.head_dim
-        kh = flat[:, :hb].contiguous().view(case.kv.dtype).view(B, H, D // x, 16, x)
-        vh = flat[:, hb:].contiguous().view(case.kv.dtype).view(B, H, 16 // x, D, x)
-        for _ in range(max(warmup // 10, 2)):
-            skv.kv_page_convert(kh, vh)
-            skv.kv_page_convert(kh, vh, direction="to_standard")
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        to_s = to_b = 0.0
-        for _ in range(n):
-            ev[0].record(st)
-            skv.kv_page_convert(kh, vh)
-            ev[1].record(st)
-            skv.kv_page_convert(kh, vh, direction="to_standard")
-            ev[2].record(st)
-            torch.cuda.synchronize()
-            to_s += ev[0].elapsed_time(ev[1]) * 1e3 / n
-            to_b += ev[1].elapsed_time(ev[2]) * 1e3 / n
-        res["convert_us"] = to_s
-        res["convert_gbs"] = moved / to_s / 1e3
-        res["convert_back_us"] = to_b
-        res["convert_back_gbs"] = moved / to_b / 1e3
-        del kh, vh, flat
-        # cache writer: one decode step's new token per sequence into the planes
-        tab = case.page_table
-        last = (case.seq_lens.long() - 1).clamp(min=0)
-        slots = tab.gather(1, (last // 16).view(-1, 1).int()).view(-1).long() * 16 + last % 16
-        knew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
-        vnew = torch.randn((cfg.bs, H, D), device=dev).to(case.kv.dtype)
-        for _ in range(5):
-            skv.kv_cache_write(knew, vnew, slots, kp, vp)
-        ev[0].record(st)
-        for _ in range(n):
-            skv.kv_cache_write(knew, vnew, slots, kp, vp)
-        ev[1].record(st)
-        torch.cuda.synchronize()
-        res["cache_write_us"] = ev[0].elapsed_time(ev[1]) * 1e3 / n
-        res["cache_write_tokens"] = cfg.bs
-        # restore the planes for the attention steps
-        skv.kv_page_shuffle(case.kv, kp, vp)
-        kv_a, kv_b = kp, vp
+        rp, kv_a, kv_b = _repack_timings(cfg, case, a.warmup, torch, skv, dev)
+        res["repack"] = rp
+        case.kv = None                       # the standard pool is not read by attention
     pool = sum(t.numel() * t.element_size() for t in (kv_a, kv_b) if t is not None)
-    ncopy = max(1, min(8, -(-ROTATE_BYTES // pool)))
+    ncopy = max(2, min(8, -(-ROTATE_BYTES // pool)))
     kvs = [(kv_a, kv_b)] + [(kv_a.clone(), None if kv_b is None else kv_b.clone())
                             for _ in range(ncopy - 1)]
     res["kv_copies"] = ncopy
     rows = cfg.total_q * cfg.q_heads * cfg.seg_max
     part_o = torch.empty(rows * cfg.head_dim, dtype=torch.float32, device=dev)
     part_lse = torch.empty(rows, dtype=torch.float32, device=dev)
-    out = torch.empty((cfg.total_q, cfg.q_heads, cfg.head_dim), dtype=skv.io_dtype(cfg.kv_dtype),
-                      device=dev)
+    iot = skv.io_dtype(cfg.kv_dtype)
+    out = torch.empty((cfg.total_q, cfg.q_heads, cfg.head_dim), dtype=iot, device=dev)
+    fout = torch.empty_like(out)
     odt = "fp16" if cfg.kv_dtype == "fp16" else "bf16"
     plan = torch.empty(skv.plan_words(cfg.bs, cfg.kv_heads, cfg.num_cus), dtype=torch.int32,
                        device=dev)
     tok = torch.empty(cfg.total_q, dtype=torch.int32, device=dev)
+    ftok = torch.empty(cfg.total_q, dtype=torch.int32, device=dev)
     kw = dict(kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=cfg.num_cus,
               seg_max=cfg.seg_max, kv_dtype=cfg.kv_dtype, layout=cfg.layout,
-              k_scale=case.k_scale, v_scale=case.v_scale, causal=cfg.causal)
+              k_scale=case.k_scale, v_scale=case.v_scale, causal=cfg.causal,
+              page_size=cfg.page_size)
+    red = dict(total_q=cfg.total_q, q_heads=cfg.q_heads, seg_max=cfg.seg_max,
+               head_dim=cfg.head_dim, out_dtype=odt)
+    calls = [0]                              # KV copy used by the next call, any arm
+    schedule = []
 
-    def step(ev=None, i=0):
-        kv_a, kv_b = kvs[i % ncopy]
+    def log(phase, arm):
+        if schedule and schedule[-1][0] == phase and schedule[-1][1] == arm:
+            schedule[-1][2] += 1
+        else:
+            schedule.append([phase, arm, 1])
+
+    def next_kv():
+        kv = kvs[calls[0] % ncopy]
+        calls[0] += 1
+        return kv
+
+    def seg_reduce(kv, p, t, o):
+        skv.segment_attn(case.q, kv[0], kv[1], case.page_table, case.seq_lens,
+                         case.cu_seqlens_q, p, t, part_o=part_o, part_lse=part_lse, **kw)
+        skv.split_reduce(part_o, part_lse, t, out=o, **red)
+
+    def planned(ev=None):
+        kv = next_kv()
         if ev:
             ev[0].record(st)
         skv.plan_build(case.seq_lens, case.cu_seqlens_q, cfg.total_q, cfg.kv_heads,
-                       cfg.num_cus, cfg.seg_max, cfg.causal, plan=plan, tok_nseg=tok)
+                       cfg.num_cus, cfg.seg_max, cfg.causal, plan=plan, tok_nseg=tok,
+                       page_size=cfg.page_size)
         if ev:
             ev[1].record(st)
-        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
+        skv.segment_attn(case.q, kv[0], kv[1], case.page_table, case.seq_lens,
                          case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
         if ev:
             ev[2].record(st)
-        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
-                         out_dtype=odt)
+        skv.split_reduce(part_o, part_lse, tok, out=out, **red)
         if ev:
             ev[3].record(st)
 
-    for i in range(warmup):
-        step(i=i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(evs[i], i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    plan_us = sum(e[0].elapsed_time(e[1]) for e in evs) * 1e3 / steps
-    seg_us = sum(e[1].elapsed_time(e[2]) for e in evs) * 1e3 / steps
-    red_us = sum(e[2].elapsed_time(e[3]) for e in evs) * 1e3 / steps
-    step_us = sum(e[0].elapsed_time(e[3]) for e in evs) * 1e3 / steps
-    segs = sorted(e[1].elapsed_time(e[2]) * 1e3 for e in evs)
-    kvb = cfg.kv_bytes()
-    call_us = seg_us + red_us
-    res.update(dict(
-        workload=cfg.name, kv_bytes=kvb, plan_us=plan_us, segment_us=seg_us,
-        segment_us_p10=segs[len(segs) // 10], segment_us_p90=segs[(9 * len(segs)) // 10],
-        segment_us_median=segs[len(segs) // 2],
-        reduce_us=red_us, attn_us_per_call=call_us, step_us=step_us, wall_s=wall,
-        kv_tb_s=kvb / call_us / 1e6, frac_of_hbm_peak=kvb / call_us / 1e3 / HBM_PEAK_GBS,
-        segment_gb_s=kvb / seg_us / 1e3, plan_T=int(plan[0].item())))
-    # the same attention call captured once in a HIP graph and replayed, as a
-    # serving loop runs decode steps: launch gaps between segment and reduce go
-    def attn_call(kv_a, kv_b):
-        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
-                         case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse, **kw)
-        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
-                         out_dtype=odt)
+    def fixed(ev=None):
+        kv = next_kv()
+        if ev:
+            ev[0].record(st)
+        skv.segment_attn(case.q, kv[0], kv[1], case.page_table, case.seq_lens,
+                         case.cu_seqlens_q, None, ftok, part_o=part_o, part_lse=part_lse,
+                         **kw)
+        if ev:
+            ev[1].record(st)
+        skv.split_reduce(part_o, part_lse, ftok, out=fout, **red)
+        if ev:
+            ev[2].record(st)
 
+    # the planned call (segment + reduce, plan built beforehand) captured once
+    # per KV copy and replayed, as a serving loop runs decode steps
+    planned()
+    log("plan for capture", "planned")
     side = torch.cuda.Stream()
     side.wait_stream(st)
     with torch.cuda.stream(side):
-        attn_call(*kvs[0])
+        seg_reduce(kvs[0], plan, tok, out)
+    log("capture warm-up", "graph")
     st.wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
-    for kv in kvs:                     # one graph per KV copy, replayed in turn
+    for kv in kvs:
         graphs.append(torch.cuda.CUDAGraph())
         with torch.cuda.graph(graphs[-1]):
-            attn_call(*kv)
-    for i in range(warmup):
-        graphs[i % ncopy].replay()
-    gev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        gev[i][0].record(st)
-        graphs[i % ncopy].replay()
-        gev[i][1].record(st)
-    torch.cuda.synchronize()
-    res["graph_us_per_call"] = sum(e[0].elapsed_time(e[1]) for e in gev) * 1e3 / steps
-    res["graph_kv_tb_s"] = kvb / res["graph_us_per_call"] / 1e6
-    del graphs
+            seg_reduce(kv, plan, tok, out)
 
-    # the fixed split on the same batch (no plan; the segment kernel writes the
-    # per-token counts): the pages' A/B comparison, on these kernels
-    def fixed_call(ev=None, i=0):
-        kv_a, kv_b = kvs[i % ncopy]
+    def graph(ev=None):
+        i = calls[0] % ncopy
+        calls[0] += 1
         if ev:
             ev[0].record(st)
-        skv.segment_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
-                         case.cu_seqlens_q, None, tok, part_o=part_o, part_lse=part_lse, **kw)
-        skv.split_reduce(part_o, part_lse, tok, total_q=cfg.total_q, q_heads=cfg.q_heads,
-                         seg_max=cfg.seg_max, head_dim=cfg.head_dim, out=out,
-                         out_dtype=odt)
+        graphs[i].replay()
         if ev:
             ev[1].record(st)
 
-    for i in range(warmup):
-        fixed_call(i=i)
-    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        fixed_call(fev[i], i)
+    run = {"planned": planned, "fixed": fixed, "graph": graph}
+    nev = {"planned": 4, "fixed": 3, "graph": 2}
+
+    # clock pre-conditioning: the planned call until its segment-kernel time settles
+    t0 = time.perf_counter()
+    pre, meds, converged = [], [], False
+    while a.precondition_s > 0:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(20)]
+        for e in evs:
+            planned(e)
+            log("precondition", "planned")
+        torch.cuda.synchronize()
+        pre += [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+        meds.append(sorted(pre[-20:])[10])
+        if len(pre) >= 100 and abs(meds[-1] - meds[-2]) <= 0.01 * meds[-2]:
+            converged = True
+            break
+        if time.perf_counter() - t0 > a.precondition_s:
+            break
+    res["precondition"] = {"launches": len(pre), "seconds": round(time.perf_counter() - t0, 3),
+                           "converged": converged,
+                           "segment_us_first20_median": round(meds[0], 2) if meds else None,
+                           "segment_us_last20_median": round(meds[-1], 2) if meds else None}
+
+    def order(i):
+        return ARMS[i % 3:] + ARMS[:i % 3]
+
+    for i in range(a.warmup):
+        for arm in order(i):
+            run[arm]()
+            log("warm-up", arm)
     torch.cuda.synchronize()
-    fixed_us = sum(e[0].elapsed_time(e[1]) for e in fev) * 1e3 / steps
-    res.update(fixed_split_us_per_call=fixed_us, fixed_split_kv_tb_s=kvb / fixed_us / 1e6,
-               fixed_split_segments=_fixed_segments(cfg))
-    del case, part_o, part_lse, out, kvs
+    evs = {arm: [] for arm in ARMS}
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        for arm in order(i):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(nev[arm])]
+            run[arm](e)
+            evs[arm].append(e)
+            log("timed", arm)
+    torch.cuda.synchronize()
+    res["wall_s"] = time.perf_counter() - t0
+    us = lambda e, i, j: e[i].elapsed_time(e[j]) * 1e3
+    kvb = cfg.kv_bytes()
+    pl = evs["planned"]
+    p_call = [us(e, 1, 3) for e in pl]
+    p_seg = [us(e, 1, 2) for e in pl]
+    f_call = [us(e, 0, 2) for e in evs["fixed"]]
+    f_seg = [us(e, 0, 1) for e in evs["fixed"]]
+    g_call = [us(e, 0, 1) for e in evs["graph"]]
+    call = sum(p_call) / len(p_call)
+    seg = sum(p_seg) / len(p_seg)
+    res.update(
+        kv_bytes=kvb, us_per_call=call, kv_tb_s=kvb / call / 1e6,
+        frac_of_hbm_peak=kvb / call / 1e3 / HBM_PEAK_GBS, segment_us=seg,
+        segment_gb_s=kvb / seg / 1e3, plan_T=int(plan[0].item()),
+        planned={"call_us": _stats(p_call), "segment_us": _stats(p_seg),
+                 "plan_us": sum(us(e, 0, 1) for e in pl) / len(pl),
+                 "reduce_us": sum(us(e, 2, 3) for e in pl) / len(pl),
+                 "step_us": sum(us(e, 0, 3) for e in pl) / len(pl)},
+        fixed={"call_us": _stats(f_call), "segment_us": _stats(f_seg),
+               "segments_per_seq": _fixed_segments(cfg),
+               "kv_tb_s": kvb / (sum(f_call) / len(f_call)) / 1e6},
+        graph={"call_us": _stats(g_call), "kv_tb_s": kvb / (sum(g_call) / len(g_call)) / 1e6})
+    # the planned and the fixed split on the same inputs: the PR's accuracy
+    # check (they differ only by the fp32 summation order across segments)
+    planned()
+    log("accuracy check", "planned")
+    fixed()
+    log("accuracy check", "fixed")
+    torch.cuda.synchronize()
+    res["plan_vs_fixed_max_abs"] = float((out.float() - fout.float()).abs().max().item())
+    if with_schedule:
+        res["segment_launch_schedule"] = schedule
+    del graphs, case, part_o, part_lse, out, fout, kvs
     torch.cuda.empty_cache()
     return res
 
@@ -316,7 +407,7 @@ def cpu_baseline(cfg, min_seconds, gen, np):
     n_gen = min(cfg.bs, 8)
     sub = gen.small_config(cfg, cfg.seq_lens[:n_gen], cfg.q_lens[:n_gen])
     case = gen.make_case(sub, "cpu")
-    q = oracle.decode_bf16(gen.raw_u16(case.q))
+    q = oracle.decode_q(gen.raw_u16(case.q), cfg.kv_dtype)
     kv = gen.raw_kv(case)
     cu = case.cu_seqlens_q.numpy()
     table, lens = case.page_table.numpy(), case.seq_lens.numpy()
@@ -339,11 +430,198 @@ def cpu_baseline(cfg, min_seconds, gen, np):
             "host_cpus": os.cpu_count()}
 
 
-def main():
-    a = _args()
+def _round(x):
+    if isinstance(x, float):
+        return round(x, 4)
+    if isinstance(x, dict):
+        return {k: _round(v) for k, v in x.items()}
+    if isinstance(x, list):
+        return [_round(v) for v in x]
+    return x
+
+
+# ---- profile summaries (rocprofv3 outputs -> profiles/) ----------------------
+
+def _short(name):
+    return name.replace("skv::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def _one(d, pat):
+    got = glob.glob(os.path.join(d, pat))
+    if not got:
+        raise FileNotFoundError(os.path.join(d, pat))
+    return got[0]
+
+
+def _bench_line(path):
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    raise ValueError(f"no bench JSON line in {path}")
+
+
+def _arm_of_segment_launches(line):
+    """(phase, arm) of every segment-kernel launch, in launch order, from the
+    schedule the profiled bench run printed."""
+    sched = line.get("segment_launch_schedule")
+    if sched is None:
+        raise ValueError("the profiled run must use --only (it prints the launch schedule)")
+    return [(ph, arm) for ph, arm, n in sched for _ in range(n)]
+
+
+def _counter_per_dispatch(path):
+    out = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            out[r["Kernel_Name"]].append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: [v for _, v in sorted(vs)] for k, vs in out.items()}
+
+
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d {d}/trace -o trace -- "
+             "python3 bench.py --only --config {wl} --no-cpu-baseline > {d}/trace.json",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {d}/fetch -o fetch -- "
+             "python3 bench.py --only --config {wl} --steps 3 --warmup 1 --precondition-s 0 "
+             "--no-cpu-baseline > {d}/fetch.json",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {d}/write -o write -- "
+             "python3 bench.py --only --config {wl} --steps 3 --warmup 1 --precondition-s 0 "
+             "--no-cpu-baseline > {d}/write.json",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d {c}/fetch -o cf -- "
+                  "python3 bench.py --copy-probe",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d {c}/write -o cw -- "
+                  "python3 bench.py --copy-probe",
+}
+
+
+def summarize(d, copy_dir=None, out_dir=None):
+    """Kernel-trace and HBM-counter summaries of one profiled workload.
+
+    d holds trace/, fetch/, write/ and the bench lines trace.json, fetch.json,
+    write.json written by the PROFILE_CMDS commands; copy_dir (default: the
+    sibling p_copy/) the two counter runs of the plain 1 GiB copy used to
+    scale the counters. Writes <workload>_kernel_trace.md and
+    <workload>_pmc.md and updates segment_traffic.json in out_dir (default
+    profiles/)."""
+    d = d.rstrip("/")
+    copy_dir = copy_dir or os.path.join(os.path.dirname(d), "p_copy")
+    tline = _bench_line(os.path.join(d, "trace.json"))
+    wl = tline["config"]["workload"].split(":")[0]
+    src_hash = tline["roofline"]["kernel_source_hash"]
+    rel = lambda p: os.path.relpath(p, ROOT)
+    fmt = dict(d=rel(d), wl=wl, c=rel(copy_dir))
+    prof = out_dir or os.path.join(ROOT, "profiles")
+    # kernel trace, per arm and phase
+    with open(_one(os.path.join(d, "trace"), "*kernel_trace.csv")) as f:
+        kt = [r for r in csv.DictReader(f) if "skv::" in r["Kernel_Name"]]
+    kt.sort(key=lambda r: int(r["Start_Timestamp"]))
+    seg = [r for r in kt if "seg_" in _short(r["Kernel_Name"])]
+    arms = _arm_of_segment_launches(tline)
+    if len(arms) != len(seg):
+        raise ValueError(f"{len(seg)} segment launches traced, schedule lists {len(arms)}")
+    groups = collections.defaultdict(list)
+    for (ph, arm), r in zip(arms, seg):
+        groups[(ph, arm)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    # the reduce follows its segment launch; the plan precedes planned launches
+    by_name = collections.defaultdict(list)
+    for r in kt:
+        by_name[_short(r["Kernel_Name"])].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    L = [f"# Kernel trace: {wl}", "",
+         "Command (repository root, one MI355X; the bench line it prints is the source of the",
+         "launch schedule used below):", "", "```", PROFILE_CMDS["trace"].format(**fmt), "```",
+         "", f"Bench line of this run: {tline['us_per_call']} us per call, "
+             f"{tline['value']} TB/s (planned arm, events); kernel sources hash {src_hash}.", "",
+         "Segment kernel, per arm (the timed steps interleave the three arms in rotated order):",
+         "", "| phase | arm | launches | avg us | median us | p10 us | p90 us | KV TB/s (avg) |",
+         "|---|---|---|---|---|---|---|---|"]
+    kvb = tline["roofline"]["algorithmic_bytes_per_launch"]
+    for (ph, arm), v in groups.items():
+        s = _stats(v)
+        L.append(f"| {ph} | {arm} | {len(v)} | {s['mean']:.1f} | {s['median']:.1f} | "
+                 f"{s['p10']:.1f} | {s['p90']:.1f} | {kvb / s['mean'] / 1e6:.3f} |")
+    L += ["", "Every launch of every library kernel (all phases):", "",
+          "| kernel | launches | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for k, v in by_name.items():
+        L.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} |")
+    timed = groups.get(("timed", "planned"))
+    if timed:
+        L += ["", f"Timed planned launches: segment kernel {sum(timed) / len(timed):.1f} us = "
+                  f"{kvb / (sum(timed) / len(timed)) / 1e3:.1f} GB/s = "
+                  f"{kvb / (sum(timed) / len(timed)) / 1e3 / HBM_PEAK_GBS:.3f} of the 8 TB/s peak "
+                  f"({kvb} algorithmic KV bytes per launch)."]
+    os.makedirs(prof, exist_ok=True)
+    with open(os.path.join(prof, f"{wl}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    # HBM counters, scaled by what they read for a plain 1 GiB copy
+    copy_kib = (1 << 30) / 1024
+    cf = _counter_per_dispatch(_one(os.path.join(copy_dir, "fetch"), "*counter_collection.csv"))
+    cw = _counter_per_dispatch(_one(os.path.join(copy_dir, "write"), "*counter_collection.csv"))
+    cfv = [v for k, vs in cf.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs]
+    cwv = [v for k, vs in cw.items() if "copyBuffer" in k or "copy" in k.lower() for v in vs]
+    f_scale = copy_kib / (sum(cfv) / len(cfv))
+    w_scale = copy_kib / (sum(cwv) / len(cwv))
+    fline = _bench_line(os.path.join(d, "fetch.json"))
+    fc = _counter_per_dispatch(_one(os.path.join(d, "fetch"), "*counter_collection.csv"))
+    wc = _counter_per_dispatch(_one(os.path.join(d, "write"), "*counter_collection.csv"))
+    farms = _arm_of_segment_launches(fline)
+    L = [f"# HBM traffic per launch: {wl}", "",
+         "Commands (repository root; one counter per run, then the calibration copy):", "",
+         "```"] + [PROFILE_CMDS[k].format(**fmt) for k in ("fetch", "write", "copy_fetch",
+                                                            "copy_write")] + [
+         f"python3 bench.py --summarize {fmt['d']}", "```", "",
+         f"Calibration (plain 1 GiB device copy): FETCH_SIZE reads {sum(cfv) / len(cfv):.0f} KiB "
+         f"for 1048576 KiB (scale {f_scale:.4f}); WRITE_SIZE reads {sum(cwv) / len(cwv):.0f} KiB "
+         f"(scale {w_scale:.4f}).", f"Kernel sources hash {src_hash}.", "",
+         "Per dispatch, averaged; the segment kernel over its planned-arm dispatches only.", "",
+         "| kernel | dispatches | FETCH_SIZE raw KiB | WRITE_SIZE raw KiB | read bytes (scaled) | "
+         "written bytes (scaled) | (read + written) / algorithmic KV bytes |",
+         "|---|---|---|---|---|---|---|"]
+    traffic = {}
+    for k in fc:
+        if "skv::" not in k:
+            continue
+        name = _short(k)
+        fk, wk = fc[k], wc.get(k, [0.0])
+        if name.startswith("seg_"):
+            if len(fk) != len(farms) or len(wk) != len(farms):
+                raise ValueError(f"{name}: {len(fk)}/{len(wk)} dispatches, "
+                                 f"schedule lists {len(farms)}")
+            fk = [v for v, (ph, arm) in zip(fk, farms) if arm == "planned"]
+            wk = [v for v, (ph, arm) in zip(wk, farms) if arm == "planned"]
+        fr, wr = sum(fk) / len(fk), sum(wk) / len(wk)
+        rb, wb = fr * 1024 * f_scale, wr * 1024 * w_scale
+        ratio = f"{(rb + wb) / kvb:.4f}" if name.startswith("seg_") else "-"
+        L.append(f"| {name} | {len(fk)} | {fr:.1f} | {wr:.1f} | {rb:.4e} | {wb:.4e} | {ratio} |")
+        if name.startswith("seg_"):
+            traffic[wl] = {"kernel": name, "kernel_source_hash": src_hash,
+                           "hbm_bytes_per_launch": round(rb + wb), "read_bytes": round(rb),
+                           "write_bytes": round(wb), "algorithmic_bytes_per_launch": kvb,
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+                           "source": f"profiles/{wl}_pmc.md"}
+    with open(os.path.join(prof, f"{wl}_pmc.md"), "w") as f:
+        f.write("\n".join(L) + "\n")
+    tj = os.path.join(prof, "segment_traffic.json")
+    old = {}
+    if os.path.exists(tj):
+        with open(tj) as f:
+            old = json.load(f)
+    old.update(traffic)
+    with open(tj, "w") as f:
+        json.dump(old, f, indent=1, sort_keys=True)
+        f.write("\n")
+    return traffic
+
+
+def main(argv=None):
+    a = _args(argv)
+    if a.summarize:
+        print(json.dumps(summarize(a.summarize)))
+        return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
-                          "n_gpus": a.gpus}))
+        print(json.dumps({"error": "this build runs on one GPU (the kernel on one GPU's share); "
+                                   "--gpus must be 1", "n_gpus": a.gpus}))
         sys.exit(2)
     import numpy as np
     import torch
@@ -363,7 +641,7 @@ def main():
         print(json.dumps({"copy_probe_bytes": 1 << 30, "launches": 5}))
         return
     cfg = configs.BY_NAME[a.config]
-    head = time_workload(cfg, a.steps, a.warmup, torch, skv, gen)
+    head = time_workload(cfg, a, torch, skv, gen, with_schedule=a.only)
     props = torch.cuda.get_device_properties(0)
     src_hash = kernel_source_hash()
     traffic = traffic_from_profiles(cfg.name, src_hash)
@@ -376,7 +654,7 @@ def main():
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(head["step_us"] / 1e3, 5),
+        "ms_per_step": round(head["planned"]["step_us"] / 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -388,16 +666,11 @@ def main():
                    "page_size": cfg.page_size, "kv_dtype": cfg.kv_dtype,
                    "layout": cfg.layout, "num_cus": cfg.num_cus, "seg_max": cfg.seg_max,
                    "parallelism": "single GPU", "kv_copies": head["kv_copies"]},
-        "us_per_call": round(head["attn_us_per_call"], 2),
+        "us_per_call": round(head["us_per_call"], 2),
         "frac_of_hbm_peak": round(head["frac_of_hbm_peak"], 4),
-        "breakdown_us": {k: round(head[k], 2) for k in
-                         ("plan_us", "segment_us", "segment_us_median", "segment_us_p10",
-                          "segment_us_p90", "reduce_us", "step_us")},
-        "graph_replay": {"us_per_call": round(head["graph_us_per_call"], 2),
-                         "kv_tb_s": round(head["graph_kv_tb_s"], 4)},
-        "fixed_split": {"us_per_call": round(head["fixed_split_us_per_call"], 2),
-                        "kv_tb_s": round(head["fixed_split_kv_tb_s"], 4),
-                        "segments_per_seq": head["fixed_split_segments"]},
+        "arms": _round({k: head[k] for k in ARMS}),
+        "plan_vs_fixed_max_abs": head["plan_vs_fixed_max_abs"],
+        "precondition": head["precondition"],
         "roofline": {"bound": "hbm", "kernel": "segment attention",
                      "achieved": round(seg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(seg_gbs / HBM_PEAK_GBS, 4),
@@ -406,19 +679,20 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
-    repack = {k: round(head[k], 2) for k in ("shuffle_us", "shuffle_gbs", "convert_us",
-                                             "convert_gbs", "convert_back_us",
-                                             "convert_back_gbs", "cache_write_us",
-                                             "cache_write_tokens") if k in head}
-    if repack:
-        line["repack"] = repack
-    if a.all:
+    if "segment_launch_schedule" in head:
+        line["segment_launch_schedule"] = head["segment_launch_schedule"]
+    if not a.only:
         wl = []
-        for c in configs.CONFIGS + configs.EXTRA:
+        for c in configs.CONFIGS + configs.EXTRA + configs.BS1:
             if c.name == cfg.name:
                 continue
-            r = time_workload(c, a.steps, a.warmup, torch, skv, gen)
-            wl.append({k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()})
+            r = time_workload(c, a, torch, skv, gen)
+            keep = ("workload", "note", "kv_bytes", "us_per_call", "kv_tb_s", "frac_of_hbm_peak",
+                    "segment_us", "segment_gb_s", "plan_T", "planned", "fixed", "graph",
+                    "plan_vs_fixed_max_abs", "precondition", "kv_copies", "repack")
+            wl.append(_round({k: r[k] for k in keep if k in r}))
+            print(f"timed {c.name}: {r['us_per_call']:.1f} us per call", file=sys.stderr,
+                  flush=True)
         line["workloads"] = wl
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seconds, gen, np)

@@ -33,10 +33,9 @@
  * (kv_dtype 1) with per-tensor fp32 dequant scales, or IEEE binary16 fp16
  * (kv_dtype 2; the RFC's decoder scope is BF16/FP16). Q and the output are
  * fp16 with an fp16 cache and bf16 otherwise.
- * Supported geometry: head_dim 64, 128 or 256 for the plan, attention, split
- * reduce and shuffle entry points (128 on kernels specialised for it, 64 and
- * 256 on a generic-width segment kernel), 128 for the in-place conversion,
- * the unshuffle and the cache writer; page_size 16 or 32 tokens for every
+ * Supported geometry: head_dim 64, 128 or 256 for every entry point (the
+ * attention runs 128 on kernels specialised for it, 64 and 256 on a
+ * generic-width segment kernel); page_size 16 or 32 tokens for every
  * entry point (the RFC's decoder scope: 16- or 32-token pages; the split-KV
  * PR's kernels use 16); 1..4 query tokens per sequence,
  * (q_heads / kv_heads) * max_q <= 64.
@@ -59,8 +58,11 @@ enum skv_status {
 };
 
 enum skv_layout { SKV_LAYOUT_STANDARD = 0, SKV_LAYOUT_SHUFFLED = 1 };
-/* Flags of the attention entry points. */
-enum skv_attn_flags { SKV_ATTN_DETERMINISTIC = 1 };
+/* Flags of the attention entry points: 0 (the default, a fixed summation
+ * order, bit-reproducible), SKV_ATTN_DETERMINISTIC (the same, stated
+ * explicitly) or SKV_ATTN_CLAIM_UNITS (run-time claimed order, fp8 KV only;
+ * see skv_paged_decode_attn). Both together are invalid. */
+enum skv_attn_flags { SKV_ATTN_DETERMINISTIC = 1, SKV_ATTN_CLAIM_UNITS = 2 };
 
 enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1, SKV_KV_FP16 = 2 };
 enum skv_convert_dir { SKV_TO_SHUFFLED = 0, SKV_TO_STANDARD = 1 };
@@ -140,20 +142,22 @@ int skv_plan_build(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
  * out          [total_q, q_heads, head_dim], the type of q, round to nearest even;
  *              a token that sees no key gets zeros
  * out_lse      fp32 [total_q, q_heads] or NULL; -inf where no key is visible
- * flags        0 or SKV_ATTN_DETERMINISTIC. With 0 and fp8 KV, the waves of
- *              a work-group take the segment's 32-token blocks in the order
- *              they claim them at run time, so they finish together; each
- *              wave's fp32 sums then run in an order that depends on timing,
- *              and results for identical inputs agree to rounding, not bit
- *              for bit. SKV_ATTN_DETERMINISTIC fixes the order (wave w takes
- *              blocks w, w + waves, ...): bit-identical results for identical
- *              inputs, 2-3% slower on fp8 KV. bf16 and fp16 KV always run in
- *              the fixed order.
+ * flags        0 or SKV_ATTN_DETERMINISTIC (the same): a fixed order (wave w
+ *              of a work-group takes the segment's 32-token blocks w,
+ *              w + waves, ...), so identical inputs give bit-identical
+ *              results [PR, Accuracy Tests: a cached output must equal the
+ *              uncached one bit for bit]. SKV_ATTN_CLAIM_UNITS (fp8 KV; a
+ *              no-op for bf16 and fp16 KV): the waves take the blocks in the
+ *              order they claim them at run time, so they finish together;
+ *              each wave's fp32 sums then run in an order that depends on
+ *              timing, and results for identical inputs agree to rounding,
+ *              not bit for bit.
  * Scale: softmax(q.k / sqrt(head_dim)).
  * Errors: EINVAL for NULL required pointers, non-positive sizes, q_heads not a
  * multiple of kv_heads, bs >= 32768, seg_max outside [1, 65535], max_q < 1,
  * scales present for bf16/fp16 or missing for fp8, kv_b NULL for SHUFFLED or
- * non-NULL for STANDARD, pt_stride < 1, an unknown layout, dtype or flag;
+ * non-NULL for STANDARD, pt_stride < 1, an unknown layout, dtype or flag,
+ * both flags at once;
  * EUNSUPPORTED for head_dim not 64, 128 or 256, page_size other than 16 or 32, max_q > 4,
  * (q_heads/kv_heads) * max_q > 64. */
 int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
@@ -229,10 +233,11 @@ int skv_kv_page_shuffle(const void* std_cache, void* k_plane, void* v_plane,
  * 0..num_blocks-1); a block listed twice is rewritten by two work-groups at
  * once (undefined result). Blocks not listed are left untouched.
  * Errors: EINVAL for NULL planes, num_blocks < 1, kv_heads < 1, a direction
- * other than the two above; EUNSUPPORTED for head_dim != 128, page_size not 16
- * or 32, elem_bytes not 1 or 2, or a block (2 * S) above 128 KiB (16-token
- * pages: kv_heads > 16 for bf16, > 32 for fp8; half that for 32-token pages):
- * the whole block is staged in on-chip memory. */
+ * other than the two above; EUNSUPPORTED for head_dim not 64, 128 or 256,
+ * page_size not 16 or 32, elem_bytes not 1 or 2, or a block (2 * S) above
+ * 128 KiB (head dim 128 with 16-token pages: kv_heads > 16 for bf16, > 32 for
+ * fp8; half that for 32-token pages or head dim 256, twice that for head dim
+ * 64): the whole block is staged in on-chip memory. */
 int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
                         int num_blocks, int kv_heads, int page_size,
                         int head_dim, int elem_bytes, int direction,
@@ -273,7 +278,8 @@ int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
  * Errors: EINVAL for NULL pointers, only one scale given, scales with
  * elem_bytes != 1, num_tokens < 1, num_blocks < 1, kv_heads < 1, a stride
  * below kv_heads * head_dim or not a multiple of the above; EUNSUPPORTED for
- * head_dim != 128, page_size not 16 or 32, elem_bytes not 1 or 2. */
+ * head_dim not 64, 128 or 256, page_size not 16 or 32, elem_bytes not 1 or
+ * 2. */
 int skv_kv_cache_write(const void* key, const void* value,
                        const int64_t* slot_mapping, int num_tokens,
                        long long key_stride, long long value_stride,

@@ -17,7 +17,7 @@ SKV_OK, SKV_EINVAL, SKV_EUNSUPPORTED, SKV_ELAUNCH = 0, 1, 2, 3
 LAYOUT = {"standard": 0, "shuffled": 1}
 CONVERT_DIR = {"to_shuffled": 0, "to_standard": 1}
 KV_DTYPE = {"bf16": 0, "fp8": 1, "fp16": 2}
-ATTN_DETERMINISTIC = 1            # flag of the attention entry points
+ATTN_CLAIM_UNITS = 2              # flag of the attention entry points (fp8: run-time order)
 
 
 def io_dtype(kv_dtype):
@@ -142,14 +142,15 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
                       *, kv_heads, max_q, num_cus, seg_max, kv_dtype="bf16",
                       layout="standard", k_scale=None, v_scale=None, causal=1,
                       part_o=None, part_lse=None, out=None, out_lse=None,
-                      page_size=16, deterministic=False, stream=None):
+                      page_size=16, claim_units=False, stream=None):
     """Enqueue segment attention + split reduce; returns (out, out_lse or None);
     q and out are fp16 with kv_dtype="fp16", else bf16.
 
     plan=None selects the fixed split (no plan launch); tok_nseg is then
-    written by the segment kernel (allocated when None). deterministic=True
-    passes SKV_ATTN_DETERMINISTIC: bit-identical results for identical
-    inputs (otherwise they agree to rounding)."""
+    written by the segment kernel (allocated when None). By default the
+    summation order is fixed (bit-identical results for identical inputs);
+    claim_units=True passes SKV_ATTN_CLAIM_UNITS (fp8 KV: run-time order,
+    results agree to rounding)."""
     total_q, q_heads, head_dim = q.shape
     bs = seq_lens.numel()
     dev = q.device
@@ -182,7 +183,7 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
         total_q, max_q, q_heads, kv_heads, head_dim, page_size, _ptr(k_scale),
         _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
         _ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(out_lse),
-        ATTN_DETERMINISTIC if deterministic else 0, _stream(stream))
+        ATTN_CLAIM_UNITS if claim_units else 0, _stream(stream))
     _check(st, "skv_paged_decode_attn")
     return out, out_lse
 
@@ -190,7 +191,7 @@ def paged_decode_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, t
 def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_nseg,
                  *, kv_heads, max_q, num_cus, seg_max, part_o, part_lse, kv_dtype="bf16",
                  layout="standard", k_scale=None, v_scale=None, causal=1, page_size=16,
-                 deterministic=False, stream=None):
+                 claim_units=False, stream=None):
     """Enqueue the segment kernel alone (partials only). plan=None: fixed split,
     tok_nseg written (allocated when None); returns (part_o, part_lse, tok_nseg)."""
     total_q, q_heads, head_dim = q.shape
@@ -210,7 +211,7 @@ def segment_attn(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_ns
         _ptr(page_table), page_table.shape[1], _ptr(seq_lens), _ptr(cu_seqlens_q), bs,
         total_q, max_q, q_heads, kv_heads, head_dim, page_size, _ptr(k_scale),
         _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
-        _ptr(part_o), _ptr(part_lse), ATTN_DETERMINISTIC if deterministic else 0,
+        _ptr(part_o), _ptr(part_lse), ATTN_CLAIM_UNITS if claim_units else 0,
         _stream(stream))
     _check(st, "skv_segment_attn")
     return part_o, part_lse, tok_nseg

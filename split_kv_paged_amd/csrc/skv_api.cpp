@@ -152,21 +152,20 @@ int skv_kv_page_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
                                    page_size, head_dim, elem_bytes, direction);
   if (st != SKV_OK) return st;
   return skv::launch_convert(k_plane, v_plane, block_ids, num_blocks, kv_heads,
-                             page_size, elem_bytes, direction, stream);
+                             page_size, head_dim, elem_bytes, direction, stream);
 }
 
 int skv_kv_page_unshuffle(const void* k_plane, const void* v_plane,
                           void* std_cache, const int32_t* block_ids,
                           int num_blocks, int kv_heads, int page_size,
                           int head_dim, int elem_bytes, void* stream) {
-  // the forward repack's argument rules; its kernel (the conversion's) is
-  // built for head dim 128 only
+  // the forward repack's argument rules
   int st = skv::check_shuffle_args(std_cache, k_plane, v_plane, num_blocks,
                                    kv_heads, page_size, head_dim, elem_bytes);
   if (st != SKV_OK) return st;
-  if (head_dim != skv::kHeadDim) return SKV_EUNSUPPORTED;
   return skv::launch_unshuffle(k_plane, v_plane, std_cache, block_ids,
-                               num_blocks, kv_heads, page_size, elem_bytes, stream);
+                               num_blocks, kv_heads, page_size, head_dim, elem_bytes,
+                               stream);
 }
 
 int skv_kv_cache_write(const void* key, const void* value,
@@ -183,8 +182,8 @@ int skv_kv_cache_write(const void* key, const void* value,
   if (st != SKV_OK) return st;
   return skv::launch_cache_write(key, value, slot_mapping, num_tokens, key_stride,
                                  value_stride, k_plane, v_plane, num_blocks,
-                                 kv_heads, page_size, elem_bytes, k_scale, v_scale,
-                                 stream);
+                                 kv_heads, page_size, head_dim, elem_bytes, k_scale,
+                                 v_scale, stream);
 }
 
 const char* skv_strerror(int status) {

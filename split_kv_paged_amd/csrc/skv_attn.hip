@@ -59,7 +59,7 @@ int launch_segments(const AttnArgs& a, void* stream) {
   sp.tok_out = nullptr;
   sp.fixed_S = 0;
   sp.page_shift = page_shift_of(a.page_size);
-  sp.claim = (a.flags & SKV_ATTN_DETERMINISTIC) ? 0 : 1;
+  sp.claim = (a.flags & SKV_ATTN_CLAIM_UNITS) ? 1 : 0;
   long long grid;
   if (a.plan) {
     grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) * a.kv_heads;

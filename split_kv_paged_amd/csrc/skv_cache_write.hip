@@ -7,13 +7,14 @@
 // [H, N/x, D, x] per block, x = 16 / element bytes; padding tokens carry a
 // negative slot.
 //
-// MI355X design (16- or 32-token pages): one wave64 per (token, kv head). The
-// token's K row is D*e bytes = D/x chunks of 16 bytes, and each chunk lands
-// whole in the K plane
-// (x consecutive channels of one row), so lanes 0 .. D/x-1 move one 16-byte
+// MI355X design (16- or 32-token pages, head dim 64, 128 or 256): one wave64
+// per (token, kv head). The token's K row is D*e bytes = D/x chunks of 16
+// bytes (at most 32), and each chunk lands whole in the K plane (x
+// consecutive channels of one row), so lanes 0 .. D/x-1 move one 16-byte
 // chunk each. In the V plane consecutive tokens of one channel share a
 // 16-byte chunk, so a token's V row scatters: lane l writes channels 2l and
-// 2l+1 (e bytes each) at stride x*e. Tokens of one block write disjoint bytes,
+// 2l+1 (e bytes each) at stride x*e, and channels 128 + 2l, 128 + 2l + 1 at
+// head dim 256. Tokens of one block write disjoint bytes,
 // so concurrent waves need no ordering. Decode steps write few tokens; the
 // kernel is launch-bound, not bandwidth-bound. With per-tensor scales, bf16
 // rows are quantised into an fp8 cache on the way (the RFC leaves the fp8
@@ -30,9 +31,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kD = kHeadDim;
 
-template <int E, int kN>
+template <int E, int kN, int kD>
 __global__ __launch_bounds__(kThreads) void cache_write_kernel(
     const uint8_t* __restrict__ key, const uint8_t* __restrict__ value,
     const int64_t* __restrict__ slots, int num_tokens, long long key_stride,
@@ -62,17 +62,19 @@ __global__ __launch_bounds__(kThreads) void cache_write_kernel(
   }
   // V: channel d -> v_plane[b, h, n / x, d, n % x]
   const size_t vbase = static_cast<size_t>(n / kX) * kD * kX + n % kX;
-  const int d = 2 * lane;
-  if constexpr (E == 2) {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + 2 * d);
-    reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d) * kX] =
-        static_cast<uint16_t>(w);
-    reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d + 1) * kX] =
-        static_cast<uint16_t>(w >> 16);
-  } else {
-    const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + d);
-    vdst[vbase + static_cast<size_t>(d) * kX] = static_cast<uint8_t>(w);
-    vdst[vbase + static_cast<size_t>(d + 1) * kX] = static_cast<uint8_t>(w >> 8);
+#pragma unroll
+  for (int d = 2 * lane; d < kD; d += 128) {
+    if constexpr (E == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + 2 * d);
+      reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d) * kX] =
+          static_cast<uint16_t>(w);
+      reinterpret_cast<uint16_t*>(vdst)[vbase + static_cast<size_t>(d + 1) * kX] =
+          static_cast<uint16_t>(w >> 16);
+    } else {
+      const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + d);
+      vdst[vbase + static_cast<size_t>(d) * kX] = static_cast<uint8_t>(w);
+      vdst[vbase + static_cast<size_t>(d + 1) * kX] = static_cast<uint8_t>(w >> 8);
+    }
   }
 }
 
@@ -99,8 +101,8 @@ __device__ __forceinline__ uint32_t e4m3fn_rne_sat(float v) {
 }
 
 // bf16 K/V rows quantised into an fp8 cache: code = e4m3fn(value / scale),
-// the division in fp32. Same placement as cache_write_kernel<1, kN>.
-template <int kN>
+// the division in fp32. Same placement as cache_write_kernel<1, kN, kD>.
+template <int kN, int kD>
 __global__ __launch_bounds__(kThreads) void cache_write_quant_kernel(
     const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
     const int64_t* __restrict__ slots, int num_tokens, long long key_stride,
@@ -141,47 +143,45 @@ __global__ __launch_bounds__(kThreads) void cache_write_quant_kernel(
         make_uint4(c[0], c[1], c[2], c[3]);
   }
   const size_t vbase = static_cast<size_t>(n / kX) * kD * kX + n % kX;
-  const int d = 2 * lane;
-  const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + d);
   uint8_t* vdst = vp + head * kPlane;
-  vdst[vbase + static_cast<size_t>(d) * kX] =
-      static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w << 16) / vs));
-  vdst[vbase + static_cast<size_t>(d + 1) * kX] =
-      static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w & 0xffff0000u) / vs));
+#pragma unroll
+  for (int d = 2 * lane; d < kD; d += 128) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + d);
+    vdst[vbase + static_cast<size_t>(d) * kX] =
+        static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w << 16) / vs));
+    vdst[vbase + static_cast<size_t>(d + 1) * kX] =
+        static_cast<uint8_t>(e4m3fn_rne_sat(__uint_as_float(w & 0xffff0000u) / vs));
+  }
 }
 
 }  // namespace
 
-int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
-                       int num_tokens, long long key_stride, long long value_stride,
-                       void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int page_size, int elem_bytes, const float* k_scale,
-                       const float* v_scale, void* stream) {
-  const long long units = static_cast<long long>(num_tokens) * kv_heads;
-  const long long blocks = (units + kWaves - 1) / kWaves;
-  if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
-  const long long num_slots = static_cast<long long>(num_blocks) * page_size;
-  auto st = static_cast<hipStream_t>(stream);
+namespace {
+
+template <int kD>
+int launch_cache_write_d(const void* key, const void* value, const int64_t* slot_mapping,
+                         int num_tokens, long long key_stride, long long value_stride,
+                         uint8_t* kp, uint8_t* vp, int kv_heads, long long num_slots,
+                         int page_size, int elem_bytes, const float* k_scale,
+                         const float* v_scale, dim3 grid, hipStream_t st) {
+  const dim3 block(kThreads);
   auto k = static_cast<const uint8_t*>(key);
   auto v = static_cast<const uint8_t*>(value);
-  auto kp = static_cast<uint8_t*>(k_plane);
-  auto vp = static_cast<uint8_t*>(v_plane);
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if (k_scale) {
     auto kq = static_cast<const uint16_t*>(key);
     auto vq = static_cast<const uint16_t*>(value);
     if (page_size == 32)
-      hipLaunchKernelGGL((cache_write_quant_kernel<32>), grid, block, 0, st, kq, vq,
+      hipLaunchKernelGGL((cache_write_quant_kernel<32, kD>), grid, block, 0, st, kq, vq,
                          slot_mapping, num_tokens, key_stride, value_stride, kp, vp,
                          kv_heads, num_slots, k_scale, v_scale);
     else
-      hipLaunchKernelGGL((cache_write_quant_kernel<16>), grid, block, 0, st, kq, vq,
+      hipLaunchKernelGGL((cache_write_quant_kernel<16, kD>), grid, block, 0, st, kq, vq,
                          slot_mapping, num_tokens, key_stride, value_stride, kp, vp,
                          kv_heads, num_slots, k_scale, v_scale);
     return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
   }
-#define SKV_W(E, N)                                                                  \
-  hipLaunchKernelGGL((cache_write_kernel<E, N>), grid, block, 0, st, k, v, slot_mapping, \
+#define SKV_W(E, N)                                                                      \
+  hipLaunchKernelGGL((cache_write_kernel<E, N, kD>), grid, block, 0, st, k, v, slot_mapping, \
                      num_tokens, key_stride, value_stride, kp, vp, kv_heads, num_slots)
   if (page_size == 32) {
     if (elem_bytes == 2) SKV_W(2, 32); else SKV_W(1, 32);
@@ -190,6 +190,39 @@ int launch_cache_write(const void* key, const void* value, const int64_t* slot_m
   }
 #undef SKV_W
   return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;
+}
+
+}  // namespace
+
+int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
+                       int num_tokens, long long key_stride, long long value_stride,
+                       void* k_plane, void* v_plane, int num_blocks, int kv_heads,
+                       int page_size, int head_dim, int elem_bytes, const float* k_scale,
+                       const float* v_scale, void* stream) {
+  const long long units = static_cast<long long>(num_tokens) * kv_heads;
+  const long long blocks = (units + kWaves - 1) / kWaves;
+  if (blocks > 0x7fffffffLL) return SKV_EUNSUPPORTED;
+  const long long num_slots = static_cast<long long>(num_blocks) * page_size;
+  auto st = static_cast<hipStream_t>(stream);
+  auto kp = static_cast<uint8_t*>(k_plane);
+  auto vp = static_cast<uint8_t*>(v_plane);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  switch (head_dim) {
+    case 64:
+      return launch_cache_write_d<64>(key, value, slot_mapping, num_tokens, key_stride,
+                                      value_stride, kp, vp, kv_heads, num_slots, page_size,
+                                      elem_bytes, k_scale, v_scale, grid, st);
+    case 128:
+      return launch_cache_write_d<128>(key, value, slot_mapping, num_tokens, key_stride,
+                                       value_stride, kp, vp, kv_heads, num_slots, page_size,
+                                       elem_bytes, k_scale, v_scale, grid, st);
+    case 256:
+      return launch_cache_write_d<256>(key, value, slot_mapping, num_tokens, key_stride,
+                                       value_stride, kp, vp, kv_heads, num_slots, page_size,
+                                       elem_bytes, k_scale, v_scale, grid, st);
+    default:
+      return SKV_EUNSUPPORTED;
+  }
 }
 
 }  // namespace skv

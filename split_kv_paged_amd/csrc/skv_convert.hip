@@ -15,7 +15,8 @@
 //  * Proposed Change §4 (Convert) and Test plan: the received blocks are
 //    converted into the shuffled planes; a round trip must restore them.
 //
-// MI355X design (16- or 32-token pages): one work-group per unit. A unit is
+// MI355X design (16- or 32-token pages, head dim 64, 128 or 256): one
+// work-group per unit. A unit is
 // a whole block (all H heads) for the in-place conversion, because the two
 // halves interleave heads:
 // writing any shuffled byte of a block destroys standard bytes of other heads
@@ -39,9 +40,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 8;             // 16-byte loads in flight per thread
-constexpr int kD = kHeadDim;
 
-template <int E, int kN>
+template <int E, int kN, int kD>
 struct Geo {
   static constexpr int kX = 16 / E;                  // elements per 16 bytes
   static constexpr int kRowChunks = 2 * kD * E / 16; // chunks per standard row
@@ -52,9 +52,9 @@ struct Geo {
 };
 
 // LDS chunk index of standard chunk c of token row n of head h
-template <int E, int kN>
+template <int E, int kN, int kD>
 __device__ __forceinline__ int slot(int h, int n, int c) {
-  using G = Geo<E, kN>;
+  using G = Geo<E, kN, kD>;
   return (h * kN + n) * G::kRowChunks + (c ^ (n & (G::kRowChunks - 1)));
 }
 
@@ -82,11 +82,11 @@ __device__ __forceinline__ void st16(uint8_t* p, uint4 v) {
 // at sa + base*s_mul, the second at sb + base*s_mul, base = (b*H + h0)*P; its
 // shuffled bytes are at kp + base and vp + base. In place: sa = kp, sb = vp,
 // s_mul = 1. Out of place: sa = std, sb = std + P, s_mul = 2, uh = 1.
-template <int E, int kN, int CAP, bool TO_SHUF>
+template <int E, int kN, int kD, int CAP, bool TO_SHUF>
 __global__ __launch_bounds__(kThreads) void repack_kernel(
     uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
     const int32_t* __restrict__ block_ids, int kv_heads, int uh) {
-  using G = Geo<E, kN>;
+  using G = Geo<E, kN, kD>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[CAP];
   const int tid = threadIdx.x;
   const int u = blockIdx.x;
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
         const int i = i0 + k * kThreads;
         if (i < total) {
           const int h = i / G::kHeadChunks, r = i % G::kHeadChunks;
-          st16(lds + 16 * slot<E, kN>(h, r / G::kRowChunks, r % G::kRowChunks), v[k]);
+          st16(lds + 16 * slot<E, kN, kD>(h, r / G::kRowChunks, r % G::kRowChunks), v[k]);
         }
       }
     }
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
     // 2a. K plane: chunk o = (h, c, n) is token n's K chunk c
     for (int o = tid; o < half; o += kThreads) {
       const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
-      gst16(K + 16 * o, ld16(lds + 16 * slot<E, kN>(h, r % kN, r / kN)));
+      gst16(K + 16 * o, ld16(lds + 16 * slot<E, kN, kD>(h, r % kN, r / kN)));
     }
     // 2b. V plane: chunk o = (h, g, d) holds tokens g*x .. g*x+x-1 of channel d
     for (int o = tid; o < half; o += kThreads) {
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
 #pragma unroll
         for (int j = 0; j < 4 / E; ++j) {
           const int n = g * G::kX + q * (4 / E) + j;
-          const uint8_t* p = lds + 16 * slot<E, kN>(h, n, cc) + off;
+          const uint8_t* p = lds + 16 * slot<E, kN, kD>(h, n, cc) + off;
           const uint32_t e = E == 2 ? *reinterpret_cast<const uint16_t*>(p) : *p;
           acc |= e << (8 * E * j);
         }
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
         const int o = o0 + k * kThreads;
         if (o < half) {
           const int h = o / G::kPlaneChunks, r = o % G::kPlaneChunks;
-          st16(lds + 16 * slot<E, kN>(h, r % kN, r / kN), v[k]);
+          st16(lds + 16 * slot<E, kN, kD>(h, r % kN, r / kN), v[k]);
         }
       }
     }
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
 #pragma unroll
             for (int j = 0; j < 4 / E; ++j) {
               const int n = g * G::kX + q * (4 / E) + j;
-              uint8_t* p = lds + 16 * slot<E, kN>(h, n, cc) + off;
+              uint8_t* p = lds + 16 * slot<E, kN, kD>(h, n, cc) + off;
               const uint32_t e = w[q] >> (8 * E * j);
               if constexpr (E == 2)
                 *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(e);
@@ -202,22 +202,22 @@ __global__ __launch_bounds__(kThreads) void repack_kernel(
     // 2. LDS image -> standard chunks
     for (int i = tid; i < total; i += kThreads) {
       const int h = i / G::kHeadChunks, r = i % G::kHeadChunks;
-      const uint4 v = ld16(lds + 16 * slot<E, kN>(h, r / G::kRowChunks, r % G::kRowChunks));
+      const uint4 v = ld16(lds + 16 * slot<E, kN, kD>(h, r / G::kRowChunks, r % G::kRowChunks));
       gst16(i < half ? A + 16 * i : B + 16 * (i - half), v);
     }
   }
 }
 
-template <int E, int kN, bool TO_SHUF>
+template <int E, int kN, int kD, bool TO_SHUF>
 int launch_cap(size_t lds_bytes, unsigned units, uint8_t* sa, uint8_t* sb,
                int s_mul, uint8_t* kp, uint8_t* vp, const int32_t* ids,
                int kv_heads, int uh, hipStream_t st) {
   const dim3 grid(units), block(kThreads);
-#define SKV_CAP(C)                                                                \
-  if (lds_bytes <= (C)) {                                                         \
-    hipLaunchKernelGGL((repack_kernel<E, kN, (C), TO_SHUF>), grid, block, 0, st, \
-                       sa, sb, s_mul, kp, vp, ids, kv_heads, uh);                 \
-    return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;                \
+#define SKV_CAP(C)                                                                    \
+  if (lds_bytes <= (C)) {                                                             \
+    hipLaunchKernelGGL((repack_kernel<E, kN, kD, (C), TO_SHUF>), grid, block, 0, st, \
+                       sa, sb, s_mul, kp, vp, ids, kv_heads, uh);                     \
+    return hipGetLastError() == hipSuccess ? SKV_OK : SKV_ELAUNCH;                    \
   }
   SKV_CAP(8 * 1024)
   SKV_CAP(16 * 1024)
@@ -228,16 +228,15 @@ int launch_cap(size_t lds_bytes, unsigned units, uint8_t* sa, uint8_t* sb,
   return SKV_EUNSUPPORTED;
 }
 
-int launch_repack(uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
-                  const int32_t* ids, long long units, int kv_heads, int uh,
-                  int page_size, int elem_bytes, bool to_shuf, void* stream) {
-  if (units > 0x7fffffffLL) return SKV_EUNSUPPORTED;
-  const size_t lds = static_cast<size_t>(uh) * page_size * 2 * kHeadDim * elem_bytes;
-  auto st = static_cast<hipStream_t>(stream);
-  const auto n = static_cast<unsigned>(units);
-#define SKV_GO(E, N)                                                                      \
-  return to_shuf ? launch_cap<E, N, true>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st) \
-                 : launch_cap<E, N, false>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st)
+template <int kD>
+int launch_repack_d(uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
+                    const int32_t* ids, unsigned n, int kv_heads, int uh, int page_size,
+                    int elem_bytes, bool to_shuf, hipStream_t st) {
+  const size_t lds = static_cast<size_t>(uh) * page_size * 2 * kD * elem_bytes;
+#define SKV_GO(E, N)                                                                   \
+  return to_shuf                                                                       \
+      ? launch_cap<E, N, kD, true>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st) \
+      : launch_cap<E, N, kD, false>(lds, n, sa, sb, s_mul, kp, vp, ids, kv_heads, uh, st)
   if (page_size == 32) {
     if (elem_bytes == 2) SKV_GO(2, 32);
     SKV_GO(1, 32);
@@ -247,28 +246,50 @@ int launch_repack(uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
 #undef SKV_GO
 }
 
+int launch_repack(uint8_t* sa, uint8_t* sb, int s_mul, uint8_t* kp, uint8_t* vp,
+                  const int32_t* ids, long long units, int kv_heads, int uh,
+                  int page_size, int head_dim, int elem_bytes, bool to_shuf, void* stream) {
+  if (units > 0x7fffffffLL) return SKV_EUNSUPPORTED;
+  auto st = static_cast<hipStream_t>(stream);
+  const auto n = static_cast<unsigned>(units);
+  switch (head_dim) {
+    case 64:
+      return launch_repack_d<64>(sa, sb, s_mul, kp, vp, ids, n, kv_heads, uh, page_size,
+                                 elem_bytes, to_shuf, st);
+    case 128:
+      return launch_repack_d<128>(sa, sb, s_mul, kp, vp, ids, n, kv_heads, uh, page_size,
+                                  elem_bytes, to_shuf, st);
+    case 256:
+      return launch_repack_d<256>(sa, sb, s_mul, kp, vp, ids, n, kv_heads, uh, page_size,
+                                  elem_bytes, to_shuf, st);
+    default:
+      return SKV_EUNSUPPORTED;
+  }
+}
+
 }  // namespace
 
 int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
-                   int num_blocks, int kv_heads, int page_size, int elem_bytes,
-                   int direction, void* stream) {
+                   int num_blocks, int kv_heads, int page_size, int head_dim,
+                   int elem_bytes, int direction, void* stream) {
   auto kp = static_cast<uint8_t*>(k_plane);
   auto vp = static_cast<uint8_t*>(v_plane);
   return launch_repack(kp, vp, 1, kp, vp, block_ids, num_blocks, kv_heads, kv_heads,
-                       page_size, elem_bytes, direction == SKV_TO_SHUFFLED, stream);
+                       page_size, head_dim, elem_bytes, direction == SKV_TO_SHUFFLED,
+                       stream);
 }
 
 int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
                      const int32_t* block_ids, int num_blocks, int kv_heads,
-                     int page_size, int elem_bytes, void* stream) {
+                     int page_size, int head_dim, int elem_bytes, void* stream) {
   auto s = static_cast<uint8_t*>(std_cache);
-  const size_t P = static_cast<size_t>(page_size) * kHeadDim * elem_bytes;
+  const size_t P = static_cast<size_t>(page_size) * head_dim * elem_bytes;
   // the planes are only read in this direction
   auto kp = const_cast<uint8_t*>(static_cast<const uint8_t*>(k_plane));
   auto vp = const_cast<uint8_t*>(static_cast<const uint8_t*>(v_plane));
   return launch_repack(s, s + P, 2, kp, vp, block_ids,
                        static_cast<long long>(num_blocks) * kv_heads, kv_heads, 1,
-                       page_size, elem_bytes, false, stream);
+                       page_size, head_dim, elem_bytes, false, stream);
 }
 
 }  // namespace skv

@@ -22,9 +22,8 @@ constexpr int kMaxConvertBytes = 128 * 1024;   // one block staged in LDS
 inline bool repack_page_size_ok(int page_size) { return page_size == 16 || page_size == 32; }
 inline int page_shift_of(int page_size) { return page_size == 32 ? 5 : 4; }   // log2
 
-// head dims of the attention, reduce and shuffle entry points (128 on the
-// specialised kernels; 64 and 256 on the generic-width segment kernel); the
-// in-place conversion, the unshuffle and the cache writer take 128 only
+// head dims of every entry point (attention: 128 on the specialised kernels,
+// 64 and 256 on the generic-width segment kernel)
 inline bool head_dim_ok(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
 
 // ---- host-only argument checks (skv_validate.cpp; no HIP headers) ----------
@@ -96,7 +95,7 @@ struct AttnArgs {
   float* part_lse;
   void* out;
   float* out_lse;
-  int flags;                 // SKV_ATTN_DETERMINISTIC or 0
+  int flags;                 // 0, SKV_ATTN_DETERMINISTIC or SKV_ATTN_CLAIM_UNITS
 };
 
 int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
@@ -110,15 +109,15 @@ int launch_shuffle(const void* std_cache, void* k_plane, void* v_plane,
                    const int32_t* block_ids, int num_blocks, int kv_heads,
                    int page_size, int head_dim, int elem_bytes, void* stream);
 int launch_convert(void* k_plane, void* v_plane, const int32_t* block_ids,
-                   int num_blocks, int kv_heads, int page_size, int elem_bytes,
-                   int direction, void* stream);
+                   int num_blocks, int kv_heads, int page_size, int head_dim,
+                   int elem_bytes, int direction, void* stream);
 int launch_unshuffle(const void* k_plane, const void* v_plane, void* std_cache,
                      const int32_t* block_ids, int num_blocks, int kv_heads,
-                     int page_size, int elem_bytes, void* stream);
+                     int page_size, int head_dim, int elem_bytes, void* stream);
 int launch_cache_write(const void* key, const void* value, const int64_t* slot_mapping,
                        int num_tokens, long long key_stride, long long value_stride,
                        void* k_plane, void* v_plane, int num_blocks, int kv_heads,
-                       int page_size, int elem_bytes, const float* k_scale,
+                       int page_size, int head_dim, int elem_bytes, const float* k_scale,
                        const float* v_scale, void* stream);
 
 }  // namespace skv

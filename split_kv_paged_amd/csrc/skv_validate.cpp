@@ -26,7 +26,8 @@ int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     const void* plan, const void* tok_nseg, int num_cus,
                     int seg_max, const void* part_o, const void* part_lse,
                     const void* out, int flags) {
-  if (flags & ~SKV_ATTN_DETERMINISTIC) return SKV_EINVAL;
+  if (flags & ~(SKV_ATTN_DETERMINISTIC | SKV_ATTN_CLAIM_UNITS)) return SKV_EINVAL;
+  if ((flags & SKV_ATTN_DETERMINISTIC) && (flags & SKV_ATTN_CLAIM_UNITS)) return SKV_EINVAL;
   (void)plan;   // NULL selects the fixed split
   if (!q || !kv_a || !page_table || !seq_lens || !cu_seqlens_q || !tok_nseg ||
       !part_o || !part_lse || !out)
@@ -81,7 +82,7 @@ int check_convert_args(const void* k_plane, const void* v_plane, int num_blocks,
     return SKV_EINVAL;
   if (direction != SKV_TO_SHUFFLED && direction != SKV_TO_STANDARD)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   const long long block = 2LL * kv_heads * page_size * head_dim * elem_bytes;
   if (block > kMaxConvertBytes) return SKV_EUNSUPPORTED;
@@ -100,7 +101,7 @@ int check_cache_write_args(const void* key, const void* value, const void* slots
   if (num_tokens < 1 || num_blocks < 1 || kv_heads < 1 || page_size < 1 ||
       head_dim < 1)
     return SKV_EINVAL;
-  if (head_dim != kHeadDim || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
+  if (!head_dim_ok(head_dim) || !repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
   if (elem_bytes != 1 && elem_bytes != 2) return SKV_EUNSUPPORTED;
   const long long row = static_cast<long long>(kv_heads) * head_dim;
   const int x = 16 / (k_scale ? 2 : elem_bytes);       // input rows: bf16 when quantising

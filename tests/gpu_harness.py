@@ -19,12 +19,13 @@ def say(*a):
 
 
 def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_max=None,
-            causal=None, fixed=False, deterministic=False):
+            causal=None, fixed=False, claim=False):
     """Plan + (optional shuffle) + attention + reduce on cuda:0. Returns a dict of
     host copies (plan, tok_nseg, out as float64, lse) plus the device planes.
     fixed=True runs the fixed split (no plan; the segment kernel writes tok_nseg,
-    which starts out holding -7 so an unwritten entry shows). deterministic
-    selects the fixed order of units within a work-group (bit-reproducible)."""
+    which starts out holding -7 so an unwritten entry shows). claim=True
+    lets fp8 waves claim their units at run time (SKV_ATTN_CLAIM_UNITS);
+    the default is the fixed, bit-reproducible order."""
     cfg = case.cfg
     layout = layout or cfg.layout
     num_cus = num_cus or cfg.num_cus
@@ -50,7 +51,7 @@ def run_hip(case, layout=None, planes=None, poison_ws=True, num_cus=None, seg_ma
         kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=num_cus, seg_max=seg_max,
         kv_dtype=cfg.kv_dtype, layout=layout, k_scale=case.k_scale, v_scale=case.v_scale,
         causal=causal, part_o=part_o, part_lse=part_lse, out_lse=out_lse,
-        page_size=cfg.page_size, deterministic=deterministic)
+        page_size=cfg.page_size, claim_units=claim)
     torch.cuda.synchronize()
     return dict(plan=None if plan is None else plan.cpu().numpy().tolist(),
                 tok=tok.cpu().numpy().tolist(),

@@ -98,13 +98,13 @@ def _attn(**kw):
     (dict(page_size=64), 2), (dict(page_size=24), 2), (dict(max_q=5), 2),
     (dict(q_heads=32, kv_heads=2, max_q=8), 2),           # rows 128 > 64 (max_q checked first)
     (dict(q_heads=64, kv_heads=2, max_q=3), 2),           # rows 96 > 64
-    (dict(flags=2), 1), (dict(flags=-1), 1), (dict(flags=3), 1),
+    (dict(flags=4), 1), (dict(flags=-1), 1), (dict(flags=3), 1),   # 3: both flags at once
 ])
 def test_attn_errors(kw, code):
     assert _attn(**kw) == code
 
 
-@pytest.mark.parametrize("flags,code", [(2, 1), (-1, 1), (4, 1), (1 << 30, 1)])
+@pytest.mark.parametrize("flags,code", [(3, 1), (-1, 1), (4, 1), (1 << 30, 1)])
 def test_segment_attn_flag_errors(flags, code):
     st = skv.load().skv_segment_attn(P, P, None, 0, 0, P, 8, P, P, 2, 2, 1, 8, 2, 128, 16, None,
                                      None, 1, P, P, 256, 64, P, P, flags, None)
@@ -152,9 +152,10 @@ def _convert(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1), (dict(d=2), 1),
-    (dict(d=-1), 1), (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(d=-1), 1), (dict(hd=96), 2), (dict(hd=512), 2), (dict(ps=64), 2), (dict(e=4), 2),
     (dict(h=17), 2), (dict(h=33, e=1), 2),               # block above 128 KiB
     (dict(h=9, ps=32), 2), (dict(h=17, ps=32, e=1), 2),
+    (dict(h=9, hd=256), 2), (dict(h=33, hd=64), 2),      # the same bound at head dims 256 and 64
 ])
 def test_convert_errors(kw, code):
     assert _convert(**kw) == code
@@ -169,7 +170,7 @@ def _unshuffle(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dst=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(nb=0), 1), (dict(h=0), 1),
-    (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(hd=96), 2), (dict(hd=512), 2), (dict(ps=64), 2), (dict(e=4), 2),
 ])
 def test_unshuffle_errors(kw, code):
     assert _unshuffle(**kw) == code
@@ -188,7 +189,7 @@ def _write(**kw):
     (dict(k=None), 1), (dict(v=None), 1), (dict(slots=None), 1), (dict(kp=None), 1),
     (dict(vp=None), 1), (dict(T=0), 1), (dict(nb=0), 1), (dict(h=0), 1),
     (dict(ks=255), 1), (dict(vs=128), 1), (dict(ks=260), 1),       # below H*D / not a multiple of x
-    (dict(hd=64), 2), (dict(hd=256), 2), (dict(ps=64), 2), (dict(e=4), 2),
+    (dict(hd=96), 2), (dict(hd=512), 2), (dict(ps=64), 2), (dict(e=4), 2),
     (dict(ksc=P), 1), (dict(vsc=P), 1),                  # one scale without the other
     (dict(ksc=P, vsc=P), 1),                              # quantising needs an fp8 cache
     (dict(ksc=P, vsc=P, e=1, ks=260), 1),                 # bf16 input rows: multiple of 8

@@ -35,11 +35,15 @@ def _host(t, e):
     return a.view(np.uint16) if e == 2 else a
 
 
-@pytest.mark.parametrize("e,H,N", [(2, 1, 16), (2, 2, 16), (2, 8, 16), (1, 2, 16), (1, 8, 16),
-                                   (2, 3, 32), (1, 4, 32)])
-def test_cache_write_bit_exact(e, H, N):
-    say("cache write", e, H, N)
-    rng = np.random.default_rng(40 + 3 * H + e)
+@pytest.mark.parametrize("e,H,N,D", [(2, 1, 16, D), (2, 2, 16, D), (2, 8, 16, D), (1, 2, 16, D),
+                                     (1, 8, 16, D), (2, 3, 32, D), (1, 4, 32, D),
+                                     (2, 2, 16, 64), (1, 3, 32, 64), (2, 3, 16, 256),
+                                     (1, 2, 32, 256)])
+def test_cache_write_bit_exact(e, H, N, D):
+    """Bit-exact against the oracle, with padding slots (-1) and slots at or
+    past the end of the cache (skipped) mixed in."""
+    say("cache write", e, H, N, D)
+    rng = np.random.default_rng(40 + 3 * H + e + D)
     dt = np.uint16 if e == 2 else np.uint8
     x = 16 // e
     B, T = 9, 70
@@ -48,6 +52,7 @@ def test_cache_write_bit_exact(e, H, N):
     vfull = rng.integers(0, 1 << (8 * e), size=(T, H * D + pad)).astype(dt)
     slots = rng.choice(B * N, size=T, replace=False).astype(np.int64)
     slots[[0, 11, 40]] = -1                                # padding tokens
+    slots[[5, 23, 61]] = [B * N, B * N + 7, 1 << 40]       # past the cache: skipped
     kp0 = rng.integers(0, 1 << (8 * e), size=(B, H, D // x, N, x)).astype(dt)
     vp0 = rng.integers(0, 1 << (8 * e), size=(B, H, N // x, D, x)).astype(dt)
     kp, vp = _dev(kp0, e), _dev(vp0, e)
@@ -128,13 +133,14 @@ def _bf16_bits(x):
         torch.int16).numpy().view(np.uint16)
 
 
-@pytest.mark.parametrize("H,N", [(1, 16), (2, 16), (8, 16), (3, 32)])
-def test_cache_write_quantises_bit_exact(H, N):
+@pytest.mark.parametrize("H,N,D", [(1, 16, D), (2, 16, D), (8, 16, D), (3, 32, D), (2, 16, 64),
+                                   (3, 32, 256)])
+def test_cache_write_quantises_bit_exact(H, N, D):
     """bf16 rows into an fp8 cache with per-tensor scales: every code equals the
     oracle's nearest-even e4m3fn code of value / scale (fp32 division),
     saturated at 448."""
-    say("cache write quantise", H, N)
-    rng = np.random.default_rng(70 + H + N)
+    say("cache write quantise", H, N, D)
+    rng = np.random.default_rng(70 + H + N + D)
     B, T = 7, 50
     ks, vs = 0.0173, 0.0211
     k = rng.normal(0, 1, size=(T, H, D)) * rng.choice([0.01, 1, 5, 50], size=(T, H, 1))
@@ -143,6 +149,7 @@ def test_cache_write_quantises_bit_exact(H, N):
     kb, vb = _bf16_bits(k), _bf16_bits(v)
     slots = rng.choice(B * N, size=T, replace=False).astype(np.int64)
     slots[[2, 9]] = -1
+    slots[[4, 30]] = [B * N, 10 ** 12]                     # past the cache: skipped
     kp0 = rng.integers(0, 256, size=(B, H, D // 16, N, 16)).astype(np.uint8)
     vp0 = rng.integers(0, 256, size=(B, H, N // 16, D, 16)).astype(np.uint8)
     kp, vp = _dev(kp0, 1), _dev(vp0, 1)

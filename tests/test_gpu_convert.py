@@ -44,16 +44,21 @@ def _random_codes(rng, shape, e):
     return rng.integers(0, 1 << (8 * e), size=shape).astype(_np_dtype(e))
 
 
-CONVERT_CASES = [(2, 1, 16), (2, 2, 16), (2, 3, 16), (2, 8, 16), (2, 16, 16), (1, 1, 16),
-                 (1, 3, 16), (1, 8, 16), (1, 32, 16),
-                 (2, 1, 32), (2, 3, 32), (2, 8, 32), (1, 5, 32), (1, 16, 32)]
+CONVERT_CASES = [(2, 1, 16, D), (2, 2, 16, D), (2, 3, 16, D), (2, 8, 16, D), (2, 16, 16, D),
+                 (1, 1, 16, D), (1, 3, 16, D), (1, 8, 16, D), (1, 32, 16, D),
+                 (2, 1, 32, D), (2, 3, 32, D), (2, 8, 32, D), (1, 5, 32, D), (1, 16, 32, D),
+                 # head dims 64 and 256, up to the 128 KiB block bound
+                 (2, 1, 16, 64), (2, 3, 16, 64), (2, 32, 16, 64), (1, 64, 16, 64),
+                 (1, 3, 32, 64), (2, 5, 32, 64),
+                 (2, 1, 16, 256), (2, 3, 16, 256), (2, 8, 16, 256), (1, 1, 16, 256),
+                 (1, 5, 32, 256), (2, 4, 32, 256)]
 
 
 @pytest.mark.parametrize("subset", [False, True])
-@pytest.mark.parametrize("e,H,N", CONVERT_CASES)
-def test_convert_in_place_and_back(e, H, N, subset):
-    say("convert", e, H, N, subset)
-    rng = np.random.default_rng(100 * H + e)
+@pytest.mark.parametrize("e,H,N,D", CONVERT_CASES)
+def test_convert_in_place_and_back(e, H, N, D, subset):
+    say("convert", e, H, N, D, subset)
+    rng = np.random.default_rng(100 * H + e + D)
     B = 23
     x = 16 // e
     std = _random_codes(rng, (B, H, N, 2 * D), e)
@@ -79,10 +84,12 @@ def test_convert_in_place_and_back(e, H, N, subset):
 
 
 @pytest.mark.parametrize("subset", [False, True])
-@pytest.mark.parametrize("e,H,N", [(2, 1, 16), (2, 3, 16), (2, 8, 16), (1, 2, 16), (1, 5, 16),
-                                   (2, 3, 32), (1, 2, 32)])
-def test_unshuffle_bit_exact(e, H, N, subset):
-    say("unshuffle", e, H, N, subset)
+@pytest.mark.parametrize("e,H,N,D", [(2, 1, 16, D), (2, 3, 16, D), (2, 8, 16, D), (1, 2, 16, D),
+                                     (1, 5, 16, D), (2, 3, 32, D), (1, 2, 32, D),
+                                     (2, 3, 16, 64), (1, 5, 32, 64), (2, 2, 32, 256),
+                                     (1, 3, 16, 256)])
+def test_unshuffle_bit_exact(e, H, N, D, subset):
+    say("unshuffle", e, H, N, D, subset)
     rng = np.random.default_rng(7 * H + e)
     B = 19
     std = _random_codes(rng, (B, H, N, 2 * D), e)
@@ -103,13 +110,13 @@ def test_unshuffle_bit_exact(e, H, N, subset):
             assert np.array_equal(got[b], fill[b]), f"unlisted block {b} written"
 
 
-@pytest.mark.parametrize("N", [16, 32])
-def test_convert_agrees_with_out_of_place_shuffle(N):
+@pytest.mark.parametrize("N,D", [(16, D), (32, D), (16, 64), (16, 256)])
+def test_convert_agrees_with_out_of_place_shuffle(N, D):
     """Same standard blocks, two routes on the GPU: the out-of-place repack and
     the in-place conversion of the byte halves write identical planes."""
-    say("convert vs shuffle", N)
+    say("convert vs shuffle", N, D)
     rng = np.random.default_rng(5)
-    B, H, e = 64, 8, 2
+    B, H, e = 64, (4 if D == 256 and N == 32 else 8), 2
     std = _random_codes(rng, (B, H, N, 2 * D), e)
     kp0, vp0 = oracle.halves_from_standard(std, elem_bytes=e)
     kp, vp = _to_dev(kp0, e), _to_dev(vp0, e)

@@ -58,8 +58,8 @@ def test_graph_replays_match_eager(dtype, layout):
     vnew = case.kv[:4, :, 0, 128:].contiguous()
     kw = dict(kv_heads=cfg.kv_heads, max_q=cfg.max_q, num_cus=cfg.num_cus,
               seg_max=cfg.seg_max, kv_dtype=dtype, layout=layout, k_scale=case.k_scale,
-              v_scale=case.v_scale, causal=cfg.causal, deterministic=True)
-    cout = torch.zeros_like(out)          # claimed units (the default order): to rounding
+              v_scale=case.v_scale, causal=cfg.causal)
+    cout = torch.zeros_like(out)          # claimed units (opt-in order): to rounding
 
     def forward():                        # library calls only: nothing else is captured
         skv.kv_page_shuffle(case.kv, kp, vp)
@@ -76,7 +76,7 @@ def test_graph_replays_match_eager(dtype, layout):
                               out=fout, **kw)
         skv.paged_decode_attn(case.q, kv_a, kv_b, case.page_table, case.seq_lens,
                               case.cu_seqlens_q, plan, tok, part_o=part_o, part_lse=part_lse,
-                              out=cout, **dict(kw, deterministic=False))
+                              out=cout, **dict(kw, claim_units=True))
 
     def restore_halves():                 # eager, before every run
         kh.copy_(kh0)

@@ -112,3 +112,47 @@ def test_head_dim_shuffle_bit_exact(D, e, N):
     gk = kp.cpu().numpy().view(np.uint16) if e == 2 else kp.cpu().numpy()
     gv = vp.cpu().numpy().view(np.uint16) if e == 2 else vp.cpu().numpy()
     assert np.array_equal(gk, wk) and np.array_equal(gv, wv)
+
+
+# long segments (num_cus 16: few segments, many blocks per work-group) so the
+# running row maxima rise many times inside one work-group
+SHARP_SHAPES = [
+    ("sharp_rows64", [0, 1, 17, 3000, 9000], [4, 4, 3, 1, 2], 32, 2, 1, 16, 64),
+    ("sharp_rows4", [15, 700, 5000], [1, 2, 1], 8, 4, 1, 16, 8),
+]
+
+
+@pytest.mark.parametrize("qmul", [6.0, 24.0])
+@pytest.mark.parametrize("layout", ["standard", "shuffled"])
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp8"])
+@pytest.mark.parametrize("shape", SHARP_SHAPES, ids=lambda s: s[0])
+@pytest.mark.parametrize("D", [64, 256])
+def test_head_dim_sharp_scores(D, shape, dt, layout, qmul):
+    """Q scaled so that scores spread over tens of units: the generic-width
+    kernel's lazy row-max rescale runs often and by large steps, and outputs
+    are dominated by a few keys (O(1) values, so the max-abs bar is tight)."""
+    say("head_dim sharp", D, shape[0], dt, layout, qmul)
+    case = _mk(shape, D, dt, layout, 16)
+    case.q.copy_((case.q.float() * qmul).to(case.q.dtype))
+    hip = run_hip(case)
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, dt)
+    say(r)
+    assert r["max_abs"] <= r["tol"], r
+    assert r["max_rel_rms"] <= 1e-2, r
+    assert r["lse_err"] <= 1e-3 * max(1.0, float(np.abs(ref_lse[np.isfinite(ref_lse)]).max())), r
+
+
+@pytest.mark.parametrize("layout", ["standard", "shuffled"])
+@pytest.mark.parametrize("shape", SHAPES[:2], ids=lambda s: s[0])
+@pytest.mark.parametrize("D", [64, 256])
+def test_head_dim_fp8_negative_scales(D, shape, layout):
+    """Negative fp8 scales flip every score and every V value."""
+    say("head_dim negative scales", D, shape[0], layout)
+    name, lens, ql, hq, hkv, causal, ncu, smax = shape
+    cfg = gen.small_config(configs.FP8_KV, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
+                           causal=causal, num_cus=ncu, seg_max=smax, seed=11 + D,
+                           head_dim=D, k_scale=-0.0173, v_scale=-0.0211)
+    case = gen.make_case(cfg, DEV)
+    hip = run_hip(case)
+    say(_check(case, hip))

@@ -111,3 +111,21 @@ UNIFORM_VERIFY_D256 = Config("uniform_verify_d256", [119_000] * 16, [4] * 16, 32
 EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64,
          UNIFORM_VERIFY_D256]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
+
+# The split-KV PR's single-sequence rows (Benchmarking and Profiling: "bs1
+# 110k / 248k", run on the fixed split, which the planner bypasses at bs 1):
+# one verify sequence of 110,000 or 248,000 tokens, 4 query tokens, 32/2
+# heads, with an e4m3fn cache (the PR's table counts one byte per element)
+# and with bf16.
+BS1_110K_FP8 = Config("bs1_110k_fp8", [110_000], [4], 32, 2, kv_dtype="fp8",
+                      k_scale=0.0173, v_scale=0.0211, seed=11,
+                      note="bs=1 x 110k, q=4, 32/2 heads, e4m3fn KV")
+BS1_248K_FP8 = Config("bs1_248k_fp8", [248_000], [4], 32, 2, kv_dtype="fp8",
+                      k_scale=0.0173, v_scale=0.0211, seed=12,
+                      note="bs=1 x 248k, q=4, 32/2 heads, e4m3fn KV")
+BS1_110K = Config("bs1_110k", [110_000], [4], 32, 2, seed=13,
+                  note="bs=1 x 110k, q=4, 32/2 heads, bf16")
+BS1_248K = Config("bs1_248k", [248_000], [4], 32, 2, seed=14,
+                  note="bs=1 x 248k, q=4, 32/2 heads, bf16")
+BS1 = [BS1_110K_FP8, BS1_248K_FP8, BS1_110K, BS1_248K]
+BY_NAME.update({c.name: c for c in BS1})
