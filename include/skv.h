@@ -288,6 +288,34 @@ int skv_kv_cache_write(const void* key, const void* value,
                        int elem_bytes, const float* k_scale,
                        const float* v_scale, void* stream);
 
+/* Bytes of the library's own device array that skv_paged_decode_attn_static
+ * keeps its partials in (per GPU, for the life of the process). */
+#define SKV_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* skv_paged_decode_attn without part_o / part_lse: for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). The partials live in a fixed device array
+ * of SKV_STATIC_SCRATCH_BYTES (64 MiB) that the library holds on every GPU it
+ * runs on until the process ends; its address is looked up on the first call
+ * made with that GPU current. This call allocates and frees nothing.
+ * Arguments, results and the other errors are those of skv_paged_decode_attn
+ * (same kernels, same summation order: identical outputs). Every call on one
+ * GPU uses that GPU's one array, so calls that overlap on one GPU (several
+ * streams or host threads at once) race and must be serialized by the caller.
+ * Errors: EUNSUPPORTED when skv_workspace_bytes(total_q, q_heads, head_dim,
+ * seg_max) exceeds SKV_STATIC_SCRATCH_BYTES (e.g. 55 query tokens x 32 heads x
+ * 64 segments at head dim 128 need 58 MB and fit); ELAUNCH when the array's
+ * device address cannot be obtained. */
+int skv_paged_decode_attn_static(const void* q, const void* kv_a, const void* kv_b,
+                                 int layout, int kv_dtype, const int32_t* page_table,
+                                 int pt_stride, const int32_t* seq_lens,
+                                 const int32_t* cu_seqlens_q, int bs, int total_q,
+                                 int max_q, int q_heads, int kv_heads, int head_dim,
+                                 int page_size, const float* k_scale,
+                                 const float* v_scale, int causal, const int32_t* plan,
+                                 int32_t* tok_nseg, int num_cus, int seg_max, void* out,
+                                 float* out_lse, int flags, void* stream);
+
 /* Static text for a status code. */
 const char* skv_strerror(int status);
 

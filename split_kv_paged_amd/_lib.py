@@ -50,6 +50,10 @@ _SIGNATURES = {
     "skv_kv_cache_write": (_c_int, [_p, _p, _p, _c_int, ctypes.c_longlong, ctypes.c_longlong,
                                     _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int, _p, _p,
                                     _p]),
+    "skv_paged_decode_attn_static": (_c_int, [_p, _p, _p, _c_int, _c_int, _p, _c_int, _p, _p,
+                                              _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                              _c_int, _p, _p, _c_int, _p, _p, _c_int, _c_int,
+                                              _p, _p, _c_int, _p]),
     "skv_strerror": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -327,3 +331,43 @@ def kv_cache_write(key, value, slot_mapping, k_plane, v_plane, k_scale=None, v_s
                                    _ptr(v_scale), _stream(stream))
     _check(st, "skv_kv_cache_write")
     return k_plane, v_plane
+
+
+STATIC_SCRATCH_BYTES = 64 << 20      # SKV_STATIC_SCRATCH_BYTES
+
+
+def paged_decode_attn_static(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, plan, tok_nseg,
+                             *, kv_heads, max_q, num_cus, seg_max, kv_dtype="bf16",
+                             layout="standard", k_scale=None, v_scale=None, causal=1,
+                             out=None, out_lse=None, page_size=16, claim_units=False,
+                             stream=None):
+    """paged_decode_attn with the partials in the library's own device array
+    (no workspace arguments; the library allocates nothing). Calls that
+    overlap on one GPU race. Returns (out, out_lse or None)."""
+    total_q, q_heads, head_dim = q.shape
+    bs = seq_lens.numel()
+    dev = q.device
+    if plan is None and tok_nseg is None:
+        tok_nseg = torch.empty(total_q, dtype=torch.int32, device=dev)
+    iot = io_dtype(kv_dtype)
+    if out is None:
+        out = torch.empty((total_q, q_heads, head_dim), dtype=iot, device=dev)
+    _need(q, iot, "q")
+    _need(out, iot, "out", total_q * q_heads * head_dim)
+    _need(page_table, torch.int32, "page_table")
+    if plan is not None:
+        _need(plan, torch.int32, "plan", plan_words(bs, kv_heads, num_cus))
+    _need(tok_nseg, torch.int32, "tok_nseg", total_q)
+    if out_lse is not None:
+        _need(out_lse, torch.float32, "out_lse", total_q * q_heads)
+    for t, n in ((kv_a, "kv_a"), (kv_b, "kv_b")):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{n}: expected a contiguous device tensor")
+    st = load().skv_paged_decode_attn_static(
+        _ptr(q), _ptr(kv_a), _ptr(kv_b), LAYOUT[layout], KV_DTYPE[kv_dtype],
+        _ptr(page_table), page_table.shape[1], _ptr(seq_lens), _ptr(cu_seqlens_q), bs,
+        total_q, max_q, q_heads, kv_heads, head_dim, page_size, _ptr(k_scale),
+        _ptr(v_scale), int(causal), _ptr(plan), _ptr(tok_nseg), num_cus, seg_max,
+        _ptr(out), _ptr(out_lse), ATTN_CLAIM_UNITS if claim_units else 0, _stream(stream))
+    _check(st, "skv_paged_decode_attn_static")
+    return out, out_lse

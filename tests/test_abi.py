@@ -202,3 +202,34 @@ def test_python_binding_raises_on_error_status():
     with pytest.raises(_lib.SkvError) as ei:
         _lib._check(2, "x")
     assert ei.value.status == 2
+
+
+def _static(**kw):
+    a = dict(q=P, kv_a=P, kv_b=None, layout=0, dtype=0, pt=P, pt_stride=8, sl=P, cu=P, bs=2,
+             total_q=2, max_q=1, q_heads=8, kv_heads=2, head_dim=128, page_size=16,
+             ks=None, vs=None, causal=1, plan=P, tok=P, num_cus=256, seg_max=64, out=P,
+             out_lse=None, flags=0)
+    a.update(kw)
+    return skv.load().skv_paged_decode_attn_static(
+        a["q"], a["kv_a"], a["kv_b"], a["layout"], a["dtype"], a["pt"], a["pt_stride"], a["sl"],
+        a["cu"], a["bs"], a["total_q"], a["max_q"], a["q_heads"], a["kv_heads"], a["head_dim"],
+        a["page_size"], a["ks"], a["vs"], a["causal"], a["plan"], a["tok"], a["num_cus"],
+        a["seg_max"], a["out"], a["out_lse"], a["flags"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(tok=None), 1), (dict(kv_b=P), 1),
+    (dict(flags=3), 1), (dict(head_dim=96), 2), (dict(max_q=5), 2),
+    # partials beyond the library's 64 MiB array: 64 x 32 x 64 x (128 + 1) x 4 B
+    (dict(total_q=64, q_heads=32, max_q=4, seg_max=64), 2),
+    (dict(total_q=8, q_heads=16, head_dim=256, seg_max=65535), 2),
+])
+def test_static_attn_errors(kw, code):
+    """Rejected on the host, before the device array is looked up."""
+    assert _static(**kw) == code
+
+
+def test_static_scratch_size_matches_header():
+    text = open(HEADER).read()
+    assert "#define SKV_STATIC_SCRATCH_BYTES (64u << 20)" in text
+    assert skv.STATIC_SCRATCH_BYTES == 64 << 20
