@@ -7,12 +7,21 @@
 //   M = max_s lse_s,  lse = M + ln sum_s e^(lse_s - M),
 //   out = sum_s e^(lse_s - lse) * o_s.
 //
-// MI355X design: one wave64 per (token, q head); lane l owns D/64 consecutive
-// channels (2l and 2l+1 at head dim 128: float2 loads, 512 contiguous bytes
-// per segment; one or four channels at head dims 64 and 256); the weights
-// are formed in fp32 registers, the output rounded to bf16 or fp16 (RNE). Traffic is
-// tiny next to the KV stream, so this kernel is latency-, not
-// bandwidth-, shaped.
+// MI355X design: lane l of a wave owns D/64 consecutive channels (2l and 2l+1
+// at head dim 128: float2 loads, 512 contiguous bytes per segment; one or four
+// channels at head dims 64 and 256); the weights are formed in fp32
+// registers, the output rounded to bf16 or fp16 (RNE). Traffic is tiny next
+// to the KV stream, so the kernel is latency-, not bandwidth-, shaped: what
+// matters is how many partial rows are in flight at once and how many
+// work-groups the launch has.
+//  * Narrow form (many (token, head) rows): one wave per row, four rows per
+//    work-group; the first 8 partial rows are loaded before the weights are
+//    known, the rest in chunks of 8 loads issued together.
+//  * Wide form (at most 1024 rows, e.g. single-sequence batches whose
+//    tokens each merge up to 64 segments): one work-group per row, its four
+//    waves each loading a quarter of the segments (up to 16 rows in flight
+//    per wave) before the weights are known; the four partial sums are added
+//    through LDS.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -67,6 +76,128 @@ __device__ __forceinline__ unsigned short to_out16(float f) {
   }
 }
 
+template <bool F16, int C>
+__device__ __forceinline__ void store_row(unsigned short* orow, const LaneVec<C>& acc) {
+  if constexpr (C == 1) {
+    orow[0] = to_out16<F16>(acc.v[0]);
+  } else if constexpr (C == 2) {
+    *reinterpret_cast<unsigned int*>(orow) =
+        static_cast<unsigned int>(to_out16<F16>(acc.v[0])) |
+        (static_cast<unsigned int>(to_out16<F16>(acc.v[1])) << 16);
+  } else {
+    *reinterpret_cast<uint2*>(orow) = make_uint2(
+        static_cast<unsigned int>(to_out16<F16>(acc.v[0])) |
+            (static_cast<unsigned int>(to_out16<F16>(acc.v[1])) << 16),
+        static_cast<unsigned int>(to_out16<F16>(acc.v[2])) |
+            (static_cast<unsigned int>(to_out16<F16>(acc.v[3])) << 16));
+  }
+}
+
+// General merge of one row by one wave, any segment count: max, then sum,
+// then the weighted rows, 64 segments at a time. Returns the lse.
+template <int D>
+__device__ float merge_general(const float* lse_p, const float* o_p, int nseg, int lane,
+                               LaneVec<D / 64>& acc) {
+  constexpr int C = D / 64;
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int s = s0 + lane;
+    float v = s < nseg ? lse_p[s] : -INFINITY;
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    M = fmaxf(M, v);
+  }
+  if (M == -INFINITY) return -INFINITY;
+  float sum = 0.f;
+  for (int s0 = 0; s0 < nseg; s0 += 64) {
+    const int s = s0 + lane;
+    float v = s < nseg ? expf(lse_p[s] - M) : 0.f;
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    sum += v;
+  }
+  const float lse = M + logf(sum);
+  for (int s = 0; s < nseg; ++s) {
+    const float w = expf(lse_p[s] - lse);
+    const LaneVec<C> o = load_lane<C>(o_p + s * D, lane);
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc.v[c] += w * o.v[c];
+  }
+  return lse;
+}
+
+// Wide form: one work-group of kWavesPerBlock waves per (token, q head) row.
+template <bool F16, int D>
+__global__ __launch_bounds__(kReduceThreads) void reduce_wide_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse,
+    const int32_t* __restrict__ tok_nseg, int q_heads, int seg_max,
+    unsigned short* __restrict__ out, float* __restrict__ out_lse) {
+  constexpr int C = D / 64;
+  constexpr int kPer = 64 / kWavesPerBlock;       // segments per wave (16)
+  __shared__ float red[kWavesPerBlock - 1][64 * C];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const long long row = blockIdx.x;
+  const int t = static_cast<int>(row / q_heads);
+  int nseg = tok_nseg[t];
+  nseg = nseg < 0 ? 0 : (nseg > seg_max ? seg_max : nseg);
+  const float* lse_p = part_lse + row * seg_max;
+  const float* o_p = part_o + row * seg_max * D;
+  unsigned short* orow = out + row * D + C * lane;
+  LaneVec<C> acc;
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc.v[c] = 0.f;
+  if (nseg > 64 || nseg == 0) {                   // uniform over the work-group
+    if (w == 0) {
+      const float lse = nseg ? merge_general<D>(lse_p, o_p, nseg, lane, acc) : -INFINITY;
+      store_row<F16, C>(orow, acc);
+      if (out_lse && lane == 0) out_lse[row] = lse;
+    }
+    return;
+  }
+  // lane s holds segment s's lse; wave w preloads rows kPer*w .. kPer*w + kPer-1
+  const float ls = lane < nseg ? lse_p[lane] : -INFINITY;
+  const int s0 = kPer * w;
+  LaneVec<C> pre[kPer];
+  if (s0 < nseg) {                                 // wave-uniform
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
+      pre[k] = load_lane<C>(o_p + kk * D, lane);
+    }
+  }
+  float M = ls;
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  float lse = -INFINITY;
+  if (M != -INFINITY) {                            // uniform over the work-group
+    const float e = lane < nseg ? expf(ls - M) : 0.f;
+    float sum = e;
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+    lse = M + logf(sum);
+    const float wl = e / sum;
+    if (s0 < nseg) {
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const float wk = __shfl(wl, s0 + k);     // 0 past nseg
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
+      }
+    }
+  }
+  if (w > 0) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) red[w - 1][C * lane + c] = acc.v[c];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll
+    for (int j = 0; j < kWavesPerBlock - 1; ++j) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc.v[c] += red[j][C * lane + c];
+    }
+    store_row<F16, C>(orow, acc);
+    if (out_lse && lane == 0) out_lse[row] = lse;
+  }
+}
+
 template <bool F16, int D>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse,
@@ -115,60 +246,51 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
 #pragma unroll
         for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
       }
-      for (int s = kPre; s < nseg; ++s) {
-        const float ws = __shfl(w, s);
-        const LaneVec<C> o = load_lane<C>(o_p + s * D, lane);
+      // the rest in chunks of kPre rows, all loads of a chunk issued together
+      // (s0 + k <= 63: lanes past nseg hold weight 0, rows past it repeat the
+      // last valid one)
+      for (int s0 = kPre; s0 < nseg; s0 += kPre) {
+        LaneVec<C> o[kPre];
 #pragma unroll
-        for (int c = 0; c < C; ++c) acc.v[c] += ws * o.v[c];
+        for (int k = 0; k < kPre; ++k) {
+          const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
+          o[k] = load_lane<C>(o_p + kk * D, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < kPre; ++k) {
+          const float ws = __shfl(w, s0 + k);
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc.v[c] += ws * o[k].v[c];
+        }
       }
     }
   } else if (nseg > 64) {
-    // general path: max, then sum, then weighted rows, 64 segments at a time
-    float M = -INFINITY;
-    for (int s0 = 0; s0 < nseg; s0 += 64) {
-      const int s = s0 + lane;
-      float v = s < nseg ? lse_p[s] : -INFINITY;
-      for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-      M = fmaxf(M, v);
-    }
-    if (M != -INFINITY) {
-      float sum = 0.f;
-      for (int s0 = 0; s0 < nseg; s0 += 64) {
-        const int s = s0 + lane;
-        float v = s < nseg ? expf(lse_p[s] - M) : 0.f;
-        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-        sum += v;
-      }
-      lse = M + logf(sum);
-      for (int s = 0; s < nseg; ++s) {
-        const float w = expf(lse_p[s] - lse);
-        const LaneVec<C> o = load_lane<C>(o_p + s * D, lane);
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc.v[c] += w * o.v[c];
-      }
-    }
+    lse = merge_general<D>(lse_p, o_p, nseg, lane, acc);
   }
-  unsigned short* orow = out + row * D + C * lane;
-  if constexpr (C == 1) {
-    orow[0] = to_out16<F16>(acc.v[0]);
-  } else if constexpr (C == 2) {
-    *reinterpret_cast<unsigned int*>(orow) =
-        static_cast<unsigned int>(to_out16<F16>(acc.v[0])) |
-        (static_cast<unsigned int>(to_out16<F16>(acc.v[1])) << 16);
-  } else {
-    *reinterpret_cast<uint2*>(orow) = make_uint2(
-        static_cast<unsigned int>(to_out16<F16>(acc.v[0])) |
-            (static_cast<unsigned int>(to_out16<F16>(acc.v[1])) << 16),
-        static_cast<unsigned int>(to_out16<F16>(acc.v[2])) |
-            (static_cast<unsigned int>(to_out16<F16>(acc.v[3])) << 16));
-  }
+  store_row<F16, C>(out + row * D + C * lane, acc);
   if (out_lse && lane == 0) out_lse[row] = lse;
 }
+
+// rows up to which the wide form (one work-group per row) is used
+constexpr long long kWideMaxRows = 1024;
 
 template <int D>
 void launch_reduce_d(const float* part_o, const float* part_lse, const int32_t* tok_nseg,
                      int total_q, int q_heads, int seg_max, bool out_f16, void* out,
                      float* out_lse, long long blocks, hipStream_t st) {
+  const long long rows = static_cast<long long>(total_q) * q_heads;
+  if (rows <= kWideMaxRows) {
+    auto o = static_cast<unsigned short*>(out);
+    if (out_f16)
+      hipLaunchKernelGGL((reduce_wide_kernel<true, D>), dim3(static_cast<unsigned>(rows)),
+                         dim3(kReduceThreads), 0, st, part_o, part_lse, tok_nseg, q_heads,
+                         seg_max, o, out_lse);
+    else
+      hipLaunchKernelGGL((reduce_wide_kernel<false, D>), dim3(static_cast<unsigned>(rows)),
+                         dim3(kReduceThreads), 0, st, part_o, part_lse, tok_nseg, q_heads,
+                         seg_max, o, out_lse);
+    return;
+  }
   if (out_f16)
     hipLaunchKernelGGL((reduce_kernel<true, D>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kReduceThreads), 0, st, part_o, part_lse, tok_nseg, total_q,
