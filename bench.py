@@ -77,9 +77,13 @@ def _args(argv=None):
     return ap.parse_args(argv)
 
 
-# the sources the segment-attention kernels are compiled from
-SEGMENT_SOURCES = ("skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip", "skv_attn_valu.hip",
-                   "skv_attn_gd.hip", "skv_attn_common.h", "skv_internal.h")
+# the sources the segment-attention kernels are compiled from: the dispatch and
+# the shared code, and one file per kernel family (by kernel-name prefix)
+SEGMENT_COMMON = ("skv_attn.hip", "skv_attn_common.h", "skv_internal.h")
+SEGMENT_KERNEL_FILES = (("seg_mfma_priv", "skv_attn_mfma_priv.hip"),
+                        ("seg_mfma", "skv_attn_mfma.hip"),
+                        ("seg_valu", "skv_attn_valu.hip"),
+                        ("seg_gd", "skv_attn_gd.hip"))
 
 
 def _code_only(text):
@@ -107,28 +111,40 @@ def _code_only(text):
     return " ".join("".join(out).split())
 
 
-def kernel_source_hash():
-    """Hash of the segment kernels' code (comments and layout ignored)."""
+def kernel_source_hash(kernel=None):
+    """Hash of the code (comments and layout ignored) of the shared segment
+    sources and of the file that defines `kernel` (a kernel name as the
+    profiler prints it), or of every segment source when kernel is None."""
+    files = list(SEGMENT_COMMON)
+    for prefix, f in SEGMENT_KERNEL_FILES:
+        if kernel is None:
+            files.append(f)
+        elif kernel.startswith(prefix):
+            files.append(f)
+            break
     h = hashlib.sha256()
     d = os.path.join(ROOT, "split_kv_paged_amd", "csrc")
-    for f in SEGMENT_SOURCES:
+    for f in files:
         with open(os.path.join(d, f), encoding="utf-8") as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(cfg_name, src_hash):
-    """HBM bytes per segment-kernel launch from the committed rocprofv3 PMC
-    summaries, only if they were taken on the current kernel sources."""
+def traffic_from_profiles(cfg_name):
+    """(HBM bytes per segment-kernel launch, kernel, its source hash) from the
+    committed rocprofv3 PMC summaries; the bytes are None unless they were
+    taken on the current sources of the kernel that produced them."""
     p = os.path.join(ROOT, "profiles", "segment_traffic.json")
     if not os.path.exists(p):
-        return None
+        return None, None, kernel_source_hash()
     with open(p) as f:
         d = json.load(f)
     e = d.get(cfg_name)
-    if not e or e.get("kernel_source_hash") != src_hash:
-        return None
-    return e.get("hbm_bytes_per_launch")
+    if not e:
+        return None, None, kernel_source_hash()
+    h = kernel_source_hash(e["kernel"])
+    return (e.get("hbm_bytes_per_launch") if e.get("kernel_source_hash") == h else None,
+            e["kernel"], h)
 
 
 def _stats(xs):
@@ -508,7 +524,6 @@ def summarize(d, copy_dir=None, out_dir=None):
     copy_dir = copy_dir or os.path.join(os.path.dirname(d), "p_copy")
     tline = _bench_line(os.path.join(d, "trace.json"))
     wl = tline["config"]["workload"].split(":")[0]
-    src_hash = tline["roofline"]["kernel_source_hash"]
     rel = lambda p: os.path.relpath(p, ROOT)
     fmt = dict(d=rel(d), wl=wl, c=rel(copy_dir))
     prof = out_dir or os.path.join(ROOT, "profiles")
@@ -517,6 +532,10 @@ def summarize(d, copy_dir=None, out_dir=None):
         kt = [r for r in csv.DictReader(f) if "skv::" in r["Kernel_Name"]]
     kt.sort(key=lambda r: int(r["Start_Timestamp"]))
     seg = [r for r in kt if "seg_" in _short(r["Kernel_Name"])]
+    seg_kernel = _short(seg[0]["Kernel_Name"]) if seg else None
+    # the sources of the segment kernel that ran, as they are now (the
+    # summary is made right after the profiled run, from the same tree)
+    src_hash = kernel_source_hash(seg_kernel)
     arms = _arm_of_segment_launches(tline)
     if len(arms) != len(seg):
         raise ValueError(f"{len(seg)} segment launches traced, schedule lists {len(arms)}")
@@ -643,8 +662,7 @@ def main(argv=None):
     cfg = configs.BY_NAME[a.config]
     head = time_workload(cfg, a, torch, skv, gen, with_schedule=a.only)
     props = torch.cuda.get_device_properties(0)
-    src_hash = kernel_source_hash()
-    traffic = traffic_from_profiles(cfg.name, src_hash)
+    traffic, traffic_kernel, src_hash = traffic_from_profiles(cfg.name)
     seg_gbs = head["segment_gb_s"]
     line = {
         "metric": "paged decode-attn effective KV TB/s (attention + reduce; us/call and "
@@ -675,7 +693,8 @@ def main(argv=None):
                      "achieved": round(seg_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(seg_gbs / HBM_PEAK_GBS, 4),
                      "algorithmic_bytes_per_launch": head["kv_bytes"],
-                     "traffic": traffic, "kernel_source_hash": src_hash},
+                     "traffic": traffic, "traffic_kernel": traffic_kernel,
+                     "kernel_source_hash": src_hash},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }

@@ -34,6 +34,12 @@
 //    online softmax in the exp2 domain as in the other kernels: masked scores
 //    are -inf, V of tokens past the segment end is zeroed, so page-tail or
 //    stale-LDS poison never reaches the accumulator.
+//  * The softmax keeps the per-token work down (at head dim 64 it, not HBM,
+//    bounds the kernel): the score scale folds into the fma before each
+//    exp2 (a negative fp8 K scale is moved into Q's sign), blocks that every
+//    row of the wave sees in full skip the masks, and the running row max
+//    moves only when a step's scores rise 2^8 above it, so most steps need
+//    no cross-lane max and no rescale.
 #include "skv_attn_common.h"
 #include "skv.h"
 
@@ -44,6 +50,15 @@ typedef short v4i16_gd __attribute__((ext_vector_type(4)));
 typedef int v2i32_gd __attribute__((ext_vector_type(2)));
 
 constexpr int kGdRingBudget = 128 * 1024;
+// the running row max lags the true one by less than this (log2 units):
+// weights stay <= 2^8, which bf16 / fp16 P and the fp32 sums carry exactly
+// enough (no loss of relative precision)
+constexpr float kGdSlackLog2 = 8.f;
+
+// 16-bit 1.0 in both halves of a word (bf16 or fp16): the V^T operand of the
+// extra P.V tile that sums each row's rounded weights
+template <bool F16>
+constexpr uint32_t kOnes2 = F16 ? 0x3c003c00u : 0x3f803f80u;
 constexpr int kGdStageTarget = 32 * 1024;
 
 template <int D, int E>
@@ -187,14 +202,24 @@ void seg_gd_kernel(SegParams p) {
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   float sm_scale = kLog2e * (D == 64 ? 0.125f : 0.0625f);        // log2(e) / sqrt(D)
   float out_scale = 1.f;
+  uint32_t qflip = 0u;
   if constexpr (E == 1) {
-    sm_scale *= p.k_scale[0];
+    // scores enter exp2 as fma(raw, c, -m) with c > 0: a negative K scale
+    // is moved into Q's sign (exact), a zero one becomes the least normal
+    const float ks = p.k_scale[0];
+    sm_scale *= fabsf(ks);
+    qflip = ks < 0.f ? 0x80008000u : 0u;
     out_scale = p.v_scale[0];
   }
+  const float c = fmaxf(sm_scale, 1.17549435e-38f);
+  const float inv_c = 1.f / c;
 
   // ---- Q of this wave's row tile (B operand: row r16, channels 32kk+8j4..+7)
   const int n = 16 * rt + r16;
   const int lim = row_limit(it, n, p.G, p.causal);
+  // every row of the wave sees at least the keys below lim_min (its first
+  // row is the most restricted; padding rows are never written)
+  const int lim_min = row_limit(it, 16 * rt, p.G, p.causal);
   const bool qok = active && n < it.rows;
   bf16x8_t qb[kKS];
   {
@@ -207,7 +232,9 @@ void seg_gd_kernel(SegParams p) {
     // the loads complete here, before any DMA is issued (padding rows: zero)
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
-      if (!qok) qb[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      const uint4 v = __builtin_bit_cast(uint4, qb[kk]);
+      qb[kk] = as_bf16x8(qok ? make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip)
+                             : make_uint4(0, 0, 0, 0));
       asm volatile("" : "+v"(qb[kk]));
     }
   }
@@ -221,7 +248,31 @@ void seg_gd_kernel(SegParams p) {
   f32x4_t oacc[kDT];
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, l = 0.f;
+  // m: running row max (log2 units, -inf before any visible key), the offset
+  // of every exponential; thr: raw scores at or below it keep m. l sums the
+  // fp32 weights (for the lse); lacc, an extra P.V tile whose V is all ones,
+  // sums the 16-bit weights P.V actually applies (every element of the lane's
+  // four holds row r16's sum), and O is normalised by it: the output is then a
+  // convex combination of V rows with the applied weights, so a dominant
+  // key's rounding cancels (under the lazy row max its weight is up to 2^8,
+  // not exactly 1)
+  float m = -INFINITY, l = 0.f, thr = -INFINITY;
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+  auto update_max = [&](float lm) {
+    if (__builtin_amdgcn_ballot_w64(lm > thr) != 0) {     // some row max must move
+      float bm = lm == -INFINITY ? -INFINITY : lm * c;
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float mn = fmaxf(m, bm);
+      const float alpha = fast_exp2(m - (mn == -INFINITY ? 0.f : mn));
+      l *= alpha;
+      lacc *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
+      m = mn;
+      thr = mn == -INFINITY ? -INFINITY : (mn + kGdSlackLog2) * inv_c;
+    }
+  };
 
   for (int i = 0; i < nst; ++i) {
     // stage i landed (own DMA), then everyone's; stage i-1's slot is free
@@ -250,28 +301,22 @@ void seg_gd_kernel(SegParams p) {
         acc = mfma_k32<F16>(kop, qb[kk], acc);
       }
       float s4[4];
-      float bm = -INFINITY;
+      float lm = -INFINITY;
+      const bool masked = tok0 + 16 > lim_min;                    // wave-uniform
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = acc[e] * sm_scale;
-        s4[e] = tok0 + 4 * j4 + e < lim ? v : -INFINITY;
-        bm = fmaxf(bm, s4[e]);
+        s4[e] = acc[e];
+        if (masked) s4[e] = tok0 + 4 * j4 + e < lim ? s4[e] : -INFINITY;
+        lm = fmaxf(lm, s4[e]);
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {
-        const float alpha = fast_exp2(m - mu);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
-        m = mn;
-      }
-      const float p0 = fast_exp2(s4[0] - mu), p1 = fast_exp2(s4[1] - mu);
-      const float p2 = fast_exp2(s4[2] - mu), p3 = fast_exp2(s4[3] - mu);
+      update_max(lm);
+      const float mu = m == -INFINITY ? 0.f : m;
+      const float p0 = fast_exp2(fmaf(s4[0], c, -mu)), p1 = fast_exp2(fmaf(s4[1], c, -mu));
+      const float p2 = fast_exp2(fmaf(s4[2], c, -mu)), p3 = fast_exp2(fmaf(s4[3], c, -mu));
       l += (p0 + p1) + (p2 + p3);
       const i16x4_t pb4 = __builtin_bit_cast(i16x4_t, make_uint2(pack2<F16>(p0, p1), pack2<F16>(p2, p3)));
+      lacc = mfma_k16<F16>(__builtin_bit_cast(i16x4_t, make_uint2(kOnes2<F16>, kOnes2<F16>)), pb4,
+                           lacc);
       // tokens 4j4 .. 4j4+3 of the sub-page; those past the segment end zeroed
       const int vend = it.seg_end - tok0 - 4 * j4;
 #pragma unroll
@@ -350,39 +395,39 @@ void seg_gd_kernel(SegParams p) {
 
       // ---- online softmax (row n; 8 NJ tokens per lane) ----
       float s[NJ][8];
-      float bm = -INFINITY;
+      float lm = -INFINITY;
+      // blocks past the end of this group's last valid block hold tokens
+      // beyond the segment end, which lim (<= the segment end) masks
+      const bool masked = tokb[NJ - 1] + 32 > lim_min;            // wave-uniform
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int pos = tokb[jb] + 16 * (e >> 2) + 4 * j4 + (e & 3);
-          const float v = sacc[jb][e >> 2][e & 3] * sm_scale;
-          s[jb][e] = pos < lim ? v : -INFINITY;
-          bm = fmaxf(bm, s[jb][e]);
+          s[jb][e] = sacc[jb][e >> 2][e & 3];
+          if (masked) {
+            const int pos = tokb[jb] + 16 * (e >> 2) + 4 * j4 + (e & 3);
+            s[jb][e] = pos < lim ? s[jb][e] : -INFINITY;
+          }
+          lm = fmaxf(lm, s[jb][e]);
         }
       }
-      bm = fmaxf(bm, __shfl_xor(bm, 16));
-      bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float mn = fmaxf(m, bm);
-      const float mu = mn == -INFINITY ? 0.f : mn;
-      if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {     // some row max moved
-        const float alpha = fast_exp2(m - mu);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= alpha;
-        m = mn;
-      }
+      update_max(lm);
+      const float mu = m == -INFINITY ? 0.f : m;
       bf16x8_t pb[NJ];
 #pragma unroll
       for (int jb = 0; jb < NJ; ++jb) {
         uint32_t pk[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float a = fast_exp2(s[jb][e] - mu), c = fast_exp2(s[jb][e + 1] - mu);
-          l += a + c;
-          pk[e >> 1] = pack2<F16>(a, c);
+          const float a = fast_exp2(fmaf(s[jb][e], c, -mu));
+          const float b = fast_exp2(fmaf(s[jb][e + 1], c, -mu));
+          pk[e >> 1] = pack2<F16>(a, b);
+          l += a + b;
         }
         pb[jb] = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
+        lacc = mfma_k32<F16>(as_bf16x8(make_uint4(kOnes2<F16>, kOnes2<F16>, kOnes2<F16>,
+                                                  kOnes2<F16>)),
+                             pb[jb], lacc);
       }
 
       // ---- O^T += V^T.P^T; element e: sub-page e/4, token 4j4 + e%4 ----
@@ -457,12 +502,12 @@ void seg_gd_kernel(SegParams p) {
   // ---- row sums across the four lane groups ----
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  float M = m, Ls = l;
+  float M = m, Ls = l, Lr = lacc[0];
   {
     // groups 1 .. G-1 hand their (m, l, O^T) to group 0 through the (now
     // idle) ring; slot k - 1 for group k
     constexpr int kG = R::kGroups;
-    constexpr int kOBytes = (kG - 1) * 4 * kDT * 1024;
+    constexpr int kOBytes = (kG - 1) * 4 * (kDT + 1) * 1024;   // O^T tiles and lacc
     static_assert(kOBytes + 2 * (kG - 1) * 4 * 16 * 4 <= kNS * R::kStageBytes, "merge fits");
     f32x4_t* oslot = reinterpret_cast<f32x4_t*>(ring);
     float(*sm_m)[16] = reinterpret_cast<float(*)[16]>(ring + kOBytes);
@@ -475,7 +520,8 @@ void seg_gd_kernel(SegParams p) {
         sm_l[slot_k][r16] = l;
       }
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) oslot[(slot_k * kDT + dt) * 64 + lane] = oacc[dt];
+      for (int dt = 0; dt < kDT; ++dt) oslot[(slot_k * (kDT + 1) + dt) * 64 + lane] = oacc[dt];
+      oslot[(slot_k * (kDT + 1) + kDT) * 64 + lane] = lacc;
     }
     __syncthreads();
     if (grp > 0 || !active) return;
@@ -485,6 +531,7 @@ void seg_gd_kernel(SegParams p) {
     const float mu = mx == -INFINITY ? 0.f : mx;
     const float f0 = fast_exp2(m - mu);
     Ls = l * f0;
+    Lr = lacc[0] * f0;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= f0;
 #pragma unroll
@@ -492,8 +539,10 @@ void seg_gd_kernel(SegParams p) {
       const int slot_k = (k - 1) * 4 + rt;
       const float f = fast_exp2(sm_m[slot_k][r16] - mu);
       Ls += sm_l[slot_k][r16] * f;
+      Lr += oslot[(slot_k * (kDT + 1) + kDT) * 64 + lane][0] * f;
 #pragma unroll
-      for (int dt = 0; dt < kDT; ++dt) oacc[dt] += oslot[(slot_k * kDT + dt) * 64 + lane] * f;
+      for (int dt = 0; dt < kDT; ++dt)
+        oacc[dt] += oslot[(slot_k * (kDT + 1) + dt) * 64 + lane] * f;
     }
     M = mu;
   }
@@ -504,7 +553,7 @@ void seg_gd_kernel(SegParams p) {
   const int h = it.g * p.G + n % p.G;
   const size_t prow = (static_cast<size_t>(t) * p.Hq + h) * p.seg_max + it.seg;
   const bool any = Ls > 0.f;
-  const float inv = any ? out_scale / Ls : 0.f;
+  const float inv = any ? out_scale / Lr : 0.f;
   float* po = p.part_o + prow * D;
 #pragma unroll
   for (int dt = 0; dt < kDT; ++dt)
