@@ -48,6 +48,10 @@ SAMPLES = {
     "uniform_verify_fp16": [0, 15],
     "uniform_verify_d64": [0, 15],
     "uniform_verify_d256": [0, 15],
+    "agentic_verify_fp8": [0, 1, 3, 4, 19],
+    "agentic16_verify_fp8": [0, 3, 9, 15],
+    "bs1_110k_fp8": [0],
+    "bs1_248k": [0],
 }
 
 
@@ -183,13 +187,14 @@ def test_full_size_convert_round_trip():
     assert torch.equal(kp, k0) and torch.equal(vp, v0)
 
 
-@pytest.mark.parametrize("name", ["agentic_skew", "fp8_kv"], ids=str)
+@pytest.mark.parametrize("name", ["agentic_skew", "fp8_kv", "bs1_110k_fp8", "bs1_248k"], ids=str)
 def test_full_size_fixed_split(name):
     """The fixed split (no plan) on a full-size skewed batch: per-token counts
     bit-exact, sampled rows against the oracle, and every output within the
     split-KV PR's planned-vs-fixed bound (Accuracy Tests: the two splits
     differ only by the fp32 summation order across segment boundaries, by at
-    most 0.007) of the planned split's."""
+    most 0.007; plus one bf16 rounding step of outputs near or above 1) of
+    the planned split's."""
     cfg = configs.BY_NAME[name]
     say("fullsize fixed", name, "generating")
     case = gen.make_case(cfg, DEV)
@@ -197,9 +202,9 @@ def test_full_size_fixed_split(name):
     hip.pop("planes")
     planned = run_hip(case)
     planned.pop("planes")
-    diff = float(np.abs(hip["out"] - planned["out"]).max())
-    say("fullsize fixed", name, "planned vs fixed max abs", diff)
-    assert diff <= 0.007
+    diff = np.abs(hip["out"] - planned["out"])
+    say("fullsize fixed", name, "planned vs fixed max abs", float(diff.max()))
+    assert np.all(diff <= 0.007 + 2.0 ** -7 * np.abs(planned["out"]))
     _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
                                              cfg.kv_heads, 16, cfg.num_cus, cfg.seg_max,
                                              cfg.causal)

@@ -333,9 +333,11 @@ def test_fixed_split_matches_oracle(spec):
     cfg = case.cfg
     hip = run_hip(case, fixed=True)
     planned = run_hip(case)
-    diff = float(np.abs(hip["out"] - planned["out"]).max())
-    say(spec[0], "planned vs fixed max abs", diff)
-    assert diff <= 0.007
+    diff = np.abs(hip["out"] - planned["out"])
+    say(spec[0], "planned vs fixed max abs", float(diff.max()))
+    # the PR's 0.007, plus one bf16 rounding step of the value (outputs near
+    # or above 1 can round one unit apart: 2^-7 at [1, 2))
+    assert np.all(diff <= 0.007 + 2.0 ** -7 * np.abs(planned["out"]))
     _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
                                              cfg.kv_heads, 16, cfg.num_cus, cfg.seg_max,
                                              cfg.causal)

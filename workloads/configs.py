@@ -17,6 +17,10 @@ SKEW_LENS = [0, 1, 5, 17, 247999, 14719, 247999, 107452, 120562, 152813, 25149,
              150337, 79806, 247999, 237602, 133244, 143097, 97199, 66000, 248000]
 SKEW_Q = [4, 4, 4, 2, 2, 3, 3, 3, 4, 2, 4, 1, 1, 4, 4, 2, 1, 2, 1, 4]
 
+# written by make_lengths.skew16_lengths(): bs=16, sum 1,850,000
+SKEW16_LENS = [0, 1, 5, 17, 28268, 46342, 175306, 70001, 199979, 247999, 27912, 247999, 65166,
+               247999, 245006, 248000]
+
 # written by make_lengths.fp8_lengths(): bs=64, median 8140, max 131072
 FP8_LENS = [3673, 6607, 63486, 18438, 1087, 8140, 3803, 9836, 1132, 11031, 10945,
             56962, 12096, 15356, 1304, 131072, 775, 31792, 5458, 2771, 3653, 3583,
@@ -108,8 +112,17 @@ UNIFORM_VERIFY_D64 = Config("uniform_verify_d64", [119_000] * 16, [4] * 16, 32, 
 UNIFORM_VERIFY_D256 = Config("uniform_verify_d256", [119_000] * 16, [4] * 16, 32, 2,
                              head_dim=256, seed=10,
                              note="bs=16 x 119k, q=4, 32/2 heads (GQA 16), head dim 256, bf16")
-EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64,
-         UNIFORM_VERIFY_D256]
+# The PR's two verify rows on agentic length distributions (4 query tokens per
+# sequence, e4m3fn KV): bs 20 / 2.32M tokens (the skew lengths above) and
+# bs 16 / 1.85M tokens
+AGENTIC_VERIFY_FP8 = Config("agentic_verify_fp8", SKEW_LENS, [4] * 20, 32, 2, kv_dtype="fp8",
+                            k_scale=0.0173, v_scale=0.0211, seed=16,
+                            note="bs=20, 2.32M tokens, q=4, 32/2 heads, e4m3fn KV")
+AGENTIC16_VERIFY_FP8 = Config("agentic16_verify_fp8", SKEW16_LENS, [4] * 16, 32, 2,
+                              kv_dtype="fp8", k_scale=0.0173, v_scale=0.0211, seed=17,
+                              note="bs=16, 1.85M tokens, q=4, 32/2 heads, e4m3fn KV")
+EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, AGENTIC_VERIFY_FP8, AGENTIC16_VERIFY_FP8,
+         UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64, UNIFORM_VERIFY_D256]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 # The split-KV PR's single-sequence rows (Benchmarking and Profiling: "bs1

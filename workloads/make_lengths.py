@@ -58,7 +58,17 @@ def fp8_lengths(seed=4, bs=64, median=8192, max_len=131072):
     return [int(v) for v in lens], [int(v) for v in q]
 
 
+def skew16_lengths():
+    """bs=16, 1.85M tokens: the same recipe with 11 lognormal draws (the PR's
+    "verify bs16, agentic length distribution, 1.85M tokens" row)."""
+    lens, _ = skew_lengths(seed=15, total=1_850_000, n_draw=11)
+    return lens
+
+
 if __name__ == "__main__":
+    l16 = skew16_lengths()
+    print("SKEW16_LENS =", l16)
+    print("sum", sum(l16))
     l3, q3 = skew_lengths()
     print("SKEW_LENS =", l3)
     print("SKEW_Q =", q3)
