@@ -399,6 +399,33 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
     return res
 
 
+def _device_clocks():
+    """Peak engine and memory clocks (MHz) as the HIP runtime reports them."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+    except OSError:
+        return {}
+    out = {}
+    # hipDeviceAttributeClockRate = 5, hipDeviceAttributeMemoryClockRate = 60 (kHz)
+    for name, attr in (("engine_clock_mhz", 5), ("memory_clock_mhz", 60)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) == 0:
+            out[name] = v.value // 1000
+    return out
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def _fixed_segments(cfg):
     """Segments per sequence of the fixed split: max(1, min(seg_max,
     pow2floor(num_cus / (bs * kv_heads))))."""
@@ -442,8 +469,7 @@ def cpu_baseline(cfg, min_seconds, gen, np):
             "sample": f"{cfg.name}: all query rows of {done} sequences taken in order "
                       f"(first {n_gen} of the batch, wrapping), {kv_bytes} KV bytes, "
                       f"numpy fp64 oracle",
-            "host": platform.processor() or platform.machine(),
-            "host_cpus": os.cpu_count()}
+            "host": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def _round(x):
@@ -696,7 +722,7 @@ def main(argv=None):
                      "traffic": traffic, "traffic_kernel": traffic_kernel,
                      "kernel_source_hash": src_hash},
         "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
+                   "arch": getattr(props, "gcnArchName", ""), **_device_clocks()},
     }
     if "segment_launch_schedule" in head:
         line["segment_launch_schedule"] = head["segment_launch_schedule"]

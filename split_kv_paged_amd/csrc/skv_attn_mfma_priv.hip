@@ -38,6 +38,8 @@
 //  * The first block is issued before Q is loaded, so the two latencies
 //    overlap. At the end the waves' (max, sum, O) are merged through LDS,
 //    wave w merging channel tile w of every row tile.
+#include <type_traits>
+
 #include "skv_attn_common.h"
 #include "skv.h"
 
@@ -347,17 +349,20 @@ void seg_mfma_priv_kernel(SegParams p) {
   // byte i%8 of the 8 bytes read by lane 2k + i/8, i.e. 8 tokens of one channel
   const int vtau = 4 * j4 + ((r16 >> 1) & 3);
 
-  for (int k = 0; cur < nblk; ++k) {
+  // the loop runs two steps per turn, one per ring slot, so each slot's LDS
+  // offsets are compile-time constants (folded into the reads' offsets)
+  auto step = [&](auto slot_index) __attribute__((always_inline)) {
+    constexpr int SI = decltype(slot_index)::value;
     const int nxt = next_unit<NW>(p, cur, &next_blk, lane);
     if (nxt < nblk) {                           // into the slot consumed last iteration
       int a, sa, b, sb;
       pids(nxt, a, sa, b, sb);
-      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + ((k + 1) & 1) * kBlockBytes, lane);
+      issue_block<SHUF, PSH>(p, it, a, sa, b, sb, wring + (SI ^ 1) * kBlockBytes, lane);
       pwait_vmcnt<kBlockInstr>();               // block cur landed
     } else {
       pwait_vmcnt<0>();
     }
-    const uint8_t* slot = wring + (k & 1) * kBlockBytes;
+    const uint8_t* slot = wring + SI * kBlockBytes;
     const uint8_t* kU[2] = {slot, slot + 2 * kUnitBytes};
     const uint8_t* vU[2] = {slot + kUnitBytes, slot + 3 * kUnitBytes};
     const int tok0 = it.seg_start + 32 * cur;
@@ -506,6 +511,11 @@ void seg_mfma_priv_kernel(SegParams p) {
         oacc[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vop, pb[t], oacc[t][dt], 0, 0, 0);
     }
     cur = nxt;
+  };
+  while (cur < nblk) {
+    step(std::integral_constant<int, 0>{});
+    if (cur >= nblk) break;
+    step(std::integral_constant<int, 1>{});
   }
 
   // ---- merge the waves' partial states; write the segment partial ----
