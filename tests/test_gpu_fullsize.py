@@ -51,6 +51,8 @@ SAMPLES = {
     "agentic_verify_fp8": [0, 1, 3, 4, 19],
     "agentic16_verify_fp8": [0, 3, 9, 15],
     "bs1_110k_fp8": [0],
+    "bs1_248k_fp8": [0],
+    "bs1_110k": [0],
     "bs1_248k": [0],
 }
 
