@@ -40,6 +40,8 @@
 //    row of the wave sees in full skip the masks, and the running row max
 //    moves only when a step's scores rise 2^8 above it, so most steps need
 //    no cross-lane max and no rescale.
+#include <type_traits>
+
 #include "skv_attn_common.h"
 #include "skv.h"
 
@@ -260,6 +262,7 @@ void seg_gd_kernel(SegParams p) {
   f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
   auto update_max = [&](float lm) {
     if (__builtin_amdgcn_ballot_w64(lm > thr) != 0) {     // some row max must move
+      asm volatile("");                   // a branch, not a select: most steps skip it
       float bm = lm == -INFINITY ? -INFINITY : lm * c;
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
@@ -404,12 +407,23 @@ void seg_gd_kernel(SegParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           s[jb][e] = sacc[jb][e >> 2][e & 3];
-          if (masked) {
+        }
+      }
+      if (masked) {
+        asm volatile("");                 // a branch, not a select: most steps skip it
+#pragma unroll
+        for (int jb = 0; jb < NJ; ++jb) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
             const int pos = tokb[jb] + 16 * (e >> 2) + 4 * j4 + (e & 3);
             s[jb][e] = pos < lim ? s[jb][e] : -INFINITY;
           }
-          lm = fmaxf(lm, s[jb][e]);
         }
+      }
+#pragma unroll
+      for (int jb = 0; jb < NJ; ++jb) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lm = fmaxf(lm, s[jb][e]);
       }
       update_max(lm);
       const float mu = m == -INFINITY ? 0.f : m;
@@ -430,7 +444,11 @@ void seg_gd_kernel(SegParams p) {
                              pb[jb], lacc);
       }
 
-      // ---- O^T += V^T.P^T; element e: sub-page e/4, token 4j4 + e%4 ----
+      // ---- O^T += V^T.P^T; element e: sub-page e/4, token 4j4 + e%4. The
+      // V-tail zeroing is compiled into a second copy of the loop, taken only
+      // by the step that holds tokens past the segment end ----
+      auto pv = [&](auto tail_tag) __attribute__((always_inline)) {
+        constexpr bool kTail = decltype(tail_tag)::value;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
         const int d = 16 * dt + r16;
@@ -485,7 +503,7 @@ void seg_gd_kernel(SegParams p) {
             w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
           }
           const int vend = it.seg_end - tokb[jb];
-          if (vend < 32) {               // zero V of tokens past the segment end
+          if (kTail && vend < 32) {      // zero V of tokens past the segment end
 #pragma unroll
             for (int q2 = 0; q2 < 4; ++q2) {
               const int rel = vend - (16 * (q2 >> 1) + 4 * j4 + 2 * (q2 & 1));
@@ -494,6 +512,13 @@ void seg_gd_kernel(SegParams p) {
           }
           oacc[dt] = mfma_k32<F16>(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb[jb], oacc[dt]);
         }
+      }
+      };
+      if (tokb[NJ - 1] + 32 > it.seg_end) {                       // wave-uniform
+        asm volatile("");
+        pv(std::true_type{});
+      } else {
+        pv(std::false_type{});
       }
     }
   }
