@@ -36,6 +36,8 @@
 //    LDS or page-tail poison (even NaN) never reaches the accumulator.
 //  * fp8 e4m3fn KV is widened to bf16 exactly before the MFMA; k_scale folds
 //    into the score scale and v_scale into the output.
+#include <type_traits>
+
 #include "skv_attn_common.h"
 #include "skv.h"
 
@@ -207,12 +209,10 @@ void seg_mfma_kernel(SegParams p) {
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
-  float sm_scale = kScoreScaleLog2;
-  float out_scale = 1.f;
-  if constexpr (E == 1) {
-    sm_scale *= p.k_scale[0];
-    out_scale = p.v_scale[0];
-  }
+  // scores enter exp2 as fma(raw, c, -m); c > 0 (16-bit KV has no scale)
+  static_assert(E == 2, "the shared-ring kernel runs 16-bit KV");
+  constexpr float c = kScoreScaleLog2;
+  constexpr float out_scale = 1.f;
 
   // page ids and sub-pages of this wave's units for a stage (sub-pages past
   // the end -> the segment's first)
@@ -242,6 +242,9 @@ void seg_mfma_kernel(SegParams p) {
   uint8_t* qstage = ring + (kNS - 1) * R::kStageBytes + wave * 4096;
   const int n = 16 * rt + r16;
   const int lim = row_limit(it, n, p.G, p.causal);
+  // every row of the wave's tile sees at least the keys below lim_min (its
+  // first row is the most restricted; padding rows are never written)
+  const int lim_min = row_limit(it, 16 * rt, p.G, p.causal);
   const bool qok = active && n < it.rows;
   {
     const int t = it.c0 + (qok ? n / p.G : 0);
@@ -339,20 +342,30 @@ void seg_mfma_kernel(SegParams p) {
     }
 
     // ---- online softmax (row n = 16*rt + r16; 8 tokens per lane) ----
+    // raw scores; the scale folds into the fma before exp2. The masks and
+    // the rescale are wave-uniform branches (kept as branches, not selects:
+    // most blocks take neither)
     float s[8];
-    float bm = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
-      const float v = sacc[e >> 2][e & 3] * sm_scale;
-      s[e] = pos < lim ? v : -INFINITY;
-      bm = fmaxf(bm, s[e]);
+    for (int e = 0; e < 8; ++e) s[e] = sacc[e >> 2][e & 3];
+    if (tok0 + 32 > lim_min) {                     // some row does not see the whole block
+      asm volatile("");
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
+        s[e] = pos < lim ? s[e] : -INFINITY;
+      }
     }
+    float bm = s[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) bm = fmaxf(bm, s[e]);
+    bm = bm == -INFINITY ? -INFINITY : bm * c;
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
     const float mn = fmaxf(m, bm);
     const float mu = mn == -INFINITY ? 0.f : mn;
     if (__builtin_amdgcn_ballot_w64(mn != m) != 0) {     // some row max moved
+      asm volatile("");
       const float alpha = fast_exp2(m - mu);
       l *= alpha;
 #pragma unroll
@@ -362,18 +375,21 @@ void seg_mfma_kernel(SegParams p) {
     uint32_t pk[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float a = fast_exp2(s[e] - mu), b = fast_exp2(s[e + 1] - mu);
+      const float a = fast_exp2(fmaf(s[e], c, -mu)), b = fast_exp2(fmaf(s[e + 1], c, -mu));
       l += a + b;
       pk[e >> 1] = pack2<F16>(a, b);
     }
     const bf16x8_t pb = as_bf16x8(make_uint4(pk[0], pk[1], pk[2], pk[3]));
 
     // ---- O^T += V^T.P^T ; element e: page e/4, token 4*j4 + e%4 ----
-    const bool tail = tok0 + 32 > it.seg_end;
     const int vend = it.seg_end - tok0;       // tokens of the block before the end
     // per-lane part of the transposing-read address in the chunk-major V tile
     const int vtr_off = (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;   // fp8 tile
     const uint8_t* vU8 = vU[r16 >> 3];        // fp8: lanes 0-7 of a group read page 0
+    // the V-tail zeroing is compiled into a second copy of the loop, taken
+    // only by the block that crosses the segment end
+    auto pv = [&](auto tail_tag) __attribute__((always_inline)) {
+      constexpr bool tail = decltype(tail_tag)::value;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + r16;
@@ -428,6 +444,13 @@ void seg_mfma_kernel(SegParams p) {
         }
       }
       oacc[dt] = mfma_k32<F16>(as_bf16x8(make_uint4(w[0], w[1], w[2], w[3])), pb, oacc[dt]);
+    }
+    };
+    if (tok0 + 32 > it.seg_end) {                   // wave-uniform
+      asm volatile("");
+      pv(std::true_type{});
+    } else {
+      pv(std::false_type{});
     }
   }
 
