@@ -593,7 +593,10 @@ void seg_mfma_priv2_kernel(SegParams p) {
   const __attribute__((address_space(4))) int32_t* ptab =
       (const __attribute__((address_space(4))) int32_t*)(
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
-  const float sm_scale = kScoreScaleLog2;
+  // scores enter exp2 as fma(raw, c, -m); c > 0 (16-bit KV has no scale)
+  constexpr float c = kScoreScaleLog2;
+  // every row sees at least the keys below lim_min (row 0 is the most restricted)
+  const int lim_min = row_limit(it, 0, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
   // this wave's k-th sub-page is the segment's sub-page wave + NW k
@@ -662,6 +665,10 @@ void seg_mfma_priv2_kernel(SegParams p) {
           SHUF ? sK + kk * 1024 + lane * 16
                : sK + r16 * kStdRow2 + std2_chunk_pos(r16, 4 * kk + j4) * 16));
     v4i16_t pb[NRT];
+    // wave-uniform: does any key of this page lie past some row's limit?
+    // (masks, rescale and V-tail zeroing stay branches, not selects: most
+    // pages take none of them)
+    const bool masked = tok0 + 16 > lim_min;
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -670,33 +677,37 @@ void seg_mfma_priv2_kernel(SegParams p) {
         acc = mfma_k32<F16>(kop[kk], qb[t][kk], acc);
       // online softmax: this lane holds tokens 4*j4 .. +3 of row 16t + r16
       float s[4];
-      float bm = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float v = acc[e] * sm_scale;
-        s[e] = tok0 + 4 * j4 + e < lim[t] ? v : -INFINITY;
-        bm = fmaxf(bm, s[e]);
+      for (int e = 0; e < 4; ++e) s[e] = acc[e];
+      if (masked) {
+        asm volatile("");
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = tok0 + 4 * j4 + e < lim[t] ? s[e] : -INFINITY;
       }
+      float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+      bm = bm == -INFINITY ? -INFINITY : bm * c;
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
       const float mn = fmaxf(m[t], bm);
       const float mu = mn == -INFINITY ? 0.f : mn;
       if (__builtin_amdgcn_ballot_w64(mn != m[t]) != 0) {  // some row max moved
+        asm volatile("");
         const float alpha = fast_exp2(m[t] - mu);
         l[t] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) oacc[t][dt] *= alpha;
         m[t] = mn;
       }
-      const float a0 = fast_exp2(s[0] - mu), a1 = fast_exp2(s[1] - mu);
-      const float a2 = fast_exp2(s[2] - mu), a3 = fast_exp2(s[3] - mu);
+      const float a0 = fast_exp2(fmaf(s[0], c, -mu)), a1 = fast_exp2(fmaf(s[1], c, -mu));
+      const float a2 = fast_exp2(fmaf(s[2], c, -mu)), a3 = fast_exp2(fmaf(s[3], c, -mu));
       l[t] += (a0 + a1) + (a2 + a3);
       pb[t] = __builtin_bit_cast(v4i16_t, make_uint2(pack2<F16>(a0, a1), pack2<F16>(a2, a3)));
     }
 
     // ---- O^T += V^T.P^T over the page's 16 tokens ----
     const int vend = it.seg_end - tok0;          // tokens of the page before the end
-    const bool tail = vend < 16;
+    auto pv = [&](auto tail_tag) __attribute__((always_inline)) {
+      constexpr bool tail = decltype(tail_tag)::value;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
       uint2 w;
@@ -721,6 +732,13 @@ void seg_mfma_priv2_kernel(SegParams p) {
 #pragma unroll
       for (int t = 0; t < NRT; ++t)
         oacc[t][dt] = mfma_k16<F16>(vop, pb[t], oacc[t][dt]);
+    }
+    };
+    if (vend < 16) {                              // wave-uniform
+      asm volatile("");
+      pv(std::true_type{});
+    } else {
+      pv(std::false_type{});
     }
   }
 

@@ -50,6 +50,7 @@ SAMPLES = {
     "uniform_verify_d256": [0, 15],
     "agentic_verify_fp8": [0, 1, 3, 4, 19],
     "agentic16_verify_fp8": [0, 3, 9, 15],
+    "skew_gqa8": [0, 3, 4, 9, 15],
     "bs1_110k_fp8": [0],
     "bs1_248k_fp8": [0],
     "bs1_110k": [0],

@@ -121,8 +121,15 @@ AGENTIC_VERIFY_FP8 = Config("agentic_verify_fp8", SKEW_LENS, [4] * 20, 32, 2, kv
 AGENTIC16_VERIFY_FP8 = Config("agentic16_verify_fp8", SKEW16_LENS, [4] * 16, 32, 2,
                               kv_dtype="fp8", k_scale=0.0173, v_scale=0.0211, seed=17,
                               note="bs=16, 1.85M tokens, q=4, 32/2 heads, e4m3fn KV")
+# a grouped-query shape with fewer query heads per KV head (32/4 heads, GQA 8:
+# 8-32 rows per work item, the 16-bit private-ring kernel) on the bs-16 agentic
+# lengths with ragged 1..4 query tokens, bf16. (With 4 KV heads the plan's
+# budget is 256 / 4 = 64 segments, so a batch of 64 or more sequences could
+# not be split at all.)
+SKEW_GQA8 = Config("skew_gqa8", SKEW16_LENS, SKEW_Q[:16], 32, 4, seed=18,
+                   note="bs=16, 1.85M tokens, q 1..4, 32/4 heads (GQA 8), bf16")
 EXTRA = [UNIFORM_VERIFY_FP8, AGENTIC_SKEW_FP8, AGENTIC_VERIFY_FP8, AGENTIC16_VERIFY_FP8,
-         UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64, UNIFORM_VERIFY_D256]
+         UNIFORM_VERIFY_FP16, UNIFORM_VERIFY_D64, UNIFORM_VERIFY_D256, SKEW_GQA8]
 BY_NAME = {c.name: c for c in CONFIGS + EXTRA}
 
 # The split-KV PR's single-sequence rows (Benchmarking and Profiling: "bs1
