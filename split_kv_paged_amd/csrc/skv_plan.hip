@@ -10,14 +10,18 @@
 // MI355X design: one 1024-thread work-group; integer math only. Feasibility is
 // monotone in T (every per-sequence count ceil(n/T) is non-increasing), so the
 // smallest feasible T is found by search between exact bounds (below):
-//  * small batches (bs <= 32): a 1024-ary search — each thread tests one
-//    candidate T against all page counts (cached in LDS), the smallest
-//    feasible candidate bounds the next pass (a few passes for any length);
-//  * large batches: a binary search whose feasibility test is a block-wide
+//  * up to 4096 sequences (page counts cached in LDS): a 16-ary search, each
+//    of the 16 waves testing one candidate T per pass with a wave-level
+//    reduction over the batch, so a pass costs one barrier and the search
+//    interval shrinks 17-fold per pass;
+//  * larger batches: a binary search whose feasibility test is a block-wide
 //    reduction over the sequences.
-// The work list is written after a block-wide exclusive scan (wave scans
-// plus one pass over the wave totals). The launch shape never depends on
-// device data, so the launch is graph-capture safe.
+// Up to 1024 sequences every thread keeps its sequence's length, page count
+// and query range in registers from the first load on, so the batch is read
+// from memory once. The work list is written after a block-wide exclusive scan
+// (wave scans plus one pass over the wave totals); the per-token counts use
+// ceil(v / (T 2^s)) = ceil(ceil(v / 2^s) / T) in 32-bit integers. The launch
+// shape never depends on device data, so the launch is graph-capture safe.
 #include <hip/hip_runtime.h>
 
 #include "skv.h"
@@ -28,7 +32,7 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kWaves = kPlanThreads / 64;
-constexpr int kSmallBs = 32;         // candidate search up to this batch size
+constexpr int kLdsBs = 4096;         // page counts cached in LDS up to this batch size
 
 __device__ __forceinline__ int pages_of(int L, int sh) {
   // ceil(L / 2^sh) (pages of 16 or 32 tokens) without forming L + 2^sh - 1
@@ -89,29 +93,48 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   __shared__ long long red_s[kWaves];
   __shared__ int red_m[kWaves];
   __shared__ int wave_tot[kWaves];
-  __shared__ int pages_lds[kSmallBs];
-  __shared__ int pass_best;
+  __shared__ int pages_lds[kLdsBs];
+  __shared__ int feas[kWaves];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int cap = num_cus / kv_heads;
   const int width = cap > bs ? cap : bs;
+  const bool one_per_thread = bs <= kPlanThreads;   // thread tid owns sequence tid
 
-  // longest sequence, total pages and non-empty sequences
+  // longest sequence, total pages and non-empty sequences (every load of the
+  // batch issued here; the owned sequence's values stay in registers)
+  int my_len = 0, my_pages = 0, my_c0 = 0, my_c1 = 0;
+  if (one_per_thread && tid < bs) {
+    my_len = seq_lens[tid];
+    my_c0 = cu_q[tid];
+    my_c1 = cu_q[tid + 1];
+  }
   long long tot = 0;
   int mx = 0, nonempty = 0;
-  for (int i = tid; i < bs; i += kPlanThreads) {
-    const int n = pages_of(seq_lens[i], page_shift);
-    if (bs <= kSmallBs) pages_lds[i] = n;
-    mx = max(mx, n);
-    tot += n;
-    nonempty += n > 0;
+  if (one_per_thread) {
+    my_pages = pages_of(my_len, page_shift);
+    if (tid < bs) pages_lds[tid] = my_pages;
+    tot = my_pages;
+    mx = my_pages;
+    nonempty = my_pages > 0;
+  } else {
+    for (int i = tid; i < bs; i += kPlanThreads) {
+      const int n = pages_of(seq_lens[i], page_shift);
+      if (bs <= kLdsBs) pages_lds[i] = n;
+      mx = max(mx, n);
+      tot += n;
+      nonempty += n > 0;
+    }
   }
-  block_sum_max(tot, mx, red_s, red_m);         // also publishes pages_lds
+  // the non-empty count travels in the high bits of the sum (tot < 2^47:
+  // at most 2^15 sequences of fewer than 2^31 / 16 pages each)
+  static_assert(kMaxBs < (1 << 15), "page total and count share one int64");
   {
-    long long ne = nonempty;
-    int unused = 0;
-    block_sum_max(ne, unused, red_s, red_m);
-    nonempty = static_cast<int>(ne);
+    long long packed = tot + (static_cast<long long>(nonempty) << 47);
+    block_sum_max(packed, mx, red_s, red_m);   // also publishes pages_lds
+    tot = packed & ((1ll << 47) - 1);
+    nonempty = static_cast<int>(packed >> 47);
   }
   const int upper = mx > 1 ? mx : 1;
 
@@ -137,39 +160,43 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
     }
     if (lo0 > hi0) lo0 = hi0;                   // cannot happen; keeps the search sane
     int lo = static_cast<int>(lo0), hi = static_cast<int>(hi0);   // hi feasible, lo-1 not
-    if (bs <= kSmallBs) {
-      // 1024-ary search: each thread tests one candidate against all page counts
-      auto feasible_local = [&](int t) {
-        long long sum = 0;
-        int m = 0;
-        for (int i = 0; i < bs; ++i) {
-          const int c = ceil_div_pos(pages_lds[i], t);
-          sum += c;
-          m = max(m, c);
+    if (bs <= kLdsBs) {
+      // 16-ary search: wave w tests candidate lo + w * step of [lo, hi)
+      while (lo < hi) {
+        const int step = (hi - lo + kWaves - 1) / kWaves;
+        const int cand = lo + wave * step;      // wave-uniform
+        if (cand < hi) {
+          long long sum = 0;
+          int m = 0;
+          for (int i = lane; i < bs; i += 64) {
+            const int c = ceil_div_pos(pages_lds[i], cand);
+            sum += c;
+            m = max(m, c);
+          }
+          for (int off = 32; off > 0; off >>= 1) {
+            sum += __shfl_xor(sum, off);
+            m = max(m, __shfl_xor(m, off));
+          }
+          if (lane == 0) feas[wave] = sum <= cap && m <= seg_max;
         }
-        return sum <= cap && m <= seg_max;
-      };
-      while (true) {
-        if (lo >= hi) { T = hi; break; }
-        const long long span = static_cast<long long>(hi) - lo + 1;
-        const int step = static_cast<int>((span + kPlanThreads - 1) / kPlanThreads);
-        const long long cand = static_cast<long long>(lo) + static_cast<long long>(tid) * step;
-        if (tid == 0) pass_best = 0x7fffffff;
         __syncthreads();
-        if (cand <= hi && feasible_local(static_cast<int>(cand))) atomicMin(&pass_best, tid);
-        __syncthreads();
-        const int best = pass_best;
-        __syncthreads();
-        if (best == 0x7fffffff) {     // answer lies after the last candidate tested
-          const int kmax = min(kPlanThreads - 1, static_cast<int>((hi - lo) / step));
-          lo = lo + kmax * step + 1;
-          continue;
+        // candidates ascend with w and feasibility is monotone: the first
+        // feasible one bounds the answer from above, the one before it below
+        int first = kWaves, last_tested = -1;
+        for (int w = 0; w < kWaves; ++w) {
+          if (lo + w * step >= hi) break;
+          last_tested = w;
+          if (first == kWaves && feas[w]) first = w;
         }
-        const int tb = lo + best * step;
-        if (best == 0 || step == 1) { T = tb; break; }
-        lo = lo + (best - 1) * step + 1;
-        hi = tb;
+        __syncthreads();                        // feas is rewritten next pass
+        if (first < kWaves) {
+          hi = lo + first * step;
+          if (first > 0) lo = lo + (first - 1) * step + 1;
+        } else {
+          lo = lo + last_tested * step + 1;
+        }
       }
+      T = hi;
     } else {
       auto feasible = [&](int t) {
         long long sum = 0;
@@ -194,30 +221,40 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(
   const int chunk = (bs + kPlanThreads - 1) / kPlanThreads;
   const int i0 = min(bs, tid * chunk), i1 = min(bs, i0 + chunk);
   int local = 0;
-  for (int i = i0; i < i1; ++i) local += ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
+  if (one_per_thread)
+    local = ceil_div_pos(my_pages, T);
+  else
+    for (int i = i0; i < i1; ++i) local += ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
   int total;
   int pos = block_exclusive_scan(local, wave_tot, total);
-  for (int i = i0; i < i1; ++i) {
-    const int ns = ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
-    for (int s = 0; s < ns; ++s) plan[1 + pos + s] = (i << 16) | s;
-    pos += ns;
+  if (one_per_thread) {
+    for (int s = 0; s < local; ++s) plan[1 + pos + s] = (tid << 16) | s;
+  } else {
+    for (int i = i0; i < i1; ++i) {
+      const int ns = ceil_div_pos(pages_of(seq_lens[i], page_shift), T);
+      for (int s = 0; s < ns; ++s) plan[1 + pos + s] = (i << 16) | s;
+      pos += ns;
+    }
   }
   for (int k = total + tid; k < width; k += kPlanThreads) plan[1 + k] = -1;
   if (tid == 0) plan[0] = T;
 
-  // per-token segment counts: ceil(visible / (T * page_size)), in 64-bit
-  const long long seg_tokens = static_cast<long long>(T) << page_shift;
-  for (int i = tid; i < bs; i += kPlanThreads) {
-    const int L = seq_lens[i];
-    const int c0 = cu_q[i], qn = cu_q[i + 1] - c0;
+  // per-token segment counts: ceil(visible / (T * page_size)), as the
+  // visible page count over T
+  auto token_counts = [&](int L, int c0, int qn) {
     for (int j = 0; j < qn; ++j) {
       long long vis = L;
       if (causal) {
         vis = static_cast<long long>(L) - qn + j + 1;
         vis = vis < 0 ? 0 : (vis > L ? L : vis);
       }
-      tok_nseg[c0 + j] = vis <= 0 ? 0 : static_cast<int>(1 + (vis - 1) / seg_tokens);
+      tok_nseg[c0 + j] = ceil_div_pos(pages_of(static_cast<int>(vis), page_shift), T);
     }
+  };
+  if (one_per_thread) {
+    if (tid < bs) token_counts(my_len, my_c0, my_c1 - my_c0);
+  } else {
+    for (int i = tid; i < bs; i += kPlanThreads) token_counts(seq_lens[i], cu_q[i], cu_q[i + 1] - cu_q[i]);
   }
 }
 

@@ -76,6 +76,36 @@ def test_plan_large_batch():
     assert plan.cpu().tolist() == wp and tok.cpu().tolist() == wt
 
 
+@pytest.mark.parametrize("bs", [1023, 1024, 1025, 4096, 4097], ids=str)
+def test_plan_batch_size_boundaries(bs):
+    """Batch sizes on both sides of the planner's internal limits (one sequence
+    per thread up to 1024; page counts cached for the wave-parallel search up
+    to 4096, a binary search beyond): short batches that fall back to one
+    segment per sequence, long ones with a work-list budget above the batch
+    size, and three sequences just under INT32_MAX tokens; plan and per-token
+    counts bit-exact."""
+    rng = np.random.default_rng(bs)
+    for trial in range(3):
+        lens = rng.integers(0, 3000 if trial == 0 else 300_000, size=bs)
+        lens[rng.random(bs) < 0.1] = 0
+        smax = int(rng.integers(1, 65))
+        ncu = 256 if trial == 0 else 65536
+        if trial == 2:
+            lens[rng.choice(bs, size=3, replace=False)] = 2**31 - 1 - rng.integers(0, 100, size=3)
+            smax = 65535
+        ql = rng.integers(1, 5, size=bs)
+        kvh = int(rng.choice([1, 2, 8]))
+        causal = trial % 2
+        cu_h = np.array(_cu(ql.tolist()), dtype=np.int32)
+        say("plan boundary", bs, trial)
+        plan, tok = skv.plan_build(torch.as_tensor(lens.astype(np.int32), device=DEV),
+                                   torch.as_tensor(cu_h, device=DEV), int(cu_h[-1]), kvh, ncu,
+                                   smax, causal)
+        wp, wt = oracle.plan_segments(lens.tolist(), cu_h, kvh, 16, ncu, smax, causal)
+        assert plan.cpu().tolist() == wp, (bs, trial)
+        assert tok.cpu().tolist() == wt, (bs, trial)
+
+
 # ---- page shuffle: bit-exact -------------------------------------------------
 
 @pytest.mark.parametrize("e,H,subset,N", [(2, 1, False, 16), (2, 3, False, 16), (2, 8, True, 16),
