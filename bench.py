@@ -30,7 +30,9 @@ last-level cache.
 
 For shuffled-page workloads the standard->shuffled repack, the in-place
 conversion of the same pool received as byte halves (and its inverse) and a
-cache write are timed on their own.
+cache write are timed on their own. "request_conversion" times the in-place
+conversion of one received request's pages, layer by layer, at 4k and 16k
+context on the geometry of the NixlConnector RFC's estimate.
 
 `--summarize DIR` turns the rocprofv3 outputs of one workload (the kernel
 trace and the two HBM counter runs whose commands it prints) into the
@@ -211,6 +213,58 @@ def _repack_timings(cfg, case, warmup, torch, skv, dev):
     res["cache_write_tokens"] = cfg.bs
     skv.kv_page_shuffle(case.kv, kp, vp)     # restore the planes for attention
     return res, kp, vp
+
+
+# One request's pages converted on arrival, on the geometry of the NixlConnector
+# RFC's estimate (Proposed Change, 4. Convert: a Qwen3-8B request carries 0.6 GB
+# of bf16 KV at 4k context and 2.4 GB at 16k; generic torch ops would take
+# roughly 1-2.5 ms and 3-10 ms): 36 layers of 8 kv heads, head dim 128, 16-token
+# pages, one in-place conversion call per layer over the request's received
+# blocks, which lie scattered in a layer pool twice their number.
+REQUEST_GEOMETRY = {"layers": 36, "kv_heads": 8, "head_dim": 128, "page_size": 16}
+RFC_TORCH_ESTIMATE_MS = {4096: [1.0, 2.5], 16384: [3.0, 10.0]}
+
+
+def time_request_conversion(ctx, torch, skv, reps=10):
+    dev = "cuda:0"
+    st = torch.cuda.current_stream()
+    L, H, D, P = (REQUEST_GEOMETRY[k] for k in ("layers", "kv_heads", "head_dim", "page_size"))
+    x = 8                                    # bf16: 16-byte chunks of 8 elements
+    nb = -(-ctx // P)
+    pool = 2 * nb
+    g = torch.Generator(device=dev)
+    g.manual_seed(ctx)
+    layers = []
+    for _ in range(L):
+        kp = torch.randint(-32768, 32768, (pool, H, D // x, P, x), dtype=torch.int16,
+                           device=dev, generator=g).view(torch.bfloat16)
+        vp = torch.randint(-32768, 32768, (pool, H, P // x, D, x), dtype=torch.int16,
+                           device=dev, generator=g).view(torch.bfloat16)
+        ids = torch.randperm(pool, device=dev, generator=g)[:nb].to(torch.int32)
+        layers.append((kp, vp, ids))
+
+    def request(direction):
+        for kp, vp, ids in layers:
+            skv.kv_page_convert(kp, vp, block_ids=ids, direction=direction)
+
+    for _ in range(2):
+        request("to_shuffled")
+        request("to_standard")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ms = []
+    for _ in range(reps):
+        e0.record(st)
+        request("to_shuffled")
+        e1.record(st)
+        request("to_standard")               # untimed: the next pass reads fresh halves
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    kv_bytes = nb * L * 2 * H * P * D * 2    # the request's K and V, all layers
+    mean = sum(ms) / len(ms)
+    return {"context_tokens": ctx, **REQUEST_GEOMETRY, "kv_bytes": kv_bytes,
+            "ms_per_request": mean, "us_per_layer": mean * 1e3 / L,
+            "read_write_tb_s": 2 * kv_bytes / (mean * 1e-3) / 1e12,
+            "rfc_torch_estimate_ms": RFC_TORCH_ESTIMATE_MS.get(ctx)}
 
 
 def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
@@ -739,6 +793,8 @@ def main(argv=None):
             print(f"timed {c.name}: {r['us_per_call']:.1f} us per call", file=sys.stderr,
                   flush=True)
         line["workloads"] = wl
+        line["request_conversion"] = [_round(time_request_conversion(c, torch, skv))
+                                      for c in sorted(RFC_TORCH_ESTIMATE_MS)]
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, a.cpu_seconds, gen, np)
     print(json.dumps(line), flush=True)
