@@ -27,7 +27,8 @@
  *     enqueued. Host-checkable argument errors are detected before any HIP
  *     call, so they can be tested without a GPU.
  *   - Device data must satisfy the stated contract (lengths, page ids,
- *     cu_seqlens_q); a violation is undefined behaviour and is not detected.
+ *     cu_seqlens_q); a violation is undefined behaviour and is not detected
+ *     by these calls. skv_check_inputs checks it on request (a debug aid).
  *
  * Element types: KV is bf16 (IEEE binary32 upper half), OCP e4m3fn fp8
  * (kv_dtype 1) with per-tensor fp32 dequant scales, or IEEE binary16 fp16
@@ -66,6 +67,15 @@ enum skv_attn_flags { SKV_ATTN_DETERMINISTIC = 1, SKV_ATTN_CLAIM_UNITS = 2 };
 
 enum skv_kv_dtype { SKV_KV_BF16 = 0, SKV_KV_FP8_E4M3FN = 1, SKV_KV_FP16 = 2 };
 enum skv_convert_dir { SKV_TO_SHUFFLED = 0, SKV_TO_STANDARD = 1 };
+/* Device-data contract violations reported by skv_check_inputs (bits). */
+enum skv_contract_violation {
+  SKV_BAD_LEN_NEGATIVE = 1,   /* seq_lens[i] < 0                                  */
+  SKV_BAD_LEN_TABLE = 2,      /* seq_lens[i] > pt_stride * page_size               */
+  SKV_BAD_CU = 4,             /* cu[0] != 0, cu[i + 1] < cu[i] or cu[bs] != total_q */
+  SKV_BAD_QLEN = 8,           /* cu[i + 1] - cu[i] > max_q                          */
+  SKV_BAD_PAGE_ID = 16        /* a page-table entry the attention reads is not a
+                                 block of the pool, i.e. outside [0, num_blocks)  */
+};
 
 /* Number of int32 words of a plan: 1 + max(num_cus / kv_heads, bs).
  * [PR, Modifications]: one word for the segment length, then the work list,
@@ -317,6 +327,25 @@ int skv_paged_decode_attn_static(const void* q, const void* kv_a, const void* kv
                                  float* out_lse, int flags, void* stream);
 
 /* Static text for a status code. */
+/* Debug check of the device data that skv_plan_build and the attention calls
+ * take on trust (the contract stated with them; optional, never run by those
+ * calls). One single-work-group launch reads seq_lens, cu_seqlens_q and the
+ * page-table entries the attention reads (entries p < ceil(L_i / page_size)
+ * of row i, at most pt_stride of them) and writes
+ *   result[0] = the OR of the skv_contract_violation bits found (0: none),
+ *   result[1] = the smallest sequence index with a violation (-1: none);
+ * cu[0] != 0 counts against sequence 0 and cu[bs] != total_q against
+ * sequence bs - 1; a sequence whose query count is negative (cu decreasing)
+ * gets SKV_BAD_CU and no SKV_BAD_QLEN. The page ids are compared with
+ * num_blocks, never dereferenced, so any input is safe to check.
+ * result: device int32 [2], written on the stream (read it after a sync).
+ * Errors: EINVAL for NULL pointers, bs outside [1, 32767], total_q < 1,
+ * max_q < 1, pt_stride < 1, num_blocks < 1; EUNSUPPORTED for page_size other
+ * than 16 or 32. */
+int skv_check_inputs(const int32_t* page_table, int pt_stride, const int32_t* seq_lens,
+                     const int32_t* cu_seqlens_q, int bs, int total_q, int max_q,
+                     int page_size, int num_blocks, int32_t* result, void* stream);
+
 const char* skv_strerror(int status);
 
 #ifdef __cplusplus

@@ -30,6 +30,8 @@ Modules:
   shuffle    standard <-> shuffled page repack, the in-place
              conversion of received byte halves (+ inverse), and
              the cache writer (new tokens at their slots)       -- pinned
+  contract   the plan and attention calls' device-data contract,
+             checked input by input                             -- pinned
 Every function is pinned by tests under tests/test_oracle_*.py against values
 the pages print, closed forms, invariants, brute force or an independent
 library routine; none is "parity unpinned".
@@ -43,6 +45,7 @@ from .merge import segment_partials, lse_merge, split_decode_attention
 from .shuffle import (shuffle_blocks, unshuffle_blocks, halves_from_standard,
                       convert_halves, revert_to_halves, write_tokens_standard,
                       write_tokens_shuffled)
+from .contract import check_inputs
 
 __all__ = [
     "decode_bf16", "decode_fp16", "decode_q", "fp16_value", "decode_e4m3fn",
@@ -53,4 +56,5 @@ __all__ = [
     "segment_partials", "lse_merge", "split_decode_attention",
     "shuffle_blocks", "unshuffle_blocks", "halves_from_standard", "convert_halves",
     "revert_to_halves", "write_tokens_standard", "write_tokens_shuffled",
+    "check_inputs",
 ]

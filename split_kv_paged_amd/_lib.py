@@ -54,6 +54,8 @@ _SIGNATURES = {
                                               _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                                               _c_int, _p, _p, _c_int, _p, _p, _c_int, _c_int,
                                               _p, _p, _c_int, _p]),
+    "skv_check_inputs": (_c_int, [_p, _c_int, _p, _p, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                  _p, _p]),
     "skv_strerror": (ctypes.c_char_p, [_c_int]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -371,3 +373,28 @@ def paged_decode_attn_static(q, kv_a, kv_b, page_table, seq_lens, cu_seqlens_q, 
         _ptr(out), _ptr(out_lse), ATTN_CLAIM_UNITS if claim_units else 0, _stream(stream))
     _check(st, "skv_paged_decode_attn_static")
     return out, out_lse
+
+
+# bits of check_inputs' first result word (enum skv_contract_violation)
+CONTRACT_BITS = {"len_negative": 1, "len_table": 2, "cu": 4, "qlen": 8, "page_id": 16}
+
+
+def check_inputs(page_table, seq_lens, cu_seqlens_q, total_q, max_q, num_blocks, page_size=16,
+                 result=None, stream=None):
+    """Enqueue the device-data contract check; returns the int32 [2] device
+    tensor it writes: [violation bits (CONTRACT_BITS), first offending
+    sequence or -1]. Read it after the stream's work is done."""
+    bs = seq_lens.numel()
+    if result is None:
+        result = torch.empty(2, dtype=torch.int32, device=seq_lens.device)
+    _need(page_table, torch.int32, "page_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(cu_seqlens_q, torch.int32, "cu_seqlens_q", bs + 1)
+    _need(result, torch.int32, "result", 2)
+    if page_table.dim() != 2 or page_table.shape[0] < bs:
+        raise ValueError("page_table: expected [bs, pt_stride]")
+    st = load().skv_check_inputs(_ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                 _ptr(cu_seqlens_q), bs, total_q, max_q, page_size, num_blocks,
+                                 _ptr(result), _stream(stream))
+    _check(st, "skv_check_inputs")
+    return result

@@ -19,7 +19,7 @@ OBJ = os.path.join(ROOT, "_build")
 
 HIP_SOURCES = ["skv_plan.hip", "skv_attn.hip", "skv_attn_mfma.hip", "skv_attn_mfma_priv.hip",
                "skv_attn_valu.hip", "skv_attn_gd.hip", "skv_reduce.hip", "skv_shuffle.hip",
-               "skv_convert.hip", "skv_cache_write.hip", "skv_static.hip"]
+               "skv_convert.hip", "skv_cache_write.hip", "skv_static.hip", "skv_check.hip"]
 HOST_SOURCES = ["skv_api.cpp", "skv_validate.cpp"]
 
 

@@ -186,6 +186,16 @@ int skv_kv_cache_write(const void* key, const void* value,
                                  v_scale, stream);
 }
 
+int skv_check_inputs(const int32_t* page_table, int pt_stride, const int32_t* seq_lens,
+                     const int32_t* cu_seqlens_q, int bs, int total_q, int max_q,
+                     int page_size, int num_blocks, int32_t* result, void* stream) {
+  int st = skv::check_inputs_args(page_table, pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
+                                  max_q, page_size, num_blocks, result);
+  if (st != SKV_OK) return st;
+  return skv::launch_check_inputs(page_table, pt_stride, seq_lens, cu_seqlens_q, bs, total_q,
+                                  max_q, page_size, num_blocks, result, stream);
+}
+
 const char* skv_strerror(int status) {
   switch (status) {
     case SKV_OK: return "ok";

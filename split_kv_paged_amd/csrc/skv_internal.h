@@ -30,6 +30,9 @@ inline bool head_dim_ok(int head_dim) { return head_dim == 64 || head_dim == 128
 int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
                     int total_q, int kv_heads, int page_size, int num_cus,
                     int seg_max, const void* plan, const void* tok_nseg);
+int check_inputs_args(const void* page_table, int pt_stride, const void* seq_lens,
+                      const void* cu_seqlens_q, int bs, int total_q, int max_q,
+                      int page_size, int num_blocks, const void* result);
 int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     int layout, int kv_dtype, const void* page_table,
                     int pt_stride, const void* seq_lens,
@@ -102,6 +105,9 @@ int launch_plan(const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
                 int total_q, int kv_heads, int page_size, int num_cus, int seg_max,
                 int causal, int32_t* plan, int32_t* tok_nseg, void* stream);
 int launch_segments(const AttnArgs& a, void* stream);
+int launch_check_inputs(const int32_t* page_table, int pt_stride, const int32_t* seq_lens,
+                        const int32_t* cu_seqlens_q, int bs, int total_q, int max_q,
+                        int page_size, int num_blocks, int32_t* result, void* stream);
 int launch_reduce(const float* part_o, const float* part_lse,
                   const int32_t* tok_nseg, int total_q, int q_heads, int head_dim,
                   int seg_max, bool out_f16, void* out, float* out_lse, void* stream);

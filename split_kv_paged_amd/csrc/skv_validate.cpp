@@ -17,6 +17,16 @@ int check_plan_args(const void* seq_lens, const void* cu_seqlens_q, int bs,
   return SKV_OK;
 }
 
+int check_inputs_args(const void* page_table, int pt_stride, const void* seq_lens,
+                      const void* cu_seqlens_q, int bs, int total_q, int max_q,
+                      int page_size, int num_blocks, const void* result) {
+  if (!page_table || !seq_lens || !cu_seqlens_q || !result) return SKV_EINVAL;
+  if (bs < 1 || bs > kMaxBs || total_q < 1 || max_q < 1 || pt_stride < 1 || num_blocks < 1)
+    return SKV_EINVAL;
+  if (!repack_page_size_ok(page_size)) return SKV_EUNSUPPORTED;
+  return SKV_OK;
+}
+
 int check_attn_args(const void* q, const void* kv_a, const void* kv_b,
                     int layout, int kv_dtype, const void* page_table,
                     int pt_stride, const void* seq_lens,

@@ -233,3 +233,29 @@ def test_static_scratch_size_matches_header():
     text = open(HEADER).read()
     assert "#define SKV_STATIC_SCRATCH_BYTES (64u << 20)" in text
     assert skv.STATIC_SCRATCH_BYTES == 64 << 20
+
+
+def _check_inputs(**kw):
+    a = dict(pt=P, pt_stride=8, sl=P, cu=P, bs=2, total_q=2, max_q=4, page_size=16, nb=64,
+             res=P)
+    a.update(kw)
+    return skv.load().skv_check_inputs(a["pt"], a["pt_stride"], a["sl"], a["cu"], a["bs"],
+                                       a["total_q"], a["max_q"], a["page_size"], a["nb"],
+                                       a["res"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pt=None), 1), (dict(sl=None), 1), (dict(cu=None), 1), (dict(res=None), 1),
+    (dict(bs=0), 1), (dict(bs=32768), 1), (dict(total_q=0), 1), (dict(max_q=0), 1),
+    (dict(pt_stride=0), 1), (dict(nb=0), 1), (dict(page_size=64), 2),
+])
+def test_check_inputs_errors(kw, code):
+    assert _check_inputs(**kw) == code
+
+
+def test_contract_bits_match_header():
+    text = open(HEADER).read()
+    for name, bit in (("LEN_NEGATIVE", 1), ("LEN_TABLE", 2), ("CU", 4), ("QLEN", 8),
+                      ("PAGE_ID", 16)):
+        assert re.search(rf"SKV_BAD_{name} = {bit}\b", text), name
+    assert sorted(skv.CONTRACT_BITS.values()) == [1, 2, 4, 8, 16]

@@ -12,12 +12,14 @@ import pytest
 
 import oracle
 import oracle.attention as att
+import oracle.contract as contract
 import oracle.fp8 as fp8
 import oracle.merge as merge
 import oracle.planner as planner
 import oracle.shuffle as shuffle
 import test_oracle_attention as TA
 import test_oracle_cache_write as TW
+import test_oracle_contract as TK
 import test_oracle_convert as TC
 import test_oracle_fp8 as TF
 import test_oracle_planner as TP
@@ -28,7 +30,7 @@ from conftest import load_golden
 def _pins():
     """(name, callable) for every pin, parametrized ones expanded."""
     pins = []
-    for mod in (TA, TC, TF, TP, TS, TW):
+    for mod in (TA, TC, TF, TP, TK, TS, TW):
         for name in dir(mod):
             if not name.startswith("test_"):
                 continue
@@ -215,6 +217,24 @@ def _write_std_wraps(std, key, value, slot_mapping):
     return TRUE_WRITE_STD(std, key, value, wrapped)
 
 
+TRUE_CHECK = contract.check_inputs
+
+
+def _check_reads_one_more(page_table, seq_lens, cu_seqlens_q, total_q, max_q, page_size,
+                          num_blocks):
+    # reads floor(L / P) + 1 entries instead of ceil(L / P): one too many when
+    # L is a whole number of pages
+    table = np.asarray(page_table)
+    lens = [int(v) for v in seq_lens]
+    mask, first = TRUE_CHECK(table, lens, cu_seqlens_q, total_q, max_q, page_size, num_blocks)
+    for i, L in enumerate(lens):
+        if L > 0 and L % page_size == 0 and L // page_size < table.shape[1]:
+            if not (0 <= int(table[i][L // page_size]) < num_blocks):
+                mask |= contract.BAD_PAGE_ID
+                first = i if first < 0 else min(first, i)
+    return mask, first
+
+
 def _encode_ties_up(values):
     v = np.asarray(values, dtype=np.float64)
     pos = fp8._E4M3FN[:0x7F]
@@ -288,6 +308,9 @@ MUTATIONS = [
       (oracle, "write_tokens_standard", _write_std_wraps)]),
     ("byte halves swapped", [(shuffle, "halves_from_standard", _halves_swapped),
                              (oracle, "halves_from_standard", _halves_swapped)]),
+    ("contract checker reads one page-table entry too many",
+     [(contract, "check_inputs", _check_reads_one_more),
+      (oracle, "check_inputs", _check_reads_one_more)]),
 ]
 
 
