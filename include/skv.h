@@ -185,8 +185,12 @@ int skv_paged_decode_attn(const void* q, const void* kv_a, const void* kv_b,
  * (part_o, part_lse) of every (token, q head, segment) that the plan lists
  * (with plan NULL: of the fixed split, and tok_nseg), without merging them. Arguments and errors as for skv_paged_decode_attn
  * (minus out and out_lse). skv_paged_decode_attn = this call followed by
- * skv_split_reduce on the same stream. Partials of several calls (e.g. over
- * disjoint page ranges) can be merged with skv_split_reduce. */
+ * skv_split_reduce on the same stream. Each call writes token t's partials at
+ * segment indices 0 .. tok_nseg[t] - 1; partials of several calls over
+ * disjoint key ranges (e.g. the shards of several GPUs) merge into attention
+ * over their union when the caller places them side by side in one buffer of
+ * the same layout (distinct segment indices, tok_nseg counting them all) and
+ * runs skv_split_reduce on it. */
 int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layout,
                      int kv_dtype, const int32_t* page_table, int pt_stride,
                      const int32_t* seq_lens, const int32_t* cu_seqlens_q, int bs,
