@@ -236,12 +236,11 @@ template <bool NT>
 __device__ __forceinline__ void dma16_lds(const void* g, uint8_t* lds_uniform) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
+  // the LDS base travels in M0, which the compiler loads for the statement
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :: "v"(g), "s"(lds) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off nt" :: "v"(g), "{m0}"(lds) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(g), "s"(lds) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, off" :: "v"(g), "{m0}"(lds) : "memory");
 }
 
 // The same from a wave-uniform base (held in SGPRs) plus a 32-bit per-lane
@@ -252,11 +251,11 @@ __device__ __forceinline__ void dma16_lds_s(const uint8_t* base_uniform, uint32_
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (__attribute__((address_space(3))) uint8_t*)(lds_uniform)));
   if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
-                 :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(off), "s"(base_uniform), "{m0}"(lds) : "memory");
   else
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(base_uniform), "s"(lds) : "memory", "m0");
+    asm volatile("global_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base_uniform), "{m0}"(lds) : "memory");
 }
 
 // 16-bit standard pages in LDS (matrix-core kernels): a page is its 16 token

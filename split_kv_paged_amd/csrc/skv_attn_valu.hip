@@ -49,7 +49,6 @@ constexpr int kHalf = kPageSize * kD * 2;      // a page's K (or V) half, bf16
 constexpr int kPage = 2 * kHalf;
 constexpr int kInstrPerPage = kPage / 1024;    // DMA instructions per page
 constexpr int kStdRow = 2 * kD * 2;            // one standard token row
-constexpr int kStdTile = kPageSize * kStdRow;  // one (block, head) standard tile
 
 template <int NW, int RING_KB>
 struct VRing {
