@@ -1,6 +1,6 @@
 // Segment attention, matrix-core variant on a ring shared by all waves, used
-// for bf16 KV with 33-64 query rows (GQA group x query tokens, four 16-row
-// tiles); the kernel itself is generic in the element type and tile count.
+// for bf16 or fp16 KV with 33-64 query rows (GQA group x query tokens, four
+// 16-row tiles).
 //
 // sglang PR #39172, "[AMD] gfx950 assembly attention: length-aware split-KV
 // for dynamic workload", Motivation and Modifications: one work-group per
@@ -34,8 +34,6 @@
 //    the accumulator is rescaled only when a row max moved. Masked lanes are
 //    forced to -inf and V of tokens past the segment end is zeroed, so stale
 //    LDS or page-tail poison (even NaN) never reaches the accumulator.
-//  * fp8 e4m3fn KV is widened to bf16 exactly before the MFMA; k_scale folds
-//    into the score scale and v_scale into the output.
 #include <type_traits>
 
 #include "skv_attn_common.h"
@@ -122,7 +120,7 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
     const bool vhalf = u & 1;
     const SubPageAddr a = sub_page<E, SHUF, PSH>(p, it.g, pids[uw], subs[uw]);
     uint8_t* dst = slot + (2 * pg + (vhalf ? 1 : 0)) * R::kUnitBytes;
-    if constexpr (E == 2 && !SHUF) {
+    if constexpr (!SHUF) {
       // bf16 standard pages: unit (page, row half h) = token rows 8h .. 8h+7
       // (K then V, 512 bytes each), two whole rows (1 KB of contiguous HBM) per
       // instruction, streamed; chunk q of row tau lands at position
@@ -136,42 +134,18 @@ __device__ __forceinline__ void issue_stage(const SegParams& p, const SegItem& i
       }
       continue;
     }
+    // shuffled planes: the K plane's chunk rows (lane reads the 16 bytes
+    // compute-lane `lane` needs for k-step i) and the V plane as it is, whole
+    // lines, streamed
     if (!vhalf) {
-      const uint8_t* tile = a.k;
 #pragma unroll
-      for (int i = 0; i < R::kUnitInstr; ++i) {
-        // lane reads the 16 bytes compute-lane `lane` needs for k-step i
-        size_t off;
-        if constexpr (SHUF) {
-          off = static_cast<size_t>(4 * i + j4) * krow + r16 * 16;
-        } else {
-          const int byte = E == 2 ? (32 * i + 8 * j4) * 2 : 64 * i + 16 * j4;
-          off = static_cast<size_t>(r16) * R::kStdRow + byte;
-        }
-        dma16_lds<SHUF>(tile + off, dst + i * 1024);   // shuffled: whole lines
-      }
+      for (int i = 0; i < R::kUnitInstr; ++i)
+        dma16_lds<true>(a.k + static_cast<size_t>(4 * i + j4) * krow + r16 * 16,
+                        dst + i * 1024);
     } else {
 #pragma unroll
-      for (int i = 0; i < R::kUnitInstr; ++i) {
-        size_t off;
-        if constexpr (SHUF) {
-          off = static_cast<size_t>(i * 64 + lane) * 16;          // plane copied as is
-        } else {
-          // chunk-major tile: bf16 [chunk pair u][token tau][32 B], fp8
-          // [chunk c][token tau][16 B]; instruction i covers 1 KB of it
-          int tau, c;
-          if constexpr (E == 2) {
-            const int u = 2 * i + (lane >> 5);
-            tau = (lane >> 1) & 15;
-            c = 2 * u + (lane & 1);
-          } else {
-            c = 4 * i + (lane >> 4);
-            tau = lane & 15;
-          }
-          off = static_cast<size_t>(tau) * R::kStdRow + kD * E + c * 16;
-        }
-        dma16_lds<SHUF>(a.v + off, dst + i * 1024);
-      }
+      for (int i = 0; i < R::kUnitInstr; ++i)
+        dma16_lds<true>(a.v + static_cast<size_t>(i * 64 + lane) * 16, dst + i * 1024);
     }
   }
 }
@@ -252,7 +226,7 @@ void seg_mfma_kernel(SegParams p) {
     const uint16_t* qr = p.q + (static_cast<size_t>(t) * p.Hq + h) * kD;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = E == 2 ? 32 * kk + 8 * j4 : 64 * (kk >> 1) + 16 * j4 + 8 * (kk & 1);
+      const int ch = 32 * kk + 8 * j4;
       dma16_lds<false>(qr + ch, qstage + kk * 1024);   // padding rows read row 0
     }
   }
@@ -316,23 +290,16 @@ void seg_mfma_kernel(SegParams p) {
 #pragma unroll
     for (int pg = 0; pg < 2; ++pg) {
       bf16x8_t kop[4];
-      if constexpr (E == 2 && !SHUF) {
+      if constexpr (!SHUF) {
         // page tile at kU[pg]: chunk 4 kk + j4 of token row r16
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(
               kU[pg] + r16 * R::kStdRow + std2_chunk_pos(r16, 4 * kk + j4) * 16));
-      } else if constexpr (E == 2) {
+      } else {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           kop[kk] = as_bf16x8(*reinterpret_cast<const uint4*>(kU[pg] + kk * 1024 + lane * 16));
-      } else {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const uint4 c = *reinterpret_cast<const uint4*>(kU[pg] + u * 1024 + lane * 16);
-          kop[2 * u] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.x, c.y)));
-          kop[2 * u + 1] = as_bf16x8(fp8x8_to_bf16x8(make_uint2(c.z, c.w)));
-        }
       }
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -383,9 +350,6 @@ void seg_mfma_kernel(SegParams p) {
 
     // ---- O^T += V^T.P^T ; element e: page e/4, token 4*j4 + e%4 ----
     const int vend = it.seg_end - tok0;       // tokens of the block before the end
-    // per-lane part of the transposing-read address in the chunk-major V tile
-    const int vtr_off = (4 * j4 + ((r16 >> 1) & 3)) * 16 + (r16 & 1) * 8;   // fp8 tile
-    const uint8_t* vU8 = vU[r16 >> 3];        // fp8: lanes 0-7 of a group read page 0
     // the V-tail zeroing is compiled into a second copy of the loop, taken
     // only by the block that crosses the segment end
     auto pv = [&](auto tail_tag) __attribute__((always_inline)) {
@@ -394,7 +358,7 @@ void seg_mfma_kernel(SegParams p) {
     for (int dt = 0; dt < 8; ++dt) {
       const int d = 16 * dt + r16;
       uint32_t w[4];
-      if constexpr (SHUF && E == 2) {
+      if constexpr (SHUF) {
 #pragma unroll
         for (int pg = 0; pg < 2; ++pg) {
           const uint2 v = *reinterpret_cast<const uint2*>(
@@ -402,12 +366,7 @@ void seg_mfma_kernel(SegParams p) {
           w[2 * pg] = v.x;
           w[2 * pg + 1] = v.y;
         }
-      } else if constexpr (SHUF) {
-        const uint32_t a = *reinterpret_cast<const uint32_t*>(vU[0] + d * 16 + 4 * j4);
-        const uint32_t b = *reinterpret_cast<const uint32_t*>(vU[1] + d * 16 + 4 * j4);
-        const uint4 c = fp8x8_to_bf16x8(make_uint2(a, b));
-        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
-      } else if constexpr (E == 2) {
+      } else {
         // transposing LDS read: in each 16-lane group, lane i receives element
         // i%4 of the 8 bytes read by lane 4k + i/4 (k = 0..3). Lane j reads
         // token tau = 4*j4 + j/4, channels 16dt + 4(j%4) .. +3, i.e. half j%2
@@ -425,16 +384,6 @@ void seg_mfma_kernel(SegParams p) {
           w[2 * pg] = u.x;
           w[2 * pg + 1] = u.y;
         }
-      } else {
-        // transposing byte read: in each 16-lane group, lane i receives byte
-        // i%8 of the 8 bytes read by lane 2k + i/8 (k = 0..7). Lane j reads
-        // page j/8, token 4*j4 + (j/2)%4, channels 16dt + 8(j%2) .. +7, so lane
-        // i ends up with the block's 8 tokens of channel 16dt + i.
-        const v2i32_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) v2i32_t*)(
-                (__attribute__((address_space(3))) uint8_t*)(vU8) + vtr_off + dt * 256));
-        const uint4 c = fp8x8_to_bf16x8(__builtin_bit_cast(uint2, v));
-        w[0] = c.x; w[1] = c.y; w[2] = c.z; w[3] = c.w;
       }
       if (tail) {                    // zero V of tokens past the segment end
 #pragma unroll
