@@ -430,6 +430,29 @@ def test_fp8_negative_k_scale(spec):
     assert r["lse_err"] <= 1e-3, r
 
 
+@pytest.mark.parametrize("head_dim", [128, 64])
+@pytest.mark.parametrize("spec", [_BY[n] for n in ("fp8_rows4_std", "fp8_rows64_std")],
+                         ids=lambda c: c[0])
+def test_fp8_zero_scales(spec, head_dim):
+    """K scale 0: every score is 0, so each row averages the V rows it sees
+    (the kernels clamp the score scale to the least normal float); V scale 0:
+    the output is 0 and the log-sum-exp unchanged."""
+    name, lens, ql, hq, hkv, dt, layout, causal, ncu, smax = spec
+    for ks, vs in ((0.0, 0.0211), (0.0173, 0.0)):
+        cfg = gen.small_config(configs.FP8_KV, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
+                               causal=causal, num_cus=ncu, seg_max=smax, seed=10,
+                               head_dim=head_dim, k_scale=ks, v_scale=vs)
+        case = gen.make_case(cfg, DEV)
+        hip = run_hip(case)
+        ref_out, ref_lse = run_oracle(case)
+        r = compare(hip["out"], hip["lse"], ref_out, ref_lse, "fp8")
+        say(name, head_dim, "scales", ks, vs, r)
+        assert r["max_abs"] <= r["tol"], r
+        assert r["lse_err"] <= 1e-3, r
+        if vs == 0.0:
+            assert np.all(hip["out"] == 0.0)
+
+
 @pytest.mark.parametrize("spec", [_BY[n] for n in ("rows8_ragged", "mfma4_g16_q4", "mfma_fp8_std",
                                                    "mfma_fp8_shuf", "fp8_rows64_std",
                                                    "fp8_rows64_shuf", "fp8_rows4_shuf",
