@@ -460,6 +460,31 @@ def test_many_short_sequences(bs, dt, layout):
         assert r["lse_err"] <= 1e-3, r
 
 
+@pytest.mark.parametrize("ncu", [1, 2, 3])
+def test_budget_below_kv_heads(ncu):
+    """num_cus below kv_heads (4): the work-list budget num_cus / kv_heads is 0,
+    so the planner falls back to one segment per non-empty sequence and the
+    fixed split to one segment; plan, counts and outputs against the oracle."""
+    say("budget", ncu)
+    lens, ql = [0, 1, 17, 300, 2049], [1, 2, 3, 4, 2]
+    cfg = gen.small_config(configs.TINY, lens, ql, q_heads=16, kv_heads=4, num_cus=ncu,
+                           seg_max=64, seed=13)
+    case = gen.make_case(cfg, DEV)
+    ref_out, ref_lse = run_oracle(case)
+    for fixed in (False, True):
+        hip = run_hip(case, fixed=fixed)
+        if fixed:
+            _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                                     cfg.kv_heads, 16, ncu, 64, cfg.causal)
+            assert hip["tok"] == want_tok
+        else:
+            wp, wt = oracle_plan(case)
+            assert hip["plan"] == wp and hip["tok"] == wt
+        r = compare(hip["out"], hip["lse"], ref_out, ref_lse, "bf16")
+        assert r["max_abs"] <= r["tol"], r
+        assert r["lse_err"] <= 1e-3, r
+
+
 @pytest.mark.parametrize("head_dim", [128, 64])
 @pytest.mark.parametrize("spec", [_BY[n] for n in ("fp8_rows4_std", "fp8_rows64_std")],
                          ids=lambda c: c[0])
