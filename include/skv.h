@@ -19,10 +19,12 @@
  * Conventions for every call:
  *   - Pointer arguments are DEVICE pointers owned by the caller (except the
  *     `stream`, a hipStream_t passed as void*; NULL is the null stream).
- *   - The library never allocates, frees or synchronizes and keeps no global
- *     state; calls only enqueue work on `stream`. Grid sizes depend on the
- *     host integers alone and no device data is read back, so every call may
- *     be captured into a HIP graph.
+ *   - The library never allocates, frees or synchronizes; calls only enqueue
+ *     work on `stream`. Its one piece of global state is the device array of
+ *     skv_paged_decode_attn_static (a fixed-size __device__ array, looked up
+ *     once per device). Grid sizes depend on the host integers alone and no
+ *     device data is read back, so every call may be captured into a HIP
+ *     graph.
  *   - Return value: SKV_OK, or an error code below; on error nothing was
  *     enqueued. Host-checkable argument errors are detected before any HIP
  *     call, so they can be tested without a GPU.
