@@ -4,7 +4,7 @@
 What is computed [PR, Motivation and Modifications; RFC, Background]: for each
 sequence of a verify/decode batch, each of its 1..4 query tokens and each query
 head, softmax(q.K^T / sqrt(D)).V over the sequence's KV tokens, which live in
-16-token pages reached through a page table; query heads map onto KV heads in
+16- or 32-token pages reached through a page table; query heads map onto KV heads in
 contiguous groups of G = Hq / Hkv (grouped-query attention).
 
 Readings where the pages are silent (each also listed in the design notes):

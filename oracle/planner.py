@@ -12,7 +12,7 @@ the tiles per segment from the first plan word.
 max(1, min(64, pow2floor(256 / (bs * kv_heads)))) segments.
 
 Readings (pages silent; also in the design notes):
-  * T counts pages ("tiles" = 16-token pages), searched over all integers
+  * T counts pages ("tiles" = pages of the given size, 16 or 32 tokens), searched over all integers
     1..max(max_pages, 1); feasibility is monotone in T, so the smallest is unique;
   * no feasible T (more non-empty sequences than num_CUs // kv_heads): T is the
     longest sequence's page count, i.e. one segment per non-empty sequence;
