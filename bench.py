@@ -13,15 +13,19 @@ PR's agentic rows (Benchmarking and Profiling). Every other workload is timed
 the same way and reported under "workloads" in the same JSON line (`--only`
 times the headline alone).
 
-Each workload is timed in three arms: the planned split (plan + segment +
-reduce), the fixed split (no plan; the PR's A/B baseline and its bs == 1
-path) and the planned call replayed from a HIP graph. The arms are
-interleaved: timed step i runs all three, in an order rotated by i, so no arm
-gains or loses from its position. Before the counted warm-up, the planned
-call is repeated until the median duration of its last 20 segment launches is
-within 1% of the 20 before (at least 100 launches, at most --precondition-s
-seconds): after the GPU has been idle, the first ~100 launches run up to 40%
-slower while clocks ramp. That phase is reported under "precondition".
+Each workload is timed in four arms: the planned split with an event
+between every launch (plan, segment kernel, reduce: the per-kernel times and
+the roofline), the planned call alone (segment + reduce between two events,
+on the plan the step before built: `value`), the fixed split (no plan; the
+PR's A/B baseline and its bs == 1 path) and the planned call replayed from a
+HIP graph. An event between the call's two launches lengthens the call by
+3-5 us, so only the first arm records one. The arms are interleaved: timed
+step i runs all four, in an order rotated by i, so no arm gains or loses from
+its position. Before the counted warm-up, the planned call is repeated until
+the median duration of its last 20 segment launches is within 1% of the 20
+before (at least 100 launches, at most --precondition-s seconds): after the
+GPU has been idle, the first ~100 launches run up to 40% slower while clocks
+ramp. That phase is reported under "precondition".
 
 Every KV pool is timed on at least two copies used in turn (more when the
 pool is small: together at least 4 GiB, at most 8 copies), one copy per call
@@ -57,7 +61,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "agentic_skew"
 ROTATE_BYTES = 4 << 30          # KV copies used in turn: together at least this
-ARMS = ("planned", "fixed", "graph")
+ARMS = ("planned", "call", "fixed", "graph")
 
 
 def _args(argv=None):
@@ -335,6 +339,14 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
         if ev:
             ev[3].record(st)
 
+    def call(ev=None):
+        kv = next_kv()
+        if ev:
+            ev[0].record(st)
+        seg_reduce(kv, plan, tok, out)
+        if ev:
+            ev[1].record(st)
+
     def fixed(ev=None):
         kv = next_kv()
         if ev:
@@ -342,11 +354,9 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
         skv.segment_attn(case.q, kv[0], kv[1], case.page_table, case.seq_lens,
                          case.cu_seqlens_q, None, ftok, part_o=part_o, part_lse=part_lse,
                          **kw)
-        if ev:
-            ev[1].record(st)
         skv.split_reduce(part_o, part_lse, ftok, out=fout, **red)
         if ev:
-            ev[2].record(st)
+            ev[1].record(st)
 
     # the planned call (segment + reduce, plan built beforehand) captured once
     # per KV copy and replayed, as a serving loop runs decode steps
@@ -374,8 +384,8 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
         if ev:
             ev[1].record(st)
 
-    run = {"planned": planned, "fixed": fixed, "graph": graph}
-    nev = {"planned": 4, "fixed": 3, "graph": 2}
+    run = {"planned": planned, "call": call, "fixed": fixed, "graph": graph}
+    nev = {"planned": 4, "call": 2, "fixed": 2, "graph": 2}
 
     # clock pre-conditioning: the planned call until its segment-kernel time settles
     t0 = time.perf_counter()
@@ -399,7 +409,7 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
                            "segment_us_last20_median": round(meds[-1], 2) if meds else None}
 
     def order(i):
-        return ARMS[i % 3:] + ARMS[:i % 3]
+        return ARMS[i % len(ARMS):] + ARMS[:i % len(ARMS)]
 
     for i in range(a.warmup):
         for arm in order(i):
@@ -421,21 +431,21 @@ def time_workload(cfg, a, torch, skv, gen, with_schedule=False):
     pl = evs["planned"]
     p_call = [us(e, 1, 3) for e in pl]
     p_seg = [us(e, 1, 2) for e in pl]
-    f_call = [us(e, 0, 2) for e in evs["fixed"]]
-    f_seg = [us(e, 0, 1) for e in evs["fixed"]]
+    c_call = [us(e, 0, 1) for e in evs["call"]]
+    f_call = [us(e, 0, 1) for e in evs["fixed"]]
     g_call = [us(e, 0, 1) for e in evs["graph"]]
-    call = sum(p_call) / len(p_call)
+    call = sum(c_call) / len(c_call)
     seg = sum(p_seg) / len(p_seg)
     res.update(
         kv_bytes=kvb, us_per_call=call, kv_tb_s=kvb / call / 1e6,
         frac_of_hbm_peak=kvb / call / 1e3 / HBM_PEAK_GBS, segment_us=seg,
         segment_gb_s=kvb / seg / 1e3, plan_T=int(plan[0].item()),
+        call={"call_us": _stats(c_call), "kv_tb_s": kvb / call / 1e6},
         planned={"call_us": _stats(p_call), "segment_us": _stats(p_seg),
                  "plan_us": sum(us(e, 0, 1) for e in pl) / len(pl),
                  "reduce_us": sum(us(e, 2, 3) for e in pl) / len(pl),
                  "step_us": sum(us(e, 0, 3) for e in pl) / len(pl)},
-        fixed={"call_us": _stats(f_call), "segment_us": _stats(f_seg),
-               "segments_per_seq": _fixed_segments(cfg),
+        fixed={"call_us": _stats(f_call), "segments_per_seq": _fixed_segments(cfg),
                "kv_tb_s": kvb / (sum(f_call) / len(f_call)) / 1e6},
         graph={"call_us": _stats(g_call), "kv_tb_s": kvb / (sum(g_call) / len(g_call)) / 1e6})
     # the planned and the fixed split on the same inputs: the PR's accuracy
@@ -631,8 +641,8 @@ def summarize(d, copy_dir=None, out_dir=None):
          "Command (repository root, one MI355X; the bench line it prints is the source of the",
          "launch schedule used below):", "", "```", PROFILE_CMDS["trace"].format(**fmt), "```",
          "", f"Bench line of this run: {tline['us_per_call']} us per call, "
-             f"{tline['value']} TB/s (planned arm, events); kernel sources hash {src_hash}.", "",
-         "Segment kernel, per arm (the timed steps interleave the three arms in rotated order):",
+             f"{tline['value']} TB/s (the call arm, events); kernel sources hash {src_hash}.", "",
+         "Segment kernel, per arm (the timed steps interleave the arms in rotated order):",
          "", "| phase | arm | launches | avg us | median us | p10 us | p90 us | KV TB/s (avg) |",
          "|---|---|---|---|---|---|---|---|"]
     kvb = tline["roofline"]["algorithmic_bytes_per_launch"]
@@ -787,7 +797,7 @@ def main(argv=None):
                 continue
             r = time_workload(c, a, torch, skv, gen)
             keep = ("workload", "note", "kv_bytes", "us_per_call", "kv_tb_s", "frac_of_hbm_peak",
-                    "segment_us", "segment_gb_s", "plan_T", "planned", "fixed", "graph",
+                    "segment_us", "segment_gb_s", "plan_T", "planned", "call", "fixed", "graph",
                     "plan_vs_fixed_max_abs", "precondition", "kv_copies", "repack")
             wl.append(_round({k: r[k] for k in keep if k in r}))
             print(f"timed {c.name}: {r['us_per_call']:.1f} us per call", file=sys.stderr,

@@ -55,4 +55,4 @@ def test_bench_line_carries_the_contract_keys():
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["unit"] == d["unit"] and c["value"] > 0
     assert c["cores"] >= 1 and c["sample"]
-    assert set(d["arms"]) == {"planned", "fixed", "graph"}
+    assert set(d["arms"]) == {"planned", "call", "fixed", "graph"}
