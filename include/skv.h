@@ -205,8 +205,9 @@ int skv_segment_attn(const void* q, const void* kv_a, const void* kv_b, int layo
 /* Split reduce alone [PR, Modifications]: for every (t, h), merges the first
  * tok_nseg[t] partials by log-sum-exp: M = max_s lse_s,
  * lse = M + ln sum_s exp(lse_s - M), out = sum_s exp(lse_s - lse) * o_s.
- * tok_nseg[t] == 0 gives zeros and lse -inf. Values of tok_nseg[t] above
- * seg_max are clamped to seg_max.
+ * A partial whose lse is -inf (a segment with no visible key) has weight 0;
+ * tok_nseg[t] == 0, or only such partials, gives zeros and lse -inf. Values
+ * of tok_nseg[t] above seg_max are clamped to seg_max.
  * Layouts as for skv_paged_decode_attn; out [total_q, q_heads, head_dim] of
  * out_dtype (SKV_KV_BF16: bf16, SKV_KV_FP16: fp16; round to nearest even);
  * out_lse may be NULL.

@@ -14,13 +14,17 @@
 // to the KV stream, so the kernel is latency-, not bandwidth-, shaped: what
 // matters is how many partial rows are in flight at once and how many
 // work-groups the launch has.
+//  * Up to 256 segments per token, each lane holds the log-sum-exps of
+//    segments lane, lane + 64, ... (all loaded at once), so the weights come
+//    from one round trip and wave-level reductions; more segments take a
+//    plain loop (max, sum, weighted rows).
 //  * Narrow form (many (token, head) rows): one wave per row, four rows per
 //    work-group; the first 8 partial rows are loaded before the weights are
 //    known, the rest in chunks of 8 loads issued together.
 //  * Wide form (at most 1024 rows, e.g. single-sequence batches whose
-//    tokens each merge up to 64 segments): one work-group per row, its four
-//    waves each loading a quarter of the segments (up to 16 rows in flight
-//    per wave) before the weights are known; the four partial sums are added
+//    tokens each merge many segments): one work-group per row; in every
+//    64-segment chunk wave w loads segments 16w .. 16w + 15 (the first
+//    chunk's before the weights are known); the four partial sums are added
 //    through LDS.
 #include <hip/hip_runtime.h>
 
@@ -115,11 +119,173 @@ __device__ float merge_general(const float* lse_p, const float* o_p, int nseg, i
     sum += v;
   }
   const float lse = M + logf(sum);
-  for (int s = 0; s < nseg; ++s) {
-    const float w = expf(lse_p[s] - lse);
-    const LaneVec<C> o = load_lane<C>(o_p + s * D, lane);
+  for (int s0 = 0; s0 < nseg; s0 += 8) {
+    LaneVec<C> o[8];
+    float l[8];
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc.v[c] += w * o.v[c];
+    for (int k = 0; k < 8; ++k) {          // rows past nseg repeat the last one, weight 0
+      const int s = s0 + k < nseg ? s0 + k : nseg - 1;
+      o[k] = load_lane<C>(o_p + s * D, lane);
+      l[k] = lse_p[s];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = s0 + k < nseg ? expf(l[k] - lse) : 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc.v[c] += w * o[k].v[c];
+    }
+  }
+  return lse;
+}
+
+// Segments whose log-sum-exps a wave holds in registers, lane l holding
+// segments l, l + 64, ... (NC of them): up to 64 * kChunks in all.
+constexpr int kChunks = 4;
+constexpr int kHeldSegs = 64 * kChunks;
+
+// The log-sum-exps of up to 64 NC segments, lane l taking segments
+// l, l + 64, ... (-inf past nseg); loaded ahead of the partial rows, so they
+// arrive first.
+template <int NC>
+__device__ __forceinline__ void load_held(const float* lse_p, int nseg, int lane,
+                                          float (&ls)[NC]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int s = 64 * c + lane;
+    ls[c] = s < nseg ? lse_p[s] : -INFINITY;
+  }
+}
+
+// Their weights: w[c] on lane l is segment 64 c + l's weight e^(lse_s - lse)
+// (0 past nseg); returns the merged lse, -inf when no segment has a finite
+// one (then every weight is 0).
+template <int NC>
+__device__ __forceinline__ float held_weights(const float (&ls)[NC], int nseg, int lane,
+                                              float (&w)[NC]) {
+  float M = ls[0];
+#pragma unroll
+  for (int c = 1; c < NC; ++c) M = fmaxf(M, ls[c]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (M == -INFINITY) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) w[c] = 0.f;
+    return -INFINITY;
+  }
+  float e[NC], sum = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    e[c] = 64 * c + lane < nseg ? expf(ls[c] - M) : 0.f;
+    sum += e[c];
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) w[c] = e[c] / sum;
+  return M + logf(sum);
+}
+
+// weight of segment s (wave-uniform, s < 64 NC) from the held weights
+template <int NC>
+__device__ __forceinline__ float held_weight(const float (&w)[NC], int s) {
+  if constexpr (NC == 1) {
+    return __shfl(w[0], s);
+  } else {
+    static_assert(NC == kChunks, "one or four chunks");
+    const int c = s >> 6;
+    const float v = c == 0 ? w[0] : (c == 1 ? w[1] : (c == 2 ? w[2] : w[3]));
+    return __shfl(v, s & 63);
+  }
+}
+
+// Narrow form, 1 <= nseg <= 64 NC: the first kPre partial rows are loaded
+// before the weights are known (one memory round trip, not two), the rest in
+// chunks of kPre rows with all loads of a chunk issued together. Rows past
+// nseg re-read the last valid row with weight 0: entries past a token's
+// segment count are unspecified and may hold NaN.
+template <int NC, int D>
+__device__ __forceinline__ float merge_held(const float* lse_p, const float* o_p, int nseg,
+                                            int lane, LaneVec<D / 64>& acc) {
+  constexpr int C = D / 64;
+  constexpr int kPre = 8;
+  float ls[NC];
+  load_held<NC>(lse_p, nseg, lane, ls);
+  LaneVec<C> pre[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int kk = k < nseg ? k : nseg - 1;
+    pre[k] = load_lane<C>(o_p + kk * D, lane);
+  }
+  float wt[NC];
+  const float lse = held_weights<NC>(ls, nseg, lane, wt);
+  if (lse == -INFINITY) return lse;
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const float wk = k < nseg ? held_weight<NC>(wt, k) : 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
+  }
+  for (int s0 = kPre; s0 < nseg; s0 += kPre) {
+    LaneVec<C> o[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
+      o[k] = load_lane<C>(o_p + kk * D, lane);
+    }
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const float ws = s0 + k < nseg ? held_weight<NC>(wt, s0 + k) : 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc.v[c] += ws * o[k].v[c];
+    }
+  }
+  return lse;
+}
+
+// Wide form's share of wave w, 1 <= nseg <= 64 NC: in every 64-segment chunk
+// segments 16 w .. 16 w + 15, the first chunk's rows loaded before the weights
+// are known. Every wave returns the merged lse.
+template <int NC, int D>
+__device__ __forceinline__ float merge_held_wide(const float* lse_p, const float* o_p,
+                                                 int nseg, int w, int lane,
+                                                 LaneVec<D / 64>& acc) {
+  constexpr int C = D / 64;
+  constexpr int kPer = 64 / kWavesPerBlock;       // segments per wave and chunk (16)
+  const int s0 = kPer * w;
+  float ls[NC];
+  load_held<NC>(lse_p, nseg, lane, ls);
+  LaneVec<C> pre[kPer];
+  if (s0 < nseg) {                                 // wave-uniform
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
+      pre[k] = load_lane<C>(o_p + kk * D, lane);
+    }
+  }
+  float wt[NC];
+  const float lse = held_weights<NC>(ls, nseg, lane, wt);
+  if (lse == -INFINITY) return lse;                // uniform over the work-group
+  if (s0 < nseg) {
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const float wk = s0 + k < nseg ? held_weight<NC>(wt, s0 + k) : 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
+    }
+  }
+  if constexpr (NC > 1) {
+    for (int b = 64 + s0; b < nseg; b += 64) {     // later chunks, wave-uniform
+      LaneVec<C> o[kPer];
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int kk = b + k < nseg ? b + k : nseg - 1;
+        o[k] = load_lane<C>(o_p + kk * D, lane);
+      }
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const float wk = b + k < nseg ? held_weight<NC>(wt, b + k) : 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc.v[c] += wk * o[k].v[c];
+      }
+    }
   }
   return lse;
 }
@@ -131,7 +297,6 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_wide_kernel(
     const int32_t* __restrict__ tok_nseg, int q_heads, int seg_max,
     unsigned short* __restrict__ out, float* __restrict__ out_lse) {
   constexpr int C = D / 64;
-  constexpr int kPer = 64 / kWavesPerBlock;       // segments per wave (16)
   __shared__ float red[kWavesPerBlock - 1][64 * C];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -145,7 +310,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_wide_kernel(
   LaneVec<C> acc;
 #pragma unroll
   for (int c = 0; c < C; ++c) acc.v[c] = 0.f;
-  if (nseg > 64 || nseg == 0) {                   // uniform over the work-group
+  if (nseg > kHeldSegs || nseg == 0) {            // uniform over the work-group
     if (w == 0) {
       const float lse = nseg ? merge_general<D>(lse_p, o_p, nseg, lane, acc) : -INFINITY;
       store_row<F16, C>(orow, acc);
@@ -153,35 +318,8 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_wide_kernel(
     }
     return;
   }
-  // lane s holds segment s's lse; wave w preloads rows kPer*w .. kPer*w + kPer-1
-  const float ls = lane < nseg ? lse_p[lane] : -INFINITY;
-  const int s0 = kPer * w;
-  LaneVec<C> pre[kPer];
-  if (s0 < nseg) {                                 // wave-uniform
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
-      pre[k] = load_lane<C>(o_p + kk * D, lane);
-    }
-  }
-  float M = ls;
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  float lse = -INFINITY;
-  if (M != -INFINITY) {                            // uniform over the work-group
-    const float e = lane < nseg ? expf(ls - M) : 0.f;
-    float sum = e;
-    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-    lse = M + logf(sum);
-    const float wl = e / sum;
-    if (s0 < nseg) {
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const float wk = __shfl(wl, s0 + k);     // 0 past nseg
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
-      }
-    }
-  }
+  const float lse = nseg <= 64 ? merge_held_wide<1, D>(lse_p, o_p, nseg, w, lane, acc)
+                               : merge_held_wide<kChunks, D>(lse_p, o_p, nseg, w, lane, acc);
   if (w > 0) {
 #pragma unroll
     for (int c = 0; c < C; ++c) red[w - 1][C * lane + c] = acc.v[c];
@@ -219,54 +357,12 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(
 #pragma unroll
   for (int c = 0; c < C; ++c) acc.v[c] = 0.f;
   float lse = -INFINITY;
-  if (nseg > 0 && nseg <= 64) {
-    // lane s holds segment s. The first kPre partial rows are loaded before
-    // the weights are known, so there is one memory round trip, not two.
-    constexpr int kPre = 8;
-    const float ls = lane < nseg ? lse_p[lane] : -INFINITY;
-    LaneVec<C> pre[kPre];
-#pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-      // rows past nseg re-read the last valid row (weight 0): entries past a
-      // token's segment count are unspecified and may hold NaN
-      const int kk = k < nseg ? k : nseg - 1;
-      pre[k] = load_lane<C>(o_p + kk * D, lane);
-    }
-    float M = ls;
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if (M != -INFINITY) {
-      const float e = lane < nseg ? expf(ls - M) : 0.f;
-      float sum = e;
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-      lse = M + logf(sum);
-      const float w = e / sum;
-#pragma unroll
-      for (int k = 0; k < kPre; ++k) {
-        const float wk = __shfl(w, k);           // 0 for k >= nseg
-#pragma unroll
-        for (int c = 0; c < C; ++c) acc.v[c] += wk * pre[k].v[c];
-      }
-      // the rest in chunks of kPre rows, all loads of a chunk issued together
-      // (s0 + k <= 63: lanes past nseg hold weight 0, rows past it repeat the
-      // last valid one)
-      for (int s0 = kPre; s0 < nseg; s0 += kPre) {
-        LaneVec<C> o[kPre];
-#pragma unroll
-        for (int k = 0; k < kPre; ++k) {
-          const int kk = s0 + k < nseg ? s0 + k : nseg - 1;
-          o[k] = load_lane<C>(o_p + kk * D, lane);
-        }
-#pragma unroll
-        for (int k = 0; k < kPre; ++k) {
-          const float ws = __shfl(w, s0 + k);
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc.v[c] += ws * o[k].v[c];
-        }
-      }
-    }
-  } else if (nseg > 64) {
+  if (nseg > 0 && nseg <= 64)
+    lse = merge_held<1, D>(lse_p, o_p, nseg, lane, acc);
+  else if (nseg > 64 && nseg <= kHeldSegs)
+    lse = merge_held<kChunks, D>(lse_p, o_p, nseg, lane, acc);
+  else if (nseg > kHeldSegs)
     lse = merge_general<D>(lse_p, o_p, nseg, lane, acc);
-  }
   store_row<F16, C>(out + row * D + C * lane, acc);
   if (out_lse && lane == 0) out_lse[row] = lse;
 }

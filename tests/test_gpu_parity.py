@@ -572,16 +572,22 @@ def test_fp8_codes_decode_exactly():
 @pytest.mark.parametrize("D", [128, 64, 256])
 @pytest.mark.parametrize("total_q", [9, 300])
 @pytest.mark.parametrize("out_dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("smax", [7, 64, 100])
+@pytest.mark.parametrize("smax", [7, 64, 100, 256, 300])
 def test_split_reduce_alone(smax, out_dtype, total_q, D):
-    """Both merge paths (up to 64 segments, one per lane, and more) in both
-    launch forms: one work-group per row (36 rows) and four rows per
-    work-group (1200 rows)."""
+    """Every merge path (up to 64 segments, up to 256 with four per lane, and
+    more) in both launch forms: one work-group per row (36 rows) and four rows
+    per work-group (1200 rows). Some segments carry no key (log-sum-exp -inf,
+    zero output, as the segment kernel writes them)."""
     rng = np.random.default_rng(3 + smax + total_q + D)
     hq = 4
     nseg = rng.integers(0, smax + 1, size=total_q).astype(np.int32)
     po = rng.standard_normal((total_q, hq, smax, D)).astype(np.float32)
     pl = (rng.standard_normal((total_q, hq, smax)) * 4).astype(np.float32)
+    empty = rng.random((total_q, hq, smax)) < 0.05
+    pl[empty] = -np.inf
+    po[empty] = 0.0
+    pl[0, 0, :] = -np.inf                      # a row whose segments all carry no key
+    po[0, 0, :] = 0.0
     for t in range(total_q):                   # entries past the count are unspecified
         po[t, :, nseg[t]:] = np.nan
         pl[t, :, nseg[t]:] = np.nan
@@ -597,12 +603,16 @@ def test_split_reduce_alone(smax, out_dtype, total_q, D):
     for t in range(total_q):
         for h in range(hq):
             k = int(nseg[t])
-            wo, wl = oracle.lse_merge(po[t, h, :k].astype(np.float64),
-                                      pl[t, h, :k].astype(np.float64), D)
+            if k == 0 or np.all(pl[t, h, :k] == -np.inf):
+                # no key behind any counted partial: the merge of nothing
+                wo, wl = np.zeros(D), -np.inf
+            else:
+                wo, wl = oracle.lse_merge(po[t, h, :k].astype(np.float64),
+                                          pl[t, h, :k].astype(np.float64), D)
             # outputs here reach |4|: rounding to bf16 (nearest even) adds up to
             # 2^-9 of the value on top of the absolute bar
             np.testing.assert_allclose(out[t, h], wo, atol=1e-2, rtol=2.0 ** -8)
-            if k == 0:
+            if k == 0 or np.all(pl[t, h, :k] == -np.inf):
                 assert lse[t, h] == -np.inf and np.all(out[t, h] == 0)
             else:
                 assert abs(lse[t, h] - wl) <= 1e-5 * max(1.0, abs(wl))
