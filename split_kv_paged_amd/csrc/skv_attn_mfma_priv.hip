@@ -462,25 +462,40 @@ void seg_mfma_priv_kernel(SegParams p) {
       }
     }
 
-    // ---- online softmax per tile (row n = 16t + r16; 8 tokens per lane) ----
-    bf16x8_t pb[NRT];
+    // ---- online softmax per tile (row n = 16t + r16; 8 tokens per lane). The
+    // masks and the rare rescale are one wave-uniform branch each for all
+    // tiles, so the exponentials of every tile and the P.V MFMAs below share
+    // one basic block and the scheduler can interleave them. ----
+    float sc[NRT][8];
 #pragma unroll
-    for (int t = 0; t < NRT; ++t) {
-      float s[8];
+    for (int t = 0; t < NRT; ++t)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s[e] = sacc[t][e >> 2][e & 3];
-      if (masked) {
+      for (int e = 0; e < 8; ++e) sc[t][e] = sacc[t][e >> 2][e & 3];
+    if (masked) {
+      asm volatile("");                          // a branch, not selects run every block
+#pragma unroll
+      for (int t = 0; t < NRT; ++t)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int pos = tok0 + 16 * (e >> 2) + 4 * j4 + (e & 3);
-          s[e] = pos < lim[t] ? s[e] : -INFINITY;
+          sc[t][e] = pos < lim[t] ? sc[t][e] : -INFINITY;
         }
-      }
-      float lm = s[0];
+    }
+    float lm[NRT];
+    bool move = false;
 #pragma unroll
-      for (int e = 1; e < 8; ++e) lm = fmaxf(lm, s[e]);
-      if (__builtin_amdgcn_ballot_w64(lm > thr[t]) != 0) {   // some row max must move
-        float bm = lm == -INFINITY ? -INFINITY : lm * c;
+    for (int t = 0; t < NRT; ++t) {
+      lm[t] = sc[t][0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) lm[t] = fmaxf(lm[t], sc[t][e]);
+      move = move || lm[t] > thr[t];
+    }
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {       // some tile's row max must move
+      asm volatile("");
+#pragma unroll
+      for (int t = 0; t < NRT; ++t) {
+        if (__builtin_amdgcn_ballot_w64(lm[t] > thr[t]) == 0) continue;
+        float bm = lm[t] == -INFINITY ? -INFINITY : lm[t] * c;
         bm = fmaxf(bm, __shfl_xor(bm, 16));
         bm = fmaxf(bm, __shfl_xor(bm, 32));
         const float mn = fmaxf(m[t], bm);
@@ -491,11 +506,16 @@ void seg_mfma_priv_kernel(SegParams p) {
         m[t] = mn;
         thr[t] = mn == -INFINITY ? -INFINITY : (mn + kSlackLog2) * inv_c;
       }
+    }
+    bf16x8_t pb[NRT];
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
       const float mu = m[t] == -INFINITY ? 0.f : m[t];   // the exp2 offset
       uint32_t pk[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float a = fast_exp2(fmaf(s[e], c, -mu)), b = fast_exp2(fmaf(s[e + 1], c, -mu));
+        const float a = fast_exp2(fmaf(sc[t][e], c, -mu));
+        const float b = fast_exp2(fmaf(sc[t][e + 1], c, -mu));
         l[t] += a + b;
         pk[e >> 1] = pack_bf16x2(a, b);
       }
