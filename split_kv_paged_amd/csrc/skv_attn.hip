@@ -60,21 +60,39 @@ int launch_segments(const AttnArgs& a, void* stream) {
   sp.fixed_S = 0;
   sp.page_shift = page_shift_of(a.page_size);
   sp.claim = (a.flags & SKV_ATTN_CLAIM_UNITS) ? 1 : 0;
-  long long grid;
+  long long grid, busy;        // work-groups, and how many of them can carry work
   if (a.plan) {
-    grid = static_cast<long long>(plan_width(a.bs, a.kv_heads, a.num_cus)) * a.kv_heads;
+    const long long w = plan_width(a.bs, a.kv_heads, a.num_cus);
+    grid = w * a.kv_heads;
+    // the work list is packed: at most seg_max segments per sequence, then -1
+    const long long most = static_cast<long long>(a.bs) * a.seg_max;
+    busy = (most < w ? most : w) * a.kv_heads;
   } else {
     // fixed split: one work-group per (sequence, segment, kv head)
     sp.fixed_S = fixed_split_count(a.bs, a.kv_heads, a.num_cus, a.seg_max);
     sp.tok_out = a.tok_nseg;
     grid = static_cast<long long>(sp.fixed_S) * a.bs * a.kv_heads;
+    busy = grid;
   }
   if (grid > 0x7fffffffLL) return SKV_EUNSUPPORTED;
   const int e = a.kv_dtype == SKV_KV_FP8_E4M3FN ? 1 : 2;
   const bool f16 = a.kv_dtype == SKV_KV_FP16;      // fp16 Q and KV (else bf16 Q)
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
-  const int rows = sp.G * a.max_q;
+  int rows = sp.G * a.max_q;
   auto st = static_cast<hipStream_t>(stream);
+  // Fewer busy work-groups than half the CUs (single-sequence batches): an fp8
+  // work-group with more than 32 query rows is bound by its arithmetic, not by
+  // HBM, so two work-groups share each item, 32 rows each, on the same XCD.
+  // Every row's arithmetic is unchanged, so the results are the same bit for
+  // bit; the second reader of each page mostly finds it in L2.
+  sp.row_split = 1;
+  sp.items = static_cast<int>(grid);
+  if (e == 1 && a.head_dim == kHeadDim && rows > 32 && 2 * busy <= a.num_cus) {
+    sp.row_split = 2;
+    sp.items = static_cast<int>(busy);
+    grid = (busy + 7) / 8 * 16;
+    rows = 32;
+  }
   // more work-groups than CUs: the shuffled vector-ALU kernel (one wave per
   // SIMD) runs two work-groups per CU with half-size rings, so that one's
   // prologue and merge overlap the other's streaming instead of leaving the

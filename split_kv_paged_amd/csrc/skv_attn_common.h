@@ -32,6 +32,8 @@ struct SegParams {
   int fixed_S;                // 0: planned split (plan); > 0: fixed split, S per sequence
   int page_shift;             // log2(tokens per page): 4 or 5
   int claim;                  // 1: waves claim their units at run time; 0: fixed order
+  int row_split;              // 1, or 2: two work-groups per item, each with half the rows
+  int items;                  // work-groups before the row split ((item, kv head) pairs)
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -156,13 +158,32 @@ struct SegItem {
   int L, c0, qn, rows;
   int seg_start, seg_end;   // absolute token range of the segment
   int seg_pages;            // fixed split: pages per segment of this sequence
+  int row0;                 // first query row of this work-group (row split: 0 or 32)
 };
+
+// The (item, kv head) index of this work-group and its share of the rows.
+// With a row split, each group of 16 consecutive work-groups holds both
+// halves of 8 items, the halves 8 apart, so that they run on the same XCD
+// (work-group b on XCD b mod 8) and the second reader of a page finds it in
+// that XCD's L2. Indices at or past p.items carry no work.
+__device__ __forceinline__ int item_of_block(const SegParams& p, int& row0) {
+  if (p.row_split < 2) {
+    row0 = 0;
+    return blockIdx.x;
+  }
+  const int r = blockIdx.x & 15;
+  row0 = r >= 8 ? 32 : 0;
+  return (blockIdx.x >> 4) * 8 + (r & 7);
+}
 
 __device__ __forceinline__ SegItem decode_fixed(const SegParams& p) {
   SegItem it;
   it.valid = 0;
-  const int widx = blockIdx.x / p.Hkv;
-  it.g = blockIdx.x - widx * p.Hkv;
+  it.seg = -1;                                  // no counts written for a missing item
+  const int bid = item_of_block(p, it.row0);
+  if (bid >= p.items) return it;
+  const int widx = bid / p.Hkv;
+  it.g = bid - widx * p.Hkv;
   it.seq = widx / p.fixed_S;
   it.seg = widx - it.seq * p.fixed_S;
   it.L = p.seq_lens[it.seq];
@@ -178,6 +199,7 @@ __device__ __forceinline__ SegItem decode_fixed(const SegParams& p) {
   const long long s1 = s0 + seg_tokens;
   it.seg_start = static_cast<int>(s0);
   it.seg_end = static_cast<int>(s1 < it.L ? s1 : it.L);
+  if (it.row0 >= it.rows) return it;            // a row half with no rows of this sequence
   it.valid = 1;
   return it;
 }
@@ -185,7 +207,7 @@ __device__ __forceinline__ SegItem decode_fixed(const SegParams& p) {
 // Fixed split: the (sequence, segment 0, kv head 0) work-group writes its
 // tokens' segment counts, ceil(visible / segment tokens), for the reduce.
 __device__ __forceinline__ void write_fixed_counts(const SegParams& p, const SegItem& it) {
-  if (p.fixed_S == 0 || it.seg != 0 || it.g != 0) return;
+  if (p.fixed_S == 0 || it.seg != 0 || it.g != 0 || it.row0 != 0) return;
   const int j = threadIdx.x;
   if (j >= it.qn) return;
   int vis = it.L;
@@ -201,8 +223,11 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   if (p.fixed_S > 0) return decode_fixed(p);
   SegItem it;
   it.valid = 0;
-  const int widx = blockIdx.x / p.Hkv;
-  it.g = blockIdx.x - widx * p.Hkv;
+  it.seg = -1;                                  // no counts written for a missing item
+  const int bid = item_of_block(p, it.row0);
+  if (bid >= p.items) return it;
+  const int widx = bid / p.Hkv;
+  it.g = bid - widx * p.Hkv;
   const int word = p.plan[1 + widx];
   if (word < 0) return it;
   it.seq = word >> 16;
@@ -218,6 +243,7 @@ __device__ __forceinline__ SegItem decode_item(const SegParams& p) {
   const long long s1 = s0 + (T << p.page_shift);
   it.seg_start = static_cast<int>(s0);
   it.seg_end = static_cast<int>(s1 < it.L ? s1 : it.L);
+  if (it.row0 >= it.rows) return it;            // a row half with no rows of this sequence
   it.valid = 1;
   return it;
 }

@@ -201,7 +201,7 @@ __device__ __forceinline__ void merge_and_write(const SegParams& p, const SegIte
         Ls += lw[w] * f;
         o += ow[w] * f;
       }
-      const int n = 16 * t + r16;
+      const int n = it.row0 + 16 * t + r16;
       if (n < it.rows) {
         const int tq = it.c0 + n / p.G;
         const int h = it.g * p.G + n % p.G;
@@ -260,8 +260,9 @@ void seg_mfma_priv_kernel(SegParams p) {
   const float inv_c = 1.f / c;
   const uint32_t qflip = ks < 0.f ? 0x80008000u : 0u;
   const float out_scale = p.v_scale[0];
-  // every row sees at least the keys below lim_min (row 0 is the most restricted)
-  const int lim_min = row_limit(it, 0, p.G, p.causal);
+  // every row sees at least the keys below lim_min (the first row is the most
+  // restricted)
+  const int lim_min = row_limit(it, it.row0, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
   // pages of block bi of the segment; pages past the end read the segment's
@@ -287,7 +288,7 @@ void seg_mfma_priv_kernel(SegParams p) {
 
   // ---- Q rows of every tile (B operand of S^T = K.Q^T) ----
   auto load_q = [&](int t, int kk) -> uint4 {
-    const int n = 16 * t + r16;
+    const int n = it.row0 + 16 * t + r16;
     const bool ok = n < it.rows;
     const int tq = it.c0 + (ok ? n / p.G : 0);
     const int h = it.g * p.G + (ok ? n % p.G : 0);
@@ -296,7 +297,7 @@ void seg_mfma_priv_kernel(SegParams p) {
     return *reinterpret_cast<const uint4*>(qr + ch);             // padding rows read row 0
   };
   auto fix_q = [&](int t, uint4 v) -> uint4 {
-    if (16 * t + r16 >= it.rows) return make_uint4(0, 0, 0, 0);
+    if (it.row0 + 16 * t + r16 >= it.rows) return make_uint4(0, 0, 0, 0);
     return make_uint4(v.x ^ qflip, v.y ^ qflip, v.z ^ qflip, v.w ^ qflip);
   };
   bf16x8_t qb[kQLds ? 1 : NRT][4];
@@ -333,7 +334,7 @@ void seg_mfma_priv_kernel(SegParams p) {
   __syncthreads();                             // Q staged, the claim counter set
   int lim[NRT];
 #pragma unroll
-  for (int t = 0; t < NRT; ++t) lim[t] = row_limit(it, 16 * t + r16, p.G, p.causal);
+  for (int t = 0; t < NRT; ++t) lim[t] = row_limit(it, it.row0 + 16 * t + r16, p.G, p.causal);
 
   f32x4_t oacc[NRT][8];
   float m[NRT], thr[NRT], l[NRT];
