@@ -62,3 +62,64 @@ def test_planned_split_rows_shared(spec):
     # two runs agree bit for bit (the fixed, deterministic order)
     again = run_hip(case, num_cus=cus_split, planes=got["planes"])
     assert np.array_equal(got["out_bits"], again["out_bits"])
+
+
+def _fixed_S(bs, kvh, ncu, smax):
+    """Segments per sequence of the fixed split (the library's rule)."""
+    q = ncu // (bs * kvh)
+    p = 1
+    while p * 2 <= q:
+        p *= 2
+    return min(p if q >= 1 else 1, smax)
+
+
+def _draw(seed):
+    """A seeded launch that takes the row split: fp8, head dim 128, more than
+    32 rows, and at most half the CUs busy."""
+    rng = np.random.default_rng(40_000 + seed)
+    while True:
+        g, max_q = [(16, 3), (16, 4), (32, 2), (12, 4), (24, 2)][int(rng.integers(0, 5))]
+        kvh = int(rng.choice([1, 2, 4]))
+        bs = int(rng.integers(1, 5))
+        smax = int(rng.integers(1, 65))
+        ncu = int(rng.integers(16, 305))
+        fixed = bool(rng.random() < 0.5)
+        busy = (_fixed_S(bs, kvh, ncu, smax) * bs if fixed
+                else min(max(ncu // kvh, bs), bs * smax)) * kvh
+        if 2 * busy <= ncu:
+            break
+    page = int(rng.choice([16, 32]))
+    lens = [int(rng.choice([0, 1, page, page + 1])) if rng.random() < 0.2
+            else int(rng.integers(2, 6000)) for _ in range(bs)]
+    ql = [int(rng.integers(1, max_q + 1)) for _ in range(bs)]
+    ql[int(rng.integers(0, bs))] = max_q
+    return dict(g=g, kvh=kvh, lens=lens, ql=ql, smax=smax, ncu=ncu, fixed=fixed, page=page,
+                layout=str(rng.choice(["standard", "shuffled"])), causal=int(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("seed", range(24), ids=lambda s: f"split{s}")
+def test_random_row_split(seed):
+    d = _draw(seed)
+    say("row split fuzz", seed, d)
+    cfg = gen.small_config(configs.FP8_KV, d["lens"], d["ql"], q_heads=d["g"] * d["kvh"],
+                           kv_heads=d["kvh"], layout=d["layout"], page_size=d["page"],
+                           seg_max=d["smax"], causal=d["causal"], num_cus=d["ncu"],
+                           seed=seed, kv_dtype="fp8")
+    case = gen.make_case(cfg, DEV)
+    got = run_hip(case, fixed=d["fixed"])
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(got["out"], got["lse"], ref_out, ref_lse, "fp8")
+    assert r["max_abs"] <= TOL["fp8"], r
+    assert r["lse_err"] <= 1e-3, r
+    if d["fixed"]:
+        # the same segments without the split: a budget of exactly the busy
+        # work-groups, rounded up to a power of two segments per sequence
+        bs = len(d["lens"])
+        S = _fixed_S(bs, d["kvh"], d["ncu"], d["smax"])
+        p2 = 1
+        while p2 < S:
+            p2 *= 2
+        whole = run_hip(case, fixed=True, num_cus=p2 * bs * d["kvh"], planes=got["planes"])
+        assert got["tok"] == whole["tok"]
+        assert np.array_equal(got["out_bits"], whole["out_bits"])
+        assert np.array_equal(got["lse"].view(np.int64), whole["lse"].view(np.int64))
