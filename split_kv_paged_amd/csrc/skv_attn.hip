@@ -80,14 +80,16 @@ int launch_segments(const AttnArgs& a, void* stream) {
   const bool shuf = a.layout == SKV_LAYOUT_SHUFFLED;
   int rows = sp.G * a.max_q;
   auto st = static_cast<hipStream_t>(stream);
-  // Fewer busy work-groups than half the CUs (single-sequence batches): an fp8
-  // work-group with more than 32 query rows is bound by its arithmetic, not by
-  // HBM, so two work-groups share each item, 32 rows each, on the same XCD.
-  // Every row's arithmetic is unchanged, so the results are the same bit for
-  // bit; the second reader of each page mostly finds it in L2.
+  // Fewer busy work-groups than half the CUs (single-sequence batches): one
+  // work-group with more than 32 query rows is bound by what a single CU
+  // computes and streams, not by HBM, so two work-groups share each item, 32
+  // rows each, on the same XCD (the second reader of each page mostly finds
+  // it in L2). For fp8 every row's arithmetic is unchanged, so the results
+  // are the same bit for bit; 16-bit KV moves from the shared-ring kernel to
+  // the private-ring one (the same sums in another order).
   sp.row_split = 1;
   sp.items = static_cast<int>(grid);
-  if (e == 1 && a.head_dim == kHeadDim && rows > 32 && 2 * busy <= a.num_cus) {
+  if (a.head_dim == kHeadDim && rows > 32 && 2 * busy <= a.num_cus) {
     sp.row_split = 2;
     sp.items = static_cast<int>(busy);
     grid = (busy + 7) / 8 * 16;

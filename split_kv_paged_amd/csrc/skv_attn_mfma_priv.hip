@@ -616,8 +616,9 @@ void seg_mfma_priv2_kernel(SegParams p) {
           p.page_table + static_cast<size_t>(it.seq) * p.pt_stride);
   // scores enter exp2 as fma(raw, c, -m); c > 0 (16-bit KV has no scale)
   constexpr float c = kScoreScaleLog2;
-  // every row sees at least the keys below lim_min (row 0 is the most restricted)
-  const int lim_min = row_limit(it, 0, p.G, p.causal);
+  // every row sees at least the keys below lim_min (the first row is the most
+  // restricted)
+  const int lim_min = row_limit(it, it.row0, p.G, p.causal);
 
   uint8_t* wring = ring[wave];
   // this wave's k-th sub-page is the segment's sub-page wave + NW k
@@ -632,7 +633,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
   int lim[NRT];
 #pragma unroll
   for (int t = 0; t < NRT; ++t) {
-    const int n = 16 * t + r16;
+    const int n = it.row0 + 16 * t + r16;
     lim[t] = row_limit(it, n, p.G, p.causal);
     const bool ok = n < it.rows;
     const int tq = it.c0 + (ok ? n / p.G : 0);
@@ -647,7 +648,7 @@ void seg_mfma_priv2_kernel(SegParams p) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       asm volatile("" : "+v"(qb[t][kk]));        // Q consumed while only page 0 is in flight
-      if (16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+      if (it.row0 + 16 * t + r16 >= it.rows) qb[t][kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
     }
 
 

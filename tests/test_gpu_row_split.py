@@ -1,10 +1,12 @@
-"""fp8 attention when fewer work-groups than half the CUs carry work (single
+"""Attention when fewer work-groups than half the CUs carry work (single
 sequences, small batches): two work-groups then share each work item, 32 query
-rows each. Every row's arithmetic is that of the unsplit launch, so on the same
-segments the outputs and log-sum-exps match it bit for bit; against the oracle
-they meet the usual bars. The unsplit reference keeps the same segments with a
-smaller CU budget (the fixed split's segment count is capped by seg_max in
-both), and ragged query counts leave some second halves without rows."""
+rows each. For fp8 every row's arithmetic is that of the unsplit launch, so on
+the same segments the outputs and log-sum-exps match it bit for bit; the
+unsplit reference keeps the same segments with a smaller CU budget (the fixed
+split's segment count is capped by seg_max in both), and ragged query counts
+leave some second halves without rows. 16-bit KV moves to the private-ring
+kernel (another summation order): checked against the oracle and for
+run-to-run identity."""
 import numpy as np
 import pytest
 
@@ -123,3 +125,30 @@ def test_random_row_split(seed):
         assert got["tok"] == whole["tok"]
         assert np.array_equal(got["out_bits"], whole["out_bits"])
         assert np.array_equal(got["lse"].view(np.int64), whole["lse"].view(np.int64))
+
+
+CASES16 = [
+    # name, kv dtype, seq_lens, q_lens, Hq, Hkv, layout, page_size, seg_max
+    ("bf16_bs1_64rows", "bf16", [50_000], [4], 32, 2, "standard", 16, 64),
+    ("fp16_bs1_48rows_shuf", "fp16", [20_001], [3], 32, 2, "shuffled", 16, 64),
+    ("bf16_bs3_ragged_p32", "bf16", [4_000, 33, 9_999], [2, 4, 1], 32, 2, "standard", 32, 8),
+]
+
+
+@pytest.mark.parametrize("fixed", [True, False], ids=["fixed", "planned"])
+@pytest.mark.parametrize("spec", CASES16, ids=lambda c: c[0])
+def test_16bit_rows_shared(spec, fixed):
+    name, dt, lens, ql, hq, hkv, layout, page, seg_max = spec
+    say("row split, 16-bit", name, "fixed" if fixed else "planned")
+    cfg = gen.small_config(configs.TINY, lens, ql, q_heads=hq, kv_heads=hkv, layout=layout,
+                           page_size=page, seg_max=seg_max, causal=1, seed=33, kv_dtype=dt,
+                           num_cus=256)
+    case = gen.make_case(cfg, DEV)
+    got = run_hip(case, fixed=fixed)
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(got["out"], got["lse"], ref_out, ref_lse, dt)
+    say(name, r)
+    assert r["max_abs"] <= TOL[dt], r
+    assert r["lse_err"] <= 1e-3, r
+    again = run_hip(case, fixed=fixed, planes=got["planes"])
+    assert np.array_equal(got["out_bits"], again["out_bits"])
