@@ -33,6 +33,8 @@ int launch_segments_gd(const SegParams& sp, int head_dim, int e, bool f16, bool 
 //    tiles per block do not fit two waves per SIMD in private form).
 // fp16 KV (with fp16 Q) takes the bf16 routes with the fp16 instructions.
 // Head dims 64 and 256 run on the generic-width kernel at every row count.
+// When at most half the CUs would be busy, more than 32 rows are split over
+// two work-groups (below), which then take the 32-row routes.
 constexpr int kValuMaxRows = 4;
 constexpr int kPrivMaxRowsBf16 = 32;
 
