@@ -85,8 +85,8 @@ int launch_segments(const AttnArgs& a, void* stream) {
   // Fewer busy work-groups than half the CUs (single-sequence batches): one
   // work-group with more than 32 query rows is bound by what a single CU
   // computes and streams, not by HBM, so two work-groups share each item, 32
-  // rows each, on the same XCD (the second reader of each page mostly finds
-  // it in L2). For fp8 every row's arithmetic is unchanged, so the results
+  // rows each, on the same XCD (so that the second reader of each page can
+  // find it in that XCD's L2). For fp8 every row's arithmetic is unchanged, so the results
   // are the same bit for bit; 16-bit KV moves from the shared-ring kernel to
   // the private-ring one (the same sums in another order).
   sp.row_split = 1;

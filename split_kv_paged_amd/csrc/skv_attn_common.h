@@ -164,8 +164,8 @@ struct SegItem {
 // The (item, kv head) index of this work-group and its share of the rows.
 // With a row split, each group of 16 consecutive work-groups holds both
 // halves of 8 items, the halves 8 apart, so that they run on the same XCD
-// (work-group b on XCD b mod 8) and the second reader of a page finds it in
-// that XCD's L2. Indices at or past p.items carry no work.
+// (work-group b on XCD b mod 8) and the second reader of a page can find it
+// in that XCD's L2. Indices at or past p.items carry no work.
 __device__ __forceinline__ int item_of_block(const SegParams& p, int& row0) {
   if (p.row_split < 2) {
     row0 = 0;
