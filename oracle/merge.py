@@ -31,11 +31,16 @@ def segment_partials(qvec, K, V, seg_tokens: int):
 def lse_merge(outs, lses, dim=None):
     """Merge normalized partials: out = sum_s exp(lse_s - lse) o_s,
     lse = M + ln sum_s exp(lse_s - M), M = max_s lse_s. No partial: zeros of
-    length `dim`, -inf."""
+    length `dim`, -inf. A partial with lse -inf covers no key and has weight
+    exp(-inf) = 0; when every partial is such, the sum has no term, which is
+    the merge of no partial (reading: the formula's 0/0 there is taken as the
+    empty merge)."""
     if len(lses) == 0:
         return np.zeros(0 if dim is None else dim), -math.inf
     lses = np.asarray(lses, dtype=np.float64)
     outs = np.asarray(outs, dtype=np.float64)
+    if np.all(lses == -math.inf):
+        return np.zeros(outs.shape[1] if dim is None else dim), -math.inf
     M = lses.max()
     tot = np.exp(lses - M).sum()
     lse = M + math.log(tot)

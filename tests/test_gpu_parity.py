@@ -603,12 +603,8 @@ def test_split_reduce_alone(smax, out_dtype, total_q, D):
     for t in range(total_q):
         for h in range(hq):
             k = int(nseg[t])
-            if k == 0 or np.all(pl[t, h, :k] == -np.inf):
-                # no key behind any counted partial: the merge of nothing
-                wo, wl = np.zeros(D), -np.inf
-            else:
-                wo, wl = oracle.lse_merge(po[t, h, :k].astype(np.float64),
-                                          pl[t, h, :k].astype(np.float64), D)
+            wo, wl = oracle.lse_merge(po[t, h, :k].astype(np.float64),
+                                      pl[t, h, :k].astype(np.float64), D)
             # outputs here reach |4|: rounding to bf16 (nearest even) adds up to
             # 2^-9 of the value on top of the absolute bar
             np.testing.assert_allclose(out[t, h], wo, atol=1e-2, rtol=2.0 ** -8)
@@ -616,3 +612,37 @@ def test_split_reduce_alone(smax, out_dtype, total_q, D):
                 assert lse[t, h] == -np.inf and np.all(out[t, h] == 0)
             else:
                 assert abs(lse[t, h] - wl) <= 1e-5 * max(1.0, abs(wl))
+
+
+@pytest.mark.parametrize("fixed", [False, True], ids=["planned", "fixed"])
+@pytest.mark.parametrize("seg_max", [100, 128, 300])
+@pytest.mark.parametrize("dt", ["bf16", "fp8"])
+def test_many_segments_per_token(dt, seg_max, fixed):
+    """More than 64 segments per query token end to end: a CU budget of
+    2 * seg_max (planned) or 4 * seg_max (fixed) for two sequences at two kv
+    heads lets the planner cut the 60k-token sequence into up to seg_max
+    segments and the fixed split into the largest power of two within seg_max,
+    so the reduce takes its four-per-lane path (up to 256) or its plain loop
+    (beyond); plan or counts bit-exact, outputs against the oracle."""
+    say("many segments", dt, seg_max, "fixed" if fixed else "planned")
+    base = configs.FP8_KV if dt == "fp8" else configs.TINY
+    cfg = gen.small_config(base, [60_000, 3_000], [4, 2], q_heads=32, kv_heads=2,
+                           num_cus=(4 if fixed else 2) * seg_max, seg_max=seg_max, seed=17,
+                           kv_dtype=dt)
+    case = gen.make_case(cfg, DEV)
+    hip = run_hip(case, fixed=fixed)
+    if fixed:
+        _, _, want_tok = oracle.fixed_split_plan(cfg.seq_lens, case.cu_seqlens_q.cpu().numpy(),
+                                                 cfg.kv_heads, cfg.page_size, cfg.num_cus,
+                                                 seg_max, cfg.causal)
+        assert hip["tok"] == want_tok
+    else:
+        wp, wt = oracle_plan(case)
+        assert hip["plan"] == wp and hip["tok"] == wt
+    if seg_max >= 128:
+        assert max(hip["tok"]) > 64, "the case reaches past 64 segments per token"
+    ref_out, ref_lse = run_oracle(case)
+    r = compare(hip["out"], hip["lse"], ref_out, ref_lse, dt)
+    say(r)
+    assert r["max_abs"] <= TOL[dt], r
+    assert r["lse_err"] <= 1e-3, r

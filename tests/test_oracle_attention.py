@@ -213,6 +213,20 @@ def test_merge_order_independent_and_empty():
     assert l == -math.inf
 
 
+def test_merge_keyless_partials_drop_out():
+    """A partial with lse -inf (no key) changes nothing: merging it in equals
+    merging the others alone, bit for bit; only such partials merge like none."""
+    rng = np.random.default_rng(9)
+    outs = rng.standard_normal((4, 64))
+    lses = rng.standard_normal(4) * 2
+    base = oracle.lse_merge(outs, lses)
+    with_empty = oracle.lse_merge(np.vstack([outs[:2], np.zeros((1, 64)), outs[2:]]),
+                                  np.concatenate([lses[:2], [-math.inf], lses[2:]]))
+    assert np.array_equal(base[0], with_empty[0]) and base[1] == with_empty[1]
+    o, l = oracle.lse_merge(np.zeros((3, 64)), [-math.inf] * 3)
+    assert l == -math.inf and np.array_equal(o, np.zeros(64))
+
+
 @pytest.mark.parametrize("pages_per_seg", [1, 2, 3, 7])
 def test_split_equals_unsplit(pages_per_seg):
     cfg, case = _case([37, 100, 16, 1, 0, 65], [1, 4, 3, 2, 1, 4])

@@ -135,6 +135,8 @@ def _merge_log2(outs, lses, dim=None):
         return np.zeros(0 if dim is None else dim), -math.inf
     lses = np.asarray(lses, dtype=np.float64)
     outs = np.asarray(outs, dtype=np.float64)
+    if np.all(lses == -math.inf):
+        return np.zeros(outs.shape[1] if dim is None else dim), -math.inf
     M = lses.max()
     tot = np.exp(lses - M).sum()
     lse = M + math.log2(tot)                             # wrong log base
